@@ -1,0 +1,356 @@
+#!/usr/bin/env python3
+"""Throughput of the weight-quantized matmul hot path on one MI355X.
+
+One step = one decode pass of a Qwen3-0.6B-shaped model with 4-bit weights:
+the 197 GEMVs of 28 layers (q 1024->2048, k/v 1024->1024, o 2048->1024,
+gate/up 1024->3072, down 3072->1024) plus the lm_head (1024->151936), all in
+ONE batched qmm_qgemv_batched launch.  `value` is algorithmic bytes moved
+per step (packed codes + fp16 scales/biases + fp16 x + fp32 y, each once)
+divided by the step time, in GB/s, with every input resident in HBM.  Two
+full copies of the weights alternate between steps, so a step never finds
+its weights in the 256 MB last-level cache.
+
+The same JSON line carries, measured in the same run:
+  roofline      the batched GEMV kernel against the 8 TB/s HBM peak, from
+                HIP events around each launch on the launch stream;
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same
+                workload, on this host's cores;
+  prefill       Qwen3-4B-shaped 4-bit GEMMs (36 layers x 7 projections) at
+                M = 128 ... 2048, TFLOP/s against the fp16 matrix-core peak;
+  moe           Qwen3-30B-A3B-shaped grouped GEMMs (128 experts, top-8) at
+                M = 512 and 2048 tokens, against their HBM roofline;
+  decode_q8     the Llama-3.2-3B-shaped 8-bit decode sweep (196 GEMVs);
+  single_gemv   one 1x1024x1024 4-bit GEMV launch (latency).
+Inputs are seeded synthetic tensors with the models' shapes (weights
+N(0, 0.02) quantized on the GPU by qmm_quantize, activations N(0, 1) fp16).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+FP16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 matrix cores (256 CU x 2.4 GHz x 4096 flop/clk)
+
+METRIC = "Q4 decode GEMV HBM GB/s (% peak) + prefill qGEMM TFLOP/s (% MFMA peak)"
+
+# HBM traffic of one batched-GEMV launch on the decode workload, from two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by the same counters
+# on a copy of known size; valid only for the kernel sources it was taken on.
+TRAFFIC = {"sources_sha256": None, "bytes_per_launch": None}
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for f in ("qgemv.hip", "qmm_device.h", "qmm_internal.h"):
+        with open(os.path.join(ROOT, "quantized_matmul_qgemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ setup --
+
+def prepare_dense(torch, qmm, w: synth.DenseWorkload, copies: int):
+    """Quantize each distinct projection once on the GPU, then make `copies`
+    x layers device copies.  Returns per copy a list of (W, S, B, X, Y, n, k)."""
+    base = {}
+    for i, p in enumerate(w.projs + w.extra):
+        layer = w.layers if i >= len(w.projs) else 0
+        wf = torch.from_numpy(synth.draw_weight((w.wid, layer, i, synth.STREAM_W), p.n, p.k)).cuda()
+        words, s, b = qmm.quantize(wf, w.bits)
+        del wf
+        base[i] = (words, s, b)
+    sets = []
+    for c in range(copies):
+        probs = []
+        for layer, i, p in w.problems():
+            words, s, b = base[i]
+            if c > 0 or layer > 0 or (i >= len(w.projs)):
+                words, s, b = words.clone(), s.clone(), b.clone()
+            x = torch.from_numpy(synth.draw_act((w.wid, layer, i, synth.STREAM_X), 1, p.k)[0]).cuda()
+            y = torch.empty(p.n, dtype=torch.float32, device="cuda")
+            probs.append((words, s, b, x, y, p.n, p.k))
+        sets.append(probs)
+    torch.cuda.synchronize()
+    return sets
+
+
+def gemv_bytes(n, k, bits):
+    return n * k * bits // 8 + 2 * 2 * n * (k // 64) + 2 * k + 4 * n
+
+
+# ------------------------------------------------------------- measuring --
+
+def time_launches(torch, launch, steps, warmup, stream):
+    """Warm up; time `steps` back-to-back calls between one event pair (the
+    step time); then time `steps` more calls with an event pair around each
+    call on the launch stream (the per-launch kernel time)."""
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        launch(warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        launch(warmup + steps + i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    return ms_step, float(np.mean(per)), float(np.median(per)), wall
+
+
+def bench_decode(torch, qmm, wl, steps, warmup, copies=2):
+    sets = prepare_dense(torch, qmm, wl, copies)
+    plans = [qmm.qgemv_batched_plan([p[:5] for p in s], wl.bits) for s in sets]
+    step_bytes = sum(gemv_bytes(p.n, p.k, wl.bits) for _, _, p in wl.problems())
+    stream = torch.cuda.current_stream()
+    ms_step, ms_launch, ms_med, wall = time_launches(
+        torch, lambda i: qmm.qgemv_batched(plans[i % copies]), steps, warmup, stream)
+    return dict(sets=sets, plans=plans, step_bytes=step_bytes, ms_step=ms_step,
+                ms_launch=ms_launch, ms_launch_median=ms_med, wall=wall)
+
+
+def bench_single_gemv(torch, qmm, steps=200, warmup=20):
+    wl = synth.SINGLE_Q4
+    sets = prepare_dense(torch, qmm, wl, 1)
+    words, s, b, x, y, n, k = sets[0][0]
+    stream = torch.cuda.current_stream()
+    ms_step, ms_launch, ms_med, _ = time_launches(
+        torch, lambda i: qmm.qgemv(words, s, b, x, wl.bits, y=y), steps, warmup, stream)
+    return {"workload": wl.name, "us_per_launch_median": round(ms_med * 1e3, 2),
+            "gb_per_s": round(gemv_bytes(n, k, 4) / (ms_med * 1e-3) / 1e9, 1)}
+
+
+def bench_prefill(torch, qmm, ms, steps=3, warmup=1):
+    wl = synth.QWEN3_4B_Q4_PREFILL
+    out = {}
+    base = {}
+    for i, p in enumerate(wl.projs):
+        wf = torch.from_numpy(synth.draw_weight((wl.wid, 0, i, synth.STREAM_W), p.n, p.k)).cuda()
+        base[i] = qmm.quantize(wf, wl.bits)
+        del wf
+    layers = [[tuple(t.clone() for t in base[i]) if layer else base[i]
+               for i in range(len(wl.projs))] for layer in range(wl.layers)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for m in ms:
+        xs = [torch.from_numpy(synth.draw_act((wl.wid, m, i, synth.STREAM_X), m, p.k)).cuda()
+              for i, p in enumerate(wl.projs)]
+        ys = [torch.empty((m, p.n), dtype=torch.float32, device="cuda") for p in wl.projs]
+
+        def step(_):
+            for L in layers:
+                for i, (words, s, b) in enumerate(L):
+                    qmm.qgemm(words, s, b, xs[i], wl.bits, y=ys[i])
+        ms_step, _, _, _ = time_launches(torch, step, steps, warmup, stream)
+        flops = 2.0 * m * sum(p.n * p.k for p in wl.projs) * wl.layers
+        tfl = flops / (ms_step * 1e-3) / 1e12
+        out[str(m)] = {"ms_per_step": round(ms_step, 3), "tflops": round(tfl, 1),
+                       "frac_of_fp16_peak": round(tfl / FP16_MFMA_PEAK_TFLOPS, 4)}
+        del xs, ys
+    del layers, base
+    torch.cuda.synchronize()
+    return out
+
+
+def bench_moe(torch, qmm, steps=10, warmup=2):
+    wl = synth.QWEN3_30B_A3B_Q4_MOE
+    out = {}
+    weights = []
+    for pi, (name, k, n, per_pair) in enumerate(synth.moe_projs(wl)):
+        ws, ss, bs = [], [], []
+        for e in range(wl.experts):
+            wf = torch.from_numpy(synth.draw_weight((wl.wid, e, pi, synth.STREAM_W), n, k)).cuda()
+            w_, s_, b_ = qmm.quantize(wf, wl.bits)
+            ws.append(w_); ss.append(s_); bs.append(b_)
+        weights.append((torch.stack(ws), torch.stack(ss), torch.stack(bs), n, k, per_pair))
+        del ws, ss, bs
+    stream = torch.cuda.current_stream()
+    for m in wl.ms:
+        calls = []
+        step_bytes = 0
+        flops = 0
+        for pi, (W, S, B, n, k, per_pair) in enumerate(weights):
+            a, ids, _ = synth.draw_moe_inputs(wl, m, pi)
+            A = torch.from_numpy(a).cuda()
+            I = torch.from_numpy(ids).cuda()
+            pairs = m * wl.top_k
+            Y = torch.empty((pairs, n), dtype=torch.float32, device="cuda")
+            wsz = qmm.qgemm_grouped_workspace_size(m, wl.top_k, wl.experts, n, k, wl.bits)
+            WS = torch.empty(wsz, dtype=torch.uint8, device="cuda")
+            used = np.unique(ids).size
+            step_bytes += used * (n * k * wl.bits // 8 + 4 * n * (k // 64)) + A.numel() * 2 \
+                + pairs * n * 4 + ids.size * 4
+            flops += 2 * pairs * n * k
+            calls.append((W, S, B, A, I, per_pair, Y, WS))
+
+        def step(_):
+            for (W, S, B, A, I, per_pair, Y, WS) in calls:
+                qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, workspace=WS)
+        ms_step, _, _, _ = time_launches(torch, step, steps, warmup, stream)
+        t = ms_step * 1e-3
+        roof = max(step_bytes / (HBM_PEAK_GBS * 1e9), flops / (FP16_MFMA_PEAK_TFLOPS * 1e12))
+        out[str(m)] = {"ms_per_step": round(ms_step, 4), "gb_per_s": round(step_bytes / t / 1e9, 1),
+                       "tflops": round(flops / t / 1e12, 2), "frac_of_roofline": round(roof / t, 4)}
+        del calls
+    del weights
+    torch.cuda.synchronize()
+    return out
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """The float64 oracle (unpack -> dequantize -> matmul) on a bounded
+    sample of the decode workload: whole layers in order, then lm_head row
+    slices, until about `budget_s` seconds of oracle time."""
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    done_bytes = 0
+    spent = 0.0
+    items = 0
+    problems = wl.problems()
+    order = [p for p in problems if p[0] < wl.layers] + \
+        [(wl.layers, len(wl.projs), synth.Proj("lm_head", 1024, 4096))] * 8
+    for layer, i, p in order:
+        if spent >= budget_s:
+            break
+        w = synth.draw_weight((wl.wid, min(layer, wl.layers), i, synth.STREAM_W), p.n, p.k)
+        codes, s, b = oracle.quantize(w, wl.bits)
+        words = oracle.pack(codes, wl.bits)
+        x = synth.draw_act((wl.wid, layer, i, synth.STREAM_X), 1, p.k)
+        t0 = time.perf_counter()
+        oracle.qmatmul_f64(words, s, b, x, wl.bits)
+        spent += time.perf_counter() - t0
+        done_bytes += gemv_bytes(p.n, p.k, wl.bits)
+        items += 1
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{items} GEMVs of the decode workload ({done_bytes / 1e6:.1f} MB algorithmic, "
+                      f"{spent:.1f} s of float64 unpack+dequant+matmul; lm_head as 4096-row slices)"}
+
+
+# ------------------------------------------------------------------- main --
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["all", "decode"], default="all",
+                    help="decode: only the headline decode workload (for profiling)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run only a 1 GiB device copy (counter calibration) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_matmul_qgemv_amd as qmm
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    qmm.lib()  # fail loudly if the HIP library is missing
+
+    if args.copy_calib:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "launches": 5}))
+        return
+
+    wl = synth.QWEN3_0_6B_Q4_DECODE
+    log("decode: preparing", wl.name)
+    d = bench_decode(torch, qmm, wl, args.steps, args.warmup)
+    value = d["step_bytes"] / (d["ms_step"] * 1e-3) / 1e9
+    achieved = d["step_bytes"] / (d["ms_launch"] * 1e-3) / 1e9
+    log(f"decode: {value:.1f} GB/s per step, kernel {achieved:.1f} GB/s")
+    traffic = None
+    if TRAFFIC["sources_sha256"] == kernel_sources_sha256():
+        traffic = TRAFFIC["bytes_per_launch"]
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.layers, "gemvs_per_step": len(wl.problems()),
+                   "bits": wl.bits, "group_size": wl.group_size,
+                   "weights_per_step": wl.weight_count(), "bytes_per_step": d["step_bytes"],
+                   "launch": "one qmm_qgemv_batched launch per step",
+                   "weight_copies_alternated": 2},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "qgemv_batched_kernel<4,16>",
+                     "launch_ms_mean": round(d["ms_launch"], 5),
+                     "launch_ms_median": round(d["ms_launch_median"], 5)},
+    }
+    del d
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if args.only == "all":
+        log("single GEMV")
+        result["single_gemv"] = bench_single_gemv(torch, qmm)
+        log("decode Q8")
+        q8 = bench_decode(torch, qmm, synth.LLAMA32_3B_Q8_DECODE, 10, 3)
+        gbs = q8["step_bytes"] / (q8["ms_launch"] * 1e-3) / 1e9
+        result["decode_q8"] = {"workload": synth.LLAMA32_3B_Q8_DECODE.name,
+                               "bytes_per_step": q8["step_bytes"], "ms_per_step": round(q8["ms_step"], 4),
+                               "gb_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del q8
+        torch.cuda.empty_cache()
+        log("prefill")
+        result["prefill"] = {"workload": synth.QWEN3_4B_Q4_PREFILL.name,
+                             "peak_tflops": FP16_MFMA_PEAK_TFLOPS,
+                             "by_m": bench_prefill(torch, qmm, synth.QWEN3_4B_Q4_PREFILL.ms)}
+        torch.cuda.empty_cache()
+        log("moe")
+        result["moe"] = {"workload": synth.QWEN3_30B_A3B_Q4_MOE.name, "by_m": bench_moe(torch, qmm)}
+    if not args.no_cpu:
+        log("cpu baseline")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * qmm.h - C ABI of the MI355X (gfx950) weight-quantized GEMV / GEMM library.
+ *
+ * What the library computes
+ * -------------------------
+ * BaseRT (native-Metal LLM inference on Apple Silicon), §3.3 "kernel fusion
+ * and specialization": matrix multiplies over group-quantized weights, one
+ * GEMV variant for decode (M = 1) and one GEMM variant for prefill (M > 1),
+ * with dequantization folded into the inner loop so that dequantized
+ * weights never reach memory.  §3.4 "prefill": the M > 1 case is a tiled
+ * GEMM on [seq_len x dim] activations and is compute-bound.  The abstract
+ * and Fig. 1 add mixture-of-experts prefill (Qwen3-30B-A3B), served here by
+ * a grouped GEMM over token-to-expert buckets.  §3 states that the runtime
+ * is reached through a C API, and §3.2 that the decode loop allocates
+ * nothing and reports errors through static thread-local buffers; this ABI
+ * follows both.
+ *
+ * For every entry point, with W_hat[n, k] = s[n, k/gs] * q[n, k] + b[n, k/gs]:
+ *     y[m, n] = sum_k x[m, k] * W_hat[n, k]          (fp32 accumulation)
+ *
+ * Data formats (all little-endian, all row-major)
+ * ----------------------------------------------
+ *   weights  W[n, k] is [out, in].  Codes q in 0 .. 2^bits - 1 are packed
+ *            along k as a little-endian bit stream: code k occupies bits
+ *            [bits*k, bits*k + bits) of its row, bit i of the stream is bit
+ *            i % 32 of uint32 word i / 32.  For bits = 4 that is 8 nibbles per
+ *            word, low nibble first; for bits = 8, 4 bytes per word, low byte
+ *            first.  Row stride: k * bits / 32 words.
+ *   scales,  fp16 bit patterns (uint16) [n, k / group_size]: the per-group
+ *   biases   step s and offset b (asymmetric min/max quantization: b is the
+ *            group minimum, s = (max - min) / (2^bits - 1)).
+ *   x        fp16 bit patterns, [m, k].
+ *   y        fp32, [m, n].
+ *
+ * Common rules
+ * ------------
+ *   * Supported: bits in {2, 4, 8}; group_size == 64; k a positive multiple
+ *     of 64; n, m >= 1 (m = 0 / t = 0 is accepted and does nothing).
+ *   * Every tensor pointer is a DEVICE pointer owned by the caller, 16-byte
+ *     aligned, and must stay valid until the stream reaches the launch.
+ *     Output buffers must not overlap inputs.
+ *   * `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue
+ *     work and return; results are valid once the stream is synchronized.
+ *   * No entry point allocates device memory, frees it or synchronizes.
+ *     Scratch memory comes from a caller-provided workspace whose size the
+ *     matching *_workspace_size query returns.
+ *   * Arguments are validated on the host before any HIP call, so every
+ *     error status below can be produced without a GPU.  On error nothing is
+ *     launched and qmm_last_error() describes the problem.
+ *   * Thread safety: stateless apart from a thread-local error message;
+ *     calls from several threads on several streams are safe.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QMM_OK = 0,
+  QMM_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, bad size, k % group_size != 0 */
+  QMM_ERR_UNSUPPORTED = 2,  /* bits or group_size outside the supported set */
+  QMM_ERR_WORKSPACE = 3,    /* workspace or plan buffer too small */
+  QMM_ERR_HIP = 4           /* a HIP launch failed; text in qmm_last_error() */
+} qmm_status;
+
+/* hipStream_t, passed as an opaque pointer so that this header needs no HIP headers. */
+typedef void* qmm_stream;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int qmm_version(void);
+
+/* Text of the last error raised on the calling thread ("" if none).  The
+ * buffer is thread-local and static (BaseRT §3.2); it stays valid until the
+ * next qmm_* call on the same thread. */
+const char* qmm_last_error(void);
+
+/* ------------------------------------------------------------ decode GEMV
+ * y[n] = sum_k x[k] * W_hat[n, k]   (BaseRT §3.3: the M = 1 decode kernel)
+ *   w       [n, k*bits/32] uint32 packed codes
+ *   scales  [n, k/group_size] fp16 bits;  biases likewise
+ *   x       [k] fp16 bits;  y [n] fp32 (overwritten)
+ * Streams every weight byte once with 128-bit loads, unpacks and scales in
+ * registers, reduces across lanes; small n gets an in-workgroup split of k.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int qmm_qgemv(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+              const uint16_t* x, float* y, int n, int k, int bits, int group_size,
+              qmm_stream stream);
+
+/* ---------------------------------------------------- batched decode GEMV
+ * Many independent GEMVs (e.g. every projection of a decode step) in ONE
+ * launch, which amortizes launch cost the way BaseRT §3 amortizes command
+ * dispatch.  Two steps:
+ *   1. qmm_qgemv_batched_plan (host only, no HIP call): from `count` problem
+ *      descriptors (device pointers inside, host array) build a plan image
+ *      in host memory `plan` of `plan_bytes`.  *plan_bytes_needed receives
+ *      the size required; if plan is NULL or too small the call returns
+ *      QMM_ERR_WORKSPACE without writing the plan.  All problems share bits
+ *      and group_size; each has its own n and k.
+ *   2. Copy the image verbatim to device memory (any copy), then call
+ *      qmm_qgemv_batched with the device copy and the host image (whose
+ *      64-byte header carries the launch geometry).  The plan stays valid
+ *      while the pointers it names do; it can be launched any number of
+ *      times.
+ * Problems must not write overlapping y ranges.  Errors: INVALID_ARG,
+ * UNSUPPORTED, WORKSPACE, HIP. */
+typedef struct {
+  const uint32_t* w;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  const uint16_t* x;
+  float* y;
+  int32_t n;
+  int32_t k;
+} qmm_gemv_problem;
+
+int qmm_qgemv_batched_plan(const qmm_gemv_problem* problems, int count, int bits,
+                           int group_size, void* plan, size_t plan_bytes,
+                           size_t* plan_bytes_needed);
+int qmm_qgemv_batched(const void* plan_device, const void* plan_host, qmm_stream stream);
+
+/* ----------------------------------------------------------- prefill GEMM
+ * y[m, n] = sum_k x[m, k] * W_hat[n, k]   (BaseRT §3.4: tiled prefill GEMM)
+ *   x [m, k] fp16 bits; y [m, n] fp32 (overwritten); other operands as GEMV.
+ * Weight tiles are dequantized to fp16 in registers (one rounding of
+ * s*q + b) and multiplied on the fp16 matrix cores with fp32 accumulation.
+ * workspace may be NULL when qmm_qgemm_workspace_size returns 0.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+size_t qmm_qgemm_workspace_size(int m, int n, int k, int bits, int group_size);
+int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+              const uint16_t* x, float* y, int m, int n, int k, int bits, int group_size,
+              void* workspace, size_t workspace_bytes, qmm_stream stream);
+
+/* --------------------------------------------- mixture-of-experts grouped
+ * Pair p = t * top_k + j routes token t to expert e = expert_ids[t, j]:
+ *     y[p, n] = sum_k A[row(p), k] * W_hat_e[n, k]
+ *   w       [E, n, k*bits/32]; scales, biases [E, n, k/group_size]
+ *   a       fp16 bits; a_row_per_pair = 0: A is [T, k] and row(p) = p / top_k
+ *           (gate / up projections read the token); 1: A is [T*top_k, k] and
+ *           row(p) = p (the down projection reads the pair's own row)
+ *   expert_ids [T, top_k] int32, each in [0, E) (not checked on the device;
+ *           an id outside the range is undefined behaviour)
+ *   y       [T*top_k, n] fp32 (overwritten)
+ * Device-side token-to-expert bucketing (histogram, scan, scatter) builds
+ * one tile list per expert in the workspace; the grouped GEMM then gathers
+ * A rows, dequantizes that expert's weight tiles and scatters output rows.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+size_t qmm_qgemm_grouped_workspace_size(int t, int top_k, int e, int n, int k, int bits,
+                                        int group_size);
+int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+                      const uint16_t* a, int a_row_per_pair, const int32_t* expert_ids,
+                      float* y, int t, int top_k, int e, int n, int k, int bits,
+                      int group_size, void* workspace, size_t workspace_bytes,
+                      qmm_stream stream);
+
+/* ------------------------------------------------ load-time quantization
+ * Asymmetric min/max quantization of a dense fp32 weight W[n, k] into the
+ * packed format above: per group, s = fp16((max - min) / L) and
+ * b = fp16(min) with L = 2^bits - 1 (fp32 arithmetic, IEEE division,
+ * round-to-nearest-even), q = clamp(rint((w - b) / s), 0, L), and q = 0 for
+ * every element when s == 0.  Work done once when a model is loaded
+ * (BaseRT §3.2 prepares everything at load time).
+ *   w_f32 [n, k] fp32; words [n, k*bits/32]; scales, biases [n, k/gs] fp16 bits.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int qmm_quantize(const float* w_f32, uint32_t* words, uint16_t* scales, uint16_t* biases,
+                 int n, int k, int bits, int group_size, qmm_stream stream);
+
+/* ------------------------------------------------------------- diagnostics
+ * Expose the device-side stages of the hot path for bit-exact checking.
+ * qmm_unpack_codes: codes[n, k] (uint8) = the codes of `w`, decoded with
+ *   the same register unpack the GEMV and GEMM kernels use.
+ * qmm_dequant: out[n, k] = W_hat as fp32 (out_is_f16 = 0; one rounding of
+ *   the exact s*q + b) or as fp16 bits (out_is_f16 = 1; one rounding, the
+ *   value the GEMM feeds to the matrix cores).
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int qmm_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,
+                     qmm_stream stream);
+int qmm_dequant(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+                void* out, int out_is_f16, int n, int k, int bits, int group_size,
+                qmm_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

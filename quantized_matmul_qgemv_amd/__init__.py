@@ -1,0 +1,17 @@
+"""Weight-quantized GEMV / GEMM / grouped-MoE GEMM for MI355X (gfx950).
+
+The compute path is libqmm.so (hand-written HIP kernels behind the C ABI in
+include/qmm.h); this package only marshals torch device tensors into it.
+"""
+from ._lib import QmmError, lib, last_error  # noqa: F401
+from .api import (  # noqa: F401
+    GemvPlan, dequant, qgemm, qgemm_grouped, qgemm_grouped_workspace_size,
+    qgemm_workspace_size, qgemv, qgemv_batched, qgemv_batched_plan, quantize,
+    unpack_codes,
+)
+
+__all__ = [
+    "QmmError", "lib", "last_error", "GemvPlan", "dequant", "qgemm", "qgemm_grouped",
+    "qgemm_grouped_workspace_size", "qgemm_workspace_size", "qgemv", "qgemv_batched",
+    "qgemv_batched_plan", "quantize", "unpack_codes",
+]

@@ -1,0 +1,77 @@
+"""ctypes binding of libqmm.so (the C ABI in include/qmm.h).
+
+Argument marshalling only: every computation runs in the HIP kernels.  If
+the library has not been built this module raises instead of falling back
+to anything else.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
+
+QMM_OK = 0
+QMM_ERR_INVALID_ARG = 1
+QMM_ERR_UNSUPPORTED = 2
+QMM_ERR_WORKSPACE = 3
+QMM_ERR_HIP = 4
+
+STATUS_NAMES = {0: "QMM_OK", 1: "QMM_ERR_INVALID_ARG", 2: "QMM_ERR_UNSUPPORTED",
+                3: "QMM_ERR_WORKSPACE", 4: "QMM_ERR_HIP"}
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class GemvProblem(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("scales", C.c_void_p), ("biases", C.c_void_p),
+                ("x", C.c_void_p), ("y", C.c_void_p), ("n", C.c_int32), ("k", C.c_int32)]
+
+
+P, I, SZ = C.c_void_p, C.c_int, C.c_size_t
+
+SIGNATURES = {
+    "qmm_version": (I, []),
+    "qmm_last_error": (C.c_char_p, []),
+    "qmm_qgemv": (I, [P, P, P, P, P, I, I, I, I, P]),
+    "qmm_qgemv_batched_plan": (I, [C.POINTER(GemvProblem), I, I, I, P, SZ, C.POINTER(SZ)]),
+    "qmm_qgemv_batched": (I, [P, P, P]),
+    "qmm_qgemm_workspace_size": (SZ, [I, I, I, I, I]),
+    "qmm_qgemm": (I, [P, P, P, P, P, I, I, I, I, I, P, SZ, P]),
+    "qmm_qgemm_grouped_workspace_size": (SZ, [I, I, I, I, I, I, I]),
+    "qmm_qgemm_grouped": (I, [P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, SZ, P]),
+    "qmm_quantize": (I, [P, P, P, P, I, I, I, I, P]),
+    "qmm_unpack_codes": (I, [P, P, I, I, I, P]),
+    "qmm_dequant": (I, [P, P, P, P, I, I, I, I, I, P]),
+}
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libqmm.so once; raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              "`python -m quantized_matmul_qgemv_amd.build`")
+        handle = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def last_error() -> str:
+    return lib().qmm_last_error().decode()
+
+
+def check(status: int) -> None:
+    if status != QMM_OK:
+        raise QmmError(status, last_error())

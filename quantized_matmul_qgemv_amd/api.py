@@ -1,0 +1,157 @@
+"""Python binding over the C ABI, with torch tensors as device buffers.
+
+Every function passes `tensor.data_ptr()` and the current HIP stream to the
+matching qmm_* entry point; all arithmetic happens in the HIP kernels.
+Tensor conventions (device tensors, contiguous):
+  packed words  int32 [n, k*bits/32]   (or [E, n, k*bits/32] for experts)
+  scales/biases int16 or float16 [n, k/64], fp16 bit patterns
+  activations   float16 [m, k] (or [k] for the GEMV)
+  outputs       float32
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import GemvProblem, check, lib
+
+GROUP = 64
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_W = (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
+_SB = (torch.int16, torch.float16) + ((torch.uint16,) if hasattr(torch, "uint16") else ())
+_X = (torch.float16,)
+_Y = (torch.float32,)
+
+
+def qgemv(w, scales, biases, x, bits: int, y=None, group_size: int = GROUP, stream=None):
+    """y[n] = sum_k x[k] * W_hat[n, k] via qmm_qgemv."""
+    n, k = w.shape[0], x.shape[-1]
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=w.device)
+    check(lib().qmm_qgemv(_dev(w, "w", _W), _dev(scales, "scales", _SB), _dev(biases, "biases", _SB),
+                          _dev(x, "x", _X), _dev(y, "y", _Y), n, k, bits, group_size, _stream(stream)))
+    return y
+
+
+@dataclass
+class GemvPlan:
+    host: C.Array          # host image (header + block records)
+    device: torch.Tensor   # device copy of the image
+    keep: tuple            # tensors the plan points into
+
+    def __len__(self):
+        return len(self.keep)
+
+
+def qgemv_batched_plan(problems, bits: int, group_size: int = GROUP) -> GemvPlan:
+    """Build a batched-GEMV plan for a list of (w, scales, biases, x, y)."""
+    arr = (GemvProblem * len(problems))()
+    for i, (w, s, b, x, y) in enumerate(problems):
+        arr[i] = GemvProblem(_dev(w, "w", _W), _dev(s, "scales", _SB), _dev(b, "biases", _SB),
+                             _dev(x, "x", _X), _dev(y, "y", _Y), w.shape[0], x.shape[-1])
+    need = C.c_size_t(0)
+    st = lib().qmm_qgemv_batched_plan(arr, len(problems), bits, group_size, None, 0, C.byref(need))
+    if st not in (_lib.QMM_OK, _lib.QMM_ERR_WORKSPACE):
+        check(st)
+    host = (C.c_uint8 * need.value)()
+    check(lib().qmm_qgemv_batched_plan(arr, len(problems), bits, group_size, host, need.value,
+                                       C.byref(need)))
+    device = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(problems[0][0].device)
+    return GemvPlan(host=host, device=device, keep=tuple(problems))
+
+
+def qgemv_batched(plan: GemvPlan, stream=None) -> None:
+    check(lib().qmm_qgemv_batched(plan.device.data_ptr(), C.addressof(plan.host), _stream(stream)))
+
+
+def qgemm_workspace_size(m, n, k, bits, group_size=GROUP) -> int:
+    return lib().qmm_qgemm_workspace_size(m, n, k, bits, group_size)
+
+
+def qgemm(w, scales, biases, x, bits: int, y=None, group_size: int = GROUP, workspace=None,
+          stream=None):
+    """y[m, n] = sum_k x[m, k] * W_hat[n, k] via qmm_qgemm."""
+    m, k = x.shape
+    n = w.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    ws_bytes = qgemm_workspace_size(m, n, k, bits, group_size)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=w.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() if workspace is not None else 0
+    check(lib().qmm_qgemm(_dev(w, "w", _W), _dev(scales, "scales", _SB), _dev(biases, "biases", _SB),
+                          _dev(x, "x", _X), _dev(y, "y", _Y), m, n, k, bits, group_size,
+                          ws_ptr, ws_len, _stream(stream)))
+    return y
+
+
+def qgemm_grouped_workspace_size(t, top_k, e, n, k, bits, group_size=GROUP) -> int:
+    return lib().qmm_qgemm_grouped_workspace_size(t, top_k, e, n, k, bits, group_size)
+
+
+def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: bool,
+                  y=None, group_size: int = GROUP, workspace=None, stream=None):
+    """Grouped MoE product via qmm_qgemm_grouped; returns y [T*top_k, n]."""
+    e, n = w.shape[0], w.shape[1]
+    t, top_k = expert_ids.shape
+    k = a.shape[1]
+    if y is None:
+        y = torch.empty((t * top_k, n), dtype=torch.float32, device=w.device)
+    ws_bytes = qgemm_grouped_workspace_size(t, top_k, e, n, k, bits, group_size)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=w.device)
+    check(lib().qmm_qgemm_grouped(_dev(w, "w", _W), _dev(scales, "scales", _SB),
+                                  _dev(biases, "biases", _SB), _dev(a, "a", _X),
+                                  int(bool(a_row_per_pair)), _dev(expert_ids, "expert_ids", (torch.int32,)),
+                                  _dev(y, "y", _Y), t, top_k, e, n, k, bits, group_size,
+                                  workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return y
+
+
+def quantize(w_f32, bits: int, group_size: int = GROUP, stream=None):
+    """Quantize fp32 W [n, k] on the device -> (words int32, scales int16, biases int16)."""
+    n, k = w_f32.shape
+    words = torch.empty((n, k * bits // 32), dtype=torch.int32, device=w_f32.device)
+    s = torch.empty((n, k // group_size), dtype=torch.int16, device=w_f32.device)
+    b = torch.empty_like(s)
+    check(lib().qmm_quantize(_dev(w_f32, "w_f32", (torch.float32,)), words.data_ptr(), s.data_ptr(),
+                             b.data_ptr(), n, k, bits, group_size, _stream(stream)))
+    return words, s, b
+
+
+def unpack_codes(w, k: int, bits: int, stream=None):
+    n = w.shape[0]
+    codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    check(lib().qmm_unpack_codes(_dev(w, "w", _W), codes.data_ptr(), n, k, bits, _stream(stream)))
+    return codes
+
+
+def dequant(w, scales, biases, k: int, bits: int, out_f16: bool, group_size: int = GROUP,
+            stream=None):
+    n = w.shape[0]
+    out = torch.empty((n, k), dtype=torch.int16 if out_f16 else torch.float32, device=w.device)
+    check(lib().qmm_dequant(_dev(w, "w", _W), _dev(scales, "scales", _SB), _dev(biases, "biases", _SB),
+                            out.data_ptr(), int(out_f16), n, k, bits, group_size, _stream(stream)))
+    return out

@@ -1,0 +1,165 @@
+// Mixture-of-experts grouped GEMM (BaseRT, native-Metal LLM inference on
+// Apple Silicon: abstract and Fig. 1, MoE prefill on Qwen3-30B-A3B).  The
+// pages give no mechanism; this one is token-to-expert bucketing followed
+// by one tile schedule per expert:
+//
+//   1. bucket (one workgroup, all in LDS): histogram of expert ids,
+//      exclusive scans of the per-expert pair counts and of the per-expert
+//      row-tile counts, scatter of pair indices into per-expert buckets,
+//      and a flat list of row tiles {expert, first bucket slot, rows}.
+//   2. grouped GEMM: the grid is an upper bound on (row tiles) x (column
+//      tiles); each workgroup reads its row tile from the list (extra
+//      workgroups exit at once), gathers its A rows through the bucket,
+//      multiplies them by its expert's weights with the GEMM tile core and
+//      scatters the output rows back to pair order.
+//
+// The order of pairs inside a bucket depends on atomic scheduling, but each
+// output row is computed on its own (the matrix-core accumulation order
+// over k does not depend on the other rows of the tile), so results are
+// bit-identical from run to run.
+#include "qgemm_core.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+
+constexpr int kBucketThreads = 1024;
+constexpr int kMaxExperts = 1024;
+
+struct MoeTile {
+  int32_t expert;
+  int32_t start;  // first slot in the sorted pair list
+  int32_t rows;
+};
+
+// Workspace layout (int32 units): [num_tiles][sorted pairs: P][tiles: 3*max_tiles]
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static int max_row_tiles(int pairs, int experts, int bm) {
+  const int by_pairs = (pairs + bm - 1) / bm + experts;
+  return by_pairs < pairs ? by_pairs : (pairs > 0 ? pairs : 1);
+}
+
+size_t grouped_workspace_bytes(int t, int top_k, int e, int n) {
+  (void)n;
+  const long pairs = (long)t * top_k;
+  const long tiles = max_row_tiles((int)pairs, e, 32);
+  return align_up((size_t)(4 + pairs + 3 * tiles) * sizeof(int32_t), 256);
+}
+
+__global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
+    const int32_t* __restrict__ ids, int pairs, int experts, int bm, int32_t* __restrict__ ws) {
+  __shared__ int32_t cnt[kMaxExperts];
+  __shared__ int32_t off[kMaxExperts];
+  __shared__ int32_t toff[kMaxExperts];
+  __shared__ int32_t cursor[kMaxExperts];
+  const int tid = threadIdx.x;
+  int32_t* num_tiles = ws;
+  int32_t* sorted = ws + 4;
+  MoeTile* tiles = reinterpret_cast<MoeTile*>(ws + 4 + pairs);
+
+  for (int e = tid; e < kMaxExperts; e += kBucketThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < pairs; p += kBucketThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < experts) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  // inclusive Hillis-Steele scans of counts and of row-tile counts
+  int c = tid < experts ? cnt[tid] : 0;
+  int tl = (c + bm - 1) / bm;
+  off[tid] = c;
+  toff[tid] = tl;
+  __syncthreads();
+  for (int d = 1; d < kBucketThreads; d <<= 1) {
+    const int a = tid >= d ? off[tid - d] : 0;
+    const int b = tid >= d ? toff[tid - d] : 0;
+    __syncthreads();
+    off[tid] += a;
+    toff[tid] += b;
+    __syncthreads();
+  }
+  const int start = off[tid] - c;     // exclusive
+  const int tstart = toff[tid] - tl;
+  __syncthreads();
+  cursor[tid] = start;
+  if (tid == kBucketThreads - 1) num_tiles[0] = toff[tid];
+  __syncthreads();
+  for (int p = tid; p < pairs; p += kBucketThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < experts) {
+      const int slot = atomicAdd(&cursor[e], 1);
+      sorted[slot] = p;
+    }
+  }
+  if (tid < experts) {
+    for (int i = 0; i < tl; ++i) {
+      const int rows = c - i * bm < bm ? c - i * bm : bm;
+      tiles[tstart + i] = MoeTile{tid, start + i * bm, rows};
+    }
+  }
+}
+
+template <int BITS, int BM, int NB>
+__global__ __launch_bounds__(kGemmThreads) void grouped_kernel(GroupedArgs a, const int32_t* __restrict__ ws,
+                                                               int n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * kAStrideHalves];
+  __shared__ int32_t pair_of[BM];
+  constexpr int BN = 4 * NB * 32;
+  const int pairs = a.t * a.top_k;
+  const int tile = blockIdx.x / n_tiles;
+  const int tn = blockIdx.x % n_tiles;
+  if (tile >= ws[0]) return;
+  const MoeTile mt = reinterpret_cast<const MoeTile*>(ws + 4 + pairs)[tile];
+  const int32_t* sorted = ws + 4;
+  for (int i = threadIdx.x; i < BM; i += blockDim.x)
+    pair_of[i] = sorted[mt.start + (i < mt.rows ? i : mt.rows - 1)];
+  __syncthreads();
+  const int top_k = a.top_k;
+  const int per_pair = a.a_row_per_pair;
+  const int rows = mt.rows;
+  auto a_row = [&](int i) { const int p = pair_of[i]; return per_pair ? p : p / top_k; };
+  auto c_row = [&](int i) { return i < rows ? pair_of[i] : -1; };
+  const int groups = a.k >> 6;
+  const size_t wstride = (size_t)a.n * groups * Fmt<BITS>::WORDS_PER_GROUP;
+  const size_t sstride = (size_t)a.n * groups;
+  gemm_tile<BITS, BM, NB>(ARows{a.a, a.k}, a_row, c_row, a.w + mt.expert * wstride,
+                          a.s + mt.expert * sstride, a.b + mt.expert * sstride, a.y, a.n,
+                          tn * BN, a.n, lds);
+}
+
+template <int BITS, int BM, int NB>
+static hipError_t launch_grouped_tile(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
+  constexpr int BN = 4 * NB * 32;
+  const int pairs = a.t * a.top_k;
+  hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(kBucketThreads), 0, st, a.ids, pairs, a.e,
+                     BM, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int n_tiles = (a.n + BN - 1) / BN;
+  const int m_tiles = max_row_tiles(pairs, a.e, BM);
+  hipLaunchKernelGGL((grouped_kernel<BITS, BM, NB>), dim3(m_tiles * n_tiles), dim3(kGemmThreads),
+                     0, st, a, ws, n_tiles);
+  return hipGetLastError();
+}
+
+template <int BITS>
+static hipError_t launch_grouped_bits(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
+  // Row tile from the mean number of pairs per expert: one tile per expert
+  // keeps each expert's weights to a single pass over HBM.
+  const int mean = (a.t * a.top_k + a.e - 1) / a.e;
+  if (mean <= 16) return launch_grouped_tile<BITS, 32, 2>(a, ws, st);
+  if (mean <= 48) return launch_grouped_tile<BITS, 64, 2>(a, ws, st);
+  return launch_grouped_tile<BITS, 128, 2>(a, ws, st);
+}
+
+hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, hipStream_t st) {
+  int32_t* w = reinterpret_cast<int32_t*>(ws);
+  switch (bits) {
+    case 2: return launch_grouped_bits<2>(a, w, st);
+    case 4: return launch_grouped_bits<4>(a, w, st);
+    case 8: return launch_grouped_bits<8>(a, w, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qmm

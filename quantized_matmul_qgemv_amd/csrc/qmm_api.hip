@@ -1,0 +1,267 @@
+// C ABI of the library (declared in include/qmm.h): argument validation on
+// the host, geometry choice, launch on the caller's stream, and a static
+// thread-local error message (BaseRT, native-Metal LLM inference on Apple
+// Silicon, §3.2: error handling through static thread-local buffers, no
+// allocation on the hot path).  Validation never calls into HIP, so every
+// error path runs without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "qmm.h"
+#include "qmm_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return QMM_OK;
+  return fail(QMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+#define CHECK_PTR(p, a)                                                                  \
+  do {                                                                                   \
+    if ((p) == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: null pointer " #p, fn);    \
+    if (!aligned((p), (a)))                                                              \
+      return fail(QMM_ERR_INVALID_ARG, "%s: " #p " is not %d-byte aligned", fn, (int)(a)); \
+  } while (0)
+
+// Maximum k of the GEMV kernels: activations of one row are staged in LDS.
+constexpr int kGemvMaxK = 16384;
+constexpr int kMaxExperts = 1024;
+
+int check_format(const char* fn, int bits, int group_size) {
+  if (bits != 2 && bits != 4 && bits != 8)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: bits=%d not supported (2, 4 or 8)", fn, bits);
+  if (group_size != 64)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: group_size=%d not supported (64)", fn, group_size);
+  return QMM_OK;
+}
+
+int check_nk(const char* fn, int n, int k) {
+  if (n < 1) return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be >= 1", fn, n);
+  if (k < 64 || k % 64 != 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: k=%d must be a positive multiple of group_size 64", fn, k);
+  return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmm_version(void) { return 100; }
+
+const char* qmm_last_error(void) { return g_err; }
+
+int qmm_qgemv(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+              const uint16_t* x, float* y, int n, int k, int bits, int group_size,
+              qmm_stream stream) {
+  const char* fn = "qmm_qgemv";
+  clear_error();
+  if (int st = check_format(fn, bits, group_size)) return st;
+  if (int st = check_nk(fn, n, k)) return st;
+  if (k > kGemvMaxK) return fail(QMM_ERR_INVALID_ARG, "%s: k=%d exceeds %d", fn, k, kGemvMaxK);
+  CHECK_PTR(w, 16);
+  CHECK_PTR(scales, 2);
+  CHECK_PTR(biases, 2);
+  CHECK_PTR(x, 16);
+  CHECK_PTR(y, 4);
+  qmm::GemvProblem p{w, scales, biases, x, y, n, k};
+  const qmm::GemvGeom g = qmm::gemv_choose(n, k);
+  return hip_status(qmm::launch_qgemv(p, bits, g, (hipStream_t)stream), fn);
+}
+
+int qmm_qgemv_batched_plan(const qmm_gemv_problem* problems, int count, int bits,
+                           int group_size, void* plan, size_t plan_bytes,
+                           size_t* plan_bytes_needed) {
+  const char* fn = "qmm_qgemv_batched_plan";
+  clear_error();
+  if (int st = check_format(fn, bits, group_size)) return st;
+  if (count < 1) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d must be >= 1", fn, count);
+  if (problems == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: null problems", fn);
+  int lpr = 16, max_groups = 0;
+  for (int i = 0; i < count; ++i) {
+    const qmm_gemv_problem& q = problems[i];
+    if (check_nk(fn, q.n, q.k)) return fail(QMM_ERR_INVALID_ARG, "%s: problem %d: n=%d k=%d invalid", fn, i, q.n, q.k);
+    if (q.k > kGemvMaxK) return fail(QMM_ERR_INVALID_ARG, "%s: problem %d: k=%d exceeds %d", fn, i, q.k, kGemvMaxK);
+    if (!q.w || !q.scales || !q.biases || !q.x || !q.y)
+      return fail(QMM_ERR_INVALID_ARG, "%s: problem %d has a null pointer", fn, i);
+    if (!aligned(q.w, 16) || !aligned(q.x, 16) || !aligned(q.y, 4) || !aligned(q.scales, 2) ||
+        !aligned(q.biases, 2))
+      return fail(QMM_ERR_INVALID_ARG, "%s: problem %d has a misaligned pointer", fn, i);
+    const int groups = q.k / 64;
+    const int l = qmm::gemv_lanes_for_groups(groups);
+    if (l < lpr) lpr = l;
+    if (groups > max_groups) max_groups = groups;
+  }
+  const int rows = qmm::gemv_rows_per_block(lpr, 4, 1);
+  long blocks = 0;
+  for (int i = 0; i < count; ++i) blocks += (problems[i].n + rows - 1) / rows;
+  if (blocks > 0x7FFFFFFFL) return fail(QMM_ERR_INVALID_ARG, "%s: too many blocks", fn);
+  const size_t need = sizeof(qmm::GemvPlanHeader) + (size_t)blocks * sizeof(qmm::GemvBlock);
+  if (plan_bytes_needed) *plan_bytes_needed = need;
+  if (plan == nullptr || plan_bytes < need)
+    return fail(QMM_ERR_WORKSPACE, "%s: plan buffer of %zu bytes, %zu needed", fn, plan_bytes, need);
+  if (!aligned(plan, 8)) return fail(QMM_ERR_INVALID_ARG, "%s: plan is not 8-byte aligned", fn);
+  qmm::GemvPlanHeader hdr;
+  memset(&hdr, 0, sizeof hdr);
+  hdr.magic = qmm::kPlanMagic;
+  hdr.version = qmm::kPlanVersion;
+  hdr.bits = bits;
+  hdr.group_size = group_size;
+  hdr.lanes_per_row = lpr;
+  hdr.rows_per_block = rows;
+  hdr.num_blocks = (int32_t)blocks;
+  hdr.max_groups = max_groups;
+  hdr.count = count;
+  unsigned char* out = static_cast<unsigned char*>(plan);
+  memcpy(out, &hdr, sizeof hdr);
+  qmm::GemvBlock* recs = reinterpret_cast<qmm::GemvBlock*>(out + sizeof hdr);
+  long bi = 0;
+  for (int i = 0; i < count; ++i) {
+    const qmm_gemv_problem& q = problems[i];
+    for (int r = 0; r < q.n; r += rows) {
+      qmm::GemvBlock blk;
+      memset(&blk, 0, sizeof blk);
+      blk.p = qmm::GemvProblem{q.w, q.scales, q.biases, q.x, q.y, q.n, q.k};
+      blk.row0 = r;
+      recs[bi++] = blk;
+    }
+  }
+  return QMM_OK;
+}
+
+int qmm_qgemv_batched(const void* plan_device, const void* plan_host, qmm_stream stream) {
+  const char* fn = "qmm_qgemv_batched";
+  clear_error();
+  if (plan_host == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: null plan_host", fn);
+  CHECK_PTR(plan_device, 64);
+  qmm::GemvPlanHeader hdr;
+  memcpy(&hdr, plan_host, sizeof hdr);
+  if (hdr.magic != qmm::kPlanMagic || hdr.version != qmm::kPlanVersion)
+    return fail(QMM_ERR_INVALID_ARG, "%s: plan_host is not a plan image", fn);
+  if (int st = check_format(fn, hdr.bits, hdr.group_size)) return st;
+  if (hdr.num_blocks < 1 || hdr.max_groups < 1 || hdr.max_groups > kGemvMaxK / 64)
+    return fail(QMM_ERR_INVALID_ARG, "%s: corrupt plan header", fn);
+  const qmm::GemvBlock* recs = reinterpret_cast<const qmm::GemvBlock*>(
+      static_cast<const unsigned char*>(plan_device) + sizeof(qmm::GemvPlanHeader));
+  return hip_status(qmm::launch_qgemv_batched(recs, hdr.num_blocks, hdr.bits, hdr.lanes_per_row,
+                                              hdr.max_groups, (hipStream_t)stream),
+                    fn);
+}
+
+size_t qmm_qgemm_workspace_size(int m, int n, int k, int bits, int group_size) {
+  (void)m; (void)n; (void)k; (void)bits; (void)group_size;
+  return 0;
+}
+
+int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+              const uint16_t* x, float* y, int m, int n, int k, int bits, int group_size,
+              void* workspace, size_t workspace_bytes, qmm_stream stream) {
+  const char* fn = "qmm_qgemm";
+  (void)workspace; (void)workspace_bytes;
+  clear_error();
+  if (int st = check_format(fn, bits, group_size)) return st;
+  if (m < 0) return fail(QMM_ERR_INVALID_ARG, "%s: m=%d must be >= 0", fn, m);
+  if (int st = check_nk(fn, n, k)) return st;
+  if (m == 0) return QMM_OK;
+  CHECK_PTR(w, 16);
+  CHECK_PTR(scales, 2);
+  CHECK_PTR(biases, 2);
+  CHECK_PTR(x, 16);
+  CHECK_PTR(y, 4);
+  qmm::GemmArgs a{w, scales, biases, x, y, m, n, k};
+  return hip_status(qmm::launch_qgemm(a, bits, (hipStream_t)stream), fn);
+}
+
+size_t qmm_qgemm_grouped_workspace_size(int t, int top_k, int e, int n, int k, int bits,
+                                        int group_size) {
+  (void)k; (void)bits; (void)group_size;
+  if (t < 0 || top_k < 1 || e < 1) return 0;
+  return qmm::grouped_workspace_bytes(t, top_k, e, n);
+}
+
+int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+                      const uint16_t* a, int a_row_per_pair, const int32_t* expert_ids,
+                      float* y, int t, int top_k, int e, int n, int k, int bits,
+                      int group_size, void* workspace, size_t workspace_bytes,
+                      qmm_stream stream) {
+  const char* fn = "qmm_qgemm_grouped";
+  clear_error();
+  if (int st = check_format(fn, bits, group_size)) return st;
+  if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
+  if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
+  if (e < 1 || e > kMaxExperts)
+    return fail(QMM_ERR_INVALID_ARG, "%s: e=%d must be in [1, %d]", fn, e, kMaxExperts);
+  if (a_row_per_pair != 0 && a_row_per_pair != 1)
+    return fail(QMM_ERR_INVALID_ARG, "%s: a_row_per_pair must be 0 or 1", fn);
+  if (int st = check_nk(fn, n, k)) return st;
+  if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
+  if (t == 0) return QMM_OK;
+  CHECK_PTR(w, 16);
+  CHECK_PTR(scales, 2);
+  CHECK_PTR(biases, 2);
+  CHECK_PTR(a, 16);
+  CHECK_PTR(expert_ids, 4);
+  CHECK_PTR(y, 4);
+  const size_t need = qmm::grouped_workspace_bytes(t, top_k, e, n);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(QMM_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+  CHECK_PTR(workspace, 16);
+  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, expert_ids, y, t, top_k, e, n, k};
+  return hip_status(qmm::launch_qgemm_grouped(ga, bits, workspace, (hipStream_t)stream), fn);
+}
+
+int qmm_quantize(const float* w_f32, uint32_t* words, uint16_t* scales, uint16_t* biases,
+                 int n, int k, int bits, int group_size, qmm_stream stream) {
+  const char* fn = "qmm_quantize";
+  clear_error();
+  if (int st = check_format(fn, bits, group_size)) return st;
+  if (int st = check_nk(fn, n, k)) return st;
+  CHECK_PTR(w_f32, 16);
+  CHECK_PTR(words, 4);
+  CHECK_PTR(scales, 2);
+  CHECK_PTR(biases, 2);
+  return hip_status(qmm::launch_quantize(w_f32, words, scales, biases, n, k, bits, (hipStream_t)stream), fn);
+}
+
+int qmm_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,
+                     qmm_stream stream) {
+  const char* fn = "qmm_unpack_codes";
+  clear_error();
+  if (int st = check_format(fn, bits, 64)) return st;
+  if (int st = check_nk(fn, n, k)) return st;
+  CHECK_PTR(w, 4);
+  CHECK_PTR(codes, 1);
+  return hip_status(qmm::launch_unpack_codes(w, codes, n, k, bits, (hipStream_t)stream), fn);
+}
+
+int qmm_dequant(const uint32_t* w, const uint16_t* scales, const uint16_t* biases, void* out,
+                int out_is_f16, int n, int k, int bits, int group_size, qmm_stream stream) {
+  const char* fn = "qmm_dequant";
+  clear_error();
+  if (int st = check_format(fn, bits, group_size)) return st;
+  if (int st = check_nk(fn, n, k)) return st;
+  if (out_is_f16 != 0 && out_is_f16 != 1)
+    return fail(QMM_ERR_INVALID_ARG, "%s: out_is_f16 must be 0 or 1", fn);
+  CHECK_PTR(w, 4);
+  CHECK_PTR(scales, 2);
+  CHECK_PTR(biases, 2);
+  CHECK_PTR(out, 4);
+  return hip_status(qmm::launch_dequant(w, scales, biases, out, out_is_f16, n, k, bits, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

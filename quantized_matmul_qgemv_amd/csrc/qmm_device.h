@@ -1,0 +1,130 @@
+// Device-side building blocks shared by the GEMV, GEMM and diagnostic
+// kernels: the packed-code format, the register unpack and small helpers.
+//
+// Unpack.  A packed uint32 word holds C = 32 / BITS codes, code i in bits
+// [BITS*i, BITS*i + BITS) (low code first along k).  The register unpack
+// turns one word into C/2 fp16 pairs without any integer-to-float
+// conversion: a code placed in the low mantissa bits of an fp16 whose
+// exponent field is fixed reads as (magic + code), exactly.  Pair p holds
+// codes (p, p + C/2) of the word, so one AND-OR with a mask that repeats in
+// both 16-bit halves extracts two codes at once:
+//
+//   code bit offset o inside its 16-bit half   magic (fp16 bits)  value
+//   o = 0                                      0x6400             1024 + q
+//   o = 2                                      0x5C00              256 + q
+//   o = 4                                      0x5400               64 + q
+//   o = 6                                      0x4C00               16 + q
+//
+// (an fp16 in [2^e, 2^(e+1)) has ulp 2^(e-10); putting q at bit o needs ulp
+// 2^-o, so the magic is 2^(10-o)).  For 8-bit codes a byte permute moves
+// bytes 1 and 3 to the low byte of each half.
+//
+// Consumers must pair activations the same way: pair p of a word spanning
+// k0 .. k0+C-1 multiplies (x[k0+p], x[k0+p+C/2]).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int BITS>
+struct Fmt {
+  static_assert(BITS == 2 || BITS == 4 || BITS == 8, "supported widths: 2, 4, 8");
+  static constexpr int CODES_PER_WORD = 32 / BITS;
+  static constexpr int PAIRS_PER_WORD = CODES_PER_WORD / 2;
+  static constexpr int WORDS_PER_GROUP = 64 * BITS / 32;  // group of 64 codes
+  static constexpr int VEC4_PER_GROUP = WORDS_PER_GROUP / 4 > 0 ? WORDS_PER_GROUP / 4 : 1;
+  static constexpr int GROUP_BYTES = WORDS_PER_GROUP * 4;
+  static constexpr int PAIRS_PER_GROUP = 32;
+};
+
+// Offset added by the magic exponent to the code of pair p.
+template <int BITS>
+__host__ __device__ constexpr float magic_value(int p) {
+  return BITS == 8 ? 1024.0f
+       : BITS == 4 ? ((p & 1) ? 64.0f : 1024.0f)
+       : (p & 3) == 0 ? 1024.0f : (p & 3) == 1 ? 256.0f : (p & 3) == 2 ? 64.0f : 16.0f;
+}
+
+template <int BITS>
+__host__ __device__ constexpr uint32_t magic_bits(int p) {
+  return BITS == 8 ? 0x64006400u
+       : BITS == 4 ? ((p & 1) ? 0x54005400u : 0x64006400u)
+       : (p & 3) == 0 ? 0x64006400u : (p & 3) == 1 ? 0x5C005C00u
+       : (p & 3) == 2 ? 0x54005400u : 0x4C004C00u;
+}
+
+// One packed word -> PAIRS_PER_WORD fp16 pairs (as raw 32-bit patterns),
+// pair p = (magic + code p, magic + code p + C/2).
+template <int BITS>
+__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t (&h)[Fmt<BITS>::PAIRS_PER_WORD]) {
+  if constexpr (BITS == 4) {
+    const uint32_t w8 = w >> 8;
+    h[0] = (w & 0x000F000Fu) | 0x64006400u;
+    h[1] = (w & 0x00F000F0u) | 0x54005400u;
+    h[2] = (w8 & 0x000F000Fu) | 0x64006400u;
+    h[3] = (w8 & 0x00F000F0u) | 0x54005400u;
+  } else if constexpr (BITS == 8) {
+    // bytes: D.b[i] = {S0:S1}.b[sel.b[i]], S1 = bytes 0..3, S0 = bytes 4..7
+    h[0] = (w & 0x00FF00FFu) | 0x64006400u;
+    h[1] = __builtin_amdgcn_perm(w, 0x64646464u, 0x00070005u);
+  } else {
+    const uint32_t w8 = w >> 8;
+    h[0] = (w & 0x00030003u) | 0x64006400u;
+    h[1] = (w & 0x000C000Cu) | 0x5C005C00u;
+    h[2] = (w & 0x00300030u) | 0x54005400u;
+    h[3] = (w & 0x00C000C0u) | 0x4C004C00u;
+    h[4] = (w8 & 0x00030003u) | 0x64006400u;
+    h[5] = (w8 & 0x000C000Cu) | 0x5C005C00u;
+    h[6] = (w8 & 0x00300030u) | 0x54005400u;
+    h[7] = (w8 & 0x00C000C0u) | 0x4C004C00u;
+  }
+}
+
+// Position (within the word's span of C codes) of the low / high element of pair p.
+template <int BITS>
+__host__ __device__ constexpr int pair_lo(int p) { return p; }
+template <int BITS>
+__host__ __device__ constexpr int pair_hi(int p) { return p + Fmt<BITS>::CODES_PER_WORD / 2; }
+
+__device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+__device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(half_t, b);
+}
+
+// acc + a.x*b.x + a.y*b.y with fp32 accumulation (v_dot2_f32_f16).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(as_half2(a), as_half2(b), acc, false);
+}
+
+}  // namespace qmm
+
+namespace qmm {
+
+// Dequantize one packed word to fp16 in register-pair order:
+// out[p] = fp16(s * q + b) for the two codes of pair p, computed as
+// v_pk_fma_f16(q, s, b) with q = (magic + q) - magic (exact), so each value
+// is the exact s*q + b rounded once to fp16.
+template <int BITS>
+__device__ __forceinline__ void dequant_word_f16(uint32_t w, half2_t s2, half2_t b2,
+                                                 half2_t (&out)[Fmt<BITS>::PAIRS_PER_WORD]) {
+  uint32_t h[Fmt<BITS>::PAIRS_PER_WORD];
+  unpack_word<BITS>(w, h);
+#pragma unroll
+  for (int p = 0; p < Fmt<BITS>::PAIRS_PER_WORD; ++p) {
+    const half2_t q = as_half2(h[p]) - as_half2(magic_bits<BITS>(p));
+    out[p] = __builtin_elementwise_fma(q, s2, b2);
+  }
+}
+
+}  // namespace qmm

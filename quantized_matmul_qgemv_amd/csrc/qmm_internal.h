@@ -1,0 +1,94 @@
+// Host-side interfaces between the C ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmm {
+
+struct GemvProblem {
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  const uint16_t* x;
+  float* y;
+  int32_t n;
+  int32_t k;
+};
+
+// One workgroup's share of a batched GEMV: rows [row0, row0 + rows) of a
+// problem.  64 bytes, read once per workgroup.
+struct alignas(64) GemvBlock {
+  GemvProblem p;
+  int32_t row0;
+  int32_t pad[3];
+};
+static_assert(sizeof(GemvBlock) == 64, "GemvBlock must stay 64 bytes");
+
+// Host image header of a batched-GEMV plan (64 bytes, followed by the
+// GemvBlock records).
+struct alignas(64) GemvPlanHeader {
+  uint32_t magic;       // 'QMMP'
+  uint32_t version;
+  int32_t bits;
+  int32_t group_size;
+  int32_t lanes_per_row;
+  int32_t rows_per_block;
+  int32_t num_blocks;
+  int32_t max_groups;
+  int32_t count;
+  int32_t pad[7];
+};
+static_assert(sizeof(GemvPlanHeader) == 64, "plan header must stay 64 bytes");
+constexpr uint32_t kPlanMagic = 0x504D4D51u;  // "QMMP"
+constexpr uint32_t kPlanVersion = 1;
+
+// Launch geometry chosen for a GEMV.
+struct GemvGeom {
+  int lanes_per_row;  // lanes cooperating on one row (power of two <= 16)
+  int row_unroll;     // rows per lane slot held in flight
+  int wave_ksplit;    // waves of a workgroup splitting one row's groups
+  int rows_per_block;
+};
+
+GemvGeom gemv_choose(int n, int k);
+int gemv_rows_per_block(int lanes_per_row, int row_unroll, int wave_ksplit);
+int gemv_lanes_for_groups(int groups);
+size_t gemv_lds_bytes(int max_groups, const GemvGeom& g);
+
+hipError_t launch_qgemv(const GemvProblem& p, int bits, const GemvGeom& g, hipStream_t st);
+hipError_t launch_qgemv_batched(const GemvBlock* blocks, int num_blocks, int bits,
+                                int lanes_per_row, int max_groups, hipStream_t st);
+
+struct GemmArgs {
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  const uint16_t* x;
+  float* y;
+  int m, n, k;
+};
+hipError_t launch_qgemm(const GemmArgs& a, int bits, hipStream_t st);
+
+struct GroupedArgs {
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  const uint16_t* a;
+  int a_row_per_pair;
+  const int32_t* ids;
+  float* y;
+  int t, top_k, e, n, k;
+};
+size_t grouped_workspace_bytes(int t, int top_k, int e, int n);
+hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, hipStream_t st);
+
+hipError_t launch_quantize(const float* w, uint32_t* words, uint16_t* s, uint16_t* b, int n,
+                           int k, int bits, hipStream_t st);
+hipError_t launch_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,
+                               hipStream_t st);
+hipError_t launch_dequant(const uint32_t* w, const uint16_t* s, const uint16_t* b, void* out,
+                          int out_is_f16, int n, int k, int bits, hipStream_t st);
+
+}  // namespace qmm

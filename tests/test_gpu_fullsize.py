@@ -1,0 +1,101 @@
+"""Parity at the workloads' full sizes, in the launch configuration that
+bench.py times, on sampled outputs the oracle computes one by one.
+
+Weights are quantized on the GPU here (as in the benchmark); the oracle
+quantizes the sampled rows from the same seeded fp32 weights itself, so the
+test also checks the GPU quantizer bit for bit at full size."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from qmm_testlib import assert_close, host, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bench  # noqa: E402
+import quantized_matmul_qgemv_amd as qmm  # noqa: E402
+
+
+def sample_rows(n, count, seed):
+    r = np.random.default_rng(seed)
+    rows = set(r.choice(n, size=min(count, n), replace=False).tolist())
+    rows.update({0, n - 1})
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("wl", [synth.QWEN3_0_6B_Q4_DECODE, synth.LLAMA32_3B_Q8_DECODE],
+                         ids=lambda w: w.name)
+def test_decode_sweep_batched_sampled(wl):
+    say("full decode sweep", wl.name)
+    sets = bench.prepare_dense(torch, qmm, wl, 1)
+    plan = qmm.qgemv_batched_plan([p[:5] for p in sets[0]], wl.bits)
+    qmm.qgemv_batched(plan)
+    torch.cuda.synchronize()
+    probs = wl.problems()
+    for idx, (layer, i, p) in enumerate(probs):
+        # every projection of the first and the last layer, and the lm_head
+        if layer not in (0, wl.layers - 1, wl.layers):
+            continue
+        words_d, s_d, b_d, x_d, y_d, n, k = sets[0][idx]
+        rows = sample_rows(n, 48, idx)
+        w_layer = wl.layers if i >= len(wl.projs) else 0
+        w = synth.draw_weight((wl.wid, w_layer, i, synth.STREAM_W), n, k)[rows]
+        codes, s, b = oracle.quantize(w, wl.bits)
+        words = oracle.pack(codes, wl.bits)
+        assert np.array_equal(host(words_d, np.uint32)[rows], words), (p.name, "codes")
+        assert np.array_equal(host(s_d, np.uint16)[rows], s) and np.array_equal(host(b_d, np.uint16)[rows], b)
+        x = synth.draw_act((wl.wid, layer, i, synth.STREAM_X), 1, k)
+        want = oracle.qmatmul_f64(words, s, b, x, wl.bits)[0]
+        assert_close(host(y_d)[rows], want, f"{wl.name} layer {layer} {p.name}")
+
+
+@pytest.mark.parametrize("m", synth.QWEN3_4B_Q4_PREFILL.ms)
+def test_prefill_layer_sampled(m):
+    wl = synth.QWEN3_4B_Q4_PREFILL
+    for i, p in enumerate(wl.projs):
+        say("full prefill", m, p.name)
+        wf = synth.draw_weight((wl.wid, 0, i, synth.STREAM_W), p.n, p.k)
+        words_d, s_d, b_d = qmm.quantize(torch.from_numpy(wf).cuda(), wl.bits)
+        x = synth.draw_act((wl.wid, m, i, synth.STREAM_X), m, p.k)
+        y = qmm.qgemm(words_d, s_d, b_d, torch.from_numpy(x).cuda(), wl.bits)
+        torch.cuda.synchronize()
+        cols = sample_rows(p.n, 32, 7 * m + i)
+        rows = sample_rows(m, 32, 11 * m + i)
+        codes, s, b = oracle.quantize(wf[cols], wl.bits)
+        want = oracle.qmatmul_f64(oracle.pack(codes, wl.bits), s, b, x[rows], wl.bits)
+        assert_close(host(y)[np.ix_(rows, cols)], want, f"prefill m={m} {p.name}")
+
+
+@pytest.mark.parametrize("m", synth.QWEN3_30B_A3B_Q4_MOE.ms)
+def test_moe_sampled(m):
+    wl = synth.QWEN3_30B_A3B_Q4_MOE
+    for pi, (name, k, n, per_pair) in enumerate(synth.moe_projs(wl)):
+        say("full moe", m, name)
+        wf = synth.draw_expert_weights(wl, pi)                        # [E, n, k] fp32
+        q = [qmm.quantize(torch.from_numpy(wf[e]).cuda(), wl.bits) for e in range(wl.experts)]
+        W = torch.stack([t[0] for t in q])
+        S = torch.stack([t[1] for t in q])
+        B = torch.stack([t[2] for t in q])
+        a, ids, logits = synth.draw_moe_inputs(wl, m, pi)
+        y = qmm.qgemm_grouped(W, S, B, torch.from_numpy(a).cuda(), torch.from_numpy(ids).cuda(),
+                              wl.bits, bool(per_pair))
+        torch.cuda.synchronize()
+        yh = host(y)
+        r = np.random.default_rng(m + pi)
+        pairs = r.choice(m * wl.top_k, size=24, replace=False)
+        cols = sample_rows(n, 24, m + pi)
+        for p in pairs:
+            e = ids.flat[p]
+            codes, s, b = oracle.quantize(wf[e][cols], wl.bits)
+            row = a[p] if per_pair else a[p // wl.top_k]
+            want = oracle.qmatmul_f64(oracle.pack(codes, wl.bits), s, b, row[None, :], wl.bits)[0]
+            assert_close(yh[p, cols], want, f"moe m={m} {name} pair {p}")
+        # routing from the oracle agrees with the ids the kernel was given
+        ids_o, _ = oracle.route(logits[:64], wl.top_k)
+        assert np.array_equal(ids_o, ids[:64])
+        del W, S, B, q

@@ -1,0 +1,247 @@
+"""GPU parity of every kernel against the CPU oracle, through the C ABI.
+
+Bit-exact: code unpack, dequantization (fp32 and fp16) and the quantizer.
+Within tolerance (relative L2 <= 1e-3, max |err| <= 1e-2 against float64):
+GEMV, batched GEMV, GEMM and the grouped MoE GEMM, on shapes that span
+several tiles with ragged tails, plus edge and degenerate cases."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from qmm_testlib import assert_close, dev, host, quantized, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import quantized_matmul_qgemv_amd as qmm  # noqa: E402
+
+BITS = (2, 4, 8)
+
+
+# ------------------------------------------------------------ bit-exact --
+
+@pytest.mark.parametrize("bits", BITS)
+def test_unpack_codes_bit_exact(bits):
+    say("unpack", bits)
+    r = np.random.default_rng(100 + bits)
+    n, k = 37, 320
+    codes = r.integers(0, 1 << bits, (n, k), dtype=np.uint8)
+    codes[0] = (1 << bits) - 1
+    codes[1] = 0
+    words = oracle.pack(codes, bits)
+    got = host(qmm.unpack_codes(dev(words), k, bits))
+    torch.cuda.synchronize()
+    assert np.array_equal(got, codes)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("f16", [False, True])
+def test_dequant_bit_exact(bits, f16):
+    say("dequant", bits, f16)
+    w, codes, words, s, b = quantized((900, bits, 0, 0), 45, 256, bits)
+    # add rows with extreme scale/bias: large, tiny and subnormal fp16 values
+    extra = np.stack([np.linspace(-60000, 60000, 256), np.linspace(-1e-3, 1e-3, 256),
+                      np.linspace(0, 2e-6, 256)]).astype(np.float32)
+    c2, s2, b2 = oracle.quantize(extra, bits)
+    codes = np.concatenate([codes, c2])
+    s = np.concatenate([s, s2])
+    b = np.concatenate([b, b2])
+    words = oracle.pack(codes, bits)
+    exact = oracle.dequant_f64(codes, s, b)
+    got = host(qmm.dequant(dev(words), dev(s), dev(b), 256, bits, out_f16=f16))
+    if f16:
+        assert np.array_equal(got.view(np.uint16), oracle.round_to_f16_bits(exact))
+    else:
+        assert np.array_equal(got, oracle.round_to_f32(exact))
+
+
+def quantize_cases():
+    r = np.random.default_rng(7)
+    rows = [synth.draw_weight((901, 0, 0, 0), 60, 512)]
+    special = np.zeros((8, 512), dtype=np.float32)
+    special[0] = (np.arange(512) % 16 / 64.0)                 # exact grid
+    special[1, :64] = 0.3                                     # constant group
+    special[2] = np.float32(0.3) + np.float32(1e-7) * np.arange(512, dtype=np.float32)
+    special[3] = r.uniform(-1000, 1000, 512)                  # wide range
+    special[4] = r.standard_normal(512) * 1e-5                # tiny values
+    special[5, ::2] = 1.0
+    special[6] = np.repeat([-1.0, 1.0], 256)
+    special[7] = r.standard_normal(512).astype(np.float32) * 0.02
+    special[7, 1:4] = np.array([0.5, 1.5, 2.5], dtype=np.float32) * (special[7, :64].max() -
+                                                                    special[7, :64].min()) / 15
+    rows.append(special.astype(np.float32))
+    return np.concatenate(rows)
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_quantize_bit_exact(bits):
+    say("quantize", bits)
+    w = quantize_cases()
+    codes, s, b = oracle.quantize(w, bits)
+    words, gs, gb = qmm.quantize(dev(w), bits)
+    assert np.array_equal(host(gs, np.uint16), s)
+    assert np.array_equal(host(gb, np.uint16), b)
+    assert np.array_equal(host(words, np.uint32), oracle.pack(codes, bits))
+
+
+# ------------------------------------------------------------------ GEMV --
+
+GEMV_SHAPES = [(1, 64), (3, 128), (37, 192), (100, 320), (1000, 1024), (1024, 1024),
+               (300, 2048), (129, 2560), (513, 3072), (64, 8192), (7, 9728)]
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("n,k", GEMV_SHAPES)
+def test_gemv_parity(bits, n, k):
+    say("gemv", bits, n, k)
+    _, _, words, s, b = quantized((902, bits, n, k), n, k, bits)
+    x = synth.draw_act((902, bits, n, 1), 1, k)
+    want = oracle.qmatmul_f64(words, s, b, x, bits)[0]
+    y = qmm.qgemv(dev(words), dev(s), dev(b), dev(x[0]), bits)
+    assert_close(host(y), want, f"gemv bits={bits} n={n} k={k}")
+
+
+def test_gemv_deterministic_and_overwrites():
+    say("gemv determinism")
+    n, k, bits = 777, 1024, 4
+    _, _, words, s, b = quantized((903, 0, 0, 0), n, k, bits)
+    x = dev(synth.draw_act((903, 0, 0, 1), 1, k)[0])
+    y1 = torch.full((n,), float("nan"), device="cuda")
+    y2 = torch.full((n,), 123.0, device="cuda")
+    qmm.qgemv(dev(words), dev(s), dev(b), x, bits, y=y1)
+    qmm.qgemv(dev(words), dev(s), dev(b), x, bits, y=y2)
+    assert torch.equal(y1, y2)
+
+
+def test_gemv_integer_closed_form():
+    """Unit scale, zero bias and integer activations: the exact result is an
+    integer matmul, representable in fp32, so the GPU must hit it exactly."""
+    say("gemv integer")
+    r = np.random.default_rng(5)
+    for bits in BITS:
+        n, k = 96, 512
+        codes = r.integers(0, 1 << bits, (n, k), dtype=np.uint8)
+        words = oracle.pack(codes, bits)
+        s = np.full((n, k // 64), 0x3C00, dtype=np.uint16)
+        b = np.zeros((n, k // 64), dtype=np.uint16)
+        xi = r.integers(-4, 5, k)
+        y = host(qmm.qgemv(dev(words), dev(s), dev(b), dev(xi.astype(np.float16)), bits))
+        assert np.array_equal(y.astype(np.float64), (codes.astype(np.int64) @ xi).astype(np.float64))
+
+
+def test_gemv_batched_mixed_shapes():
+    say("gemv batched")
+    bits = 4
+    shapes = [(2048, 1024), (1024, 1024), (1024, 2048), (3072, 1024), (1024, 3072), (999, 1024)]
+    probs, wants, ys = [], [], []
+    for i, (n, k) in enumerate(shapes):
+        _, _, words, s, b = quantized((904, i, 0, 0), n, k, bits)
+        x = synth.draw_act((904, i, 0, 1), 1, k)
+        y = torch.full((n,), float("nan"), device="cuda")
+        probs.append((dev(words), dev(s), dev(b), dev(x[0]), y))
+        wants.append(oracle.qmatmul_f64(words, s, b, x, bits)[0])
+        ys.append(y)
+    plan = qmm.qgemv_batched_plan(probs, bits)
+    qmm.qgemv_batched(plan)
+    for (n, k), y, want in zip(shapes, ys, wants):
+        assert_close(host(y), want, f"batched n={n} k={k}")
+    first = [y.clone() for y in ys]
+    qmm.qgemv_batched(plan)
+    for a, b in zip(first, ys):
+        assert torch.equal(a, b)
+    for (w, s, b, x, _), y in zip(probs, ys):
+        single = qmm.qgemv(w, s, b, x, bits)
+        assert_close(host(single), host(y), "single vs batched")
+
+
+# ------------------------------------------------------------------ GEMM --
+
+GEMM_SHAPES = [(1, 32, 64), (2, 100, 128), (3, 256, 192), (17, 300, 320), (33, 1024, 128),
+               (64, 512, 256), (65, 96, 512), (127, 384, 256), (128, 1024, 2560),
+               (129, 640, 512), (300, 1000, 1024), (513, 257, 640)]
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+def test_gemm_parity(bits, m, n, k):
+    say("gemm", bits, m, n, k)
+    _, _, words, s, b = quantized((905, bits, n, k), n, k, bits)
+    x = synth.draw_act((905, bits, m, 1), m, k)
+    want = oracle.qmatmul_f64(words, s, b, x, bits)
+    y = qmm.qgemm(dev(words), dev(s), dev(b), dev(x), bits)
+    assert_close(host(y), want, f"gemm bits={bits} m={m} n={n} k={k}")
+
+
+def test_gemm_rows_equal_gemv_and_deterministic():
+    say("gemm rows")
+    m, n, k, bits = 70, 520, 1024, 4
+    _, _, words, s, b = quantized((906, 0, 0, 0), n, k, bits)
+    x = synth.draw_act((906, 0, 0, 1), m, k)
+    W, S, B, X = dev(words), dev(s), dev(b), dev(x)
+    y = qmm.qgemm(W, S, B, X, bits)
+    y2 = qmm.qgemm(W, S, B, X, bits)
+    assert torch.equal(y, y2)
+    for row in (0, 31, 32, 69):
+        g = qmm.qgemv(W, S, B, X[row].contiguous(), bits)
+        assert_close(host(y[row]), host(g), f"row {row}")
+
+
+# --------------------------------------------------------------- grouped --
+
+def grouped_inputs(key, e, n, k, bits, t, top_k, ids=None):
+    r = np.random.default_rng(list(key))
+    ws = [quantized(key + (ei,), n, k, bits) for ei in range(e)]
+    words = np.stack([q[2] for q in ws])
+    s = np.stack([q[3] for q in ws])
+    b = np.stack([q[4] for q in ws])
+    if ids is None:
+        ids = synth.topk_ids(r.standard_normal((t, e)), top_k)
+    x = synth.draw_act(key + (1000,), t, k)
+    h = synth.draw_act(key + (1001,), t * top_k, k)
+    return words, s, b, np.ascontiguousarray(ids, dtype=np.int32), x, h
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("e,n,k,t,top_k", [(8, 96, 128, 37, 3), (16, 300, 256, 100, 4),
+                                           (128, 64, 128, 512, 8), (5, 520, 640, 64, 2)])
+def test_grouped_parity(bits, e, n, k, t, top_k):
+    say("grouped", bits, e, n, k, t, top_k)
+    words, s, b, ids, x, h = grouped_inputs((907, bits, e, n), e, n, k, bits, t, top_k)
+    W, S, B, I = dev(words), dev(s), dev(b), dev(ids)
+    for per_pair, a in ((False, x), (True, h)):
+        want = oracle.grouped_f64(words, s, b, a, ids, bits, per_pair)
+        y = qmm.qgemm_grouped(W, S, B, dev(a), I, bits, per_pair)
+        assert_close(host(y), want, f"grouped per_pair={per_pair}")
+
+
+def test_grouped_edge_cases():
+    bits, e, n, k, t, top_k = 4, 6, 200, 192, 50, 2
+    cases = {
+        "all on one expert": np.tile(np.array([[3, 3]]), (t, 1)),
+        "unused experts": np.stack([np.array([0, 5])] * t),
+        "skewed": np.stack([[i % 2, 2 + (i % 3 == 0)] for i in range(t)]),
+    }
+    for name, ids in cases.items():
+        say("grouped edge", name)
+        words, s, b, ids, x, h = grouped_inputs((908, 0, 0, 0), e, n, k, bits, t, top_k, ids=ids)
+        want = oracle.grouped_f64(words, s, b, x, ids, bits, False)
+        y = qmm.qgemm_grouped(dev(words), dev(s), dev(b), dev(x), dev(ids), bits, False)
+        assert_close(host(y), want, name)
+    # a single expert equals the dense GEMM, bit for bit (same tile core)
+    say("grouped E=1")
+    words, s, b, ids, x, h = grouped_inputs((909, 0, 0, 0), 1, n, k, bits, 64, 1,
+                                            ids=np.zeros((64, 1)))
+    y = qmm.qgemm_grouped(dev(words), dev(s), dev(b), dev(x), dev(ids), bits, False)
+    want = oracle.qmatmul_f64(words[0], s[0], b[0], x, bits)
+    assert_close(host(y), want, "E=1")
+    # determinism across runs
+    words, s, b, ids, x, h = grouped_inputs((910, 0, 0, 0), 16, 256, 256, bits, 200, 4)
+    args = (dev(words), dev(s), dev(b), dev(h), dev(ids), bits, True)
+    assert torch.equal(qmm.qgemm_grouped(*args), qmm.qgemm_grouped(*args))
+    # zero tokens: nothing launched, output untouched
+    y = torch.full((0, 256), 1.0, device="cuda")
+    qmm.qgemm_grouped(dev(words), dev(s), dev(b), dev(h[:0]), dev(ids[:0]), bits, True, y=y)
