@@ -100,7 +100,7 @@ def qgemm(w, scales, biases, x, bits: int, y=None, group_size: int = GROUP, work
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=w.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() if workspace is not None else 0
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check(lib().qmm_qgemm(_dev(w, "w", _W), _dev(scales, "scales", _SB), _dev(biases, "biases", _SB),
                           _dev(x, "x", _X), _dev(y, "y", _Y), m, n, k, bits, group_size,
                           ws_ptr, ws_len, _stream(stream)))
@@ -126,7 +126,8 @@ def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: b
                                   _dev(biases, "biases", _SB), _dev(a, "a", _X),
                                   int(bool(a_row_per_pair)), _dev(expert_ids, "expert_ids", (torch.int32,)),
                                   _dev(y, "y", _Y), t, top_k, e, n, k, bits, group_size,
-                                  workspace.data_ptr(), workspace.numel(), _stream(stream)))
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)))
     return y
 
 

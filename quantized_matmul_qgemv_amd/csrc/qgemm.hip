@@ -1,57 +1,150 @@
 // Prefill GEMM over group-quantized weights: y[m, n] = sum_k x[m, k] W_hat[n, k]
 // (BaseRT, native-Metal LLM inference on Apple Silicon, §3.4: tile
 // geometry chosen per sequence-length range).  The tile core is in
-// qgemm_core.h; this file picks the tile and maps workgroups to tiles.
+// qgemm_core.h; this file picks the tile, maps workgroups to tiles and,
+// when there are too few tiles to fill the 256 CUs, splits k.
+//
+// Workgroup -> tile mapping.  Workgroups are dealt round-robin to the 8
+// XCDs (each with its own L2).  Tiles that share weight columns (same
+// column tile and k split, different row tiles) are numbered consecutively
+// and each XCD gets a contiguous range of tile numbers, so a weight column
+// tile is read from HBM into one L2 and reused there by all its row tiles.
+//
+// Split-k.  With S splits, workgroup (tile, split) accumulates the groups
+// [split*G/S, (split+1)*G/S) and writes its fp32 partial tile to the
+// workspace; qgemm_reduce_kernel then sums the S partials of every output
+// in split order, so the result does not depend on scheduling.
 #include "qgemm_core.h"
 #include "qmm_internal.h"
 
 namespace qmm {
 
-template <int BITS, int BM, int NB>
-__global__ __launch_bounds__(kGemmThreads) void qgemm_kernel(GemmArgs a, int n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * kAStrideHalves];
+constexpr int kXcds = 8;
+
+struct GemmGrid {
+  int n_tiles, m_tiles, splits, gps_split;  // groups per split
+  int xcd_remap;
+  long stride;                               // floats between partial tiles of two splits
+};
+
+template <int BITS, int BM, int NB, int GPS>
+__global__ __launch_bounds__(kGemmThreads) void qgemm_kernel(GemmArgs a, GemmGrid gr, float* partial) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * (64 * GPS + 8)];
   constexpr int BN = 4 * NB * 32;
-  // Consecutive workgroups take consecutive column tiles of the same rows
-  // tile; column tiles that share weights are then spread over XCDs only
-  // across row tiles.
-  const int tile = blockIdx.x;
-  const int tn = tile % n_tiles;
-  const int tm = tile / n_tiles;
+  const int total = gr.n_tiles * gr.m_tiles * gr.splits;
+  int t = blockIdx.x;
+  if (gr.xcd_remap) t = (t % kXcds) * (total / kXcds) + t / kXcds;
+  const int tm = t % gr.m_tiles;
+  const int rest = t / gr.m_tiles;
+  const int split = rest % gr.splits;
+  const int tn = rest / gr.splits;
   const int m0 = tm * BM;
   const int n0 = tn * BN;
   const int m = a.m;
   auto a_row = [&](int i) { const int r = m0 + i; return r < m ? r : m - 1; };
   auto c_row = [&](int i) { const int r = m0 + i; return r < m ? r : -1; };
-  gemm_tile<BITS, BM, NB>(ARows{a.x, a.k}, a_row, c_row, a.w, a.s, a.b, a.y, a.n, n0, a.n, lds);
+  float* out = gr.splits == 1 ? a.y : partial + (size_t)split * gr.stride;
+  const int g0 = split * gr.gps_split;
+  const int g1 = g0 + gr.gps_split;
+  gemm_tile<BITS, BM, NB, GPS>(ARows{a.x, a.k}, a_row, c_row, a.w, a.s, a.b, out, a.n, n0, a.n,
+                               g0, g1, lds);
 }
 
-template <int BITS, int BM, int NB>
-static hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
+// y[i] = sum over splits of partial[split * stride + i], in split order.
+__global__ __launch_bounds__(256) void qgemm_reduce_kernel(const float* __restrict__ partial,
+                                                           float* __restrict__ y, long count,
+                                                           long stride, int splits) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float acc = partial[i];
+  for (int s = 1; s < splits; ++s) acc += partial[(size_t)s * stride + i];
+  y[i] = acc;
+}
+
+// Partial tiles of one split are `partial_stride` floats apart (a multiple
+// of 64 floats, so every split starts 256-byte aligned).
+static long partial_stride(int m, int n) { return ((long)m * n + 63) / 64 * 64; }
+
+// ------------------------------------------------------------------ host --
+
+// Tile / split choice for one GEMM.
+struct GemmPlan {
+  int bm, nb, gps, splits;
+};
+
+static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+static GemmPlan gemm_plan(int m, int n, int k, int bits) {
+  const int groups = k / 64;
+  GemmPlan p;
+  p.bm = m <= 32 ? 32 : m <= 64 ? 64 : 128;
+  const int gps = groups % 2 == 0 ? 2 : 1;
+  p.gps = gps;
+  // column tile: the wide tile unless it leaves too few workgroups
+  const long tiles_wide = (long)ceil_div(n, 256) * ceil_div(m, p.bm);
+  p.nb = tiles_wide >= 256 ? 2 : 1;
+  const long tiles = (long)ceil_div(n, 128 * p.nb) * ceil_div(m, p.bm);
+  // split k when the tiles cannot fill the CUs, as long as every split keeps
+  // at least 4 pipeline steps and the fp32 partials stay within a few times
+  // the weight bytes
+  int splits = 1;
+  const long steps = groups / gps;
+  const double wbytes = (double)n * k * bits / 8;
+  while (tiles * splits * 2 <= 512 && steps % (splits * 2) == 0 && steps / (splits * 2) >= 4 &&
+         (double)(splits * 2) * m * n * 4.0 <= 4.0 * wbytes)
+    splits *= 2;
+  p.splits = splits;
+  return p;
+}
+
+size_t gemm_workspace_bytes(int m, int n, int k, int bits) {
+  const GemmPlan p = gemm_plan(m, n, k, bits);
+  return p.splits > 1 ? (size_t)p.splits * partial_stride(m, n) * sizeof(float) : 0;
+}
+
+template <int BITS, int BM, int NB, int GPS>
+static hipError_t launch_tile(const GemmArgs& a, const GemmPlan& p, float* ws, hipStream_t st) {
   constexpr int BN = 4 * NB * 32;
-  const int n_tiles = (a.n + BN - 1) / BN;
-  const int m_tiles = (a.m + BM - 1) / BM;
-  hipLaunchKernelGGL((qgemm_kernel<BITS, BM, NB>), dim3(n_tiles * m_tiles), dim3(kGemmThreads), 0,
-                     st, a, n_tiles);
+  GemmGrid gr;
+  gr.n_tiles = ceil_div(a.n, BN);
+  gr.m_tiles = ceil_div(a.m, BM);
+  gr.splits = p.splits;
+  gr.gps_split = (a.k / 64) / p.splits;
+  const int total = gr.n_tiles * gr.m_tiles * gr.splits;
+  gr.xcd_remap = total % kXcds == 0 ? 1 : 0;
+  gr.stride = partial_stride(a.m, a.n);
+  hipLaunchKernelGGL((qgemm_kernel<BITS, BM, NB, GPS>), dim3(total), dim3(kGemmThreads), 0, st, a,
+                     gr, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  const long count = (long)a.m * a.n;
+  hipLaunchKernelGGL(qgemm_reduce_kernel, dim3(ceil_div(count, 256)), dim3(256), 0, st, ws, a.y,
+                     count, gr.stride, p.splits);
   return hipGetLastError();
 }
 
-template <int BITS>
-static hipError_t launch_bits(const GemmArgs& a, hipStream_t st) {
-  // Tile choice: the largest row tile that the rows fill, then the wider
-  // column tile only when it still leaves at least two workgroups per CU.
-  const int cus = 256;
-  if (a.m <= 32) return launch_tile<BITS, 32, 1>(a, st);
-  if (a.m <= 64) return launch_tile<BITS, 64, 1>(a, st);
-  const long tiles_wide = (long)((a.n + 255) / 256) * ((a.m + 127) / 128);
-  if (tiles_wide >= 2 * cus) return launch_tile<BITS, 128, 2>(a, st);
-  return launch_tile<BITS, 128, 1>(a, st);
+template <int BITS, int BM>
+static hipError_t launch_bm(const GemmArgs& a, const GemmPlan& p, float* ws, hipStream_t st) {
+  if (p.nb == 2) return p.gps == 2 ? launch_tile<BITS, BM, 2, 2>(a, p, ws, st) : launch_tile<BITS, BM, 2, 1>(a, p, ws, st);
+  return p.gps == 2 ? launch_tile<BITS, BM, 1, 2>(a, p, ws, st) : launch_tile<BITS, BM, 1, 1>(a, p, ws, st);
 }
 
-hipError_t launch_qgemm(const GemmArgs& a, int bits, hipStream_t st) {
+template <int BITS>
+static hipError_t launch_bits(const GemmArgs& a, const GemmPlan& p, float* ws, hipStream_t st) {
+  switch (p.bm) {
+    case 32: return launch_bm<BITS, 32>(a, p, ws, st);
+    case 64: return launch_bm<BITS, 64>(a, p, ws, st);
+    default: return launch_bm<BITS, 128>(a, p, ws, st);
+  }
+}
+
+hipError_t launch_qgemm(const GemmArgs& a, int bits, void* workspace, hipStream_t st) {
+  const GemmPlan p = gemm_plan(a.m, a.n, a.k, bits);
+  float* ws = reinterpret_cast<float*>(workspace);
   switch (bits) {
-    case 2: return launch_bits<2>(a, st);
-    case 4: return launch_bits<4>(a, st);
-    case 8: return launch_bits<8>(a, st);
+    case 2: return launch_bits<2>(a, p, ws, st);
+    case 4: return launch_bits<4>(a, p, ws, st);
+    case 8: return launch_bits<8>(a, p, ws, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -7,7 +7,7 @@
 // tiled GEMM whose arithmetic intensity grows with the sequence length;
 // §3.3: dequantization happens inside the inner loop.
 //
-// Workgroup = 4 wave64s, tile BM x BN, k-step = one 64-code group.
+// Workgroup = 4 wave64s, tile BM x BN (BN = 4 waves x NB x 32).
 //   * The 4 waves split the tile's columns: wave w owns columns
 //     [w*NB*32, (w+1)*NB*32).  So each weight column is dequantized by
 //     exactly one wave (no redundant unpack work).
@@ -22,8 +22,11 @@
 //     inside one MFMA as long as both operands agree, so the A tile is
 //     written to LDS with the same order applied inside every 16-wide span
 //     of k; the MFMA's A operand is then one ds_read_b128 per lane.
-//   * A is double-buffered in LDS (one barrier per k-step); the next
-//     k-step's A and packed-B loads are issued before the current MFMAs.
+//   * A is double-buffered in LDS (one barrier per pipeline step of GPS
+//     groups); the next step's A and packed-B loads are issued before the
+//     current step's MFMAs.
+//   * The caller chooses the k range, so a tile can be split over k across
+//     workgroups (partial tiles are summed by a separate, ordered pass).
 #pragma once
 
 #include "qmm_device.h"
@@ -31,7 +34,6 @@
 namespace qmm {
 
 constexpr int kGemmThreads = 256;
-constexpr int kAStrideHalves = 72;  // 64 halves of one k-step + 8 pad (144 B rows)
 
 // LDS position p (0..15) inside a 16-wide span of k holds source k = perm16(p).
 template <int BITS>
@@ -65,18 +67,17 @@ struct BRaw {
 };
 
 template <int BITS>
-__device__ __forceinline__ void load_braw(BRaw<BITS>& r, const uint32_t* __restrict__ wcol,
-                                          const uint16_t* __restrict__ scol,
-                                          const uint16_t* __restrict__ bcol, int g, int h) {
+__device__ __forceinline__ void load_braw(BRaw<BITS>& r, gptr<uint32_t> wcol, gptr<uint16_t> scol,
+                                          gptr<uint16_t> bcol, int g, int h) {
   constexpr int WPG = Fmt<BITS>::WORDS_PER_GROUP;
-  const uint32_t* p = wcol + (size_t)g * WPG + h * (WPG / 2);
+  gptr<uint32_t> p = wcol + (size_t)g * WPG + h * (WPG / 2);
   if constexpr (BITS == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    const u32x2 v = *reinterpret_cast<gptr<u32x2>>(p);
     r.w[0] = v.x; r.w[1] = v.y;
   } else {
 #pragma unroll
     for (int i = 0; i < WPG / 2 / 4; ++i) {
-      const u32x4 v = reinterpret_cast<const u32x4*>(p)[i];
+      const u32x4 v = reinterpret_cast<gptr<u32x4>>(p)[i];
       r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
     }
   }
@@ -118,19 +119,31 @@ struct ARows {
   int k;
 };
 
-// One BM x BN output tile over all k.  a_row(i) gives the source row of
-// tile row i (already clamped to a valid row); c_row(i) gives the output
-// row or -1 to skip; n0/n_valid bound the columns.
-template <int BITS, int BM, int NB, typename ARowFn, typename CRowFn>
+// One BM x BN output tile over the k groups [g_begin, g_end).  a_row(i)
+// gives the source row of tile row i (already clamped to a valid row);
+// c_row(i) gives the output row or -1 to skip; columns are bounded by n.
+// Each pipeline step covers GPS groups (GPS*64 values of k): while the
+// matrix cores work on step i, the loads of step i+1 are in flight, so a
+// larger GPS hides more memory latency per barrier.  (g_end - g_begin) must
+// be a multiple of GPS.  lds holds 2 * BM * (64*GPS + 8) halves.
+template <int BITS, int BM, int NB, int GPS, typename ARowFn, typename CRowFn>
 __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_row,
-                                          const uint32_t* __restrict__ w,
-                                          const uint16_t* __restrict__ s,
-                                          const uint16_t* __restrict__ b, float* __restrict__ y,
-                                          int ldy, int n0, int n, uint16_t* lds) {
+                                          const uint32_t* __restrict__ w_,
+                                          const uint16_t* __restrict__ s_,
+                                          const uint16_t* __restrict__ b_, float* __restrict__ y_,
+                                          int ldy, int n0, int n, int g_begin, int g_end,
+                                          uint16_t* lds) {
   constexpr int MB = BM / 32;
-  constexpr int SPANS = BM * 4;                       // 16-wide spans per k-step
+  constexpr int SPAN_ROW = 4 * GPS;                  // 16-wide spans per tile row per step
+  constexpr int SPANS = BM * SPAN_ROW;
   constexpr int SPT = (SPANS + kGemmThreads - 1) / kGemmThreads;
   constexpr int WPG = Fmt<BITS>::WORDS_PER_GROUP;
+  constexpr int AST = 64 * GPS + 8;                  // LDS row stride in halves (16 B pad)
+  const gptr<uint32_t> w = to_global(w_);
+  const gptr<uint16_t> s = to_global(s_);
+  const gptr<uint16_t> b = to_global(b_);
+  const gptr_mut<float> y = to_global_mut(y_);
+  const gptr<uint16_t> abase = to_global(A.base);
   const int groups = A.k >> 6;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,9 +152,9 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   const int h = lane >> 5;
 
   // weight columns of this lane
-  const uint32_t* wcol[NB];
-  const uint16_t* scol[NB];
-  const uint16_t* bcol[NB];
+  gptr<uint32_t> wcol[NB];
+  gptr<uint16_t> scol[NB];
+  gptr<uint16_t> bcol[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     int col = n0 + (wave * NB + nb) * 32 + l32;
@@ -152,17 +165,17 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   }
 
   // A spans of this thread
-  const uint16_t* asrc[SPT];
+  gptr<uint16_t> asrc[SPT];
   int aoff[SPT];
   bool aon[SPT];
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
     const int sp = tid + i * kGemmThreads;
     aon[i] = sp < SPANS;
-    const int r = (sp >> 2) < BM ? (sp >> 2) : BM - 1;
-    const int c = sp & 3;
-    asrc[i] = A.base + (size_t)a_row(r) * A.k + c * 16;
-    aoff[i] = r * kAStrideHalves + c * 16;
+    const int r = (sp / SPAN_ROW) < BM ? (sp / SPAN_ROW) : BM - 1;
+    const int c = sp % SPAN_ROW;
+    asrc[i] = abase + (size_t)a_row(r) * A.k + c * 16;
+    aoff[i] = r * AST + c * 16;
   }
 
   float16_t acc[MB][NB];
@@ -174,12 +187,12 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
   uint32_t araw[SPT][8];
-  BRaw<BITS> braw[NB];
+  BRaw<BITS> braw[GPS][NB];
   auto load_a = [&](int g) {
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       if (aon[i]) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(asrc[i] + (size_t)g * 64);
+        gptr<u32x4> p = reinterpret_cast<gptr<u32x4>>(asrc[i] + (size_t)g * 64);
         const u32x4 v0 = p[0], v1 = p[1];
         araw[i][0] = v0.x; araw[i][1] = v0.y; araw[i][2] = v0.z; araw[i][3] = v0.w;
         araw[i][4] = v1.x; araw[i][5] = v1.y; araw[i][6] = v1.z; araw[i][7] = v1.w;
@@ -187,7 +200,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
     }
   };
   auto store_a = [&](int buf) {
-    uint16_t* dst = lds + buf * (BM * kAStrideHalves);
+    uint16_t* dst = lds + buf * (BM * AST);
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       if (aon[i]) {
@@ -201,37 +214,47 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   };
   auto load_b = [&](int g) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) load_braw<BITS>(braw[nb], wcol[nb], scol[nb], bcol[nb], g, h);
+    for (int q = 0; q < GPS; ++q)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        load_braw<BITS>(braw[q][nb], wcol[nb], scol[nb], bcol[nb], g + q, h);
   };
 
-  load_a(0);
-  load_b(0);
-  store_a(0);
+  if (g_begin < g_end) {
+    load_a(g_begin);
+    load_b(g_begin);
+    store_a(0);
+  }
   __syncthreads();
 
-  for (int g = 0; g < groups; ++g) {
-    const int buf = g & 1;
-    BRaw<BITS> cur[NB];
+  for (int g = g_begin, step = 0; g < g_end; g += GPS, ++step) {
+    const int buf = step & 1;
+    BRaw<BITS> cur[GPS][NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) cur[nb] = braw[nb];
-    const bool more = g + 1 < groups;
+    for (int q = 0; q < GPS; ++q)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) cur[q][nb] = braw[q][nb];
+    const bool more = g + GPS < g_end;
     if (more) {
-      load_a(g + 1);
-      load_b(g + 1);
+      load_a(g + GPS);
+      load_b(g + GPS);
     }
-    const uint16_t* abuf = lds + buf * (BM * kAStrideHalves);
+    const uint16_t* abuf = lds + buf * (BM * AST);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      half8_t bop[NB];
+    for (int q = 0; q < GPS; ++q) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) bop[nb] = b_operand<BITS>(cur[nb], j);
+      for (int j = 0; j < 4; ++j) {
+        half8_t bop[NB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const half8_t aop = *reinterpret_cast<const half8_t*>(
-            abuf + (mb * 32 + l32) * kAStrideHalves + h * 32 + j * 8);
+        for (int nb = 0; nb < NB; ++nb) bop[nb] = b_operand<BITS>(cur[q][nb], j);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop[nb], acc[mb][nb], 0, 0, 0);
+        for (int mb = 0; mb < MB; ++mb) {
+          const half8_t aop = *reinterpret_cast<const half8_t*>(
+              abuf + (mb * 32 + l32) * AST + q * 64 + h * 32 + j * 8);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop[nb], acc[mb][nb], 0, 0, 0);
+        }
       }
     }
     if (more) store_a(buf ^ 1);

@@ -11,8 +11,14 @@
 //   * LPR consecutive lanes share a row; lane lr takes the row's groups
 //     lr, lr + LPR, lr + 2*LPR, ...  so one wave-wide 128-bit load covers
 //     64/LPR rows with contiguous, fully used 16-byte pieces;
-//   * each lane keeps UR rows in flight (independent accumulators) and the
-//     next group's loads are issued before the current group is consumed;
+//   * each lane keeps UR rows in flight (128 bytes of codes per lane for 4
+//     and 8 bits, 64 for 2 bits), and
+//     the loads of the next step are issued before the current step is
+//     consumed (two register buffers used alternately);
+//   * a workgroup can run several passes of rows over the same activations
+//     (the prefetch then runs across pass boundaries); one pass per
+//     workgroup measured best, since the dispatcher balances short
+//     workgroups across CUs better than long ones;
 //   * for small n, WK waves of a workgroup split a row's groups and meet in
 //     LDS (deterministic, no atomics).
 // Activations are staged once per workgroup in LDS in "paired" order (the
@@ -20,8 +26,8 @@
 // with two per-group constants:
 //     C[g] = sum_{k in g} magic(k) * x[k]       X[g] = sum_{k in g} x[k]
 // so that   sum_k q_k x_k = dot(magic + q, x) - C[g]   needs no per-code
-// subtraction: each packed word costs one shift, a few AND-ORs and one
-// v_dot2_f32_f16 per two codes.
+// subtraction: each packed 4-bit word costs one shift, four AND-ORs and
+// four v_dot2_f32_f16.
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -35,63 +41,90 @@ template <int BITS, int LPR, int UR, int WK>
 struct GemvCfg {
   static constexpr int WR = kGemvWaves / WK;   // waves along rows
   static constexpr int RPW = 64 / LPR;         // rows per wave per pass
-  static constexpr int ROWS = WR * UR * RPW;   // rows per workgroup
+  static constexpr int ROWS = WR * UR * RPW;   // rows per workgroup pass
 };
 
-// Stage x[0 .. 64*groups) into LDS: paired halves plus (C[g], X[g]).
+// Stage x[0 .. 64*groups) into LDS: paired halves plus (C[g], X[g]).  Four
+// consecutive threads share a group (16 codes each), so the staging that
+// every workgroup waits for at its barrier is short.
 template <int BITS>
-__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int groups,
-                                        unsigned char* xp, float2* cx) {
+__device__ __forceinline__ void stage_x(gptr<uint16_t> x, int groups, unsigned char* xp,
+                                        float2* cx) {
   using F = Fmt<BITS>;
   constexpr int C = F::CODES_PER_WORD;
   constexpr int PPW = F::PAIRS_PER_WORD;
-  for (int g = threadIdx.x; g < groups; g += blockDim.x) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)g * 64);
-    uint32_t d[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4 v = src[i];
-      d[4 * i + 0] = v.x; d[4 * i + 1] = v.y; d[4 * i + 2] = v.z; d[4 * i + 3] = v.w;
-    }
-    uint32_t out[32];
+  constexpr int WPQ = 16 / C > 0 ? 16 / C : 1;  // words per quarter group
+  static_assert(16 % C == 0, "a quarter group must hold whole words");
+  const int rounds = (4 * groups + blockDim.x - 1) / blockDim.x;  // uniform trip count
+  for (int r = 0; r < rounds; ++r) {
+    const int t = threadIdx.x + r * blockDim.x;
+    const int g = t >> 2;
+    const int part = t & 3;
+    const bool on = g < groups;
     float csum = 0.0f, xsum = 0.0f;
+    if (on) {
+      gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(x + (size_t)g * 64 + part * 16);
+      uint32_t d[8];
+      const u32x4 v0 = src[0], v1 = src[1];
+      d[0] = v0.x; d[1] = v0.y; d[2] = v0.z; d[3] = v0.w;
+      d[4] = v1.x; d[5] = v1.y; d[6] = v1.z; d[7] = v1.w;
+      uint32_t out[8];
 #pragma unroll
-    for (int wd = 0; wd < F::WORDS_PER_GROUP; ++wd) {
+      for (int wd = 0; wd < WPQ; ++wd) {
 #pragma unroll
-      for (int p = 0; p < PPW; ++p) {
-        const int klo = wd * C + pair_lo<BITS>(p);
-        const int khi = wd * C + pair_hi<BITS>(p);
-        const uint32_t lo = (d[klo >> 1] >> (16 * (klo & 1))) & 0xFFFFu;
-        const uint32_t hi = (d[khi >> 1] >> (16 * (khi & 1))) & 0xFFFFu;
-        out[wd * PPW + p] = lo | (hi << 16);
-        const float xl = f16_bits_to_f32((uint16_t)lo);
-        const float xh = f16_bits_to_f32((uint16_t)hi);
-        csum += magic_value<BITS>(p) * xl;
-        csum += magic_value<BITS>(p) * xh;
-        xsum += xl;
-        xsum += xh;
+        for (int p = 0; p < PPW; ++p) {
+          const int klo = wd * C + pair_lo<BITS>(p);
+          const int khi = wd * C + pair_hi<BITS>(p);
+          const uint32_t lo = (d[klo >> 1] >> (16 * (klo & 1))) & 0xFFFFu;
+          const uint32_t hi = (d[khi >> 1] >> (16 * (khi & 1))) & 0xFFFFu;
+          out[wd * PPW + p] = lo | (hi << 16);
+          const float xl = f16_bits_to_f32((uint16_t)lo);
+          const float xh = f16_bits_to_f32((uint16_t)hi);
+          csum += magic_value<BITS>(p) * xl;
+          csum += magic_value<BITS>(p) * xh;
+          xsum += xl;
+          xsum += xh;
+        }
       }
+      // pairs of this quarter: 8 dwords at pair index part*8 of the group
+      u32x4* dst = reinterpret_cast<u32x4*>(xp + (size_t)g * kXStride + part * 32);
+      dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+      dst[1] = u32x4{out[4], out[5], out[6], out[7]};
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(xp + (size_t)g * kXStride);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dst[i] = u32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
-    cx[g] = make_float2(csum, xsum);
+    csum += __shfl_xor(csum, 1);
+    xsum += __shfl_xor(xsum, 1);
+    csum += __shfl_xor(csum, 2);
+    xsum += __shfl_xor(xsum, 2);
+    if (on && part == 0) cx[g] = make_float2(csum, xsum);
   }
 }
 
+// Register buffer of one step: UR rows x one group per lane.
+template <int BITS, int UR>
+struct StepBuf {
+  u32x4 w[UR][Fmt<BITS>::VEC4_PER_GROUP];
+  uint16_t s[UR], b[UR];
+};
+
 template <int BITS, int LPR, int UR, int WK>
-__device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, unsigned char* smem) {
+__device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int nrows,
+                                           unsigned char* smem) {
   using F = Fmt<BITS>;
   using Cfg = GemvCfg<BITS, LPR, UR, WK>;
   constexpr int V4 = F::VEC4_PER_GROUP;
   constexpr int WPG = F::WORDS_PER_GROUP;
   constexpr int PPW = F::PAIRS_PER_WORD;
+  using Buf = StepBuf<BITS, UR>;
 
   const int groups = P.k >> 6;
   unsigned char* xp = smem;
   float2* cx = reinterpret_cast<float2*>(smem + (size_t)groups * kXStride);
   float* red = reinterpret_cast<float*>(cx + groups);
+
+  const gptr<uint32_t> W = to_global(P.w);
+  const gptr<uint16_t> S = to_global(P.s);
+  const gptr<uint16_t> B = to_global(P.b);
+  const gptr_mut<float> Y = to_global_mut(P.y);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -100,142 +133,150 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, unsig
   const int slot = lane / LPR;
   const int lr = lane % LPR;
   const int T = groups / LPR;
+  const int tcount = T > wk ? (T - wk + WK - 1) / WK : 0;  // k-steps of this wave per pass
+  const int npass = (nrows + Cfg::ROWS - 1) / Cfg::ROWS;
+  const int nsteps = npass * tcount;
+  const int row_end = (row0 + nrows < P.n ? row0 + nrows : P.n);
+  const int lane_row = row0 + wr * UR * Cfg::RPW + slot;  // + pass*ROWS + u*RPW
+  const size_t rstride = (size_t)groups * WPG;
 
-  int rows[UR];
-  const uint32_t* wrow[UR];
-  const uint16_t* srow[UR];
-  const uint16_t* brow[UR];
-#pragma unroll
-  for (int u = 0; u < UR; ++u) {
-    const int r = row0 + (wr * UR + u) * Cfg::RPW + slot;
-    rows[u] = r;
-    const size_t rc = (size_t)(r < P.n ? r : P.n - 1);
-    wrow[u] = P.w + rc * (size_t)groups * WPG;
-    srow[u] = P.s + rc * (size_t)groups;
-    brow[u] = P.b + rc * (size_t)groups;
-  }
-
-  u32x4 wv[UR][V4];
-  uint16_t sv[UR], bv[UR];
-  auto issue = [&](int t) {
-    const int g = t * LPR + lr;
+  // step -> (pass, t): incremental counters for the issuing side
+  int ip = 0, it = 0;
+  auto issue = [&](Buf& bf) {
+    const int g = (wk + it * WK) * LPR + lr;
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
-      if constexpr (BITS == 2) {
-        // a 2-bit group is 16 bytes: one load
-        wv[u][0] = *reinterpret_cast<const u32x4*>(wrow[u] + (size_t)g * WPG);
-      } else {
+      int r = lane_row + ip * Cfg::ROWS + u * Cfg::RPW;
+      r = r < row_end ? r : row_end - 1;
+      gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(W + (size_t)r * rstride + (size_t)g * WPG);
 #pragma unroll
-        for (int v = 0; v < V4; ++v)
-          wv[u][v] = reinterpret_cast<const u32x4*>(wrow[u] + (size_t)g * WPG)[v];
-      }
-      sv[u] = srow[u][g];
-      bv[u] = brow[u][g];
+      for (int v = 0; v < V4; ++v) bf.w[u][v] = src[v];
+      bf.s[u] = S[(size_t)r * groups + g];
+      bf.b[u] = B[(size_t)r * groups + g];
     }
+    if (++it == tcount) { it = 0; ++ip; }
   };
-
-  int t = wk;
-  if (t < T) issue(t);
-  stage_x<BITS>(P.x, groups, xp, cx);
-  __syncthreads();
 
   float acc[UR];
 #pragma unroll
   for (int u = 0; u < UR; ++u) acc[u] = 0.0f;
 
-  for (; t < T; t += WK) {
-    u32x4 cw[UR][V4];
-    uint16_t cs[UR], cb[UR];
-#pragma unroll
-    for (int u = 0; u < UR; ++u) {
-#pragma unroll
-      for (int v = 0; v < V4; ++v) cw[u][v] = wv[u][v];
-      cs[u] = sv[u];
-      cb[u] = bv[u];
-    }
-    const int g = t * LPR + lr;
-    if (t + WK < T) issue(t + WK);
-
-    uint32_t xr[32];
-    const u32x4* xpv = reinterpret_cast<const u32x4*>(xp + (size_t)g * kXStride);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4 v = xpv[i];
-      xr[4 * i] = v.x; xr[4 * i + 1] = v.y; xr[4 * i + 2] = v.z; xr[4 * i + 3] = v.w;
-    }
+  int cp = 0, ct = 0;  // consuming side
+  auto consume = [&](const Buf& bf) {
+    const int g = (wk + ct * WK) * LPR + lr;
+    const unsigned char* xg = xp + (size_t)g * kXStride;
     const float2 c = cx[g];
-
+    float a0[UR], a1[UR];
 #pragma unroll
-    for (int u = 0; u < UR; ++u) {
-      float a0 = 0.0f, a1 = 0.0f;
+    for (int u = 0; u < UR; ++u) a0[u] = a1[u] = 0.0f;
+    // word-major: the activation pairs of one word are read from LDS once
+    // and used for all UR rows, so only PPW of them are live at a time
 #pragma unroll
-      for (int j = 0; j < WPG; ++j) {
-        const u32x4 v = cw[u][j >> 2];
+    for (int j = 0; j < WPG; ++j) {
+      uint32_t xr[PPW];
+      if constexpr (PPW == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(xg + j * 8);
+        xr[0] = v.x; xr[1] = v.y;
+      } else {
+#pragma unroll
+        for (int q = 0; q < PPW / 4; ++q) {
+          const u32x4 v = reinterpret_cast<const u32x4*>(xg + j * PPW * 4)[q];
+          xr[4 * q] = v.x; xr[4 * q + 1] = v.y; xr[4 * q + 2] = v.z; xr[4 * q + 3] = v.w;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UR; ++u) {
+        const u32x4 v = bf.w[u][j >> 2];
         const uint32_t word = (j & 3) == 0 ? v.x : (j & 3) == 1 ? v.y : (j & 3) == 2 ? v.z : v.w;
         uint32_t h[PPW];
         unpack_word<BITS>(word, h);
 #pragma unroll
         for (int p = 0; p < PPW; ++p) {
-          if ((p & 1) == 0) a0 = dot2(h[p], xr[j * PPW + p], a0);
-          else              a1 = dot2(h[p], xr[j * PPW + p], a1);
+          if ((p & 1) == 0) a0[u] = dot2(h[p], xr[p], a0[u]);
+          else              a1[u] = dot2(h[p], xr[p], a1[u]);
         }
       }
-      const float s = f16_bits_to_f32(cs[u]);
-      const float b = f16_bits_to_f32(cb[u]);
-      acc[u] = fmaf(s, (a0 + a1) - c.x, fmaf(b, c.y, acc[u]));
+    }
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const float s = f16_bits_to_f32(bf.s[u]);
+      const float b = f16_bits_to_f32(bf.b[u]);
+      acc[u] = fmaf(s, (a0[u] + a1[u]) - c.x, fmaf(b, c.y, acc[u]));
+    }
+    if (++ct == tcount) {
+      if constexpr (WK == 1) {
+        // end of a pass: reduce over the row's lanes and store
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          float v = acc[u];
+#pragma unroll
+          for (int m = LPR / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+          const int r = lane_row + cp * Cfg::ROWS + u * Cfg::RPW;
+          if (lr == 0 && r < row_end) Y[r] = v;
+          acc[u] = 0.0f;
+        }
+      }
+      ct = 0;
+      ++cp;
+    }
+  };
+
+  Buf b0, b1;
+  if (nsteps > 0) issue(b0);
+  stage_x<BITS>(to_global(P.x), groups, xp, cx);
+  __syncthreads();
+
+  for (int st = 0; st < nsteps; st += 2) {
+    if (st + 1 < nsteps) issue(b1);
+    consume(b0);
+    if (st + 1 < nsteps) {
+      if (st + 2 < nsteps) issue(b0);
+      consume(b1);
     }
   }
 
+  if constexpr (WK > 1) {
+    // one pass only (the host guarantees it): reduce lanes, then waves in LDS
 #pragma unroll
-  for (int u = 0; u < UR; ++u) {
-    float v = acc[u];
+    for (int u = 0; u < UR; ++u) {
+      float v = acc[u];
 #pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    acc[u] = v;
-  }
-
-  if constexpr (WK == 1) {
-    if (lr == 0) {
-#pragma unroll
-      for (int u = 0; u < UR; ++u)
-        if (rows[u] < P.n) P.y[rows[u]] = acc[u];
-    }
-  } else {
-    if (lr == 0) {
-#pragma unroll
-      for (int u = 0; u < UR; ++u)
-        red[((wr * UR + u) * Cfg::RPW + slot) * WK + wk] = acc[u];
+      for (int m = LPR / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+      if (lr == 0) red[((wr * UR + u) * Cfg::RPW + slot) * WK + wk] = v;
     }
     __syncthreads();
     if (wk == 0 && lr == 0) {
 #pragma unroll
       for (int u = 0; u < UR; ++u) {
-        const float* r = red + ((wr * UR + u) * Cfg::RPW + slot) * WK;
-        float v = r[0];
+        const float* rr = red + ((wr * UR + u) * Cfg::RPW + slot) * WK;
+        float v = rr[0];
 #pragma unroll
-        for (int i = 1; i < WK; ++i) v += r[i];
-        if (rows[u] < P.n) P.y[rows[u]] = v;
+        for (int i = 1; i < WK; ++i) v += rr[i];
+        const int r = lane_row + u * Cfg::RPW;
+        if (r < row_end) Y[r] = v;
       }
     }
   }
 }
 
 template <int BITS, int LPR, int UR, int WK>
-__global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(GemvProblem P) {
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4))) void qgemv_kernel(GemvProblem P, int rows_per_block) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  gemv_block<BITS, LPR, UR, WK>(P, blockIdx.x * GemvCfg<BITS, LPR, UR, WK>::ROWS, smem);
+  gemv_block<BITS, LPR, UR, WK>(P, blockIdx.x * rows_per_block, rows_per_block, smem);
 }
 
-template <int BITS, int LPR>
-__global__ __launch_bounds__(kGemvThreads) void qgemv_batched_kernel(const GemvBlock* __restrict__ blocks) {
+template <int BITS, int LPR, int UR>
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4))) void qgemv_batched_kernel(const GemvBlock* __restrict__ blocks) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const GemvBlock blk = blocks[blockIdx.x];
-  gemv_block<BITS, LPR, 4, 1>(blk.p, blk.row0, smem);
+  gemv_block<BITS, LPR, UR, 1>(blk.p, blk.row0, blk.nrows, smem);
 }
 
 // ------------------------------------------------------------------ host --
 
-int gemv_rows_per_block(int lpr, int ur, int wk) { return (kGemvWaves / wk) * ur * (64 / lpr); }
+int gemv_row_unroll(int bits) { return bits == 8 ? 2 : 4; }
+
+int gemv_rows_per_pass(int lpr, int ur, int wk) { return (kGemvWaves / wk) * ur * (64 / lpr); }
 
 int gemv_lanes_for_groups(int groups) {
   int lpr = 16;
@@ -243,44 +284,46 @@ int gemv_lanes_for_groups(int groups) {
   return lpr;
 }
 
-GemvGeom gemv_choose(int n, int k) {
+GemvGeom gemv_choose(int n, int k, int bits) {
   const int groups = k / 64;
   GemvGeom g;
   g.lanes_per_row = gemv_lanes_for_groups(groups);
   const int T = groups / g.lanes_per_row;
   const int target = 1024;  // workgroups wanted to fill 256 CUs several times over
-  g.row_unroll = 4;
+  g.row_unroll = gemv_row_unroll(bits);
   g.wave_ksplit = 1;
   auto blocks = [&](int ur, int wk) {
-    const int r = gemv_rows_per_block(g.lanes_per_row, ur, wk);
+    const int r = gemv_rows_per_pass(g.lanes_per_row, ur, wk);
     return (n + r - 1) / r;
   };
-  if (blocks(4, 1) < target) g.row_unroll = 1;
+  if (blocks(g.row_unroll, 1) < target) g.row_unroll = 1;
   if (blocks(g.row_unroll, 1) < target && T >= 4) g.wave_ksplit = 4;
-  g.rows_per_block = gemv_rows_per_block(g.lanes_per_row, g.row_unroll, g.wave_ksplit);
+  g.rows_per_pass = gemv_rows_per_pass(g.lanes_per_row, g.row_unroll, g.wave_ksplit);
+  g.passes = 1;  // short workgroups balance best (see qmm_qgemv_batched_plan)
   return g;
 }
 
 size_t gemv_lds_bytes(int max_groups, const GemvGeom& g) {
   size_t bytes = (size_t)max_groups * (kXStride + sizeof(float2));
-  if (g.wave_ksplit > 1) bytes += (size_t)g.rows_per_block * g.wave_ksplit * sizeof(float);
+  if (g.wave_ksplit > 1) bytes += (size_t)g.rows_per_pass * g.wave_ksplit * sizeof(float);
   return bytes;
 }
 
 template <int BITS, int LPR, int UR, int WK>
-static hipError_t launch_one(const GemvProblem& p, hipStream_t st, size_t lds) {
-  constexpr int ROWS = GemvCfg<BITS, LPR, UR, WK>::ROWS;
-  const unsigned grid = (unsigned)((p.n + ROWS - 1) / ROWS);
-  hipLaunchKernelGGL((qgemv_kernel<BITS, LPR, UR, WK>), dim3(grid), dim3(kGemvThreads), lds, st, p);
+static hipError_t launch_one(const GemvProblem& p, const GemvGeom& g, hipStream_t st, size_t lds) {
+  const int rows = GemvCfg<BITS, LPR, UR, WK>::ROWS * g.passes;
+  const unsigned grid = (unsigned)((p.n + rows - 1) / rows);
+  hipLaunchKernelGGL((qgemv_kernel<BITS, LPR, UR, WK>), dim3(grid), dim3(kGemvThreads), lds, st, p,
+                     rows);
   return hipGetLastError();
 }
 
 template <int BITS, int LPR>
 static hipError_t launch_lpr(const GemvProblem& p, const GemvGeom& g, hipStream_t st, size_t lds) {
-  if (g.row_unroll == 4 && g.wave_ksplit == 1) return launch_one<BITS, LPR, 4, 1>(p, st, lds);
-  if (g.row_unroll == 1 && g.wave_ksplit == 1) return launch_one<BITS, LPR, 1, 1>(p, st, lds);
-  if (g.row_unroll == 1 && g.wave_ksplit == 4) return launch_one<BITS, LPR, 1, 4>(p, st, lds);
-  if (g.row_unroll == 4 && g.wave_ksplit == 4) return launch_one<BITS, LPR, 4, 4>(p, st, lds);
+  constexpr int URB = BITS == 8 ? 2 : 4;
+  if (g.row_unroll == URB && g.wave_ksplit == 1) return launch_one<BITS, LPR, URB, 1>(p, g, st, lds);
+  if (g.row_unroll == 1 && g.wave_ksplit == 1) return launch_one<BITS, LPR, 1, 1>(p, g, st, lds);
+  if (g.row_unroll == 1 && g.wave_ksplit == 4) return launch_one<BITS, LPR, 1, 4>(p, g, st, lds);
   return hipErrorInvalidValue;
 }
 
@@ -309,8 +352,9 @@ hipError_t launch_qgemv(const GemvProblem& p, int bits, const GemvGeom& g, hipSt
 template <int BITS, int LPR>
 static hipError_t launch_batched_one(const GemvBlock* blocks, int num_blocks, size_t lds,
                                      hipStream_t st) {
-  hipLaunchKernelGGL((qgemv_batched_kernel<BITS, LPR>), dim3(num_blocks), dim3(kGemvThreads), lds,
-                     st, blocks);
+  constexpr int URB = BITS == 8 ? 2 : 4;
+  hipLaunchKernelGGL((qgemv_batched_kernel<BITS, LPR, URB>), dim3(num_blocks), dim3(kGemvThreads),
+                     lds, st, blocks);
   return hipGetLastError();
 }
 
@@ -329,7 +373,8 @@ static hipError_t launch_batched_bits(const GemvBlock* blocks, int num_blocks, i
 
 hipError_t launch_qgemv_batched(const GemvBlock* blocks, int num_blocks, int bits,
                                 int lanes_per_row, int max_groups, hipStream_t st) {
-  GemvGeom g{lanes_per_row, 4, 1, gemv_rows_per_block(lanes_per_row, 4, 1)};
+  GemvGeom g{lanes_per_row, gemv_row_unroll(bits), 1,
+             gemv_rows_per_pass(lanes_per_row, gemv_row_unroll(bits), 1), 1};
   const size_t lds = gemv_lds_bytes(max_groups, g);
   switch (bits) {
     case 2: return launch_batched_bits<2>(blocks, num_blocks, lanes_per_row, lds, st);

@@ -6,6 +6,7 @@
 // error path runs without a GPU.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "qmm.h"
@@ -80,7 +81,7 @@ int qmm_qgemv(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
   CHECK_PTR(x, 16);
   CHECK_PTR(y, 4);
   qmm::GemvProblem p{w, scales, biases, x, y, n, k};
-  const qmm::GemvGeom g = qmm::gemv_choose(n, k);
+  const qmm::GemvGeom g = qmm::gemv_choose(n, k, bits);
   return hip_status(qmm::launch_qgemv(p, bits, g, (hipStream_t)stream), fn);
 }
 
@@ -107,9 +108,30 @@ int qmm_qgemv_batched_plan(const qmm_gemv_problem* problems, int count, int bits
     if (l < lpr) lpr = l;
     if (groups > max_groups) max_groups = groups;
   }
-  const int rows = qmm::gemv_rows_per_block(lpr, 4, 1);
+  const int rows = qmm::gemv_rows_per_pass(lpr, qmm::gemv_row_unroll(bits), 1);
+  // Passes per workgroup.  One pass per workgroup measured best on the decode
+  // sweeps: the hardware dispatcher then balances thousands of short
+  // workgroups across the CUs, where longer multi-pass workgroups leave a
+  // tail.  QMM_GEMV_TARGET_BLOCKS sets a workgroup target instead (tuning
+  // sweeps), weighting each pass by its k.
+  double target = 1e12;
+  if (const char* env = getenv("QMM_GEMV_TARGET_BLOCKS")) {
+    const double v = atof(env);
+    if (v >= 1.0) target = v;
+  }
+  double units = 0.0;
+  for (int i = 0; i < count; ++i)
+    units += (double)((problems[i].n + rows - 1) / rows) * problems[i].k / 1024.0;
+  const double base = units / target < 1.0 ? 1.0 : units / target;
+  auto passes_of = [&](int k) {
+    const int p = (int)(base * 1024.0 / k + 0.5);
+    return p < 1 ? 1 : (p > 16 ? 16 : p);
+  };
   long blocks = 0;
-  for (int i = 0; i < count; ++i) blocks += (problems[i].n + rows - 1) / rows;
+  for (int i = 0; i < count; ++i) {
+    const int chunk = rows * passes_of(problems[i].k);
+    blocks += (problems[i].n + chunk - 1) / chunk;
+  }
   if (blocks > 0x7FFFFFFFL) return fail(QMM_ERR_INVALID_ARG, "%s: too many blocks", fn);
   const size_t need = sizeof(qmm::GemvPlanHeader) + (size_t)blocks * sizeof(qmm::GemvBlock);
   if (plan_bytes_needed) *plan_bytes_needed = need;
@@ -133,11 +155,13 @@ int qmm_qgemv_batched_plan(const qmm_gemv_problem* problems, int count, int bits
   long bi = 0;
   for (int i = 0; i < count; ++i) {
     const qmm_gemv_problem& q = problems[i];
-    for (int r = 0; r < q.n; r += rows) {
+    const int chunk = rows * passes_of(q.k);
+    for (int r = 0; r < q.n; r += chunk) {
       qmm::GemvBlock blk;
       memset(&blk, 0, sizeof blk);
       blk.p = qmm::GemvProblem{q.w, q.scales, q.biases, q.x, q.y, q.n, q.k};
       blk.row0 = r;
+      blk.nrows = q.n - r < chunk ? q.n - r : chunk;
       recs[bi++] = blk;
     }
   }
@@ -164,15 +188,15 @@ int qmm_qgemv_batched(const void* plan_device, const void* plan_host, qmm_stream
 }
 
 size_t qmm_qgemm_workspace_size(int m, int n, int k, int bits, int group_size) {
-  (void)m; (void)n; (void)k; (void)bits; (void)group_size;
-  return 0;
+  if (m < 1 || n < 1 || k < 64 || k % 64 != 0 || group_size != 64) return 0;
+  if (bits != 2 && bits != 4 && bits != 8) return 0;
+  return qmm::gemm_workspace_bytes(m, n, k, bits);
 }
 
 int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
               const uint16_t* x, float* y, int m, int n, int k, int bits, int group_size,
               void* workspace, size_t workspace_bytes, qmm_stream stream) {
   const char* fn = "qmm_qgemm";
-  (void)workspace; (void)workspace_bytes;
   clear_error();
   if (int st = check_format(fn, bits, group_size)) return st;
   if (m < 0) return fail(QMM_ERR_INVALID_ARG, "%s: m=%d must be >= 0", fn, m);
@@ -183,8 +207,14 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
   CHECK_PTR(biases, 2);
   CHECK_PTR(x, 16);
   CHECK_PTR(y, 4);
+  const size_t need = qmm::gemm_workspace_bytes(m, n, k, bits);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(QMM_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    CHECK_PTR(workspace, 16);
+  }
   qmm::GemmArgs a{w, scales, biases, x, y, m, n, k};
-  return hip_status(qmm::launch_qgemm(a, bits, (hipStream_t)stream), fn);
+  return hip_status(qmm::launch_qgemm(a, bits, workspace, (hipStream_t)stream), fn);
 }
 
 size_t qmm_qgemm_grouped_workspace_size(int t, int top_k, int e, int n, int k, int bits,

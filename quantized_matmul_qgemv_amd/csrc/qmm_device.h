@@ -34,6 +34,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int BITS>
 struct Fmt {
@@ -62,30 +63,41 @@ __host__ __device__ constexpr uint32_t magic_bits(int p) {
        : (p & 3) == 2 ? 0x54005400u : 0x4C004C00u;
 }
 
+// (a & mask) | magic in ONE instruction.  The compiler splits it into
+// v_and_b32 + v_or_b32 with literal operands (a VOP3 instruction on this
+// chip takes no literal and at most one SGPR), doubling the unpack cost;
+// here the mask sits in an SGPR and the magic in a VGPR, both hoisted out
+// of every loop by the compiler.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(magic));
+  return d;
+}
+
 // One packed word -> PAIRS_PER_WORD fp16 pairs (as raw 32-bit patterns),
 // pair p = (magic + code p, magic + code p + C/2).
 template <int BITS>
 __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t (&h)[Fmt<BITS>::PAIRS_PER_WORD]) {
   if constexpr (BITS == 4) {
     const uint32_t w8 = w >> 8;
-    h[0] = (w & 0x000F000Fu) | 0x64006400u;
-    h[1] = (w & 0x00F000F0u) | 0x54005400u;
-    h[2] = (w8 & 0x000F000Fu) | 0x64006400u;
-    h[3] = (w8 & 0x00F000F0u) | 0x54005400u;
+    h[0] = and_or(w, 0x000F000Fu, 0x64006400u);
+    h[1] = and_or(w, 0x00F000F0u, 0x54005400u);
+    h[2] = and_or(w8, 0x000F000Fu, 0x64006400u);
+    h[3] = and_or(w8, 0x00F000F0u, 0x54005400u);
   } else if constexpr (BITS == 8) {
     // bytes: D.b[i] = {S0:S1}.b[sel.b[i]], S1 = bytes 0..3, S0 = bytes 4..7
-    h[0] = (w & 0x00FF00FFu) | 0x64006400u;
+    h[0] = and_or(w, 0x00FF00FFu, 0x64006400u);
     h[1] = __builtin_amdgcn_perm(w, 0x64646464u, 0x00070005u);
   } else {
     const uint32_t w8 = w >> 8;
-    h[0] = (w & 0x00030003u) | 0x64006400u;
-    h[1] = (w & 0x000C000Cu) | 0x5C005C00u;
-    h[2] = (w & 0x00300030u) | 0x54005400u;
-    h[3] = (w & 0x00C000C0u) | 0x4C004C00u;
-    h[4] = (w8 & 0x00030003u) | 0x64006400u;
-    h[5] = (w8 & 0x000C000Cu) | 0x5C005C00u;
-    h[6] = (w8 & 0x00300030u) | 0x54005400u;
-    h[7] = (w8 & 0x00C000C0u) | 0x4C004C00u;
+    h[0] = and_or(w, 0x00030003u, 0x64006400u);
+    h[1] = and_or(w, 0x000C000Cu, 0x5C005C00u);
+    h[2] = and_or(w, 0x00300030u, 0x54005400u);
+    h[3] = and_or(w, 0x00C000C0u, 0x4C004C00u);
+    h[4] = and_or(w8, 0x00030003u, 0x64006400u);
+    h[5] = and_or(w8, 0x000C000Cu, 0x5C005C00u);
+    h[6] = and_or(w8, 0x00300030u, 0x54005400u);
+    h[7] = and_or(w8, 0x00C000C0u, 0x4C004C00u);
   }
 }
 
@@ -94,6 +106,20 @@ template <int BITS>
 __host__ __device__ constexpr int pair_lo(int p) { return p; }
 template <int BITS>
 __host__ __device__ constexpr int pair_hi(int p) { return p + Fmt<BITS>::CODES_PER_WORD / 2; }
+
+// Pointers that reach a kernel inside a structure loaded from memory are
+// generic (flat) pointers to the compiler; flat loads count against both
+// the vector-memory and the LDS wait counters, so every LDS wait would also
+// wait for all outstanding weight loads.  Casting to the global address
+// space restores global_load/global_store.
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+template <typename T>
+using gptr_mut = __attribute__((address_space(1))) T*;
+template <typename T>
+__device__ __forceinline__ gptr<T> to_global(const T* p) { return (gptr<T>)(p); }
+template <typename T>
+__device__ __forceinline__ gptr_mut<T> to_global_mut(T* p) { return (gptr_mut<T>)(p); }
 
 __device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 __device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }

@@ -17,12 +17,13 @@ struct GemvProblem {
   int32_t k;
 };
 
-// One workgroup's share of a batched GEMV: rows [row0, row0 + rows) of a
+// One workgroup's share of a batched GEMV: rows [row0, row0 + nrows) of a
 // problem.  64 bytes, read once per workgroup.
 struct alignas(64) GemvBlock {
   GemvProblem p;
   int32_t row0;
-  int32_t pad[3];
+  int32_t nrows;
+  int32_t pad[2];
 };
 static_assert(sizeof(GemvBlock) == 64, "GemvBlock must stay 64 bytes");
 
@@ -34,7 +35,7 @@ struct alignas(64) GemvPlanHeader {
   int32_t bits;
   int32_t group_size;
   int32_t lanes_per_row;
-  int32_t rows_per_block;
+  int32_t rows_per_block;  // rows per workgroup pass
   int32_t num_blocks;
   int32_t max_groups;
   int32_t count;
@@ -49,11 +50,13 @@ struct GemvGeom {
   int lanes_per_row;  // lanes cooperating on one row (power of two <= 16)
   int row_unroll;     // rows per lane slot held in flight
   int wave_ksplit;    // waves of a workgroup splitting one row's groups
-  int rows_per_block;
+  int rows_per_pass;  // rows one pass of a workgroup covers
+  int passes;         // passes per workgroup (rows per workgroup = passes * rows_per_pass)
 };
 
-GemvGeom gemv_choose(int n, int k);
-int gemv_rows_per_block(int lanes_per_row, int row_unroll, int wave_ksplit);
+GemvGeom gemv_choose(int n, int k, int bits);
+int gemv_row_unroll(int bits);
+int gemv_rows_per_pass(int lanes_per_row, int row_unroll, int wave_ksplit);
 int gemv_lanes_for_groups(int groups);
 size_t gemv_lds_bytes(int max_groups, const GemvGeom& g);
 
@@ -69,7 +72,8 @@ struct GemmArgs {
   float* y;
   int m, n, k;
 };
-hipError_t launch_qgemm(const GemmArgs& a, int bits, hipStream_t st);
+size_t gemm_workspace_bytes(int m, int n, int k, int bits);
+hipError_t launch_qgemm(const GemmArgs& a, int bits, void* workspace, hipStream_t st);
 
 struct GroupedArgs {
   const uint32_t* w;

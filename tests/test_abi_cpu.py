@@ -108,22 +108,24 @@ def test_batched_plan_host_only(L):
     hdr = (C.c_int32 * 16).from_buffer(buf)
     assert hdr[0] == 0x504D4D51 and hdr[2] == 4 and hdr[3] == 64
     lpr, rows, blocks, max_groups, count = hdr[4], hdr[5], hdr[6], hdr[7], hdr[8]
-    assert lpr == 16 and max_groups == 48 and count == 3
-    assert blocks == sum((n + rows - 1) // rows for n, _ in shapes)
+    assert lpr == 16 and max_groups == 48 and count == 3 and rows == 64
     assert need.value == 64 + 64 * blocks
     # block records: pointers and row ranges tile every problem exactly once
     rec = (C.c_int64 * (8 * blocks)).from_buffer(buf, 64)
     seen = {}
     for bi in range(blocks):
         r = rec[8 * bi: 8 * bi + 8]
-        n_k = C.c_int64(r[5]).value
+        n_k = r[5] & 0xFFFFFFFFFFFFFFFF
         n, k = n_k & 0xFFFFFFFF, n_k >> 32
-        row0 = r[6] & 0xFFFFFFFF
-        seen.setdefault(r[0], []).append((row0, n, k))
+        rr = r[6] & 0xFFFFFFFFFFFFFFFF
+        row0, nrows = rr & 0xFFFFFFFF, rr >> 32
+        seen.setdefault(r[0], []).append((row0, nrows, n, k))
     for i, (n, k) in enumerate(shapes):
-        rows0 = sorted(x[0] for x in seen[A * (i + 1)])
-        assert rows0 == list(range(0, n, rows))
-        assert all(x[1] == n and x[2] == k for x in seen[A * (i + 1)])
+        recs = sorted(seen[A * (i + 1)])
+        assert all(x[2] == n and x[3] == k for x in recs)
+        assert recs[0][0] == 0 and all(a[0] + a[1] == b[0] for a, b in zip(recs, recs[1:]))
+        assert recs[-1][0] + recs[-1][1] == n
+        assert all(x[1] % rows == 0 for x in recs[:-1])
     # corrupt header / bad problem
     bad = (C.c_uint8 * 64)()
     expect(L.qmm_qgemv_batched(A, bad, None), INV, "not a plan image")

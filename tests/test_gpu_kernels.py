@@ -162,7 +162,9 @@ def test_gemv_batched_mixed_shapes():
 
 GEMM_SHAPES = [(1, 32, 64), (2, 100, 128), (3, 256, 192), (17, 300, 320), (33, 1024, 128),
                (64, 512, 256), (65, 96, 512), (127, 384, 256), (128, 1024, 2560),
-               (129, 640, 512), (300, 1000, 1024), (513, 257, 640)]
+               (129, 640, 512), (300, 1000, 1024), (513, 257, 640),
+               # few tiles and long k: split over k with an ordered reduction
+               (1, 4096, 4096), (16, 2048, 8192), (64, 4096, 4096), (200, 1024, 2560)]
 
 
 @pytest.mark.parametrize("bits", BITS)
@@ -174,6 +176,23 @@ def test_gemm_parity(bits, m, n, k):
     want = oracle.qmatmul_f64(words, s, b, x, bits)
     y = qmm.qgemm(dev(words), dev(s), dev(b), dev(x), bits)
     assert_close(host(y), want, f"gemm bits={bits} m={m} n={n} k={k}")
+
+
+def test_gemm_split_k_workspace_and_determinism():
+    say("gemm split-k")
+    m, n, k, bits = 64, 2048, 4096, 4
+    need = qmm.qgemm_workspace_size(m, n, k, bits)
+    assert need >= 2 * m * n * 4, "this shape is expected to split k"
+    _, _, words, s, b = quantized((911, 0, 0, 0), n, k, bits)
+    x = synth.draw_act((911, 0, 0, 1), m, k)
+    W, S, B, X = dev(words), dev(s), dev(b), dev(x)
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")   # garbage is fine
+    y1 = qmm.qgemm(W, S, B, X, bits, workspace=ws)
+    y2 = qmm.qgemm(W, S, B, X, bits, workspace=ws)
+    assert torch.equal(y1, y2)
+    assert_close(host(y1), oracle.qmatmul_f64(words, s, b, x, bits), "split-k")
+    with pytest.raises(qmm.QmmError):
+        qmm.qgemm(W, S, B, X, bits, workspace=ws[: need - 1])
 
 
 def test_gemm_rows_equal_gemv_and_deterministic():
