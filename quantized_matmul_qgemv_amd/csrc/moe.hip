@@ -99,10 +99,10 @@ __global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
   }
 }
 
-template <int BITS, int BM, int NB, int GPS>
+template <int BITS, int BM, int NB, bool SBQ>
 __global__ __launch_bounds__(kGemmThreads) void grouped_kernel(GroupedArgs a, const int32_t* __restrict__ ws,
                                                                int n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * (64 * GPS + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * kAStride];
   __shared__ int32_t pair_of[BM];
   constexpr int BN = 4 * NB * 32;
   const int pairs = a.t * a.top_k;
@@ -122,12 +122,12 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_kernel(GroupedArgs a, co
   const int groups = a.k >> 6;
   const size_t wstride = (size_t)a.n * groups * Fmt<BITS>::WORDS_PER_GROUP;
   const size_t sstride = (size_t)a.n * groups;
-  gemm_tile<BITS, BM, NB, GPS>(ARows{a.a, a.k}, a_row, c_row, a.w + mt.expert * wstride,
+  gemm_tile<BITS, BM, NB, SBQ>(ARows{a.a, a.k}, a_row, c_row, a.w + mt.expert * wstride,
                                a.s + mt.expert * sstride, a.b + mt.expert * sstride, a.y, a.n,
                                tn * BN, a.n, 0, groups, lds);
 }
 
-template <int BITS, int BM, int NB, int GPS>
+template <int BITS, int BM, int NB, bool SBQ>
 static hipError_t launch_grouped_tile(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
   constexpr int BN = 4 * NB * 32;
   const int pairs = a.t * a.top_k;
@@ -137,25 +137,25 @@ static hipError_t launch_grouped_tile(const GroupedArgs& a, int32_t* ws, hipStre
   if (err != hipSuccess) return err;
   const int n_tiles = (a.n + BN - 1) / BN;
   const int m_tiles = max_row_tiles(pairs, a.e, BM);
-  hipLaunchKernelGGL((grouped_kernel<BITS, BM, NB, GPS>), dim3(m_tiles * n_tiles), dim3(kGemmThreads),
+  hipLaunchKernelGGL((grouped_kernel<BITS, BM, NB, SBQ>), dim3(m_tiles * n_tiles), dim3(kGemmThreads),
                      0, st, a, ws, n_tiles);
   return hipGetLastError();
 }
 
-template <int BITS, int GPS>
-static hipError_t launch_grouped_gps(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
+template <int BITS, bool SBQ>
+static hipError_t launch_grouped_sbq(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
   // Row tile from the mean number of pairs per expert: one tile per expert
   // keeps each expert's weights to a single pass over HBM.
   const int mean = (a.t * a.top_k + a.e - 1) / a.e;
-  if (mean <= 16) return launch_grouped_tile<BITS, 32, 2, GPS>(a, ws, st);
-  if (mean <= 48) return launch_grouped_tile<BITS, 64, 2, GPS>(a, ws, st);
-  return launch_grouped_tile<BITS, 128, 2, GPS>(a, ws, st);
+  if (mean <= 16) return launch_grouped_tile<BITS, 32, 2, SBQ>(a, ws, st);
+  if (mean <= 48) return launch_grouped_tile<BITS, 64, 2, SBQ>(a, ws, st);
+  return launch_grouped_tile<BITS, 128, 2, SBQ>(a, ws, st);
 }
 
 template <int BITS>
 static hipError_t launch_grouped_bits(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
-  return (a.k / 64) % 2 == 0 ? launch_grouped_gps<BITS, 2>(a, ws, st)
-                             : launch_grouped_gps<BITS, 1>(a, ws, st);
+  return (a.k / 64) % 4 == 0 ? launch_grouped_sbq<BITS, true>(a, ws, st)
+                             : launch_grouped_sbq<BITS, false>(a, ws, st);
 }
 
 hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, hipStream_t st) {

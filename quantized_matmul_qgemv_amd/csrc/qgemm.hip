@@ -14,6 +14,9 @@
 // [split*G/S, (split+1)*G/S) and writes its fp32 partial tile to the
 // workspace; qgemm_reduce_kernel then sums the S partials of every output
 // in split order, so the result does not depend on scheduling.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "qgemm_core.h"
 #include "qmm_internal.h"
 
@@ -27,9 +30,9 @@ struct GemmGrid {
   long stride;                               // floats between partial tiles of two splits
 };
 
-template <int BITS, int BM, int NB, int GPS>
-__global__ __launch_bounds__(kGemmThreads) void qgemm_kernel(GemmArgs a, GemmGrid gr, float* partial) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * (64 * GPS + 8)];
+template <int BITS, int BM, int NB, bool SBQ>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2))) void qgemm_kernel(GemmArgs a, GemmGrid gr, float* partial) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * kAStride];
   constexpr int BN = 4 * NB * 32;
   const int total = gr.n_tiles * gr.m_tiles * gr.splits;
   int t = blockIdx.x;
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(kGemmThreads) void qgemm_kernel(GemmArgs a, GemmGri
   float* out = gr.splits == 1 ? a.y : partial + (size_t)split * gr.stride;
   const int g0 = split * gr.gps_split;
   const int g1 = g0 + gr.gps_split;
-  gemm_tile<BITS, BM, NB, GPS>(ARows{a.x, a.k}, a_row, c_row, a.w, a.s, a.b, out, a.n, n0, a.n,
+  gemm_tile<BITS, BM, NB, SBQ>(ARows{a.x, a.k}, a_row, c_row, a.w, a.s, a.b, out, a.n, n0, a.n,
                                g0, g1, lds);
 }
 
@@ -69,7 +72,7 @@ static long partial_stride(int m, int n) { return ((long)m * n + 63) / 64 * 64; 
 
 // Tile / split choice for one GEMM.
 struct GemmPlan {
-  int bm, nb, gps, splits;
+  int bm, nb, splits;
 };
 
 static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
@@ -78,22 +81,31 @@ static GemmPlan gemm_plan(int m, int n, int k, int bits) {
   const int groups = k / 64;
   GemmPlan p;
   p.bm = m <= 32 ? 32 : m <= 64 ? 64 : 128;
-  const int gps = groups % 2 == 0 ? 2 : 1;
-  p.gps = gps;
   // column tile: the wide tile unless it leaves too few workgroups
   const long tiles_wide = (long)ceil_div(n, 256) * ceil_div(m, p.bm);
   p.nb = tiles_wide >= 256 ? 2 : 1;
   const long tiles = (long)ceil_div(n, 128 * p.nb) * ceil_div(m, p.bm);
   // split k when the tiles cannot fill the CUs, as long as every split keeps
-  // at least 4 pipeline steps and the fp32 partials stay within a few times
+  // at least 8 pipeline steps and the fp32 partials stay within a few times
   // the weight bytes
   int splits = 1;
-  const long steps = groups / gps;
+  const long steps = groups;
   const double wbytes = (double)n * k * bits / 8;
-  while (tiles * splits * 2 <= 512 && steps % (splits * 2) == 0 && steps / (splits * 2) >= 4 &&
+  while (tiles * splits * 2 <= 512 && steps % (splits * 2) == 0 && steps / (splits * 2) >= 8 &&
          (double)(splits * 2) * m * n * 4.0 <= 4.0 * wbytes)
     splits *= 2;
   p.splits = splits;
+  // QMM_GEMM_FORCE="bm,nb,splits" overrides the choice (tuning sweeps); it
+  // is ignored unless it is a valid configuration for this shape.
+  if (const char* env = getenv("QMM_GEMM_FORCE")) {
+    int bm = 0, nb = 0, sp = 0;
+    if (sscanf(env, "%d,%d,%d", &bm, &nb, &sp) == 3 && (bm == 32 || bm == 64 || bm == 128) &&
+        (nb == 1 || nb == 2) && sp >= 1 && groups % sp == 0) {
+      p.bm = bm;
+      p.nb = nb;
+      p.splits = sp;
+    }
+  }
   return p;
 }
 
@@ -102,7 +114,7 @@ size_t gemm_workspace_bytes(int m, int n, int k, int bits) {
   return p.splits > 1 ? (size_t)p.splits * partial_stride(m, n) * sizeof(float) : 0;
 }
 
-template <int BITS, int BM, int NB, int GPS>
+template <int BITS, int BM, int NB, bool SBQ>
 static hipError_t launch_tile(const GemmArgs& a, const GemmPlan& p, float* ws, hipStream_t st) {
   constexpr int BN = 4 * NB * 32;
   GemmGrid gr;
@@ -113,7 +125,7 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmPlan& p, float* ws, h
   const int total = gr.n_tiles * gr.m_tiles * gr.splits;
   gr.xcd_remap = total % kXcds == 0 ? 1 : 0;
   gr.stride = partial_stride(a.m, a.n);
-  hipLaunchKernelGGL((qgemm_kernel<BITS, BM, NB, GPS>), dim3(total), dim3(kGemmThreads), 0, st, a,
+  hipLaunchKernelGGL((qgemm_kernel<BITS, BM, NB, SBQ>), dim3(total), dim3(kGemmThreads), 0, st, a,
                      gr, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
@@ -125,8 +137,11 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmPlan& p, float* ws, h
 
 template <int BITS, int BM>
 static hipError_t launch_bm(const GemmArgs& a, const GemmPlan& p, float* ws, hipStream_t st) {
-  if (p.nb == 2) return p.gps == 2 ? launch_tile<BITS, BM, 2, 2>(a, p, ws, st) : launch_tile<BITS, BM, 2, 1>(a, p, ws, st);
-  return p.gps == 2 ? launch_tile<BITS, BM, 1, 2>(a, p, ws, st) : launch_tile<BITS, BM, 1, 1>(a, p, ws, st);
+  // quad scale loads need every split to start and end on a multiple of 4 groups
+  const bool sbq = ((a.k / 64) / p.splits) % 4 == 0;
+  if (p.nb == 2)
+    return sbq ? launch_tile<BITS, BM, 2, true>(a, p, ws, st) : launch_tile<BITS, BM, 2, false>(a, p, ws, st);
+  return sbq ? launch_tile<BITS, BM, 1, true>(a, p, ws, st) : launch_tile<BITS, BM, 1, false>(a, p, ws, st);
 }
 
 template <int BITS>

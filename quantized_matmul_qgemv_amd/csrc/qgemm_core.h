@@ -22,9 +22,9 @@
 //     inside one MFMA as long as both operands agree, so the A tile is
 //     written to LDS with the same order applied inside every 16-wide span
 //     of k; the MFMA's A operand is then one ds_read_b128 per lane.
-//   * A is double-buffered in LDS (one barrier per pipeline step of GPS
-//     groups); the next step's A and packed-B loads are issued before the
-//     current step's MFMAs.
+//   * Software-pipelined: packed B is loaded 3 steps ahead (registers), A 2
+//     steps ahead (registers, then a double-buffered LDS tile); one barrier
+//     per step.
 //   * The caller chooses the k range, so a tile can be split over k across
 //     workgroups (partial tiles are summed by a separate, ordered pass).
 #pragma once
@@ -66,7 +66,7 @@ struct BRaw {
   uint16_t s, b;
 };
 
-template <int BITS>
+template <int BITS, bool WITH_SB = true>
 __device__ __forceinline__ void load_braw(BRaw<BITS>& r, gptr<uint32_t> wcol, gptr<uint16_t> scol,
                                           gptr<uint16_t> bcol, int g, int h) {
   constexpr int WPG = Fmt<BITS>::WORDS_PER_GROUP;
@@ -81,8 +81,10 @@ __device__ __forceinline__ void load_braw(BRaw<BITS>& r, gptr<uint32_t> wcol, gp
       r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
     }
   }
-  r.s = scol[g];
-  r.b = bcol[g];
+  if constexpr (WITH_SB) {
+    r.s = scol[g];
+    r.b = bcol[g];
+  }
 }
 
 // B operand (8 fp16 values) of k16 step j (0..3) from a lane's raw half-group.
@@ -122,11 +124,19 @@ struct ARows {
 // One BM x BN output tile over the k groups [g_begin, g_end).  a_row(i)
 // gives the source row of tile row i (already clamped to a valid row);
 // c_row(i) gives the output row or -1 to skip; columns are bounded by n.
-// Each pipeline step covers GPS groups (GPS*64 values of k): while the
-// matrix cores work on step i, the loads of step i+1 are in flight, so a
-// larger GPS hides more memory latency per barrier.  (g_end - g_begin) must
-// be a multiple of GPS.  lds holds 2 * BM * (64*GPS + 8) halves.
-template <int BITS, int BM, int NB, int GPS, typename ARowFn, typename CRowFn>
+//
+// Software pipeline, one 64-code group per step (i = step index):
+//   * packed B (weights) is loaded 3 steps ahead into a ring of 4 register
+//     buffers: it comes straight from HBM and has the longest latency;
+//   * A (activations) is loaded 2 steps ahead into 2 register buffers and
+//     written to one of 2 LDS slots at the end of the step before its use;
+//   * one barrier per step.
+// The loop is unrolled by 4 so that every ring index is a compile-time
+// constant (register arrays indexed at run time would spill).
+// lds holds 2 * BM * AST halves.
+constexpr int kAStride = 72;  // LDS row stride in halves: 64 + 8 pad (144 B)
+
+template <int BITS, int BM, int NB, bool SBQ, typename ARowFn, typename CRowFn>
 __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_row,
                                           const uint32_t* __restrict__ w_,
                                           const uint16_t* __restrict__ s_,
@@ -134,11 +144,9 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
                                           int ldy, int n0, int n, int g_begin, int g_end,
                                           uint16_t* lds) {
   constexpr int MB = BM / 32;
-  constexpr int SPAN_ROW = 4 * GPS;                  // 16-wide spans per tile row per step
-  constexpr int SPANS = BM * SPAN_ROW;
+  constexpr int SPANS = BM * 4;  // 16-wide spans of A per step
   constexpr int SPT = (SPANS + kGemmThreads - 1) / kGemmThreads;
   constexpr int WPG = Fmt<BITS>::WORDS_PER_GROUP;
-  constexpr int AST = 64 * GPS + 8;                  // LDS row stride in halves (16 B pad)
   const gptr<uint32_t> w = to_global(w_);
   const gptr<uint16_t> s = to_global(s_);
   const gptr<uint16_t> b = to_global(b_);
@@ -151,7 +159,6 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  // weight columns of this lane
   gptr<uint32_t> wcol[NB];
   gptr<uint16_t> scol[NB];
   gptr<uint16_t> bcol[NB];
@@ -164,18 +171,18 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
     bcol[nb] = b + (size_t)col * groups;
   }
 
-  // A spans of this thread
   gptr<uint16_t> asrc[SPT];
   int aoff[SPT];
   bool aon[SPT];
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
-    const int sp = tid + i * kGemmThreads;
-    aon[i] = sp < SPANS;
-    const int r = (sp / SPAN_ROW) < BM ? (sp / SPAN_ROW) : BM - 1;
-    const int c = sp % SPAN_ROW;
+    const int sp0 = tid + i * kGemmThreads;
+    aon[i] = sp0 < SPANS;
+    const int sp = sp0 % SPANS;
+    const int r = sp >> 2;
+    const int c = sp & 3;
     asrc[i] = abase + (size_t)a_row(r) * A.k + c * 16;
-    aoff[i] = r * AST + c * 16;
+    aoff[i] = r * kAStride + c * 16;
   }
 
   float16_t acc[MB][NB];
@@ -186,80 +193,137 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-  uint32_t araw[SPT][8];
-  BRaw<BITS> braw[GPS][NB];
-  auto load_a = [&](int g) {
+  uint32_t ra[2][SPT][8];   // A register stages
+  BRaw<BITS> rb[4][NB];     // B register ring
+
+  // Loads are never predicated: a load under a branch makes the compiler's
+  // wait-count bookkeeping fall back to waiting for every outstanding load,
+  // which would drain the prefetch pipeline each step.  Threads without a
+  // span of their own (BM = 32) reload a valid span and skip the LDS store;
+  // steps past the end reload the last group.
+  auto load_a = [&](uint32_t (&dst)[SPT][8], int g) {
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
-      if (aon[i]) {
-        gptr<u32x4> p = reinterpret_cast<gptr<u32x4>>(asrc[i] + (size_t)g * 64);
-        const u32x4 v0 = p[0], v1 = p[1];
-        araw[i][0] = v0.x; araw[i][1] = v0.y; araw[i][2] = v0.z; araw[i][3] = v0.w;
-        araw[i][4] = v1.x; araw[i][5] = v1.y; araw[i][6] = v1.z; araw[i][7] = v1.w;
-      }
+      gptr<u32x4> p = reinterpret_cast<gptr<u32x4>>(asrc[i] + (size_t)g * 64);
+      const u32x4 v0 = p[0], v1 = p[1];
+      dst[i][0] = v0.x; dst[i][1] = v0.y; dst[i][2] = v0.z; dst[i][3] = v0.w;
+      dst[i][4] = v1.x; dst[i][5] = v1.y; dst[i][6] = v1.z; dst[i][7] = v1.w;
     }
   };
-  auto store_a = [&](int buf) {
-    uint16_t* dst = lds + buf * (BM * AST);
+  auto store_a = [&](const uint32_t (&src)[SPT][8], int slot) {
+    uint16_t* dst = lds + slot * (BM * kAStride);
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       if (aon[i]) {
         uint32_t o[8];
-        permute_span<BITS>(araw[i], o);
+        permute_span<BITS>(src[i], o);
         u32x4* d = reinterpret_cast<u32x4*>(dst + aoff[i]);
         d[0] = u32x4{o[0], o[1], o[2], o[3]};
         d[1] = u32x4{o[4], o[5], o[6], o[7]};
       }
     }
   };
-  auto load_b = [&](int g) {
+  auto load_b = [&](BRaw<BITS> (&dst)[NB], int g) {
 #pragma unroll
-    for (int q = 0; q < GPS; ++q)
+    for (int nb = 0; nb < NB; ++nb)
+      load_braw<BITS, !SBQ>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h);
+  };
+  // SBQ: scales and biases of four consecutive groups come in one 8-byte
+  // load per column (a 2-byte load touches as many cache lines as a wide
+  // one, so per-group loads made the scale stream as costly as the codes).
+  // The caller guarantees g_begin and g_end are multiples of 4.
+  u32x2 sqc[NB], bqc[NB], sqn[NB], bqn[NB];
+  auto load_sbq = [&](u32x2 (&sq)[NB], u32x2 (&bq)[NB], int g4) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        load_braw<BITS>(braw[q][nb], wcol[nb], scol[nb], bcol[nb], g + q, h);
+    for (int nb = 0; nb < NB; ++nb) {
+      sq[nb] = *reinterpret_cast<gptr<u32x2>>(scol[nb] + g4);
+      bq[nb] = *reinterpret_cast<gptr<u32x2>>(bcol[nb] + g4);
+    }
+  };
+  auto set_sb = [&](BRaw<BITS> (&cur)[NB], int q) {
+    if constexpr (SBQ) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t sw = (q >> 1) ? sqc[nb].y : sqc[nb].x;
+        const uint32_t bw = (q >> 1) ? bqc[nb].y : bqc[nb].x;
+        cur[nb].s = (uint16_t)(sw >> (16 * (q & 1)));
+        cur[nb].b = (uint16_t)(bw >> (16 * (q & 1)));
+      }
+    }
+  };
+  // The A operands of k16 step j+1 are read from LDS while the matrix
+  // cores work on step j (two operand buffers), so LDS latency stays off
+  // the MFMA issue path.
+  auto compute = [&](int slot, const BRaw<BITS> (&cur)[NB]) {
+    const uint16_t* abuf = lds + slot * (BM * kAStride) + l32 * kAStride + h * 32;
+    half8_t aop[2][MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      aop[0][mb] = *reinterpret_cast<const half8_t*>(abuf + mb * 32 * kAStride);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < 3) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          aop[(j + 1) & 1][mb] =
+              *reinterpret_cast<const half8_t*>(abuf + mb * 32 * kAStride + (j + 1) * 8);
+      }
+      half8_t bop[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) bop[nb] = b_operand<BITS>(cur[nb], j);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[j & 1][mb], bop[nb], acc[mb][nb], 0, 0, 0);
+    }
   };
 
-  if (g_begin < g_end) {
-    load_a(g_begin);
-    load_b(g_begin);
-    store_a(0);
+  const int nsteps = g_end - g_begin;
+  const int glast = g_end - 1;
+  auto gclamp = [&](int i) { const int g = g_begin + i; return g < glast ? g : glast; };
+  auto g4clamp = [&](int i) { const int g = g_begin + i; return g < g_end ? g : g_end - 4; };
+  // prologue: B for steps 0..2, A for steps 0..1, A(0) into LDS slot 0
+  if (nsteps > 0) {
+    if constexpr (SBQ) load_sbq(sqc, bqc, g_begin);
+    load_a(ra[0], gclamp(0));
+    load_b(rb[0], gclamp(0));
+    load_b(rb[1], gclamp(1));
+    load_a(ra[1], gclamp(1));
+    load_b(rb[2], gclamp(2));
+    store_a(ra[0], 0);
   }
   __syncthreads();
 
-  for (int g = g_begin, step = 0; g < g_end; g += GPS, ++step) {
-    const int buf = step & 1;
-    BRaw<BITS> cur[GPS][NB];
-#pragma unroll
-    for (int q = 0; q < GPS; ++q)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) cur[q][nb] = braw[q][nb];
-    const bool more = g + GPS < g_end;
-    if (more) {
-      load_a(g + GPS);
-      load_b(g + GPS);
-    }
-    const uint16_t* abuf = lds + buf * (BM * AST);
-#pragma unroll
-    for (int q = 0; q < GPS; ++q) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        half8_t bop[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) bop[nb] = b_operand<BITS>(cur[q][nb], j);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const half8_t aop = *reinterpret_cast<const half8_t*>(
-              abuf + (mb * 32 + l32) * AST + q * 64 + h * 32 + j * 8);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop[nb], acc[mb][nb], 0, 0, 0);
-        }
-      }
-    }
-    if (more) store_a(buf ^ 1);
-    __syncthreads();
+  // step i: B(i+3) -> rb[(i+3)%4], A(i+2) -> ra[i%2]; compute slot i%2 with
+  // rb[i%4]; A(i+1) (ra[(i+1)%2]) -> LDS slot (i+1)%2; barrier.  Loads and
+  // the store past the last step are harmless repeats of the last group.
+#define QMM_GEMM_STEP(I)                                         \
+  {                                                              \
+    load_b(rb[((I) + 3) & 3], gclamp(i + (I) + 3));              \
+    load_a(ra[(I) & 1], gclamp(i + (I) + 2));                    \
+    if (SBQ && (I) == 1) load_sbq(sqn, bqn, g4clamp(i + 4));     \
+    set_sb(rb[(I) & 3], (I));                                    \
+    compute((I) & 1, rb[(I) & 3]);                               \
+    store_a(ra[((I) + 1) & 1], ((I) + 1) & 1);                   \
+    __syncthreads();                                             \
   }
+  int i = 0;
+  for (; i + 4 <= nsteps; i += 4) {
+    QMM_GEMM_STEP(0)
+    QMM_GEMM_STEP(1)
+    QMM_GEMM_STEP(2)
+    QMM_GEMM_STEP(3)
+    if constexpr (SBQ) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) { sqc[nb] = sqn[nb]; bqc[nb] = bqn[nb]; }
+    }
+  }
+  const int rem = nsteps - i;
+  if (rem > 0) QMM_GEMM_STEP(0)
+  if (rem > 1) QMM_GEMM_STEP(1)
+  if (rem > 2) QMM_GEMM_STEP(2)
+#undef QMM_GEMM_STEP
 
   // epilogue: D[i][j] of a 32x32 block sits in lane (j + 32*((i/4)%2)),
   // register (i/8)*4 + i%4.
