@@ -46,56 +46,90 @@ struct GemvCfg {
 
 // Stage x[0 .. 64*groups) into LDS: paired halves plus (C[g], X[g]).  Four
 // consecutive threads share a group (16 codes each), so the staging that
-// every workgroup waits for at its barrier is short.
+// every workgroup waits for at its barrier is short.  It is split in two:
+// stage_x_load issues the activation loads (before the weight loads, so
+// that waiting for x never waits for the weight stream, loads completing
+// in order) and stage_x_store pairs, sums and writes them to LDS.
+constexpr int kXRounds = 1;  // quarter-groups per thread held in registers (k <= 4096)
+
+struct XStage {
+  uint32_t d[kXRounds][8];
+};
+
+__device__ __forceinline__ void stage_x_load(gptr<uint16_t> x, int groups, XStage& xs) {
+#pragma unroll
+  for (int r = 0; r < kXRounds; ++r) {
+    int t = threadIdx.x + r * kGemvThreads;
+    const int last = 4 * groups - 1;
+    t = t < last ? t : last;  // unpredicated: repeat the last quarter
+    gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(x + (size_t)(t >> 2) * 64 + (t & 3) * 16);
+    const u32x4 v0 = src[0], v1 = src[1];
+    xs.d[r][0] = v0.x; xs.d[r][1] = v0.y; xs.d[r][2] = v0.z; xs.d[r][3] = v0.w;
+    xs.d[r][4] = v1.x; xs.d[r][5] = v1.y; xs.d[r][6] = v1.z; xs.d[r][7] = v1.w;
+  }
+}
+
+// One quarter group (16 codes) -> paired halves in LDS and its share of (C, X).
 template <int BITS>
-__device__ __forceinline__ void stage_x(gptr<uint16_t> x, int groups, unsigned char* xp,
-                                        float2* cx) {
+__device__ __forceinline__ void stage_quarter(const uint32_t (&d)[8], int g, int part, bool on,
+                                              unsigned char* xp, float2* cx) {
   using F = Fmt<BITS>;
   constexpr int C = F::CODES_PER_WORD;
   constexpr int PPW = F::PAIRS_PER_WORD;
   constexpr int WPQ = 16 / C > 0 ? 16 / C : 1;  // words per quarter group
   static_assert(16 % C == 0, "a quarter group must hold whole words");
-  const int rounds = (4 * groups + blockDim.x - 1) / blockDim.x;  // uniform trip count
-  for (int r = 0; r < rounds; ++r) {
-    const int t = threadIdx.x + r * blockDim.x;
-    const int g = t >> 2;
-    const int part = t & 3;
-    const bool on = g < groups;
-    float csum = 0.0f, xsum = 0.0f;
-    if (on) {
-      gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(x + (size_t)g * 64 + part * 16);
-      uint32_t d[8];
-      const u32x4 v0 = src[0], v1 = src[1];
-      d[0] = v0.x; d[1] = v0.y; d[2] = v0.z; d[3] = v0.w;
-      d[4] = v1.x; d[5] = v1.y; d[6] = v1.z; d[7] = v1.w;
-      uint32_t out[8];
+  float csum = 0.0f, xsum = 0.0f;
+  uint32_t out[8];
 #pragma unroll
-      for (int wd = 0; wd < WPQ; ++wd) {
+  for (int wd = 0; wd < WPQ; ++wd) {
 #pragma unroll
-        for (int p = 0; p < PPW; ++p) {
-          const int klo = wd * C + pair_lo<BITS>(p);
-          const int khi = wd * C + pair_hi<BITS>(p);
-          const uint32_t lo = (d[klo >> 1] >> (16 * (klo & 1))) & 0xFFFFu;
-          const uint32_t hi = (d[khi >> 1] >> (16 * (khi & 1))) & 0xFFFFu;
-          out[wd * PPW + p] = lo | (hi << 16);
-          const float xl = f16_bits_to_f32((uint16_t)lo);
-          const float xh = f16_bits_to_f32((uint16_t)hi);
-          csum += magic_value<BITS>(p) * xl;
-          csum += magic_value<BITS>(p) * xh;
-          xsum += xl;
-          xsum += xh;
-        }
-      }
-      // pairs of this quarter: 8 dwords at pair index part*8 of the group
-      u32x4* dst = reinterpret_cast<u32x4*>(xp + (size_t)g * kXStride + part * 32);
-      dst[0] = u32x4{out[0], out[1], out[2], out[3]};
-      dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+    for (int p = 0; p < PPW; ++p) {
+      const int klo = wd * C + pair_lo<BITS>(p);
+      const int khi = wd * C + pair_hi<BITS>(p);
+      const uint32_t lo = (d[klo >> 1] >> (16 * (klo & 1))) & 0xFFFFu;
+      const uint32_t hi = (d[khi >> 1] >> (16 * (khi & 1))) & 0xFFFFu;
+      out[wd * PPW + p] = lo | (hi << 16);
+      const float xl = f16_bits_to_f32((uint16_t)lo);
+      const float xh = f16_bits_to_f32((uint16_t)hi);
+      csum += magic_value<BITS>(p) * xl;
+      csum += magic_value<BITS>(p) * xh;
+      xsum += xl;
+      xsum += xh;
     }
-    csum += __shfl_xor(csum, 1);
-    xsum += __shfl_xor(xsum, 1);
-    csum += __shfl_xor(csum, 2);
-    xsum += __shfl_xor(xsum, 2);
-    if (on && part == 0) cx[g] = make_float2(csum, xsum);
+  }
+  if (on) {
+    // pairs of this quarter: 8 dwords at pair index part*8 of the group
+    u32x4* dst = reinterpret_cast<u32x4*>(xp + (size_t)g * kXStride + part * 32);
+    dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+    dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+  }
+  csum += __shfl_xor(csum, 1);
+  xsum += __shfl_xor(xsum, 1);
+  csum += __shfl_xor(csum, 2);
+  xsum += __shfl_xor(xsum, 2);
+  if (on && part == 0) cx[g] = make_float2(csum, xsum);
+}
+
+template <int BITS>
+__device__ __forceinline__ void stage_x_store(gptr<uint16_t> x, int groups, const XStage& xs,
+                                              unsigned char* xp, float2* cx) {
+  const int quarters = 4 * groups;
+#pragma unroll
+  for (int r = 0; r < kXRounds; ++r) {
+    const int t = threadIdx.x + r * kGemvThreads;
+    stage_quarter<BITS>(xs.d[r], t >> 2, t & 3, t < quarters, xp, cx);
+  }
+  // quarters beyond the register rounds (k > 8192): load and stage directly
+  const int rounds = (quarters + kGemvThreads - 1) / kGemvThreads;  // uniform
+  for (int r = kXRounds; r < rounds; ++r) {
+    const int t0 = threadIdx.x + r * kGemvThreads;
+    const int t = t0 < quarters ? t0 : quarters - 1;
+    gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(x + (size_t)(t >> 2) * 64 + (t & 3) * 16);
+    uint32_t d[8];
+    const u32x4 v0 = src[0], v1 = src[1];
+    d[0] = v0.x; d[1] = v0.y; d[2] = v0.z; d[3] = v0.w;
+    d[4] = v1.x; d[5] = v1.y; d[6] = v1.z; d[7] = v1.w;
+    stage_quarter<BITS>(d, t0 >> 2, t0 & 3, t0 < quarters, xp, cx);
   }
 }
 
@@ -143,7 +177,8 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   // step -> (pass, t): incremental counters for the issuing side
   int ip = 0, it = 0;
   auto issue = [&](Buf& bf) {
-    const int g = (wk + it * WK) * LPR + lr;
+    int g = (wk + it * WK) * LPR + lr;
+    g = g < groups ? g : groups - 1;  // only a wave with no k-steps (WK > 1) goes past
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
       int r = lane_row + ip * Cfg::ROWS + u * Cfg::RPW;
@@ -221,9 +256,15 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
     }
   };
 
+  // The first step's loads are issued unconditionally (a load under a
+  // branch makes the compiler wait for every outstanding load at the join),
+  // after the activation loads, so the staging below waits for x only.
   Buf b0, b1;
-  if (nsteps > 0) issue(b0);
-  stage_x<BITS>(to_global(P.x), groups, xp, cx);
+  const gptr<uint16_t> X = to_global(P.x);
+  XStage xs;
+  stage_x_load(X, groups, xs);
+  issue(b0);
+  stage_x_store<BITS>(X, groups, xs, xp, cx);
   __syncthreads();
 
   for (int st = 0; st < nsteps; st += 2) {
