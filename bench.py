@@ -48,12 +48,20 @@ METRIC = "Q4 decode GEMV HBM GB/s (% peak) + prefill qGEMM TFLOP/s (% MFMA peak)
 # HBM traffic of one batched-GEMV launch on the decode workload, from two
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by the same counters
 # on a copy of known size; valid only for the kernel sources it was taken on.
-TRAFFIC = {"sources_sha256": None, "bytes_per_launch": None}
+TRAFFIC = {
+    # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on `bench.py --only decode`
+    # (KiB per dispatch of qgemv_batched_kernel<4,16,4>) and on
+    # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
+    # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
+    "fetch_kib": 166790.0, "fetch_scale": 1073741824 / (524300.0 * 1024),
+    "write_kib": 1939.0, "write_scale": 1073741824 / (1048576.0 * 1024),
+    "sources_sha256": "6c03c63cb1a490e1301b79198ef2ecb010dddaee849dd2fe5a09ff2c0ff5b4ab",
+}
 
 
 def kernel_sources_sha256() -> str:
     h = hashlib.sha256()
-    for f in ("qgemv.hip", "qmm_device.h", "qmm_internal.h"):
+    for f in ("qgemv.hip", "qmm_api.hip", "qmm_device.h", "qmm_internal.h"):
         with open(os.path.join(ROOT, "quantized_matmul_qgemv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -255,8 +263,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["all", "decode"], default="all",
-                    help="decode: only the headline decode workload (for profiling)")
+    ap.add_argument("--only", choices=["all", "decode", "prefill", "moe"], default="all",
+                    help="run one workload only (for profiling); prefill and moe print "
+                         "their own section as the JSON line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration) and exit")
@@ -283,6 +292,15 @@ def main():
                           "launches": 5}))
         return
 
+    if args.only in ("prefill", "moe"):
+        if args.only == "prefill":
+            out = {"workload": synth.QWEN3_4B_Q4_PREFILL.name, "peak_tflops": FP16_MFMA_PEAK_TFLOPS,
+                   "by_m": bench_prefill(torch, qmm, synth.QWEN3_4B_Q4_PREFILL.ms)}
+        else:
+            out = {"workload": synth.QWEN3_30B_A3B_Q4_MOE.name, "by_m": bench_moe(torch, qmm)}
+        print(json.dumps(out), flush=True)
+        return
+
     wl = synth.QWEN3_0_6B_Q4_DECODE
     log("decode: preparing", wl.name)
     d = bench_decode(torch, qmm, wl, args.steps, args.warmup)
@@ -293,7 +311,8 @@ def main():
     log(f"decode: {value:.1f} GB/s")
     traffic = None
     if TRAFFIC["sources_sha256"] == kernel_sources_sha256():
-        traffic = TRAFFIC["bytes_per_launch"]
+        traffic = round(TRAFFIC["fetch_kib"] * 1024 * TRAFFIC["fetch_scale"]
+                        + TRAFFIC["write_kib"] * 1024 * TRAFFIC["write_scale"])
     result = {
         "metric": METRIC,
         "value": round(value, 1),
