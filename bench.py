@@ -145,7 +145,12 @@ def bench_single_gemv(torch, qmm, steps=200, warmup=20):
             "gb_per_s": round(gemv_bytes(n, k, 4) / (ms * 1e-3) / 1e9, 1)}
 
 
-def bench_prefill(torch, qmm, ms, steps=3, warmup=1):
+# Projections of one layer that read the same activations run as one batched
+# launch: q, k and v; o; gate and up; down.
+PREFILL_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+
+
+def bench_prefill(torch, qmm, ms, steps=3, warmup=1, batched=True):
     wl = synth.QWEN3_4B_Q4_PREFILL
     out = {}
     base = {}
@@ -161,16 +166,30 @@ def bench_prefill(torch, qmm, ms, steps=3, warmup=1):
         xs = [torch.from_numpy(synth.draw_act((wl.wid, m, i, synth.STREAM_X), m, p.k)).cuda()
               for i, p in enumerate(wl.projs)]
         ys = [torch.empty((m, p.n), dtype=torch.float32, device="cuda") for p in wl.projs]
+        if batched:
+            names = [p.name for p in wl.projs]
+            plans = [[qmm.qgemm_batched_plan(
+                [(*L[names.index(nm)], xs[names.index(nm)], ys[names.index(nm)]) for nm in grp],
+                wl.bits) for grp in PREFILL_GROUPS] for L in layers]
 
-        def step(_):
-            for L in layers:
-                for i, (words, s, b) in enumerate(L):
-                    qmm.qgemm(words, s, b, xs[i], wl.bits, y=ys[i])
+            def step(_):
+                for lp in plans:
+                    for plan in lp:
+                        qmm.qgemm_batched(plan)
+        else:
+            def step(_):
+                for L in layers:
+                    for i, (words, s, b) in enumerate(L):
+                        qmm.qgemm(words, s, b, xs[i], wl.bits, y=ys[i])
         ms_step, _ = time_launches(torch, step, steps, warmup, stream)
         flops = 2.0 * m * sum(p.n * p.k for p in wl.projs) * wl.layers
         tfl = flops / (ms_step * 1e-3) / 1e12
         out[str(m)] = {"ms_per_step": round(ms_step, 3), "tflops": round(tfl, 1),
                        "frac_of_fp16_peak": round(tfl / FP16_MFMA_PEAK_TFLOPS, 4)}
+        if batched:
+            out[str(m)]["tiles"] = {"+".join(g): "{bm}x{n}/S{splits}".format(n=pl.header["nb"] * 128, **pl.header)
+                                    for g, pl in zip(PREFILL_GROUPS, plans[0])}
+            del plans
         del xs, ys
     del layers, base
     torch.cuda.synchronize()

@@ -135,6 +135,48 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
               const uint16_t* x, float* y, int m, int n, int k, int bits, int group_size,
               void* workspace, size_t workspace_bytes, qmm_stream stream);
 
+/* ---------------------------------------------------- batched prefill GEMM
+ * Several independent y_p = x_p W_hat_p^T (same arithmetic as qmm_qgemm) in
+ * ONE launch: e.g. the q, k and v projections of a layer, or gate and up,
+ * whose tiles together fill the chip where each alone would not (BaseRT
+ * §3.4 tiled prefill GEMM; §3 amortized dispatch).  Two steps, as for the
+ * batched GEMV:
+ *   1. qmm_qgemm_batched_plan (host only, no HIP call): from `count`
+ *      problem descriptors (device pointers, host array) choose one tile
+ *      shape and k-split count for the batch and write the plan image into
+ *      host memory `plan` of `plan_bytes`.  *plan_bytes_needed receives the
+ *      image size and *workspace_bytes_needed the device workspace size
+ *      (0 when k is not split); if plan is NULL or too small the call
+ *      returns QMM_ERR_WORKSPACE without writing the image.  Each problem
+ *      has its own m >= 0, n >= 1 and k (a multiple of 64); all share bits
+ *      and group_size.  A problem with m = 0 is skipped (its x and y may be
+ *      NULL).
+ *   2. Copy the image verbatim to device memory (16-byte aligned), then
+ *      call qmm_qgemm_batched with the device copy, the host image and the
+ *      workspace.
+ * Workspace (contents on entry do not matter): with k split, each split
+ * writes an fp32 partial tile there and a second, short kernel adds the
+ * partials of every tile in split order, so results are identical from run
+ * to run.  Calls that share a workspace must not run concurrently.
+ * Problems must not write overlapping y ranges.  Errors: INVALID_ARG,
+ * UNSUPPORTED, WORKSPACE, HIP. */
+typedef struct {
+  const uint32_t* w;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  const uint16_t* x;
+  float* y;
+  int32_t m;
+  int32_t n;
+  int32_t k;
+} qmm_gemm_problem;
+
+int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits,
+                           int group_size, void* plan, size_t plan_bytes,
+                           size_t* plan_bytes_needed, size_t* workspace_bytes_needed);
+int qmm_qgemm_batched(const void* plan_device, const void* plan_host, void* workspace,
+                      size_t workspace_bytes, qmm_stream stream);
+
 /* --------------------------------------------- mixture-of-experts grouped
  * Pair p = t * top_k + j routes token t to expert e = expert_ids[t, j]:
  *     y[p, n] = sum_k A[row(p), k] * W_hat_e[n, k]

@@ -32,6 +32,12 @@ class GemvProblem(C.Structure):
                 ("x", C.c_void_p), ("y", C.c_void_p), ("n", C.c_int32), ("k", C.c_int32)]
 
 
+class GemmProblem(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("scales", C.c_void_p), ("biases", C.c_void_p),
+                ("x", C.c_void_p), ("y", C.c_void_p), ("m", C.c_int32), ("n", C.c_int32),
+                ("k", C.c_int32)]
+
+
 P, I, SZ = C.c_void_p, C.c_int, C.c_size_t
 
 SIGNATURES = {
@@ -42,6 +48,9 @@ SIGNATURES = {
     "qmm_qgemv_batched": (I, [P, P, P]),
     "qmm_qgemm_workspace_size": (SZ, [I, I, I, I, I]),
     "qmm_qgemm": (I, [P, P, P, P, P, I, I, I, I, I, P, SZ, P]),
+    "qmm_qgemm_batched_plan": (I, [C.POINTER(GemmProblem), I, I, I, P, SZ, C.POINTER(SZ),
+                                   C.POINTER(SZ)]),
+    "qmm_qgemm_batched": (I, [P, P, P, SZ, P]),
     "qmm_qgemm_grouped_workspace_size": (SZ, [I, I, I, I, I, I, I]),
     "qmm_qgemm_grouped": (I, [P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, SZ, P]),
     "qmm_quantize": (I, [P, P, P, P, I, I, I, I, P]),

@@ -16,7 +16,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import GemvProblem, check, lib
+from ._lib import GemmProblem, GemvProblem, check, lib
 
 GROUP = 64
 
@@ -105,6 +105,53 @@ def qgemm(w, scales, biases, x, bits: int, y=None, group_size: int = GROUP, work
                           _dev(x, "x", _X), _dev(y, "y", _Y), m, n, k, bits, group_size,
                           ws_ptr, ws_len, _stream(stream)))
     return y
+
+
+@dataclass
+class GemmBatchPlan:
+    host: C.Array              # host image (header, problems, tile records)
+    device: torch.Tensor       # device copy of the image
+    workspace: torch.Tensor    # split-k partial tiles
+    keep: tuple                # tensors the plan points into
+
+    def __len__(self):
+        return len(self.keep)
+
+    @property
+    def header(self) -> dict:
+        """Tile choice recorded in the image (for logs and tests)."""
+        raw = bytes(self.host)[:48]
+        f = __import__("struct").unpack("<IIiiiiiiiiii", raw)
+        return {"bits": f[2], "bm": f[4], "nb": f[5], "sbq": f[6], "count": f[7],
+                "num_tiles": f[8], "split_tiles": f[9], "splits": f[10]}
+
+
+def qgemm_batched_plan(problems, bits: int, group_size: int = GROUP) -> GemmBatchPlan:
+    """Plan one launch for a list of (w, scales, biases, x, y) GEMM problems."""
+    arr = (GemmProblem * len(problems))()
+    for i, (w, s, b, x, y) in enumerate(problems):
+        arr[i] = GemmProblem(_dev(w, "w", _W), _dev(s, "scales", _SB), _dev(b, "biases", _SB),
+                             _dev(x, "x", _X), _dev(y, "y", _Y), x.shape[0], w.shape[0],
+                             x.shape[1])
+    need, ws = C.c_size_t(0), C.c_size_t(0)
+    st = lib().qmm_qgemm_batched_plan(arr, len(problems), bits, group_size, None, 0,
+                                      C.byref(need), C.byref(ws))
+    if st not in (_lib.QMM_OK, _lib.QMM_ERR_WORKSPACE):
+        check(st)
+    host = (C.c_uint8 * need.value)()
+    check(lib().qmm_qgemm_batched_plan(arr, len(problems), bits, group_size, host, need.value,
+                                       C.byref(need), C.byref(ws)))
+    dev_ = problems[0][0].device
+    device = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(dev_)
+    workspace = torch.empty(max(ws.value, 16), dtype=torch.uint8, device=dev_)
+    return GemmBatchPlan(host=host, device=device, workspace=workspace, keep=tuple(problems))
+
+
+def qgemm_batched(plan: GemmBatchPlan, stream=None) -> None:
+    check(lib().qmm_qgemm_batched(plan.device.data_ptr(), C.addressof(plan.host),
+                                  plan.workspace.data_ptr(),
+                                  plan.workspace.numel() * plan.workspace.element_size(),
+                                  _stream(stream)))
 
 
 def qgemm_grouped_workspace_size(t, top_k, e, n, k, bits, group_size=GROUP) -> int:

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqmm.so")
 
-SOURCES = ("qmm_api.hip", "qgemv.hip", "qgemm.hip", "moe.hip", "quant.hip")
+SOURCES = ("qmm_api.hip", "qgemv.hip", "qgemm.hip", "qgemm_batched.hip", "moe.hip", "quant.hip")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -123,8 +123,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_kernel(GroupedArgs a, co
   const size_t wstride = (size_t)a.n * groups * Fmt<BITS>::WORDS_PER_GROUP;
   const size_t sstride = (size_t)a.n * groups;
   gemm_tile<BITS, BM, NB, SBQ>(ARows{a.a, a.k}, a_row, c_row, a.w + mt.expert * wstride,
-                               a.s + mt.expert * sstride, a.b + mt.expert * sstride, a.y, a.n,
-                               tn * BN, a.n, 0, groups, lds);
+                               a.s + mt.expert * sstride, a.b + mt.expert * sstride, a.y + tn * BN,
+                               a.n, tn * BN, a.n, 0, groups, lds);
 }
 
 template <int BITS, int BM, int NB, bool SBQ>

@@ -18,6 +18,7 @@
 #include <stdlib.h>
 
 #include "qgemm_core.h"
+#include "qgemm_wide.h"
 #include "qmm_internal.h"
 
 namespace qmm {
@@ -49,8 +50,34 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
   float* out = gr.splits == 1 ? a.y : partial + (size_t)split * gr.stride;
   const int g0 = split * gr.gps_split;
   const int g1 = g0 + gr.gps_split;
-  gemm_tile<BITS, BM, NB, SBQ>(ARows{a.x, a.k}, a_row, c_row, a.w, a.s, a.b, out, a.n, n0, a.n,
-                               g0, g1, lds);
+  gemm_tile<BITS, BM, NB, SBQ>(ARows{a.x, a.k}, a_row, c_row, a.w, a.s, a.b, out + n0, a.n, n0,
+                               a.n, g0, g1, lds);
+}
+
+// 256 x 256 tiles, one workgroup per CU (qgemm_wide.h); same tile order as
+// qgemm_kernel.
+template <int BITS, bool SBQ>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1))) void qgemm_wide_kernel(GemmArgs a, GemmGrid gr, float* partial) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kWideLdsHalves];
+  constexpr int BM = kWideBM;
+  constexpr int BN = 256;
+  const int total = gr.n_tiles * gr.m_tiles * gr.splits;
+  int t = blockIdx.x;
+  if (gr.xcd_remap) t = (t % kXcds) * (total / kXcds) + t / kXcds;
+  const int tm = t % gr.m_tiles;
+  const int rest = t / gr.m_tiles;
+  const int split = rest % gr.splits;
+  const int tn = rest / gr.splits;
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+  const int m = a.m;
+  auto a_row = [&](int i) { const int r = m0 + i; return r < m ? r : m - 1; };
+  auto c_row = [&](int i) { const int r = m0 + i; return r < m ? r : -1; };
+  float* out = gr.splits == 1 ? a.y : partial + (size_t)split * gr.stride;
+  const int g0 = split * gr.gps_split;
+  const int g1 = g0 + gr.gps_split;
+  gemm_tile_wide<BITS, SBQ>(ARows{a.x, a.k}, a_row, c_row, a.w, a.s, a.b, out + n0, a.n, n0, a.n,
+                            g0, g1, lds);
 }
 
 // y[i] = sum over splits of partial[split * stride + i], in split order.
@@ -78,34 +105,9 @@ struct GemmPlan {
 static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 static GemmPlan gemm_plan(int m, int n, int k, int bits) {
-  const int groups = k / 64;
+  (void)bits;
   GemmPlan p;
-  p.bm = m <= 32 ? 32 : m <= 64 ? 64 : 128;
-  // column tile: the wide tile unless it leaves too few workgroups
-  const long tiles_wide = (long)ceil_div(n, 256) * ceil_div(m, p.bm);
-  p.nb = tiles_wide >= 256 ? 2 : 1;
-  const long tiles = (long)ceil_div(n, 128 * p.nb) * ceil_div(m, p.bm);
-  // split k when the tiles cannot fill the CUs, as long as every split keeps
-  // at least 8 pipeline steps and the fp32 partials stay within a few times
-  // the weight bytes
-  int splits = 1;
-  const long steps = groups;
-  const double wbytes = (double)n * k * bits / 8;
-  while (tiles * splits * 2 <= 512 && steps % (splits * 2) == 0 && steps / (splits * 2) >= 8 &&
-         (double)(splits * 2) * m * n * 4.0 <= 4.0 * wbytes)
-    splits *= 2;
-  p.splits = splits;
-  // QMM_GEMM_FORCE="bm,nb,splits" overrides the choice (tuning sweeps); it
-  // is ignored unless it is a valid configuration for this shape.
-  if (const char* env = getenv("QMM_GEMM_FORCE")) {
-    int bm = 0, nb = 0, sp = 0;
-    if (sscanf(env, "%d,%d,%d", &bm, &nb, &sp) == 3 && (bm == 32 || bm == 64 || bm == 128) &&
-        (nb == 1 || nb == 2) && sp >= 1 && groups % sp == 0) {
-      p.bm = bm;
-      p.nb = nb;
-      p.splits = sp;
-    }
-  }
+  gemm_choose(m, n, k, &p.bm, &p.nb, &p.splits);
   return p;
 }
 
@@ -135,6 +137,25 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmPlan& p, float* ws, h
   return hipGetLastError();
 }
 
+template <int BITS, bool SBQ>
+static hipError_t launch_wide(const GemmArgs& a, const GemmPlan& p, float* ws, hipStream_t st) {
+  GemmGrid gr;
+  gr.n_tiles = ceil_div(a.n, 256);
+  gr.m_tiles = ceil_div(a.m, kWideBM);
+  gr.splits = p.splits;
+  gr.gps_split = (a.k / 64) / p.splits;
+  const int total = gr.n_tiles * gr.m_tiles * gr.splits;
+  gr.xcd_remap = total % kXcds == 0 ? 1 : 0;
+  gr.stride = partial_stride(a.m, a.n);
+  hipLaunchKernelGGL((qgemm_wide_kernel<BITS, SBQ>), dim3(total), dim3(kGemmThreads), 0, st, a, gr, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  const long count = (long)a.m * a.n;
+  hipLaunchKernelGGL(qgemm_reduce_kernel, dim3(ceil_div(count, 256)), dim3(256), 0, st, ws, a.y,
+                     count, gr.stride, p.splits);
+  return hipGetLastError();
+}
+
 template <int BITS, int BM>
 static hipError_t launch_bm(const GemmArgs& a, const GemmPlan& p, float* ws, hipStream_t st) {
   // quad scale loads need every split to start and end on a multiple of 4 groups
@@ -149,6 +170,9 @@ static hipError_t launch_bits(const GemmArgs& a, const GemmPlan& p, float* ws, h
   switch (p.bm) {
     case 32: return launch_bm<BITS, 32>(a, p, ws, st);
     case 64: return launch_bm<BITS, 64>(a, p, ws, st);
+    case 256:
+      return ((a.k / 64) / p.splits) % 4 == 0 ? launch_wide<BITS, true>(a, p, ws, st)
+                                              : launch_wide<BITS, false>(a, p, ws, st);
     default: return launch_bm<BITS, 128>(a, p, ws, st);
   }
 }

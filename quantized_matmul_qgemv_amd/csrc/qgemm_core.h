@@ -26,7 +26,7 @@
 //     steps ahead (registers, then a double-buffered LDS tile); one barrier
 //     per step.
 //   * The caller chooses the k range, so a tile can be split over k across
-//     workgroups (partial tiles are summed by a separate, ordered pass).
+//     workgroups (partial tiles are summed in split order afterwards).
 #pragma once
 
 #include "qmm_device.h"
@@ -45,16 +45,18 @@ __host__ __device__ constexpr int perm16(int p) {
                    : (((p & 1) << 3) | (p >> 1));
 }
 
-// Permute 16 halves (8 dwords, natural k order) into LDS span order.
+// Permute 16 halves (8 dwords, natural k order) into LDS span order, one
+// v_perm_b32 per output dword.
 template <int BITS>
 __device__ __forceinline__ void permute_span(const uint32_t (&in)[8], uint32_t (&out)[8]) {
 #pragma unroll
   for (int o = 0; o < 8; ++o) {
     const int k0 = perm16<BITS>(2 * o);
     const int k1 = perm16<BITS>(2 * o + 1);
-    const uint32_t lo = (in[k0 >> 1] >> (16 * (k0 & 1))) & 0xFFFFu;
-    const uint32_t hi = (in[k1 >> 1] >> (16 * (k1 & 1))) & 0xFFFFu;
-    out[o] = lo | (hi << 16);
+    // selector bytes 0..3 pick from the second source, 4..7 from the first
+    const uint32_t lo = (k0 & 1) ? 0x0302u : 0x0100u;
+    const uint32_t hi = (k1 & 1) ? 0x07060000u : 0x05040000u;
+    out[o] = __builtin_amdgcn_perm(in[k1 >> 1], in[k0 >> 1], lo | hi);
   }
 }
 
@@ -123,7 +125,9 @@ struct ARows {
 
 // One BM x BN output tile over the k groups [g_begin, g_end).  a_row(i)
 // gives the source row of tile row i (already clamped to a valid row);
-// c_row(i) gives the output row or -1 to skip; columns are bounded by n.
+// c_row(i) gives the output row or -1 to skip.  Weight columns start at n0
+// and are bounded by n; output column n0 + c goes to y_tile[row * ldy + c]
+// (y_tile points at the tile's first column).
 //
 // Software pipeline, one 64-code group per step (i = step index):
 //   * packed B (weights) is loaded 3 steps ahead into a ring of 4 register
@@ -140,7 +144,7 @@ template <int BITS, int BM, int NB, bool SBQ, typename ARowFn, typename CRowFn>
 __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_row,
                                           const uint32_t* __restrict__ w_,
                                           const uint16_t* __restrict__ s_,
-                                          const uint16_t* __restrict__ b_, float* __restrict__ y_,
+                                          const uint16_t* __restrict__ b_, float* __restrict__ y_tile,
                                           int ldy, int n0, int n, int g_begin, int g_end,
                                           uint16_t* lds) {
   constexpr int MB = BM / 32;
@@ -150,7 +154,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   const gptr<uint32_t> w = to_global(w_);
   const gptr<uint16_t> s = to_global(s_);
   const gptr<uint16_t> b = to_global(b_);
-  const gptr_mut<float> y = to_global_mut(y_);
+  const gptr_mut<float> y = to_global_mut(y_tile);
   const gptr<uint16_t> abase = to_global(A.base);
   const int groups = A.k >> 6;
   const int tid = threadIdx.x;
@@ -337,12 +341,12 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = n0 + (wave * NB + nb) * 32 + l32;
+      const int lc = (wave * NB + nb) * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = mb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
         const int row = c_row(i);
-        if (row >= 0 && col < n) y[(size_t)row * ldy + col] = acc[mb][nb][r];
+        if (row >= 0 && n0 + lc < n) y[(size_t)row * ldy + lc] = acc[mb][nb][r];
       }
     }
   }

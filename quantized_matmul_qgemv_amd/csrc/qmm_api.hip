@@ -217,6 +217,83 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
   return hip_status(qmm::launch_qgemm(a, bits, workspace, (hipStream_t)stream), fn);
 }
 
+int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits,
+                           int group_size, void* plan, size_t plan_bytes,
+                           size_t* plan_bytes_needed, size_t* workspace_bytes_needed) {
+  const char* fn = "qmm_qgemm_batched_plan";
+  clear_error();
+  if (int st = check_format(fn, bits, group_size)) return st;
+  if (count < 1) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d must be >= 1", fn, count);
+  if (count > (1 << 20)) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d too large", fn, count);
+  if (problems == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: null problems", fn);
+  qmm::GemmBatchProblem* probs = static_cast<qmm::GemmBatchProblem*>(
+      calloc((size_t)count, sizeof(qmm::GemmBatchProblem)));
+  if (probs == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: out of host memory", fn);
+  for (int i = 0; i < count; ++i) {
+    const qmm_gemm_problem& q = problems[i];
+    int bad = 0;
+    // an empty problem (m = 0) is never read or written: x and y may be null
+    if (q.m < 0 || check_nk(fn, q.n, q.k)) bad = 1;
+    else if (!q.w || !q.scales || !q.biases || (q.m > 0 && (!q.x || !q.y))) bad = 2;
+    else if (!aligned(q.w, 16) || !aligned(q.x, 16) || !aligned(q.y, 4) ||
+             !aligned(q.scales, 2) || !aligned(q.biases, 2)) bad = 3;
+    if (bad) {
+      free(probs);
+      return fail(QMM_ERR_INVALID_ARG, "%s: problem %d: %s", fn, i,
+                  bad == 1 ? "bad m, n or k" : bad == 2 ? "null pointer" : "misaligned pointer");
+    }
+    probs[i].w = q.w;
+    probs[i].s = q.scales;
+    probs[i].b = q.biases;
+    probs[i].x = q.x;
+    probs[i].y = q.y;
+    probs[i].m = q.m;
+    probs[i].n = q.n;
+    probs[i].k = q.k;
+  }
+  const size_t need = qmm::gemm_batch_build(probs, count, bits, nullptr, 0);
+  if (plan_bytes_needed) *plan_bytes_needed = need;
+  if (plan == nullptr || plan_bytes < need) {
+    free(probs);
+    return fail(QMM_ERR_WORKSPACE, "%s: plan buffer of %zu bytes, %zu needed", fn, plan_bytes, need);
+  }
+  if (!aligned(plan, 8)) {
+    free(probs);
+    return fail(QMM_ERR_INVALID_ARG, "%s: plan is not 8-byte aligned", fn);
+  }
+  qmm::gemm_batch_build(probs, count, bits, plan, plan_bytes);
+  free(probs);
+  qmm::GemmBatchHeader hdr;
+  memcpy(&hdr, plan, sizeof hdr);
+  if (workspace_bytes_needed) *workspace_bytes_needed = (size_t)hdr.workspace_bytes;
+  return QMM_OK;
+}
+
+int qmm_qgemm_batched(const void* plan_device, const void* plan_host, void* workspace,
+                      size_t workspace_bytes, qmm_stream stream) {
+  const char* fn = "qmm_qgemm_batched";
+  clear_error();
+  if (plan_host == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: null plan_host", fn);
+  CHECK_PTR(plan_device, 16);
+  qmm::GemmBatchHeader hdr;
+  memcpy(&hdr, plan_host, sizeof hdr);
+  if (hdr.magic != qmm::kBatchMagic || hdr.version != qmm::kBatchVersion)
+    return fail(QMM_ERR_INVALID_ARG, "%s: plan_host is not a batched-GEMM plan image", fn);
+  if (int st = check_format(fn, hdr.bits, hdr.group_size)) return st;
+  if (hdr.count < 1 || hdr.num_tiles < 0 || hdr.splits < 1 ||
+      !(hdr.bm == 32 || hdr.bm == 64 || hdr.bm == 128 || hdr.bm == 256) ||
+      !(hdr.nb == 1 || hdr.nb == 2) || (hdr.bm == 256 && hdr.nb != 2))
+    return fail(QMM_ERR_INVALID_ARG, "%s: corrupt plan header", fn);
+  if (hdr.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < hdr.workspace_bytes)
+      return fail(QMM_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                  (size_t)hdr.workspace_bytes);
+    CHECK_PTR(workspace, 16);
+  }
+  if (hdr.num_tiles == 0) return QMM_OK;
+  return hip_status(qmm::launch_qgemm_batched(plan_device, hdr, workspace, (hipStream_t)stream), fn);
+}
+
 size_t qmm_qgemm_grouped_workspace_size(int t, int top_k, int e, int n, int k, int bits,
                                         int group_size) {
   (void)k; (void)bits; (void)group_size;

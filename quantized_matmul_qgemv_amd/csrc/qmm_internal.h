@@ -75,6 +75,66 @@ struct GemmArgs {
 size_t gemm_workspace_bytes(int m, int n, int k, int bits);
 hipError_t launch_qgemm(const GemmArgs& a, int bits, void* workspace, hipStream_t st);
 
+// Batched GEMM plan image: header, problem table, tile records.
+struct alignas(64) GemmBatchProblem {
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  const uint16_t* x;
+  float* y;
+  int32_t m, n, k;
+  int32_t pad[3];
+};
+static_assert(sizeof(GemmBatchProblem) == 64, "GemmBatchProblem must stay 64 bytes");
+
+// One workgroup: output tile (m0, n0) of a problem, groups [g0, g1).  With
+// splits > 1 the tile's fp32 partial goes to workspace slot
+// sid * splits + split (bm x bn floats, row-major); a reduce kernel sums the
+// slots of each split tile in split order into y.  problem < 0: no work.
+struct GemmTileRec {
+  int32_t problem;
+  int32_t m0, n0;
+  int32_t g0, g1;
+  int32_t split, splits;
+  int32_t sid;
+};
+static_assert(sizeof(GemmTileRec) == 32, "GemmTileRec must stay 32 bytes");
+
+// Split tile sid: where its sum goes.
+struct GemmSplitTile {
+  int32_t problem, m0, n0, pad;
+};
+
+struct alignas(64) GemmBatchHeader {
+  uint32_t magic;        // 'QMMB'
+  uint32_t version;
+  int32_t bits;
+  int32_t group_size;
+  int32_t bm, nb;        // tile: bm rows x (nb * 128) columns
+  int32_t sbq;           // every k range is a multiple of 4 groups
+  int32_t count;         // problems
+  int32_t num_tiles;     // tile records (grid size)
+  int32_t split_tiles;   // tiles whose k is split (GemmSplitTile records after the tiles)
+  int32_t splits;
+  int32_t pad0;
+  uint64_t workspace_bytes;
+  uint64_t pad1;
+};
+static_assert(sizeof(GemmBatchHeader) == 64, "GemmBatchHeader must stay 64 bytes");
+constexpr uint32_t kBatchMagic = 0x424D4D51u;  // "QMMB"
+constexpr uint32_t kBatchVersion = 1;
+
+// Tile and split count for one GEMM (k split evenly), from the batch planner's
+// cost model; honours QMM_GEMM_FORCE.
+void gemm_choose(int m, int n, int k, int* bm, int* nb, int* splits);
+
+// Choose the tile and split count for a batch and write the plan image.
+// Returns the image size; writes nothing when out is null or too small.
+size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, void* out,
+                        size_t out_bytes);
+hipError_t launch_qgemm_batched(const void* plan_device, const GemmBatchHeader& hdr,
+                                void* workspace, hipStream_t st);
+
 struct GroupedArgs {
   const uint32_t* w;
   const uint16_t* s;

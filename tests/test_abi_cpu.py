@@ -8,7 +8,7 @@ import re
 import pytest
 
 from quantized_matmul_qgemv_amd import _lib
-from quantized_matmul_qgemv_amd._lib import GemvProblem
+from quantized_matmul_qgemv_amd._lib import GemmProblem, GemvProblem
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qmm.h")
 
@@ -133,3 +133,117 @@ def test_batched_plan_host_only(L):
     expect(L.qmm_qgemv_batched_plan(probs, 3, 4, 64, buf, need.value, C.byref(need)), INV, "problem 1")
     probs[1] = GemvProblem(A, A, A, MIS, A, 1024, 3072)
     expect(L.qmm_qgemv_batched_plan(probs, 3, 4, 64, buf, need.value, C.byref(need)), INV, "misaligned")
+
+
+def gemm_batch_plan(L, shapes, bits=4, env=None):
+    """Build a batched-GEMM plan on the host for (m, n, k) shapes; decode it."""
+    import struct
+    old = os.environ.pop("QMM_GEMM_FORCE", None)
+    if env:
+        os.environ["QMM_GEMM_FORCE"] = env
+    try:
+        probs = (GemmProblem * len(shapes))()
+        for i, (m, n, k) in enumerate(shapes):
+            probs[i] = GemmProblem(A * (i + 1), A, A, A, A * (i + 1) + 0x1000, m, n, k)
+        need, ws = C.c_size_t(0), C.c_size_t(0)
+        expect(L.qmm_qgemm_batched_plan(probs, len(shapes), bits, 64, None, 0, C.byref(need),
+                                        C.byref(ws)), WSP, "plan buffer")
+        buf = (C.c_uint8 * need.value)()
+        assert L.qmm_qgemm_batched_plan(probs, len(shapes), bits, 64, buf, need.value,
+                                        C.byref(need), C.byref(ws)) == 0
+    finally:
+        os.environ.pop("QMM_GEMM_FORCE", None)
+        if old is not None:
+            os.environ["QMM_GEMM_FORCE"] = old
+    raw = bytes(buf)
+    f = struct.unpack_from("<IIiiiiiiiiiiQ", raw, 0)
+    hdr = dict(zip(["magic", "version", "bits", "gs", "bm", "nb", "sbq", "count", "num_tiles",
+                    "split_tiles", "splits", "pad", "ws"], f))
+    off = 64 + 64 * len(shapes)
+    recs = [struct.unpack_from("<8i", raw, off + 32 * i) for i in range(hdr["num_tiles"])]
+    off2 = off + 32 * hdr["num_tiles"]
+    hdr["split_recs"] = [struct.unpack_from("<4i", raw, off2 + 16 * i)[:3] for i in range(hdr["split_tiles"])]
+    assert need.value == off2 + 16 * hdr["split_tiles"] and ws.value == hdr["ws"]
+    return hdr, recs
+
+
+@pytest.mark.parametrize("shapes", [
+    [(2048, 4096, 2560), (2048, 1024, 2560), (2048, 1024, 2560)],   # q, k, v
+    [(2048, 9728, 2560), (2048, 9728, 2560)],                         # gate, up
+    [(128, 2560, 9728)],                                              # down at M=128
+    [(128, 4096, 2560), (128, 1024, 2560), (128, 1024, 2560)],
+    [(70, 520, 1024), (1, 64, 64), (0, 128, 128), (300, 200, 192)],   # ragged, m=0, k=3 groups
+])
+def test_batched_gemm_plan_covers_every_tile(L, shapes):
+    hdr, recs = gemm_batch_plan(L, shapes)
+    assert hdr["magic"] == 0x424D4D51 and hdr["count"] == len(shapes)
+    bm, bn, S = hdr["bm"], hdr["nb"] * 128, hdr["splits"]
+    assert bm in (32, 64, 128, 256) and hdr["num_tiles"] % 8 == 0
+    live = [r for r in recs if r[0] >= 0]
+    tiles = {}
+    for p, m0, n0, g0, g1, sp, sps, sid in live:
+        assert sps == S and 0 <= sp < S and g0 < g1
+        if hdr["sbq"]:
+            assert g0 % 4 == 0 and g1 % 4 == 0
+        tiles.setdefault((p, m0, n0), []).append((sp, g0, g1, sid))
+    want = 0
+    sids = set()
+    for p, (m, n, k) in enumerate(shapes):
+        G = k // 64
+        for m0 in range(0, m, bm):
+            for n0 in range(0, n, bn):
+                want += 1
+                parts = sorted(tiles.pop((p, m0, n0)))
+                assert [x[0] for x in parts] == list(range(S))
+                assert parts[0][1] == 0 and parts[-1][2] == G
+                assert all(a[2] == b[1] for a, b in zip(parts, parts[1:]))
+                assert len({x[3] for x in parts}) == 1
+                sids.add(parts[0][3])
+                if S > 1:
+                    assert hdr["split_recs"][parts[0][3]] == (p, m0, n0)
+    assert not tiles, "records outside the problems"
+    assert len(live) == want * S
+    if S > 1:
+        assert sids == set(range(hdr["split_tiles"])) and hdr["split_tiles"] == want
+        assert hdr["ws"] == hdr["split_tiles"] * S * bm * bn * 4
+    else:
+        assert hdr["ws"] == 0
+
+
+def test_batched_gemm_plan_force_and_errors(L):
+    hdr, _ = gemm_batch_plan(L, [(2048, 2560, 9728)], env="256,2,4")
+    assert (hdr["bm"], hdr["nb"], hdr["splits"], hdr["sbq"]) == (256, 2, 4, 1)
+    hdr, _ = gemm_batch_plan(L, [(64, 512, 192)], env="64,1,3")
+    assert (hdr["bm"], hdr["splits"], hdr["sbq"]) == (64, 3, 0)
+    probs = (GemmProblem * 2)()
+    probs[0] = GemmProblem(A, A, A, A, A, 64, 128, 128)
+    probs[1] = GemmProblem(A, A, A, A, A, 64, 128, 100)
+    need, ws = C.c_size_t(0), C.c_size_t(0)
+    expect(L.qmm_qgemm_batched_plan(probs, 2, 4, 64, None, 0, C.byref(need), C.byref(ws)), INV,
+           "problem 1")
+    probs[1] = GemmProblem(A, A, A, MIS, A, 64, 128, 128)
+    expect(L.qmm_qgemm_batched_plan(probs, 2, 4, 64, None, 0, C.byref(need), C.byref(ws)), INV,
+           "misaligned")
+    probs[1] = GemmProblem(A, A, A, A, A, -1, 128, 128)
+    expect(L.qmm_qgemm_batched_plan(probs, 2, 4, 64, None, 0, C.byref(need), C.byref(ws)), INV,
+           "problem 1")
+    expect(L.qmm_qgemm_batched_plan(probs, 0, 4, 64, None, 0, C.byref(need), C.byref(ws)), INV,
+           "count=0")
+    expect(L.qmm_qgemm_batched_plan(probs, 2, 3, 64, None, 0, C.byref(need), C.byref(ws)), UNS,
+           "bits=3")
+    bad = (C.c_uint8 * 64)()
+    expect(L.qmm_qgemm_batched(A, bad, None, 0, None), INV, "not a batched-GEMM plan")
+    # a split plan refuses a missing or short workspace before any launch
+    probs1 = (GemmProblem * 1)()
+    probs1[0] = GemmProblem(A, A, A, A, A, 64, 512, 4096)
+    os.environ["QMM_GEMM_FORCE"] = "64,1,4"
+    try:
+        assert L.qmm_qgemm_batched_plan(probs1, 1, 4, 64, None, 0, C.byref(need), C.byref(ws)) == WSP
+        buf = (C.c_uint8 * need.value)()
+        assert L.qmm_qgemm_batched_plan(probs1, 1, 4, 64, buf, need.value, C.byref(need),
+                                        C.byref(ws)) == 0
+    finally:
+        os.environ.pop("QMM_GEMM_FORCE", None)
+    assert ws.value > 0
+    expect(L.qmm_qgemm_batched(A, buf, None, 0, None), WSP, "workspace")
+    expect(L.qmm_qgemm_batched(A, buf, A, ws.value - 1, None), WSP, "workspace")

@@ -180,7 +180,7 @@ def test_gemm_parity(bits, m, n, k):
 
 def test_gemm_split_k_workspace_and_determinism():
     say("gemm split-k")
-    m, n, k, bits = 64, 2048, 4096, 4
+    m, n, k, bits = 16, 2048, 8192, 4
     need = qmm.qgemm_workspace_size(m, n, k, bits)
     assert need >= 2 * m * n * 4, "this shape is expected to split k"
     _, _, words, s, b = quantized((911, 0, 0, 0), n, k, bits)
@@ -193,6 +193,61 @@ def test_gemm_split_k_workspace_and_determinism():
     assert_close(host(y1), oracle.qmatmul_f64(words, s, b, x, bits), "split-k")
     with pytest.raises(qmm.QmmError):
         qmm.qgemm(W, S, B, X, bits, workspace=ws[: need - 1])
+
+
+# ---------------------------------------------------------- batched GEMM --
+
+BATCH_SHAPES = [(70, 520, 1024), (33, 256, 256), (300, 200, 192), (1, 64, 64), (0, 128, 128),
+                (257, 384, 512)]
+BATCH_CFGS = [(256, 2), (128, 2), (128, 1), (64, 2), (64, 1), (32, 2), (32, 1)]
+
+
+def _batch_inputs(bits, shapes, seed):
+    ins, wants = [], []
+    for i, (m, n, k) in enumerate(shapes):
+        _, _, words, s, b = quantized((seed, bits, i, 0), n, k, bits)
+        x = synth.draw_act((seed, bits, i, 1), m, k)
+        wants.append(oracle.qmatmul_f64(words, s, b, x, bits) if m else np.zeros((0, n)))
+        y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+        ins.append((dev(words), dev(s), dev(b), dev(x) if m else torch.zeros((0, k), dtype=torch.float16, device="cuda"), y))
+    return ins, wants
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_gemm_batched_parity(bits):
+    say("gemm batched", bits)
+    ins, wants = _batch_inputs(bits, BATCH_SHAPES, 921)
+    plan = qmm.qgemm_batched_plan(ins, bits)
+    qmm.qgemm_batched(plan)
+    for (m, n, k), t, want in zip(BATCH_SHAPES, ins, wants):
+        assert_close(host(t[4]), want, f"batched bits={bits} m={m} n={n} k={k} {plan.header}")
+
+
+@pytest.mark.parametrize("bm,nb", BATCH_CFGS)
+@pytest.mark.parametrize("splits", [1, 3])
+def test_gemm_batched_forced_tiles_and_split_k(bm, nb, splits, monkeypatch):
+    """Every tile shape, with and without k split: parity and identical
+    results on a second call over a dirtied workspace."""
+    bits = 4
+    say("gemm batched forced", bm, nb, splits)
+    shapes = [(70, 520, 1024), (300, 200, 768), (1, 64, 256)]
+    ins, wants = _batch_inputs(bits, shapes, 922)
+    monkeypatch.setenv("QMM_GEMM_FORCE", f"{bm},{nb},{splits}")
+    plan = qmm.qgemm_batched_plan(ins, bits)
+    monkeypatch.delenv("QMM_GEMM_FORCE")
+    h = plan.header
+    assert (h["bm"], h["nb"], h["splits"]) == (bm, nb, splits), h
+    qmm.qgemm_batched(plan)
+    first = [t[4].clone() for t in ins]
+    for (m, n, k), y, want in zip(shapes, first, wants):
+        assert_close(host(y), want, f"forced {bm}x{nb} S={splits} m={m} n={n} k={k}")
+    for t in ins:
+        t[4].fill_(float("nan"))
+    plan.workspace.fill_(0xAB)
+    qmm.qgemm_batched(plan)
+    torch.cuda.synchronize()
+    for y0, t in zip(first, ins):
+        assert torch.equal(y0, t[4])
 
 
 def test_gemm_rows_equal_gemv_and_deterministic():
