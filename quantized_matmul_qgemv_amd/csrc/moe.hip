@@ -4,9 +4,10 @@
 // by one tile schedule per expert:
 //
 //   1. bucket (one workgroup, all in LDS): histogram of expert ids,
-//      exclusive scans of the per-expert pair counts and of the per-expert
-//      row-tile counts, scatter of pair indices into per-expert buckets,
-//      and a flat list of row tiles {expert, first bucket slot, rows}.
+//      exclusive scans (wave shuffles, then across waves) of the per-expert
+//      pair counts and of the per-expert row-tile counts, scatter of pair
+//      indices into per-expert buckets, and a flat list of row tiles
+//      {expert, first bucket slot, rows}.
 //   2. grouped GEMM: the grid is an upper bound on (row tiles) x (column
 //      tiles); each workgroup reads its row tile from the list (extra
 //      workgroups exit at once), gathers its A rows through the bucket,
@@ -17,6 +18,9 @@
 // output row is computed on its own (the matrix-core accumulation order
 // over k does not depend on the other rows of the tile), so results are
 // bit-identical from run to run.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "qgemm_core.h"
 #include "qmm_internal.h"
 
@@ -46,50 +50,86 @@ size_t grouped_workspace_bytes(int t, int top_k, int e, int n) {
   return align_up((size_t)(4 + pairs + 3 * tiles) * sizeof(int32_t), 256);
 }
 
+// Inclusive sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Ids held in registers per thread (pairs beyond 16 * 1024 are read twice).
+constexpr int kBucketIdsPerThread = 16;
+
 __global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
     const int32_t* __restrict__ ids, int pairs, int experts, int bm, int32_t* __restrict__ ws) {
+  static_assert(kBucketThreads == kMaxExperts, "one thread per expert slot");
+  constexpr int kWaves = kBucketThreads / 64;
   __shared__ int32_t cnt[kMaxExperts];
-  __shared__ int32_t off[kMaxExperts];
-  __shared__ int32_t toff[kMaxExperts];
   __shared__ int32_t cursor[kMaxExperts];
+  __shared__ int32_t wtot[2][kWaves];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   int32_t* num_tiles = ws;
   int32_t* sorted = ws + 4;
   MoeTile* tiles = reinterpret_cast<MoeTile*>(ws + 4 + pairs);
 
-  for (int e = tid; e < kMaxExperts; e += kBucketThreads) cnt[e] = 0;
+  cnt[tid] = 0;
+  int myid[kBucketIdsPerThread];
+#pragma unroll
+  for (int i = 0; i < kBucketIdsPerThread; ++i) {
+    const int p = tid + i * kBucketThreads;
+    const int e = p < pairs ? ids[p] : -1;
+    myid[i] = (e >= 0 && e < experts) ? e : -1;
+  }
   __syncthreads();
-  for (int p = tid; p < pairs; p += kBucketThreads) {
+  // histogram of expert ids (invalid ids are skipped)
+#pragma unroll
+  for (int i = 0; i < kBucketIdsPerThread; ++i)
+    if (myid[i] >= 0) atomicAdd(&cnt[myid[i]], 1);
+  for (int p = tid + kBucketIdsPerThread * kBucketThreads; p < pairs; p += kBucketThreads) {
     const int e = ids[p];
     if (e >= 0 && e < experts) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  // inclusive Hillis-Steele scans of counts and of row-tile counts
-  int c = tid < experts ? cnt[tid] : 0;
-  int tl = (c + bm - 1) / bm;
-  off[tid] = c;
-  toff[tid] = tl;
-  __syncthreads();
-  for (int d = 1; d < kBucketThreads; d <<= 1) {
-    const int a = tid >= d ? off[tid - d] : 0;
-    const int b = tid >= d ? toff[tid - d] : 0;
-    __syncthreads();
-    off[tid] += a;
-    toff[tid] += b;
-    __syncthreads();
+  // exclusive scans of the pair counts and of the row-tile counts:
+  // within each wave by lane shuffles, then over the 16 wave totals
+  const int c = tid < experts ? cnt[tid] : 0;
+  const int tl = (c + bm - 1) / bm;
+  const int ic = wave_inclusive_sum(c);
+  const int it = wave_inclusive_sum(tl);
+  if (lane == 63) {
+    wtot[0][wave] = ic;
+    wtot[1][wave] = it;
   }
-  const int start = off[tid] - c;     // exclusive
-  const int tstart = toff[tid] - tl;
   __syncthreads();
-  cursor[tid] = start;
-  if (tid == kBucketThreads - 1) num_tiles[0] = toff[tid];
-  __syncthreads();
-  for (int p = tid; p < pairs; p += kBucketThreads) {
-    const int e = ids[p];
-    if (e >= 0 && e < experts) {
-      const int slot = atomicAdd(&cursor[e], 1);
-      sorted[slot] = p;
+  if (wave == 0) {
+    const int a0 = lane < kWaves ? wtot[0][lane] : 0;
+    const int a1 = lane < kWaves ? wtot[1][lane] : 0;
+    const int s0 = wave_inclusive_sum(a0);
+    const int s1 = wave_inclusive_sum(a1);
+    if (lane < kWaves) {
+      wtot[0][lane] = s0 - a0;  // exclusive prefix of the wave totals
+      wtot[1][lane] = s1 - a1;
     }
+    if (lane == kWaves - 1) num_tiles[0] = s1;
+  }
+  __syncthreads();
+  const int start = wtot[0][wave] + ic - c;
+  const int tstart = wtot[1][wave] + it - tl;
+  cursor[tid] = start;
+  __syncthreads();
+  // scatter pair indices into their expert's bucket
+#pragma unroll
+  for (int i = 0; i < kBucketIdsPerThread; ++i)
+    if (myid[i] >= 0) sorted[atomicAdd(&cursor[myid[i]], 1)] = tid + i * kBucketThreads;
+  for (int p = tid + kBucketIdsPerThread * kBucketThreads; p < pairs; p += kBucketThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < experts) sorted[atomicAdd(&cursor[e], 1)] = p;
   }
   if (tid < experts) {
     for (int i = 0; i < tl; ++i) {
@@ -144,12 +184,23 @@ static hipError_t launch_grouped_tile(const GroupedArgs& a, int32_t* ws, hipStre
 
 template <int BITS, bool SBQ>
 static hipError_t launch_grouped_sbq(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
-  // Row tile from the mean number of pairs per expert: one tile per expert
-  // keeps each expert's weights to a single pass over HBM.
+  // Row tile from the mean number of pairs per expert (one row tile per
+  // expert keeps each expert's weights to a single pass over HBM); 128-wide
+  // column tiles double the workgroups per expert, which measured faster on
+  // the Qwen3-30B-A3B-shaped layers at 512 and 2048 tokens.
   const int mean = (a.t * a.top_k + a.e - 1) / a.e;
-  if (mean <= 16) return launch_grouped_tile<BITS, 32, 2, SBQ>(a, ws, st);
-  if (mean <= 48) return launch_grouped_tile<BITS, 64, 2, SBQ>(a, ws, st);
-  return launch_grouped_tile<BITS, 128, 2, SBQ>(a, ws, st);
+  int bm = mean <= 16 ? 32 : mean <= 48 ? 64 : 128, nb = 1;
+  // QMM_MOE_FORCE="bm,nb" overrides the tile (tuning sweeps).
+  if (const char* env = getenv("QMM_MOE_FORCE")) {
+    int fb = 0, fn = 0;
+    if (sscanf(env, "%d,%d", &fb, &fn) == 2 && (fb == 32 || fb == 64 || fb == 128) && (fn == 1 || fn == 2)) {
+      bm = fb;
+      nb = fn;
+    }
+  }
+  if (bm == 32) return nb == 2 ? launch_grouped_tile<BITS, 32, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 32, 1, SBQ>(a, ws, st);
+  if (bm == 64) return nb == 2 ? launch_grouped_tile<BITS, 64, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 64, 1, SBQ>(a, ws, st);
+  return nb == 2 ? launch_grouped_tile<BITS, 128, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 128, 1, SBQ>(a, ws, st);
 }
 
 template <int BITS>
