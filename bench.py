@@ -53,9 +53,9 @@ TRAFFIC = {
     # (KiB per dispatch of qgemv_batched_kernel<4,16,4>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 166790.0, "fetch_scale": 1073741824 / (524300.0 * 1024),
+    "fetch_kib": 166787.5, "fetch_scale": 1073741824 / (524300.0 * 1024),
     "write_kib": 1939.0, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "6c03c63cb1a490e1301b79198ef2ecb010dddaee849dd2fe5a09ff2c0ff5b4ab",
+    "sources_sha256": "32f55790dd41e64a48a6d4a8446474a50898d7228b4a81cdf93f435842d107f8",
 }
 
 
