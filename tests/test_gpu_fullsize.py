@@ -56,19 +56,36 @@ def test_decode_sweep_batched_sampled(wl):
 
 @pytest.mark.parametrize("m", synth.QWEN3_4B_Q4_PREFILL.ms)
 def test_prefill_layer_sampled(m):
+    """One layer as bench.py runs it (q+k+v, o, gate+up, down as four batched
+    launches with the planner's tiles and splits), and every projection
+    again through the single-GEMM entry point."""
     wl = synth.QWEN3_4B_Q4_PREFILL
+    names = [p.name for p in wl.projs]
+    wfs, dev_w, xs, ys = [], [], [], []
     for i, p in enumerate(wl.projs):
-        say("full prefill", m, p.name)
         wf = synth.draw_weight((wl.wid, 0, i, synth.STREAM_W), p.n, p.k)
-        words_d, s_d, b_d = qmm.quantize(torch.from_numpy(wf).cuda(), wl.bits)
-        x = synth.draw_act((wl.wid, m, i, synth.STREAM_X), m, p.k)
-        y = qmm.qgemm(words_d, s_d, b_d, torch.from_numpy(x).cuda(), wl.bits)
+        wfs.append(wf)
+        dev_w.append(qmm.quantize(torch.from_numpy(wf).cuda(), wl.bits))
+        xs.append(synth.draw_act((wl.wid, m, i, synth.STREAM_X), m, p.k))
+        ys.append(torch.full((m, p.n), float("nan"), dtype=torch.float32, device="cuda"))
+    xd = [torch.from_numpy(x).cuda() for x in xs]
+    for grp in bench.PREFILL_GROUPS:
+        say("full prefill batched", m, "+".join(grp))
+        plan = qmm.qgemm_batched_plan(
+            [(*dev_w[names.index(nm)], xd[names.index(nm)], ys[names.index(nm)]) for nm in grp], wl.bits)
+        qmm.qgemm_batched(plan)
+    torch.cuda.synchronize()
+    for i, p in enumerate(wl.projs):
+        say("full prefill single", m, p.name)
+        y1 = qmm.qgemm(*dev_w[i], xd[i], wl.bits)
         torch.cuda.synchronize()
         cols = sample_rows(p.n, 32, 7 * m + i)
         rows = sample_rows(m, 32, 11 * m + i)
-        codes, s, b = oracle.quantize(wf[cols], wl.bits)
-        want = oracle.qmatmul_f64(oracle.pack(codes, wl.bits), s, b, x[rows], wl.bits)
-        assert_close(host(y)[np.ix_(rows, cols)], want, f"prefill m={m} {p.name}")
+        codes, s, b = oracle.quantize(wfs[i][cols], wl.bits)
+        want = oracle.qmatmul_f64(oracle.pack(codes, wl.bits), s, b, xs[i][rows], wl.bits)
+        assert_close(host(ys[i])[np.ix_(rows, cols)], want, f"prefill batched m={m} {p.name}")
+        assert_close(host(y1)[np.ix_(rows, cols)], want, f"prefill single m={m} {p.name}")
+        assert not torch.isnan(ys[i]).any(), f"prefill batched m={m} {p.name}: unwritten outputs"
 
 
 @pytest.mark.parametrize("m", synth.QWEN3_30B_A3B_Q4_MOE.ms)
