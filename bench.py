@@ -11,11 +11,14 @@ full copies of the weights alternate between steps, so a step never finds
 its weights in the 256 MB last-level cache.
 
 The same JSON line carries, measured in the same run:
-  roofline      the batched GEMV kernel against the 8 TB/s HBM peak, from
-                HIP events around each launch on the launch stream;
+  roofline      the batched GEMV kernel against the 8 TB/s HBM peak: the
+                timed region between two HIP events on the launch stream,
+                divided by the launches in it (one per step), plus the HBM
+                traffic rocprofv3 counted for the same kernel;
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same
                 workload, on this host's cores;
-  prefill       Qwen3-4B-shaped 4-bit GEMMs (36 layers x 7 projections) at
+  prefill       Qwen3-4B-shaped 4-bit GEMMs (36 layers x 7 projections, run
+                as 4 batched launches per layer: q+k+v, o, gate+up, down) at
                 M = 128 ... 2048, TFLOP/s against the fp16 matrix-core peak;
   moe           Qwen3-30B-A3B-shaped grouped GEMMs (128 experts, top-8) at
                 M = 512 and 2048 tokens, against their HBM roofline;
