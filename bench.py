@@ -22,6 +22,8 @@ The same JSON line carries, measured in the same run:
                 M = 128 ... 2048, TFLOP/s against the fp16 matrix-core peak;
   moe           Qwen3-30B-A3B-shaped grouped GEMMs (128 experts, top-8) at
                 M = 512 and 2048 tokens, against their HBM roofline;
+  decode_context the lm_head alone, the decode pass as 197 sequential launches
+                replayed as one HIP graph, and that graph's per-launch floor;
   decode_q8     the Llama-3.2-3B-shaped 8-bit decode sweep (196 GEMVs);
   single_gemv   one 1x1024x1024 4-bit GEMV launch (latency).
 Inputs are seeded synthetic tensors with the models' shapes (weights
@@ -146,6 +148,57 @@ def bench_single_gemv(torch, qmm, steps=200, warmup=20):
         torch, lambda i: qmm.qgemv(words, s, b, x, wl.bits, y=y), steps, warmup, stream)
     return {"workload": wl.name, "us_per_launch": round(ms * 1e3, 2),
             "gb_per_s": round(gemv_bytes(n, k, 4) / (ms * 1e-3) / 1e9, 1)}
+
+
+def bench_decode_extras(torch, qmm, wl, sets, steps=20, warmup=3):
+    """Context for the batched headline, on the same weight copies:
+      lm_head      the 1024 -> 151936 projection alone, one qmm_qgemv launch;
+      graph_197    the decode pass as 197 sequential qmm_qgemv launches (the
+                   order a dependent decode would need) replayed as one HIP graph;
+      graph_floor  the same graph shape with 197 one-element kernels: the
+                   per-launch floor that the sequential form pays."""
+    stream = torch.cuda.current_stream()
+    copies = len(sets)
+    out = {}
+    lm = [st[-1] for st in sets]
+    ms, _ = time_launches(torch, lambda i: qmm.qgemv(*lm[i % copies][:4], wl.bits, y=lm[i % copies][4]),
+                          steps, warmup, stream)
+    nb = gemv_bytes(lm[0][5], lm[0][6], wl.bits)
+    out["lm_head"] = {"n": lm[0][5], "k": lm[0][6], "us_per_launch": round(ms * 1e3, 2),
+                      "gb_per_s": round(nb / (ms * 1e-3) / 1e9, 1)}
+
+    def capture(body):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            body()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                body()
+        torch.cuda.synchronize()
+        return g
+
+    def seq(st):
+        def body():
+            for (w, s_, b, x, y, n, k) in st:
+                qmm.qgemv(w, s_, b, x, wl.bits, y=y)
+        return body
+    graphs = [capture(seq(st)) for st in sets]
+    ms_g, _ = time_launches(torch, lambda i: graphs[i % copies].replay(), steps, warmup, stream)
+    step_bytes = sum(gemv_bytes(p.n, p.k, wl.bits) for _, _, p in wl.problems())
+    out["graph_197"] = {"launches": len(sets[0]), "ms_per_pass": round(ms_g, 4),
+                        "gb_per_s": round(step_bytes / (ms_g * 1e-3) / 1e9, 1)}
+    tiny = torch.zeros(1, device="cuda")
+
+    def empty():
+        for _ in range(len(sets[0])):
+            tiny.add_(1.0)
+    g0 = capture(empty)
+    ms_0, _ = time_launches(torch, lambda i: g0.replay(), steps, warmup, stream)
+    out["graph_floor"] = {"launches": len(sets[0]), "us_per_launch": round(ms_0 * 1e3 / len(sets[0]), 3)}
+    del graphs, g0
+    return out
 
 
 # Projections of one layer that read the same activations run as one batched
@@ -359,6 +412,9 @@ def main():
                      "bytes_per_launch": d["step_bytes"],
                      "launch_ms_mean": round(d["ms_step"], 5)},
     }
+    if args.only == "all":
+        log("decode extras")
+        result["decode_context"] = bench_decode_extras(torch, qmm, wl, d["sets"])
     del d
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
