@@ -344,6 +344,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--gemm", metavar="M,N,K",
+                    help="run only qmm_qgemm on one 4-bit shape, --steps times (for counters), and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -365,6 +367,18 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "launches": 5}))
+        return
+
+    if args.gemm:
+        m, n, k = (int(v) for v in args.gemm.split(","))
+        wq = qmm.quantize(torch.from_numpy(synth.draw_weight((9, m, n, k), n, k)).cuda(), 4)
+        x = torch.from_numpy(synth.draw_act((9, m, n, k + 1), m, k)).cuda()
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(qmm.qgemm_workspace_size(m, n, k, 4), 16), dtype=torch.uint8, device="cuda")
+        ms_call, _ = time_launches(torch, lambda i: qmm.qgemm(*wq, x, 4, y=y, workspace=ws),
+                                   args.steps, args.warmup, torch.cuda.current_stream())
+        print(json.dumps({"gemm": [m, n, k], "ms_per_call": round(ms_call, 4),
+                          "tflops": round(2.0 * m * n * k / (ms_call * 1e-3) / 1e12, 1)}), flush=True)
         return
 
     if args.only in ("prefill", "moe"):
