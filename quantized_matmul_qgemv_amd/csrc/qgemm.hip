@@ -1,8 +1,10 @@
 // Prefill GEMM over group-quantized weights: y[m, n] = sum_k x[m, k] W_hat[n, k]
 // (BaseRT, native-Metal LLM inference on Apple Silicon, §3.4: tile
-// geometry chosen per sequence-length range).  The tile core is in
-// qgemm_core.h; this file picks the tile, maps workgroups to tiles and,
-// when there are too few tiles to fill the 256 CUs, splits k.
+// geometry chosen per sequence-length range).  The tile cores are in
+// qgemm_core.h and qgemm_wide.h; the tile shape and k-split count come from
+// the planner shared with the batched GEMM (gemm_choose in
+// qgemm_batched.hip); this file maps workgroups to tiles and sums split-k
+// partials.
 //
 // Workgroup -> tile mapping.  Workgroups are dealt round-robin to the 8
 // XCDs (each with its own L2).  Tiles that share weight columns (same
@@ -14,9 +16,6 @@
 // [split*G/S, (split+1)*G/S) and writes its fp32 partial tile to the
 // workspace; qgemm_reduce_kernel then sums the S partials of every output
 // in split order, so the result does not depend on scheduling.
-#include <stdio.h>
-#include <stdlib.h>
-
 #include "qgemm_core.h"
 #include "qgemm_wide.h"
 #include "qmm_internal.h"
