@@ -6,8 +6,9 @@
 //
 // The kernel is HBM-bound: every packed weight byte is read exactly once.
 // Work decomposition (one workgroup = 4 wave64s):
-//   * a "unit" is one 64-code group of one row: GROUP_BYTES (16/32/64 B
-//     for 2/4/8 bits) of codes plus one fp16 scale and one fp16 bias;
+//   * a "unit" is one 64-code group of one row: GROUP_BYTES (8 * bits:
+//     16/24/32/40/48/64 B for 2/3/4/5/6/8 bits) of codes plus one fp16
+//     scale and one fp16 bias;
 //   * LPR consecutive lanes share a row; lane lr takes the row's groups
 //     lr, lr + LPR, lr + 2*LPR, ...  so one wave-wide 128-bit load covers
 //     64/LPR rows with contiguous, fully used 16-byte pieces;
@@ -27,7 +28,11 @@
 //     C[g] = sum_{k in g} magic(k) * x[k]       X[g] = sum_{k in g} x[k]
 // so that   sum_k q_k x_k = dot(magic + q, x) - C[g]   needs no per-code
 // subtraction: each packed 4-bit word costs one shift, four AND-ORs and
-// four v_dot2_f32_f16.
+// four v_dot2_f32_f16.  3/5/6-bit codes are unpacked per 8-code chunk
+// (unpack_chunk in qmm_device.h) into pairs of adjacent codes, so for those
+// widths x stays in natural order in LDS.
+#include <type_traits>
+
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -74,27 +79,41 @@ template <int BITS>
 __device__ __forceinline__ void stage_quarter(const uint32_t (&d)[8], int g, int part, bool on,
                                               unsigned char* xp, float2* cx) {
   using F = Fmt<BITS>;
-  constexpr int C = F::CODES_PER_WORD;
-  constexpr int PPW = F::PAIRS_PER_WORD;
-  constexpr int WPQ = 16 / C > 0 ? 16 / C : 1;  // words per quarter group
-  static_assert(16 % C == 0, "a quarter group must hold whole words");
   float csum = 0.0f, xsum = 0.0f;
   uint32_t out[8];
+  if constexpr (F::CHUNKED) {
+    // chunk pairs are adjacent codes: x stays in natural order
 #pragma unroll
-  for (int wd = 0; wd < WPQ; ++wd) {
-#pragma unroll
-    for (int p = 0; p < PPW; ++p) {
-      const int klo = wd * C + pair_lo<BITS>(p);
-      const int khi = wd * C + pair_hi<BITS>(p);
-      const uint32_t lo = (d[klo >> 1] >> (16 * (klo & 1))) & 0xFFFFu;
-      const uint32_t hi = (d[khi >> 1] >> (16 * (khi & 1))) & 0xFFFFu;
-      out[wd * PPW + p] = lo | (hi << 16);
-      const float xl = f16_bits_to_f32((uint16_t)lo);
-      const float xh = f16_bits_to_f32((uint16_t)hi);
-      csum += magic_value<BITS>(p) * xl;
-      csum += magic_value<BITS>(p) * xh;
+    for (int i = 0; i < 8; ++i) {
+      out[i] = d[i];
+      const float xl = f16_bits_to_f32((uint16_t)(d[i] & 0xFFFFu));
+      const float xh = f16_bits_to_f32((uint16_t)(d[i] >> 16));
+      csum += chunk_magic_value<BITS>((2 * i) & 7) * xl;
+      csum += chunk_magic_value<BITS>((2 * i + 1) & 7) * xh;
       xsum += xl;
       xsum += xh;
+    }
+  } else {
+    constexpr int C = F::CODES_PER_WORD;
+    constexpr int PPW = F::PAIRS_PER_WORD;
+    constexpr int WPQ = 16 / C > 0 ? 16 / C : 1;  // words per quarter group
+    static_assert(16 % C == 0, "a quarter group must hold whole words");
+#pragma unroll
+    for (int wd = 0; wd < WPQ; ++wd) {
+#pragma unroll
+      for (int p = 0; p < PPW; ++p) {
+        const int klo = wd * C + pair_lo<BITS>(p);
+        const int khi = wd * C + pair_hi<BITS>(p);
+        const uint32_t lo = (d[klo >> 1] >> (16 * (klo & 1))) & 0xFFFFu;
+        const uint32_t hi = (d[khi >> 1] >> (16 * (khi & 1))) & 0xFFFFu;
+        out[wd * PPW + p] = lo | (hi << 16);
+        const float xl = f16_bits_to_f32((uint16_t)lo);
+        const float xh = f16_bits_to_f32((uint16_t)hi);
+        csum += magic_value<BITS>(p) * xl;
+        csum += magic_value<BITS>(p) * xh;
+        xsum += xl;
+        xsum += xh;
+      }
     }
   }
   if (on) {
@@ -133,10 +152,25 @@ __device__ __forceinline__ void stage_x_store(gptr<uint16_t> x, int groups, cons
   }
 }
 
-// Register buffer of one step: UR rows x one group per lane.
-template <int BITS, int UR>
+// Register buffer of one step: UR rows x one group per lane.  3/5/6-bit
+// groups (24/40/48 bytes) are loaded with 8-byte loads unless 16-byte
+// aligned (6 bits).
+template <int BITS>
+struct GroupLoad {
+  static constexpr int BYTES = Fmt<BITS>::GROUP_BYTES;
+  static constexpr int VB = BYTES % 16 == 0 ? 16 : 8;  // bytes per load
+  static constexpr int NV = BYTES / VB;                // loads per group
+};
+
+template <int BITS, int UR, bool CH = Fmt<BITS>::CHUNKED>
 struct StepBuf {
   u32x4 w[UR][Fmt<BITS>::VEC4_PER_GROUP];
+  uint16_t s[UR], b[UR];
+};
+
+template <int BITS, int UR>
+struct StepBuf<BITS, UR, true> {
+  uint32_t w[UR][Fmt<BITS>::WORDS_PER_GROUP];
   uint16_t s[UR], b[UR];
 };
 
@@ -183,9 +217,28 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
     for (int u = 0; u < UR; ++u) {
       int r = lane_row + ip * Cfg::ROWS + u * Cfg::RPW;
       r = r < row_end ? r : row_end - 1;
-      gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(W + (size_t)r * rstride + (size_t)g * WPG);
+      if constexpr (F::CHUNKED) {
+        using GL = GroupLoad<BITS>;
+        if constexpr (GL::VB == 16) {
+          gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(W + (size_t)r * rstride + (size_t)g * WPG);
 #pragma unroll
-      for (int v = 0; v < V4; ++v) bf.w[u][v] = src[v];
+          for (int v = 0; v < GL::NV; ++v) {
+            const u32x4 t = src[v];
+            bf.w[u][4 * v] = t.x; bf.w[u][4 * v + 1] = t.y; bf.w[u][4 * v + 2] = t.z; bf.w[u][4 * v + 3] = t.w;
+          }
+        } else {
+          gptr<u32x2> src = reinterpret_cast<gptr<u32x2>>(W + (size_t)r * rstride + (size_t)g * WPG);
+#pragma unroll
+          for (int v = 0; v < GL::NV; ++v) {
+            const u32x2 t = src[v];
+            bf.w[u][2 * v] = t.x; bf.w[u][2 * v + 1] = t.y;
+          }
+        }
+      } else {
+        gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(W + (size_t)r * rstride + (size_t)g * WPG);
+#pragma unroll
+        for (int v = 0; v < V4; ++v) bf.w[u][v] = src[v];
+      }
       bf.s[u] = S[(size_t)r * groups + g];
       bf.b[u] = B[(size_t)r * groups + g];
     }
@@ -204,6 +257,32 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
     float a0[UR], a1[UR];
 #pragma unroll
     for (int u = 0; u < UR; ++u) a0[u] = a1[u] = 0.0f;
+    if constexpr (F::CHUNKED) {
+      // chunk-major: 8 codes = 4 natural pairs of x (16 bytes of LDS)
+      auto chunk = [&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        const u32x4 xv = reinterpret_cast<const u32x4*>(xg)[m];
+        const uint32_t xr[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          uint32_t vlo, vhi, h[4];
+          chunk_window<BITS * m, WPG>(bf.w[u], vlo, vhi);
+          unpack_chunk<BITS>(vlo, vhi, h);
+          a0[u] = dot2(h[0], xr[0], a0[u]);
+          a1[u] = dot2(h[1], xr[1], a1[u]);
+          a0[u] = dot2(h[2], xr[2], a0[u]);
+          a1[u] = dot2(h[3], xr[3], a1[u]);
+        }
+      };
+      chunk(std::integral_constant<int, 0>{});
+      chunk(std::integral_constant<int, 1>{});
+      chunk(std::integral_constant<int, 2>{});
+      chunk(std::integral_constant<int, 3>{});
+      chunk(std::integral_constant<int, 4>{});
+      chunk(std::integral_constant<int, 5>{});
+      chunk(std::integral_constant<int, 6>{});
+      chunk(std::integral_constant<int, 7>{});
+    } else {
     // word-major: the activation pairs of one word are read from LDS once
     // and used for all UR rows, so only PPW of them are live at a time
 #pragma unroll
@@ -231,6 +310,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
           else              a1[u] = dot2(h[p], xr[p], a1[u]);
         }
       }
+    }
     }
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
@@ -315,7 +395,10 @@ __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4)
 
 // ------------------------------------------------------------------ host --
 
-int gemv_row_unroll(int bits) { return bits == 8 ? 2 : 4; }
+// Rows in flight per lane: fewer for the wider formats (register budget).
+constexpr int gemv_ur(int bits) { return bits >= 5 ? 2 : 4; }
+
+int gemv_row_unroll(int bits) { return gemv_ur(bits); }
 
 int gemv_rows_per_pass(int lpr, int ur, int wk) { return (kGemvWaves / wk) * ur * (64 / lpr); }
 
@@ -361,7 +444,7 @@ static hipError_t launch_one(const GemvProblem& p, const GemvGeom& g, hipStream_
 
 template <int BITS, int LPR>
 static hipError_t launch_lpr(const GemvProblem& p, const GemvGeom& g, hipStream_t st, size_t lds) {
-  constexpr int URB = BITS == 8 ? 2 : 4;
+  constexpr int URB = gemv_ur(BITS);
   if (g.row_unroll == URB && g.wave_ksplit == 1) return launch_one<BITS, LPR, URB, 1>(p, g, st, lds);
   if (g.row_unroll == 1 && g.wave_ksplit == 1) return launch_one<BITS, LPR, 1, 1>(p, g, st, lds);
   if (g.row_unroll == 1 && g.wave_ksplit == 4) return launch_one<BITS, LPR, 1, 4>(p, g, st, lds);
@@ -384,7 +467,10 @@ static hipError_t launch_bits(const GemvProblem& p, const GemvGeom& g, hipStream
 hipError_t launch_qgemv(const GemvProblem& p, int bits, const GemvGeom& g, hipStream_t st) {
   switch (bits) {
     case 2: return launch_bits<2>(p, g, st);
+    case 3: return launch_bits<3>(p, g, st);
     case 4: return launch_bits<4>(p, g, st);
+    case 5: return launch_bits<5>(p, g, st);
+    case 6: return launch_bits<6>(p, g, st);
     case 8: return launch_bits<8>(p, g, st);
     default: return hipErrorInvalidValue;
   }
@@ -393,7 +479,7 @@ hipError_t launch_qgemv(const GemvProblem& p, int bits, const GemvGeom& g, hipSt
 template <int BITS, int LPR>
 static hipError_t launch_batched_one(const GemvBlock* blocks, int num_blocks, size_t lds,
                                      hipStream_t st) {
-  constexpr int URB = BITS == 8 ? 2 : 4;
+  constexpr int URB = gemv_ur(BITS);
   hipLaunchKernelGGL((qgemv_batched_kernel<BITS, LPR, URB>), dim3(num_blocks), dim3(kGemvThreads),
                      lds, st, blocks);
   return hipGetLastError();
@@ -419,7 +505,10 @@ hipError_t launch_qgemv_batched(const GemvBlock* blocks, int num_blocks, int bit
   const size_t lds = gemv_lds_bytes(max_groups, g);
   switch (bits) {
     case 2: return launch_batched_bits<2>(blocks, num_blocks, lanes_per_row, lds, st);
+    case 3: return launch_batched_bits<3>(blocks, num_blocks, lanes_per_row, lds, st);
     case 4: return launch_batched_bits<4>(blocks, num_blocks, lanes_per_row, lds, st);
+    case 5: return launch_batched_bits<5>(blocks, num_blocks, lanes_per_row, lds, st);
+    case 6: return launch_batched_bits<6>(blocks, num_blocks, lanes_per_row, lds, st);
     case 8: return launch_batched_bits<8>(blocks, num_blocks, lanes_per_row, lds, st);
     default: return hipErrorInvalidValue;
   }

@@ -38,8 +38,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int BITS>
 struct Fmt {
-  static_assert(BITS == 2 || BITS == 4 || BITS == 8, "supported widths: 2, 4, 8");
-  static constexpr int CODES_PER_WORD = 32 / BITS;
+  static_assert(BITS >= 2 && BITS <= 8 && BITS != 7, "supported widths: 2, 3, 4, 5, 6, 8");
+  // 3-, 5- and 6-bit codes straddle word boundaries and are unpacked per
+  // 8-code chunk (BITS bytes, see unpack_chunk); the others per word.
+  static constexpr bool CHUNKED = (32 % BITS) != 0;
+  static constexpr int CODES_PER_WORD = CHUNKED ? 0 : 32 / BITS;
   static constexpr int PAIRS_PER_WORD = CODES_PER_WORD / 2;
   static constexpr int WORDS_PER_GROUP = 64 * BITS / 32;  // group of 64 codes
   static constexpr int VEC4_PER_GROUP = WORDS_PER_GROUP / 4 > 0 ? WORDS_PER_GROUP / 4 : 1;
@@ -131,6 +134,92 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
 // acc + a.x*b.x + a.y*b.y with fp32 accumulation (v_dot2_f32_f16).
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2(as_half2(a), as_half2(b), acc, false);
+}
+
+// ---------------------------------------------------------------------------
+// 3-, 5- and 6-bit codes: chunk unpack.
+//
+// Eight consecutive codes fill exactly BITS bytes, so every 8-code chunk
+// starts on a byte boundary and its codes sit at the same bit positions in
+// every chunk.  Let V be the 64-bit value whose low byte is the chunk's
+// first byte (vlo = V[31:0], vhi = V[63:32]) and S = (V >> 4)[31:0].  Pair t
+// of a chunk is (code 2t, code 2t+1), in natural k order.  Each code is
+// read through a 16-bit window that starts on a byte of V (or of S when the
+// code would otherwise sit too high in its window): the code must lie at a
+// bit offset o with o + BITS <= 10 so that the magic fp16 2^(10-o), whose
+// ulp is 2^-o, reads as (2^(10-o) + code) exactly.  One v_perm_b32 moves
+// both windows into place (lo window -> bits 0..15, hi window -> bits
+// 16..31), one AND-OR keeps the two code fields and sets the magics.
+//
+// Code positions (bit offset inside the chunk) and windows:
+//   3-bit: 0,3,6,9,12,15,18,21          all from V bytes 0..3
+//   5-bit: 0,5,10,15,20,25,30,35         codes 3 and 6 from S (offset 7 and 6 in V are too high)
+//   6-bit: 0,6,12,18,24,30,36,42         codes 1 and 5 from S
+// Table entries: {src0, src1, selector, mask, magic}; v_perm_b32(src0,
+// src1, sel) takes byte i of the result from byte sel.b[i] of the 8-byte
+// value src0:src1 (bytes 0..3 = src1, 4..7 = src0).
+struct ChunkPair {
+  int src0, src1;  // 0 = vlo, 1 = vhi, 2 = S
+  uint32_t sel, mask, magic;
+};
+
+template <int BITS>
+__host__ __device__ constexpr ChunkPair chunk_pair(int t) {
+  if constexpr (BITS == 3) {
+    return t == 0 ? ChunkPair{0, 0, 0x01000100u, 0x00380007u, 0x58006400u}   // offsets 0 | 3
+         : t == 1 ? ChunkPair{0, 0, 0x02010100u, 0x000E01C0u, 0x60004C00u}   // 6 | 1
+         : t == 2 ? ChunkPair{0, 0, 0x02010201u, 0x03800070u, 0x48005400u}   // 4 | 7
+                  : ChunkPair{0, 0, 0x03020302u, 0x00E0001Cu, 0x50005C00u};  // 2 | 5
+  } else if constexpr (BITS == 5) {
+    return t == 0 ? ChunkPair{0, 0, 0x01000100u, 0x03E0001Fu, 0x50006400u}   // 0 | 5
+         : t == 1 ? ChunkPair{2, 0, 0x05050101u, 0x00F8007Cu, 0x58005C00u}   // 2 | S:3
+         : t == 2 ? ChunkPair{0, 0, 0x03030302u, 0x003E01F0u, 0x60005400u}   // 4 | 1
+                  : ChunkPair{1, 2, 0x04040303u, 0x00F8007Cu, 0x58005C00u};  // S:2 | 3
+  } else {
+    static_assert(BITS == 6, "chunk tables exist for 3, 5 and 6 bits");
+    return t == 0 ? ChunkPair{2, 0, 0x04040000u, 0x00FC003Fu, 0x5C006400u}   // 0 | S:2
+         : t == 1 ? ChunkPair{0, 0, 0x02020201u, 0x00FC03F0u, 0x5C005400u}   // 4 | 2
+         : t == 2 ? ChunkPair{2, 0, 0x07070303u, 0x00FC003Fu, 0x5C006400u}   // 0 | S:2
+                  : ChunkPair{1, 1, 0x01010100u, 0x00FC03F0u, 0x5C005400u};  // 4 | 2
+  }
+}
+
+// Offset added by the magic to code c (0..7) of a chunk.
+template <int BITS>
+__host__ __device__ constexpr float chunk_magic_value(int c) {
+  const uint32_t m = (c & 1) ? (chunk_pair<BITS>(c >> 1).magic >> 16) : (chunk_pair<BITS>(c >> 1).magic & 0xFFFFu);
+  // fp16 with zero mantissa: 2^(exponent - 15)
+  return (float)(1u << ((m >> 10) - 15));
+}
+
+// The 64-bit window V of the chunk starting at byte SB of w[0 .. NW).
+// Words past the end are never needed for the code bits (they are clamped
+// to the last word and only feed masked-off bytes).
+template <int SB, int NW>
+__device__ __forceinline__ void chunk_window(const uint32_t* w, uint32_t& vlo, uint32_t& vhi) {
+  constexpr int j = SB / 4, o = SB % 4;
+  constexpr int j1 = j + 1 < NW ? j + 1 : NW - 1;
+  constexpr int j2 = j + 2 < NW ? j + 2 : NW - 1;
+  if constexpr (o == 0) {
+    vlo = w[j];
+    vhi = w[j1];
+  } else {
+    vlo = __builtin_amdgcn_alignbyte(w[j1], w[j], o);
+    vhi = __builtin_amdgcn_alignbyte(w[j2], w[j1], o);
+  }
+}
+
+// One 8-code chunk -> 4 fp16 pairs (raw 32-bit patterns),
+// pair t = (magic + code 2t, magic + code 2t+1).
+template <int BITS>
+__device__ __forceinline__ void unpack_chunk(uint32_t vlo, uint32_t vhi, uint32_t (&h)[4]) {
+  const uint32_t sv = __builtin_amdgcn_alignbit(vhi, vlo, 4);
+  auto pick = [&](int i) { return i == 0 ? vlo : i == 1 ? vhi : sv; };
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const ChunkPair c = chunk_pair<BITS>(t);
+    h[t] = and_or(__builtin_amdgcn_perm(pick(c.src0), pick(c.src1), c.sel), c.mask, c.magic);
+  }
 }
 
 }  // namespace qmm

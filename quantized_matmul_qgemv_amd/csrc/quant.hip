@@ -8,8 +8,9 @@
 // at model load, so this runs once per weight, not per token.
 //
 // The diagnostic kernels decode codes and dequantized values with the very
-// register routines the GEMV (unpack_word) and GEMM (dequant_word_f16) use,
-// so their outputs pin those routines bit for bit.
+// register routines the GEMV (unpack_word, unpack_chunk) and GEMM
+// (dequant_word_f16, and the chunk dequantization) use, so their outputs pin
+// those routines bit for bit.
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -56,13 +57,87 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
       t = fminf(fmaxf(t, 0.0f), levels);
       q = (uint32_t)t;
     }
-    out[(i * BITS) >> 5] |= q << ((i * BITS) & 31);
+    const int bit = i * BITS;
+    out[bit >> 5] |= q << (bit & 31);
+    if ((bit & 31) + BITS > 32) out[(bit >> 5) + 1] |= q >> (32 - (bit & 31));  // straddles a word
   }
   uint32_t* dst = words + gid * F::WORDS_PER_GROUP;
 #pragma unroll
   for (int j = 0; j < F::WORDS_PER_GROUP; ++j) dst[j] = out[j];
   s_out[gid] = __builtin_bit_cast(uint16_t, s16);
   b_out[gid] = __builtin_bit_cast(uint16_t, b16);
+}
+
+// 3/5/6 bits: the 64-bit window of chunk c (8 codes, BITS bytes, starting
+// at byte BITS*c of the flat word array of `words` words).
+template <int BITS>
+__device__ __forceinline__ void chunk_window_rt(const uint32_t* __restrict__ w, long words, long c,
+                                                uint32_t& vlo, uint32_t& vhi) {
+  const long byte = (long)BITS * c;
+  const long j = byte >> 2;
+  const uint32_t o = (uint32_t)(byte & 3);
+  // words past the end only feed bytes outside the chunk: clamp
+  const long j1 = j + 1 < words ? j + 1 : words - 1;
+  const long j2 = j + 2 < words ? j + 2 : words - 1;
+  const uint32_t w0 = w[j], w1 = w[j1], w2 = w[j2];
+  vlo = __builtin_amdgcn_alignbyte(w1, w0, o);
+  vhi = __builtin_amdgcn_alignbyte(w2, w1, o);
+}
+
+// One thread per 8-code chunk (3/5/6 bits).
+template <int BITS>
+__global__ __launch_bounds__(256) void unpack_chunks_kernel(const uint32_t* __restrict__ w,
+                                                            uint8_t* __restrict__ codes,
+                                                            long words, long chunks) {
+  const long c = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= chunks) return;
+  uint32_t vlo, vhi, h[4];
+  chunk_window_rt<BITS>(w, words, c, vlo, vhi);
+  unpack_chunk<BITS>(vlo, vhi, h);
+  uint8_t* dst = codes + c * 8;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const half2_t v = as_half2(h[t]);
+    dst[2 * t] = (uint8_t)((float)v.x - chunk_magic_value<BITS>(2 * t));
+    dst[2 * t + 1] = (uint8_t)((float)v.y - chunk_magic_value<BITS>(2 * t + 1));
+  }
+}
+
+// One thread per 8-code chunk (3/5/6 bits); a chunk lies in one group.
+// fp16 output: v_pk_fma_f16(q, s, b) on q = (magic + q) - magic, as in the
+// GEMM's weight operand.
+template <int BITS, bool F16>
+__global__ __launch_bounds__(256) void dequant_chunks_kernel(const uint32_t* __restrict__ w,
+                                                             const uint16_t* __restrict__ s,
+                                                             const uint16_t* __restrict__ b,
+                                                             void* __restrict__ out, long words,
+                                                             long chunks) {
+  const long c = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= chunks) return;
+  const long g = c >> 3;  // 8 chunks per 64-code group
+  uint32_t vlo, vhi, h[4];
+  chunk_window_rt<BITS>(w, words, c, vlo, vhi);
+  unpack_chunk<BITS>(vlo, vhi, h);
+  if constexpr (F16) {
+    const half_t sh = __builtin_bit_cast(half_t, s[g]);
+    const half_t bh = __builtin_bit_cast(half_t, b[g]);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + c * 8);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const half2_t q = as_half2(h[t]) - as_half2(chunk_pair<BITS>(t).magic);
+      dst[t] = as_u32(__builtin_elementwise_fma(q, half2_t{sh, sh}, half2_t{bh, bh}));
+    }
+  } else {
+    const float sf = f16_bits_to_f32(s[g]);
+    const float bf = f16_bits_to_f32(b[g]);
+    float* dst = reinterpret_cast<float*>(out) + c * 8;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const half2_t v = as_half2(h[t]);
+      dst[2 * t] = fmaf(sf, (float)v.x - chunk_magic_value<BITS>(2 * t), bf);
+      dst[2 * t + 1] = fmaf(sf, (float)v.y - chunk_magic_value<BITS>(2 * t + 1), bf);
+    }
+  }
 }
 
 // One thread per packed word.
@@ -132,12 +207,17 @@ hipError_t launch_quantize(const float* w, uint32_t* words, uint16_t* s, uint16_
                            int k, int bits, hipStream_t st) {
   const int groups = k / 64;
   const unsigned grid = blocks_for((long)n * groups);
+#define QMM_Q(B) hipLaunchKernelGGL(quantize_kernel<B>, dim3(grid), dim3(256), 0, st, w, words, s, b, n, groups)
   switch (bits) {
-    case 2: hipLaunchKernelGGL(quantize_kernel<2>, dim3(grid), dim3(256), 0, st, w, words, s, b, n, groups); break;
-    case 4: hipLaunchKernelGGL(quantize_kernel<4>, dim3(grid), dim3(256), 0, st, w, words, s, b, n, groups); break;
-    case 8: hipLaunchKernelGGL(quantize_kernel<8>, dim3(grid), dim3(256), 0, st, w, words, s, b, n, groups); break;
+    case 2: QMM_Q(2); break;
+    case 3: QMM_Q(3); break;
+    case 4: QMM_Q(4); break;
+    case 5: QMM_Q(5); break;
+    case 6: QMM_Q(6); break;
+    case 8: QMM_Q(8); break;
     default: return hipErrorInvalidValue;
   }
+#undef QMM_Q
   return hipGetLastError();
 }
 
@@ -145,12 +225,19 @@ hipError_t launch_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, 
                                hipStream_t st) {
   const long words = (long)n * k * bits / 32;
   const unsigned grid = blocks_for(words);
+  const long chunks = (long)n * k / 8;
+  const unsigned cgrid = blocks_for(chunks);
+#define QMM_UC(B) hipLaunchKernelGGL(unpack_chunks_kernel<B>, dim3(cgrid), dim3(256), 0, st, w, codes, words, chunks)
   switch (bits) {
+    case 3: QMM_UC(3); break;
+    case 5: QMM_UC(5); break;
+    case 6: QMM_UC(6); break;
     case 2: hipLaunchKernelGGL(unpack_codes_kernel<2>, dim3(grid), dim3(256), 0, st, w, codes, words); break;
     case 4: hipLaunchKernelGGL(unpack_codes_kernel<4>, dim3(grid), dim3(256), 0, st, w, codes, words); break;
     case 8: hipLaunchKernelGGL(unpack_codes_kernel<8>, dim3(grid), dim3(256), 0, st, w, codes, words); break;
     default: return hipErrorInvalidValue;
   }
+#undef QMM_UC
   return hipGetLastError();
 }
 
@@ -158,23 +245,33 @@ hipError_t launch_dequant(const uint32_t* w, const uint16_t* s, const uint16_t* 
                           int out_is_f16, int n, int k, int bits, hipStream_t st) {
   const long words = (long)n * k * bits / 32;
   const unsigned grid = blocks_for(words);
+  const long chunks = (long)n * k / 8;
+  const unsigned cgrid = blocks_for(chunks);
 #define QMM_DQ(B, H) hipLaunchKernelGGL((dequant_kernel<B, H>), dim3(grid), dim3(256), 0, st, w, s, b, out, words)
+#define QMM_DQC(B, H) hipLaunchKernelGGL((dequant_chunks_kernel<B, H>), dim3(cgrid), dim3(256), 0, st, w, s, b, out, words, chunks)
   if (out_is_f16) {
     switch (bits) {
       case 2: QMM_DQ(2, true); break;
+      case 3: QMM_DQC(3, true); break;
       case 4: QMM_DQ(4, true); break;
+      case 5: QMM_DQC(5, true); break;
+      case 6: QMM_DQC(6, true); break;
       case 8: QMM_DQ(8, true); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (bits) {
       case 2: QMM_DQ(2, false); break;
+      case 3: QMM_DQC(3, false); break;
       case 4: QMM_DQ(4, false); break;
+      case 5: QMM_DQC(5, false); break;
+      case 6: QMM_DQC(6, false); break;
       case 8: QMM_DQ(8, false); break;
       default: return hipErrorInvalidValue;
     }
   }
 #undef QMM_DQ
+#undef QMM_DQC
   return hipGetLastError();
 }
 

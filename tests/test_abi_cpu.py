@@ -48,7 +48,9 @@ def expect(status, code, fragment):
 
 
 def test_gemv_errors(L):
-    expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 3, 64, None), UNS, "bits=3")
+    expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 7, 64, None), UNS, "bits=7")
+    expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 1, 64, None), UNS, "bits=1")
+    expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 16, 64, None), UNS, "bits=16")
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 4, 32, None), UNS, "group_size=32")
     expect(L.qmm_qgemv(A, A, A, A, A, 0, 64, 4, 64, None), INV, "n=0")
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 100, 4, 64, None), INV, "k=100")

@@ -19,12 +19,13 @@ if not torch.cuda.is_available():
 
 import quantized_matmul_qgemv_amd as qmm  # noqa: E402
 
-BITS = (2, 4, 8)
+BITS = (2, 4, 8)               # every kernel
+BITS_ALL = (2, 3, 4, 5, 6, 8)  # GEMV, quantizer and diagnostics
 
 
 # ------------------------------------------------------------ bit-exact --
 
-@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("bits", BITS_ALL)
 def test_unpack_codes_bit_exact(bits):
     say("unpack", bits)
     r = np.random.default_rng(100 + bits)
@@ -38,7 +39,7 @@ def test_unpack_codes_bit_exact(bits):
     assert np.array_equal(got, codes)
 
 
-@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("bits", BITS_ALL)
 @pytest.mark.parametrize("f16", [False, True])
 def test_dequant_bit_exact(bits, f16):
     say("dequant", bits, f16)
@@ -77,7 +78,7 @@ def quantize_cases():
     return np.concatenate(rows)
 
 
-@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("bits", BITS_ALL)
 def test_quantize_bit_exact(bits):
     say("quantize", bits)
     w = quantize_cases()
@@ -94,7 +95,7 @@ GEMV_SHAPES = [(1, 64), (3, 128), (37, 192), (100, 320), (1000, 1024), (1024, 10
                (300, 2048), (129, 2560), (513, 3072), (64, 8192), (7, 9728)]
 
 
-@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("bits", BITS_ALL)
 @pytest.mark.parametrize("n,k", GEMV_SHAPES)
 def test_gemv_parity(bits, n, k):
     say("gemv", bits, n, k)
@@ -122,7 +123,7 @@ def test_gemv_integer_closed_form():
     integer matmul, representable in fp32, so the GPU must hit it exactly."""
     say("gemv integer")
     r = np.random.default_rng(5)
-    for bits in BITS:
+    for bits in BITS_ALL:
         n, k = 96, 512
         codes = r.integers(0, 1 << bits, (n, k), dtype=np.uint8)
         words = oracle.pack(codes, bits)
@@ -133,9 +134,9 @@ def test_gemv_integer_closed_form():
         assert np.array_equal(y.astype(np.float64), (codes.astype(np.int64) @ xi).astype(np.float64))
 
 
-def test_gemv_batched_mixed_shapes():
-    say("gemv batched")
-    bits = 4
+@pytest.mark.parametrize("bits", BITS_ALL)
+def test_gemv_batched_mixed_shapes(bits):
+    say("gemv batched", bits)
     shapes = [(2048, 1024), (1024, 1024), (1024, 2048), (3072, 1024), (1024, 3072), (999, 1024)]
     probs, wants, ys = [], [], []
     for i, (n, k) in enumerate(shapes):
