@@ -25,7 +25,9 @@
  *            [bits*k, bits*k + bits) of its row, bit i of the stream is bit
  *            i % 32 of uint32 word i / 32.  For bits = 4 that is 8 nibbles per
  *            word, low nibble first; for bits = 8, 4 bytes per word, low byte
- *            first.  Row stride: k * bits / 32 words.
+ *            first; 3-, 5- and 6-bit codes straddle word boundaries (every 8
+ *            codes fill exactly `bits` bytes).  Row stride: k * bits / 32
+ *            words; a 64-code group is 8 * bits bytes.
  *   scales,  fp16 bit patterns (uint16) [n, k / group_size]: the per-group
  *   biases   step s and offset b (asymmetric min/max quantization: b is the
  *            group minimum, s = (max - min) / (2^bits - 1)).
@@ -34,7 +36,7 @@
  *
  * Common rules
  * ------------
- *   * Supported: bits in {2, 4, 8}; group_size == 64; k a positive multiple
+ *   * Supported: bits in {2, 3, 4, 5, 6, 8}; group_size == 64; k a positive multiple
  *     of 64; n, m >= 1 (m = 0 / t = 0 is accepted and does nothing).
  *   * Every tensor pointer is a DEVICE pointer owned by the caller, 16-byte
  *     aligned, and must stay valid until the stream reaches the launch.

@@ -213,7 +213,10 @@ hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, hipStr
   int32_t* w = reinterpret_cast<int32_t*>(ws);
   switch (bits) {
     case 2: return launch_grouped_bits<2>(a, w, st);
+    case 3: return launch_grouped_bits<3>(a, w, st);
     case 4: return launch_grouped_bits<4>(a, w, st);
+    case 5: return launch_grouped_bits<5>(a, w, st);
+    case 6: return launch_grouped_bits<6>(a, w, st);
     case 8: return launch_grouped_bits<8>(a, w, st);
     default: return hipErrorInvalidValue;
   }

@@ -181,7 +181,10 @@ hipError_t launch_qgemm(const GemmArgs& a, int bits, void* workspace, hipStream_
   float* ws = reinterpret_cast<float*>(workspace);
   switch (bits) {
     case 2: return launch_bits<2>(a, p, ws, st);
+    case 3: return launch_bits<3>(a, p, ws, st);
     case 4: return launch_bits<4>(a, p, ws, st);
+    case 5: return launch_bits<5>(a, p, ws, st);
+    case 6: return launch_bits<6>(a, p, ws, st);
     case 8: return launch_bits<8>(a, p, ws, st);
     default: return hipErrorInvalidValue;
   }

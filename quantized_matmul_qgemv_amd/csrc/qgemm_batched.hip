@@ -332,7 +332,10 @@ hipError_t launch_qgemm_batched(const void* plan_device, const GemmBatchHeader& 
   float* partials = static_cast<float*>(workspace);
   switch (h.bits) {
     case 2: launch_batched_bits<2>(probs, tiles, h, partials, st); break;
+    case 3: launch_batched_bits<3>(probs, tiles, h, partials, st); break;
     case 4: launch_batched_bits<4>(probs, tiles, h, partials, st); break;
+    case 5: launch_batched_bits<5>(probs, tiles, h, partials, st); break;
+    case 6: launch_batched_bits<6>(probs, tiles, h, partials, st); break;
     case 8: launch_batched_bits<8>(probs, tiles, h, partials, st); break;
     default: return hipErrorInvalidValue;
   }

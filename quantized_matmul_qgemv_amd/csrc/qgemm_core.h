@@ -22,6 +22,9 @@
 //     inside one MFMA as long as both operands agree, so the A tile is
 //     written to LDS with the same order applied inside every 16-wide span
 //     of k; the MFMA's A operand is then one ds_read_b128 per lane.
+//     3/5/6-bit weights are unpacked per 8-code chunk in natural order
+//     (lane half h at k16 step j takes chunk 4h + j, which is exactly the
+//     span of k it reads from LDS), so for them the A tile is stored as is.
 //   * Software-pipelined: packed B is loaded 3 steps ahead (registers), A 2
 //     steps ahead (registers, then a double-buffered LDS tile); one barrier
 //     per step.
@@ -73,7 +76,18 @@ __device__ __forceinline__ void load_braw(BRaw<BITS>& r, gptr<uint32_t> wcol, gp
                                           gptr<uint16_t> bcol, int g, int h) {
   constexpr int WPG = Fmt<BITS>::WORDS_PER_GROUP;
   gptr<uint32_t> p = wcol + (size_t)g * WPG + h * (WPG / 2);
-  if constexpr (BITS == 2) {
+  if constexpr (BITS == 6) {
+    // half a 48-byte group: 8-byte aligned
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const u32x2 v = reinterpret_cast<gptr<u32x2>>(p)[i];
+      r.w[2 * i] = v.x; r.w[2 * i + 1] = v.y;
+    }
+  } else if constexpr (BITS == 3 || BITS == 5) {
+    // half a 24- or 40-byte group: 4-byte aligned
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) r.w[i] = p[i];
+  } else if constexpr (BITS == 2) {
     const u32x2 v = *reinterpret_cast<gptr<u32x2>>(p);
     r.w[0] = v.x; r.w[1] = v.y;
   } else {
@@ -108,11 +122,30 @@ __device__ __forceinline__ half8_t b_operand(const BRaw<BITS>& r, int j) {
     dequant_word_f16<8>(r.w[2 * j], s2, b2, d0);
     dequant_word_f16<8>(r.w[2 * j + 1], s2, b2, d1);
     o = u32x4{as_u32(d0[0]), as_u32(d0[1]), as_u32(d1[0]), as_u32(d1[1])};
-  } else {
+  } else if constexpr (BITS == 2) {
     half2_t d[8];
     dequant_word_f16<2>(r.w[j >> 1], s2, b2, d);
     const int q = (j & 1) * 4;
     o = u32x4{as_u32(d[q]), as_u32(d[q + 1]), as_u32(d[q + 2]), as_u32(d[q + 3])};
+  } else {
+    // chunk j of the lane's half group (BITS words): byte offset BITS*j.
+    // j is a constant once the caller's loop is unrolled, so the switch folds.
+    constexpr int NW = BRaw<BITS>::WORDS;
+    uint32_t vlo, vhi, h[4];
+    switch (j) {
+      case 0: chunk_window<0, NW>(r.w, vlo, vhi); break;
+      case 1: chunk_window<BITS, NW>(r.w, vlo, vhi); break;
+      case 2: chunk_window<2 * BITS, NW>(r.w, vlo, vhi); break;
+      default: chunk_window<3 * BITS, NW>(r.w, vlo, vhi); break;
+    }
+    unpack_chunk<BITS>(vlo, vhi, h);
+    uint32_t d[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const half2_t q = as_half2(h[t]) - as_half2(chunk_pair<BITS>(t).magic);
+      d[t] = as_u32(__builtin_elementwise_fma(q, s2, b2));
+    }
+    o = u32x4{d[0], d[1], d[2], d[3]};
   }
   return __builtin_bit_cast(half8_t, o);
 }
@@ -220,7 +253,12 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
     for (int i = 0; i < SPT; ++i) {
       if (aon[i]) {
         uint32_t o[8];
-        permute_span<BITS>(src[i], o);
+        if constexpr (Fmt<BITS>::CHUNKED) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = src[i][e];
+        } else {
+          permute_span<BITS>(src[i], o);
+        }
         u32x4* d = reinterpret_cast<u32x4*>(dst + aoff[i]);
         d[0] = u32x4{o[0], o[1], o[2], o[3]};
         d[1] = u32x4{o[4], o[5], o[6], o[7]};

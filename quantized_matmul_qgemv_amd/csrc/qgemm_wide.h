@@ -100,7 +100,12 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       uint32_t o[8];
-      permute_span<BITS>(src[i], o);
+      if constexpr (Fmt<BITS>::CHUNKED) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = src[i][e];
+      } else {
+        permute_span<BITS>(src[i], o);
+      }
       u32x4* d = reinterpret_cast<u32x4*>(slot + aoff[i]);
       d[0] = u32x4{o[0], o[1], o[2], o[3]};
       d[1] = u32x4{o[4], o[5], o[6], o[7]};

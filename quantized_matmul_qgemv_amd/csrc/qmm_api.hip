@@ -44,7 +44,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 constexpr int kGemvMaxK = 16384;
 constexpr int kMaxExperts = 1024;
 
-// GEMV, quantizer and diagnostics: 2, 3, 4, 5, 6 and 8 bits.
+// Every entry point: 2, 3, 4, 5, 6 and 8 bits, groups of 64.
 int check_format(const char* fn, int bits, int group_size) {
   if (bits < 2 || bits > 8 || bits == 7)
     return fail(QMM_ERR_UNSUPPORTED, "%s: bits=%d not supported (2, 3, 4, 5, 6 or 8)", fn, bits);
@@ -53,12 +53,7 @@ int check_format(const char* fn, int bits, int group_size) {
   return QMM_OK;
 }
 
-// GEMM, batched GEMM and grouped GEMM: 2, 4 and 8 bits.
-int check_gemm_format(const char* fn, int bits, int group_size) {
-  if (bits != 2 && bits != 4 && bits != 8)
-    return fail(QMM_ERR_UNSUPPORTED, "%s: bits=%d not supported (2, 4 or 8)", fn, bits);
-  return check_format(fn, bits, group_size);
-}
+
 
 int check_nk(const char* fn, int n, int k) {
   if (n < 1) return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be >= 1", fn, n);
@@ -197,7 +192,7 @@ int qmm_qgemv_batched(const void* plan_device, const void* plan_host, qmm_stream
 
 size_t qmm_qgemm_workspace_size(int m, int n, int k, int bits, int group_size) {
   if (m < 1 || n < 1 || k < 64 || k % 64 != 0 || group_size != 64) return 0;
-  if (bits != 2 && bits != 4 && bits != 8) return 0;
+  if (bits < 2 || bits > 8 || bits == 7) return 0;
   return qmm::gemm_workspace_bytes(m, n, k, bits);
 }
 
@@ -206,7 +201,7 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
               void* workspace, size_t workspace_bytes, qmm_stream stream) {
   const char* fn = "qmm_qgemm";
   clear_error();
-  if (int st = check_gemm_format(fn, bits, group_size)) return st;
+  if (int st = check_format(fn, bits, group_size)) return st;
   if (m < 0) return fail(QMM_ERR_INVALID_ARG, "%s: m=%d must be >= 0", fn, m);
   if (int st = check_nk(fn, n, k)) return st;
   if (m == 0) return QMM_OK;
@@ -230,7 +225,7 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
                            size_t* plan_bytes_needed, size_t* workspace_bytes_needed) {
   const char* fn = "qmm_qgemm_batched_plan";
   clear_error();
-  if (int st = check_gemm_format(fn, bits, group_size)) return st;
+  if (int st = check_format(fn, bits, group_size)) return st;
   if (count < 1) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d must be >= 1", fn, count);
   if (count > (1 << 20)) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d too large", fn, count);
   if (problems == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: null problems", fn);
@@ -287,7 +282,7 @@ int qmm_qgemm_batched(const void* plan_device, const void* plan_host, void* work
   memcpy(&hdr, plan_host, sizeof hdr);
   if (hdr.magic != qmm::kBatchMagic || hdr.version != qmm::kBatchVersion)
     return fail(QMM_ERR_INVALID_ARG, "%s: plan_host is not a batched-GEMM plan image", fn);
-  if (int st = check_gemm_format(fn, hdr.bits, hdr.group_size)) return st;
+  if (int st = check_format(fn, hdr.bits, hdr.group_size)) return st;
   if (hdr.count < 1 || hdr.num_tiles < 0 || hdr.splits < 1 ||
       !(hdr.bm == 32 || hdr.bm == 64 || hdr.bm == 128 || hdr.bm == 256) ||
       !(hdr.nb == 1 || hdr.nb == 2) || (hdr.bm == 256 && hdr.nb != 2))
@@ -316,7 +311,7 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
                       qmm_stream stream) {
   const char* fn = "qmm_qgemm_grouped";
   clear_error();
-  if (int st = check_gemm_format(fn, bits, group_size)) return st;
+  if (int st = check_format(fn, bits, group_size)) return st;
   if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
   if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
   if (e < 1 || e > kMaxExperts)

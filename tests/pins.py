@@ -245,7 +245,7 @@ def check_dot_exact_rational(o, seed=4):
     """4x64 brute force: y from the oracle equals the exact rational
     sum_k x_k * (s*q_k + b) within gamma_K * sum|x * W_hat|."""
     r = np.random.default_rng(seed)
-    for bits in (2, 4, 8):
+    for bits in (2, 3, 4, 5, 6, 8):
         w = (r.standard_normal((4, 64)) * 0.02).astype(np.float32)
         x = r.standard_normal((2, 64)).astype(np.float16)
         q, s, b = o.quantize(w, bits)

@@ -66,7 +66,7 @@ def test_gemv_errors(L):
 def test_gemm_errors(L):
     expect(L.qmm_qgemm(A, A, A, A, A, -1, 8, 64, 4, 64, None, 0, None), INV, "m=-1")
     expect(L.qmm_qgemm(A, A, A, A, A, 4, 8, 96, 4, 64, None, 0, None), INV, "k=96")
-    expect(L.qmm_qgemm(A, A, A, A, A, 4, 8, 64, 5, 64, None, 0, None), UNS, "bits=5")
+    expect(L.qmm_qgemm(A, A, A, A, A, 4, 8, 64, 7, 64, None, 0, None), UNS, "bits=7")
     expect(L.qmm_qgemm(A, A, A, MIS, A, 4, 8, 64, 4, 64, None, 0, None), INV, "x is not")
     assert L.qmm_qgemm_workspace_size(2048, 9728, 2560, 4, 64) == 0
 
@@ -86,8 +86,8 @@ def test_grouped_errors(L):
            INV, "top_k=0")
     expect(L.qmm_qgemm_grouped(A, A, A, A, 0, A + 2, A, 512, 8, 128, 768, 2048, 4, 64, A, ws, None),
            INV, "expert_ids is not 4-byte aligned")
-    expect(L.qmm_qgemm_grouped(A, A, A, A, 0, A, A, 512, 8, 128, 768, 2048, 6, 64, A, ws, None),
-           UNS, "bits=6")
+    expect(L.qmm_qgemm_grouped(A, A, A, A, 0, A, A, 512, 8, 128, 768, 2048, 7, 64, A, ws, None),
+           UNS, "bits=7")
 
 
 def test_other_errors(L):
@@ -231,8 +231,8 @@ def test_batched_gemm_plan_force_and_errors(L):
            "problem 1")
     expect(L.qmm_qgemm_batched_plan(probs, 0, 4, 64, None, 0, C.byref(need), C.byref(ws)), INV,
            "count=0")
-    expect(L.qmm_qgemm_batched_plan(probs, 2, 3, 64, None, 0, C.byref(need), C.byref(ws)), UNS,
-           "bits=3")
+    expect(L.qmm_qgemm_batched_plan(probs, 2, 7, 64, None, 0, C.byref(need), C.byref(ws)), UNS,
+           "bits=7")
     bad = (C.c_uint8 * 64)()
     expect(L.qmm_qgemm_batched(A, bad, None, 0, None), INV, "not a batched-GEMM plan")
     # a split plan refuses a missing or short workspace before any launch

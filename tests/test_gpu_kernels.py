@@ -1,4 +1,5 @@
-"""GPU parity of every kernel against the CPU oracle, through the C ABI.
+"""GPU parity of every kernel against the CPU oracle, through the C ABI, for
+2-, 3-, 4-, 5-, 6- and 8-bit weights.
 
 Bit-exact: code unpack, dequantization (fp32 and fp16) and the quantizer.
 Within tolerance (relative L2 <= 1e-3, max |err| <= 1e-2 against float64):
@@ -19,13 +20,12 @@ if not torch.cuda.is_available():
 
 import quantized_matmul_qgemv_amd as qmm  # noqa: E402
 
-BITS = (2, 4, 8)               # every kernel
-BITS_ALL = (2, 3, 4, 5, 6, 8)  # GEMV, quantizer and diagnostics
+BITS = (2, 3, 4, 5, 6, 8)
 
 
 # ------------------------------------------------------------ bit-exact --
 
-@pytest.mark.parametrize("bits", BITS_ALL)
+@pytest.mark.parametrize("bits", BITS)
 def test_unpack_codes_bit_exact(bits):
     say("unpack", bits)
     r = np.random.default_rng(100 + bits)
@@ -39,7 +39,7 @@ def test_unpack_codes_bit_exact(bits):
     assert np.array_equal(got, codes)
 
 
-@pytest.mark.parametrize("bits", BITS_ALL)
+@pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("f16", [False, True])
 def test_dequant_bit_exact(bits, f16):
     say("dequant", bits, f16)
@@ -78,7 +78,7 @@ def quantize_cases():
     return np.concatenate(rows)
 
 
-@pytest.mark.parametrize("bits", BITS_ALL)
+@pytest.mark.parametrize("bits", BITS)
 def test_quantize_bit_exact(bits):
     say("quantize", bits)
     w = quantize_cases()
@@ -95,7 +95,7 @@ GEMV_SHAPES = [(1, 64), (3, 128), (37, 192), (100, 320), (1000, 1024), (1024, 10
                (300, 2048), (129, 2560), (513, 3072), (64, 8192), (7, 9728)]
 
 
-@pytest.mark.parametrize("bits", BITS_ALL)
+@pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("n,k", GEMV_SHAPES)
 def test_gemv_parity(bits, n, k):
     say("gemv", bits, n, k)
@@ -123,7 +123,7 @@ def test_gemv_integer_closed_form():
     integer matmul, representable in fp32, so the GPU must hit it exactly."""
     say("gemv integer")
     r = np.random.default_rng(5)
-    for bits in BITS_ALL:
+    for bits in BITS:
         n, k = 96, 512
         codes = r.integers(0, 1 << bits, (n, k), dtype=np.uint8)
         words = oracle.pack(codes, bits)
@@ -134,7 +134,7 @@ def test_gemv_integer_closed_form():
         assert np.array_equal(y.astype(np.float64), (codes.astype(np.int64) @ xi).astype(np.float64))
 
 
-@pytest.mark.parametrize("bits", BITS_ALL)
+@pytest.mark.parametrize("bits", BITS)
 def test_gemv_batched_mixed_shapes(bits):
     say("gemv batched", bits)
     shapes = [(2048, 1024), (1024, 1024), (1024, 2048), (3072, 1024), (1024, 3072), (999, 1024)]
@@ -224,13 +224,13 @@ def test_gemm_batched_parity(bits):
         assert_close(host(t[4]), want, f"batched bits={bits} m={m} n={n} k={k} {plan.header}")
 
 
+@pytest.mark.parametrize("bits", [4, 3, 5, 6])
 @pytest.mark.parametrize("bm,nb", BATCH_CFGS)
 @pytest.mark.parametrize("splits", [1, 3])
-def test_gemm_batched_forced_tiles_and_split_k(bm, nb, splits, monkeypatch):
+def test_gemm_batched_forced_tiles_and_split_k(bits, bm, nb, splits, monkeypatch):
     """Every tile shape, with and without k split: parity and identical
     results on a second call over a dirtied workspace."""
-    bits = 4
-    say("gemm batched forced", bm, nb, splits)
+    say("gemm batched forced", bits, bm, nb, splits)
     shapes = [(70, 520, 1024), (300, 200, 768), (1, 64, 256)]
     ins, wants = _batch_inputs(bits, shapes, 922)
     monkeypatch.setenv("QMM_GEMM_FORCE", f"{bm},{nb},{splits}")
