@@ -25,6 +25,9 @@ The same JSON line carries, measured in the same run:
   decode_context the lm_head alone, the decode pass as 197 sequential launches
                 replayed as one HIP graph, and that graph's per-launch floor;
   decode_q8     the Llama-3.2-3B-shaped 8-bit decode sweep (196 GEMVs);
+  decode_formats the Qwen3-0.6B-shaped decode pass with 2-, 3-, 5- and 6-bit
+                weights (one batched launch each);
+  gemm_formats  one 2048 x 9728 x 2560 prefill GEMM per weight width;
   single_gemv   one 1x1024x1024 4-bit GEMV launch (latency).
 Inputs are seeded synthetic tensors with the models' shapes (weights
 N(0, 0.02) quantized on the GPU by qmm_quantize, activations N(0, 1) fp16).
@@ -32,6 +35,7 @@ N(0, 0.02) quantized on the GPU by qmm_quantize, activations N(0, 1) fp16).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -58,9 +62,9 @@ TRAFFIC = {
     # (KiB per dispatch of qgemv_batched_kernel<4,16,4>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 166787.5, "fetch_scale": 1073741824 / (524300.0 * 1024),
+    "fetch_kib": 166803.5, "fetch_scale": 1073741824 / (524301.3 * 1024),
     "write_kib": 1939.0, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "32f55790dd41e64a48a6d4a8446474a50898d7228b4a81cdf93f435842d107f8",
+    "sources_sha256": "74cd8cc7fdbca88c2327974439554286c6b998dda6f59715095c3f8a9cda630b",
 }
 
 
@@ -137,6 +141,45 @@ def bench_decode(torch, qmm, wl, steps, warmup, copies=2):
     ms_step, wall = time_launches(
         torch, lambda i: qmm.qgemv_batched(plans[i % copies]), steps, warmup, stream)
     return dict(sets=sets, plans=plans, step_bytes=step_bytes, ms_step=ms_step, wall=wall)
+
+
+def bench_decode_formats(torch, qmm, wl, bits_list=(2, 3, 5, 6), steps=20, warmup=3):
+    """The same decode pass (one batched launch of all its GEMVs) with the
+    weights quantized to other widths: streaming rate per format."""
+    out = {}
+    for bits in bits_list:
+        w = dataclasses.replace(wl, bits=bits, name=f"{wl.name}@q{bits}")
+        d = bench_decode(torch, qmm, w, steps, warmup)
+        gbs = d["step_bytes"] / (d["ms_step"] * 1e-3) / 1e9
+        out[f"q{bits}"] = {"bytes_per_step": d["step_bytes"], "ms_per_step": round(d["ms_step"], 5),
+                           "gb_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del d
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_gemm_formats(torch, qmm, m=2048, n=9728, k=2560, bits_list=(2, 3, 4, 5, 6, 8),
+                       steps=20, warmup=3):
+    """One M x N x K prefill GEMM (the gate projection at M = 2048) per
+    weight width, TFLOP/s against the fp16 matrix-core peak."""
+    out = {}
+    wf = torch.from_numpy(synth.draw_weight((9, m, n, k), n, k)).cuda()
+    x = torch.from_numpy(synth.draw_act((9, m, n, k + 1), m, k)).cuda()
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for bits in bits_list:
+        wq = qmm.quantize(wf, bits)
+        ws = torch.empty(max(qmm.qgemm_workspace_size(m, n, k, bits), 16), dtype=torch.uint8, device="cuda")
+        ms_call, _ = time_launches(torch, lambda i: qmm.qgemm(*wq, x, bits, y=y, workspace=ws),
+                                   steps, warmup, stream)
+        tfl = 2.0 * m * n * k / (ms_call * 1e-3) / 1e12
+        out[f"q{bits}"] = {"ms_per_call": round(ms_call, 4), "tflops": round(tfl, 1),
+                           "frac_of_fp16_peak": round(tfl / FP16_MFMA_PEAK_TFLOPS, 4)}
+        del wq, ws
+    del wf, x, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_single_gemv(torch, qmm, steps=200, warmup=20):
@@ -443,11 +486,15 @@ def main():
                                "gb_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         del q8
         torch.cuda.empty_cache()
+        log("decode formats")
+        result["decode_formats"] = {"workload": wl.name + " shapes", **bench_decode_formats(torch, qmm, wl)}
         log("prefill")
         result["prefill"] = {"workload": synth.QWEN3_4B_Q4_PREFILL.name,
                              "peak_tflops": FP16_MFMA_PEAK_TFLOPS,
                              "by_m": bench_prefill(torch, qmm, synth.QWEN3_4B_Q4_PREFILL.ms)}
         torch.cuda.empty_cache()
+        log("gemm formats")
+        result["gemm_formats"] = {"shape": [2048, 9728, 2560], **bench_gemm_formats(torch, qmm)}
         log("moe")
         result["moe"] = {"workload": synth.QWEN3_30B_A3B_Q4_MOE.name, "by_m": bench_moe(torch, qmm)}
     if not args.no_cpu:
