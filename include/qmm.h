@@ -36,8 +36,8 @@
  *
  * Common rules
  * ------------
- *   * Supported: bits in {2, 3, 4, 5, 6, 8}; group_size == 64; k a positive multiple
- *     of 64; n, m >= 1 (m = 0 / t = 0 is accepted and does nothing).
+ *   * Supported: bits in {2, 3, 4, 5, 6, 8}; group_size in {32, 64, 128}; k a positive
+ *     multiple of 64 and of group_size; n, m >= 1 (m = 0 / t = 0 is accepted and does nothing).
  *   * Every tensor pointer is a DEVICE pointer owned by the caller, 16-byte
  *     aligned, and must stay valid until the stream reaches the launch.
  *     Output buffers must not overlap inputs.

@@ -161,10 +161,10 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_kernel(GroupedArgs a, co
   auto c_row = [&](int i) { return i < rows ? pair_of[i] : -1; };
   const int groups = a.k >> 6;
   const size_t wstride = (size_t)a.n * groups * Fmt<BITS>::WORDS_PER_GROUP;
-  const size_t sstride = (size_t)a.n * groups;
+  const size_t sstride = (size_t)a.n * (a.k / a.group_size);
   gemm_tile<BITS, BM, NB, SBQ>(ARows{a.a, a.k}, a_row, c_row, a.w + mt.expert * wstride,
                                a.s + mt.expert * sstride, a.b + mt.expert * sstride, a.y + tn * BN,
-                               a.n, tn * BN, a.n, 0, groups, lds);
+                               a.n, tn * BN, a.n, 0, groups, lds, a.group_size);
 }
 
 template <int BITS, int BM, int NB, bool SBQ>
@@ -205,7 +205,7 @@ static hipError_t launch_grouped_sbq(const GroupedArgs& a, int32_t* ws, hipStrea
 
 template <int BITS>
 static hipError_t launch_grouped_bits(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
-  return (a.k / 64) % 4 == 0 ? launch_grouped_sbq<BITS, true>(a, ws, st)
+  return (a.k / 64) % 4 == 0 && a.group_size == 64 ? launch_grouped_sbq<BITS, true>(a, ws, st)
                              : launch_grouped_sbq<BITS, false>(a, ws, st);
 }
 

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int g0 = split * gr.gps_split;
   const int g1 = g0 + gr.gps_split;
   gemm_tile<BITS, BM, NB, SBQ>(ARows{a.x, a.k}, a_row, c_row, a.w, a.s, a.b, out + n0, a.n, n0,
-                               a.n, g0, g1, lds);
+                               a.n, g0, g1, lds, a.group_size);
 }
 
 // 256 x 256 tiles, one workgroup per CU (qgemm_wide.h); same tile order as
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1)
   const int g0 = split * gr.gps_split;
   const int g1 = g0 + gr.gps_split;
   gemm_tile_wide<BITS, SBQ>(ARows{a.x, a.k}, a_row, c_row, a.w, a.s, a.b, out + n0, a.n, n0, a.n,
-                            g0, g1, lds);
+                            g0, g1, lds, a.group_size);
 }
 
 // y[i] = sum over splits of partial[split * stride + i], in split order.
@@ -158,7 +158,7 @@ static hipError_t launch_wide(const GemmArgs& a, const GemmPlan& p, float* ws, h
 template <int BITS, int BM>
 static hipError_t launch_bm(const GemmArgs& a, const GemmPlan& p, float* ws, hipStream_t st) {
   // quad scale loads need every split to start and end on a multiple of 4 groups
-  const bool sbq = ((a.k / 64) / p.splits) % 4 == 0;
+  const bool sbq = ((a.k / 64) / p.splits) % 4 == 0 && a.group_size == 64;
   if (p.nb == 2)
     return sbq ? launch_tile<BITS, BM, 2, true>(a, p, ws, st) : launch_tile<BITS, BM, 2, false>(a, p, ws, st);
   return sbq ? launch_tile<BITS, BM, 1, true>(a, p, ws, st) : launch_tile<BITS, BM, 1, false>(a, p, ws, st);
@@ -170,7 +170,7 @@ static hipError_t launch_bits(const GemmArgs& a, const GemmPlan& p, float* ws, h
     case 32: return launch_bm<BITS, 32>(a, p, ws, st);
     case 64: return launch_bm<BITS, 64>(a, p, ws, st);
     case 256:
-      return ((a.k / 64) / p.splits) % 4 == 0 ? launch_wide<BITS, true>(a, p, ws, st)
+      return ((a.k / 64) / p.splits) % 4 == 0 && a.group_size == 64 ? launch_wide<BITS, true>(a, p, ws, st)
                                               : launch_wide<BITS, false>(a, p, ws, st);
     default: return launch_bm<BITS, 128>(a, p, ws, st);
   }

@@ -71,9 +71,14 @@ struct BRaw {
   uint16_t s, b;
 };
 
+// Scale/bias index of lane half h at 64-code step g for groups of gs codes.
+__device__ __forceinline__ int sb_index(int g, int h, int gs) {
+  return gs == 64 ? g : gs == 32 ? 2 * g + h : (g >> 1);
+}
+
 template <int BITS, bool WITH_SB = true>
 __device__ __forceinline__ void load_braw(BRaw<BITS>& r, gptr<uint32_t> wcol, gptr<uint16_t> scol,
-                                          gptr<uint16_t> bcol, int g, int h) {
+                                          gptr<uint16_t> bcol, int g, int h, int gs) {
   constexpr int WPG = Fmt<BITS>::WORDS_PER_GROUP;
   gptr<uint32_t> p = wcol + (size_t)g * WPG + h * (WPG / 2);
   if constexpr (BITS == 6) {
@@ -98,8 +103,9 @@ __device__ __forceinline__ void load_braw(BRaw<BITS>& r, gptr<uint32_t> wcol, gp
     }
   }
   if constexpr (WITH_SB) {
-    r.s = scol[g];
-    r.b = bcol[g];
+    const int si = sb_index(g, h, gs);
+    r.s = scol[si];
+    r.b = bcol[si];
   }
 }
 
@@ -156,7 +162,8 @@ struct ARows {
   int k;
 };
 
-// One BM x BN output tile over the k groups [g_begin, g_end).  a_row(i)
+// One BM x BN output tile over the k groups [g_begin, g_end).  gs is the
+// scale group size (32, 64 or 128 codes; SBQ only with 64).  a_row(i)
 // gives the source row of tile row i (already clamped to a valid row);
 // c_row(i) gives the output row or -1 to skip.  Weight columns start at n0
 // and are bounded by n; output column n0 + c goes to y_tile[row * ldy + c]
@@ -179,7 +186,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
                                           const uint16_t* __restrict__ s_,
                                           const uint16_t* __restrict__ b_, float* __restrict__ y_tile,
                                           int ldy, int n0, int n, int g_begin, int g_end,
-                                          uint16_t* lds) {
+                                          uint16_t* lds, int gs = 64) {
   constexpr int MB = BM / 32;
   constexpr int SPANS = BM * 4;  // 16-wide spans of A per step
   constexpr int SPT = (SPANS + kGemmThreads - 1) / kGemmThreads;
@@ -190,6 +197,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   const gptr_mut<float> y = to_global_mut(y_tile);
   const gptr<uint16_t> abase = to_global(A.base);
   const int groups = A.k >> 6;
+  const int sgroups = A.k / gs;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -204,8 +212,8 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
     int col = n0 + (wave * NB + nb) * 32 + l32;
     col = col < n ? col : n - 1;
     wcol[nb] = w + (size_t)col * groups * WPG;
-    scol[nb] = s + (size_t)col * groups;
-    bcol[nb] = b + (size_t)col * groups;
+    scol[nb] = s + (size_t)col * sgroups;
+    bcol[nb] = b + (size_t)col * sgroups;
   }
 
   gptr<uint16_t> asrc[SPT];
@@ -268,7 +276,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   auto load_b = [&](BRaw<BITS> (&dst)[NB], int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      load_braw<BITS, !SBQ>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h);
+      load_braw<BITS, !SBQ>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs);
   };
   // SBQ: scales and biases of four consecutive groups come in one 8-byte
   // load per column (a 2-byte load touches as many cache lines as a wide

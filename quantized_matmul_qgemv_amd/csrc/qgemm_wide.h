@@ -33,7 +33,7 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
                                                const uint16_t* __restrict__ s_,
                                                const uint16_t* __restrict__ b_,
                                                float* __restrict__ y_tile, int ldy, int n0, int n,
-                                               int g_begin, int g_end, uint16_t* lds) {
+                                               int g_begin, int g_end, uint16_t* lds, int gs = 64) {
   constexpr int BM = kWideBM;
   constexpr int MB = BM / 32;
   constexpr int NB = 2;
@@ -46,6 +46,7 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
   const gptr_mut<float> y = to_global_mut(y_tile);
   const gptr<uint16_t> abase = to_global(A.base);
   const int groups = A.k >> 6;
+  const int sgroups = A.k / gs;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -60,8 +61,8 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
     int col = n0 + (wave * NB + nb) * 32 + l32;
     col = col < n ? col : n - 1;
     wcol[nb] = w + (size_t)col * groups * WPG;
-    scol[nb] = s + (size_t)col * groups;
-    bcol[nb] = b + (size_t)col * groups;
+    scol[nb] = s + (size_t)col * sgroups;
+    bcol[nb] = b + (size_t)col * sgroups;
   }
   gptr<uint16_t> asrc[SPT];
   int aoff[SPT];
@@ -114,7 +115,7 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
   auto load_b = [&](BRaw<BITS> (&dst)[NB], int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      load_braw<BITS, !SBQ>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h);
+      load_braw<BITS, !SBQ>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs);
   };
   auto load_sbq = [&](u32x2 (&sq)[NB], u32x2 (&bq)[NB], int g4) {
 #pragma unroll

@@ -75,9 +75,9 @@ __device__ __forceinline__ void stage_x_load(gptr<uint16_t> x, int groups, XStag
 }
 
 // One quarter group (16 codes) -> paired halves in LDS and its share of (C, X).
-template <int BITS>
+template <int BITS, int GS>
 __device__ __forceinline__ void stage_quarter(const uint32_t (&d)[8], int g, int part, bool on,
-                                              unsigned char* xp, float2* cx) {
+                                              unsigned char* xp, float* cx) {
   using F = Fmt<BITS>;
   float csum = 0.0f, xsum = 0.0f;
   uint32_t out[8];
@@ -124,19 +124,24 @@ __device__ __forceinline__ void stage_quarter(const uint32_t (&d)[8], int g, int
   }
   csum += __shfl_xor(csum, 1);
   xsum += __shfl_xor(xsum, 1);
-  csum += __shfl_xor(csum, 2);
-  xsum += __shfl_xor(xsum, 2);
-  if (on && part == 0) cx[g] = make_float2(csum, xsum);
+  if constexpr (GS == 32) {
+    // (C, X) of each 32-code half: {C_lo, X_lo, C_hi, X_hi} per group
+    if (on && (part & 1) == 0) reinterpret_cast<float2*>(cx)[2 * g + (part >> 1)] = make_float2(csum, xsum);
+  } else {
+    csum += __shfl_xor(csum, 2);
+    xsum += __shfl_xor(xsum, 2);
+    if (on && part == 0) reinterpret_cast<float2*>(cx)[g] = make_float2(csum, xsum);
+  }
 }
 
-template <int BITS>
+template <int BITS, int GS>
 __device__ __forceinline__ void stage_x_store(gptr<uint16_t> x, int groups, const XStage& xs,
-                                              unsigned char* xp, float2* cx) {
+                                              unsigned char* xp, float* cx) {
   const int quarters = 4 * groups;
 #pragma unroll
   for (int r = 0; r < kXRounds; ++r) {
     const int t = threadIdx.x + r * kGemvThreads;
-    stage_quarter<BITS>(xs.d[r], t >> 2, t & 3, t < quarters, xp, cx);
+    stage_quarter<BITS, GS>(xs.d[r], t >> 2, t & 3, t < quarters, xp, cx);
   }
   // quarters beyond the register rounds (k > 8192): load and stage directly
   const int rounds = (quarters + kGemvThreads - 1) / kGemvThreads;  // uniform
@@ -148,7 +153,7 @@ __device__ __forceinline__ void stage_x_store(gptr<uint16_t> x, int groups, cons
     const u32x4 v0 = src[0], v1 = src[1];
     d[0] = v0.x; d[1] = v0.y; d[2] = v0.z; d[3] = v0.w;
     d[4] = v1.x; d[5] = v1.y; d[6] = v1.z; d[7] = v1.w;
-    stage_quarter<BITS>(d, t0 >> 2, t0 & 3, t0 < quarters, xp, cx);
+    stage_quarter<BITS, GS>(d, t0 >> 2, t0 & 3, t0 < quarters, xp, cx);
   }
 }
 
@@ -162,19 +167,23 @@ struct GroupLoad {
   static constexpr int NV = BYTES / VB;                // loads per group
 };
 
-template <int BITS, int UR, bool CH = Fmt<BITS>::CHUNKED>
+// SBN scale/bias pairs per 64-code group: 2 for groups of 32, else 1.
+template <int BITS, int UR, int SBN, bool CH = Fmt<BITS>::CHUNKED>
 struct StepBuf {
   u32x4 w[UR][Fmt<BITS>::VEC4_PER_GROUP];
-  uint16_t s[UR], b[UR];
+  uint16_t s[UR][SBN], b[UR][SBN];
 };
 
-template <int BITS, int UR>
-struct StepBuf<BITS, UR, true> {
+template <int BITS, int UR, int SBN>
+struct StepBuf<BITS, UR, SBN, true> {
   uint32_t w[UR][Fmt<BITS>::WORDS_PER_GROUP];
-  uint16_t s[UR], b[UR];
+  uint16_t s[UR][SBN], b[UR][SBN];
 };
 
-template <int BITS, int LPR, int UR, int WK>
+// GS: codes per scale/bias group (32, 64 or 128); the kernel works in
+// 64-code units throughout, with two scale groups per unit for GS = 32 and
+// one scale group per two units for GS = 128.
+template <int BITS, int LPR, int UR, int WK, int GS>
 __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int nrows,
                                            unsigned char* smem) {
   using F = Fmt<BITS>;
@@ -182,12 +191,14 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   constexpr int V4 = F::VEC4_PER_GROUP;
   constexpr int WPG = F::WORDS_PER_GROUP;
   constexpr int PPW = F::PAIRS_PER_WORD;
-  using Buf = StepBuf<BITS, UR>;
+  constexpr int SBN = GS == 32 ? 2 : 1;
+  using Buf = StepBuf<BITS, UR, SBN>;
 
   const int groups = P.k >> 6;
+  const int sgroups = P.k / GS;  // scale groups per row
   unsigned char* xp = smem;
-  float2* cx = reinterpret_cast<float2*>(smem + (size_t)groups * kXStride);
-  float* red = reinterpret_cast<float*>(cx + groups);
+  float* cx = reinterpret_cast<float*>(smem + (size_t)groups * kXStride);  // 2 or 4 floats per unit
+  float* red = cx + (size_t)groups * 2 * SBN;
 
   const gptr<uint32_t> W = to_global(P.w);
   const gptr<uint16_t> S = to_global(P.s);
@@ -239,8 +250,12 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
 #pragma unroll
         for (int v = 0; v < V4; ++v) bf.w[u][v] = src[v];
       }
-      bf.s[u] = S[(size_t)r * groups + g];
-      bf.b[u] = B[(size_t)r * groups + g];
+#pragma unroll
+      for (int q = 0; q < SBN; ++q) {
+        const size_t si = (size_t)r * sgroups + (GS == 32 ? 2 * g + q : GS == 128 ? (g >> 1) : g);
+        bf.s[u][q] = S[si];
+        bf.b[u][q] = B[si];
+      }
     }
     if (++it == tcount) { it = 0; ++ip; }
   };
@@ -253,7 +268,6 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   auto consume = [&](const Buf& bf) {
     const int g = (wk + ct * WK) * LPR + lr;
     const unsigned char* xg = xp + (size_t)g * kXStride;
-    const float2 c = cx[g];
     float a0[UR], a1[UR];
 #pragma unroll
     for (int u = 0; u < UR; ++u) a0[u] = a1[u] = 0.0f;
@@ -268,10 +282,19 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
           uint32_t vlo, vhi, h[4];
           chunk_window<BITS * m, WPG>(bf.w[u], vlo, vhi);
           unpack_chunk<BITS>(vlo, vhi, h);
-          a0[u] = dot2(h[0], xr[0], a0[u]);
-          a1[u] = dot2(h[1], xr[1], a1[u]);
-          a0[u] = dot2(h[2], xr[2], a0[u]);
-          a1[u] = dot2(h[3], xr[3], a1[u]);
+          if constexpr (GS == 32) {
+            // chunks 0..3 are the first 32-code scale group, 4..7 the second
+            float& a = m < 4 ? a0[u] : a1[u];
+            a = dot2(h[0], xr[0], a);
+            a = dot2(h[1], xr[1], a);
+            a = dot2(h[2], xr[2], a);
+            a = dot2(h[3], xr[3], a);
+          } else {
+            a0[u] = dot2(h[0], xr[0], a0[u]);
+            a1[u] = dot2(h[1], xr[1], a1[u]);
+            a0[u] = dot2(h[2], xr[2], a0[u]);
+            a1[u] = dot2(h[3], xr[3], a1[u]);
+          }
         }
       };
       chunk(std::integral_constant<int, 0>{});
@@ -306,17 +329,34 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
         unpack_word<BITS>(word, h);
 #pragma unroll
         for (int p = 0; p < PPW; ++p) {
-          if ((p & 1) == 0) a0[u] = dot2(h[p], xr[p], a0[u]);
-          else              a1[u] = dot2(h[p], xr[p], a1[u]);
+          if constexpr (GS == 32) {
+            // words 0 .. WPG/2-1 hold the first 32-code scale group
+            if (j < WPG / 2) a0[u] = dot2(h[p], xr[p], a0[u]);
+            else             a1[u] = dot2(h[p], xr[p], a1[u]);
+          } else {
+            if ((p & 1) == 0) a0[u] = dot2(h[p], xr[p], a0[u]);
+            else              a1[u] = dot2(h[p], xr[p], a1[u]);
+          }
         }
       }
     }
     }
+    if constexpr (GS == 32) {
+      const float4 c = reinterpret_cast<const float4*>(cx)[g];  // C_lo, X_lo, C_hi, X_hi
 #pragma unroll
-    for (int u = 0; u < UR; ++u) {
-      const float s = f16_bits_to_f32(bf.s[u]);
-      const float b = f16_bits_to_f32(bf.b[u]);
-      acc[u] = fmaf(s, (a0[u] + a1[u]) - c.x, fmaf(b, c.y, acc[u]));
+      for (int u = 0; u < UR; ++u) {
+        const float s0 = f16_bits_to_f32(bf.s[u][0]), b0 = f16_bits_to_f32(bf.b[u][0]);
+        const float s1 = f16_bits_to_f32(bf.s[u][1]), b1 = f16_bits_to_f32(bf.b[u][1]);
+        acc[u] = fmaf(s0, a0[u] - c.x, fmaf(b0, c.y, fmaf(s1, a1[u] - c.z, fmaf(b1, c.w, acc[u]))));
+      }
+    } else {
+      const float2 c = reinterpret_cast<const float2*>(cx)[g];
+#pragma unroll
+      for (int u = 0; u < UR; ++u) {
+        const float s = f16_bits_to_f32(bf.s[u][0]);
+        const float b = f16_bits_to_f32(bf.b[u][0]);
+        acc[u] = fmaf(s, (a0[u] + a1[u]) - c.x, fmaf(b, c.y, acc[u]));
+      }
     }
     if (++ct == tcount) {
       if constexpr (WK == 1) {
@@ -344,7 +384,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   XStage xs;
   stage_x_load(X, groups, xs);
   issue(b0);
-  stage_x_store<BITS>(X, groups, xs, xp, cx);
+  stage_x_store<BITS, GS>(X, groups, xs, xp, cx);
   __syncthreads();
 
   for (int st = 0; st < nsteps; st += 2) {
@@ -380,17 +420,17 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   }
 }
 
-template <int BITS, int LPR, int UR, int WK>
+template <int BITS, int LPR, int UR, int WK, int GS>
 __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4))) void qgemv_kernel(GemvProblem P, int rows_per_block) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  gemv_block<BITS, LPR, UR, WK>(P, blockIdx.x * rows_per_block, rows_per_block, smem);
+  gemv_block<BITS, LPR, UR, WK, GS>(P, blockIdx.x * rows_per_block, rows_per_block, smem);
 }
 
-template <int BITS, int LPR, int UR>
+template <int BITS, int LPR, int UR, int GS>
 __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4))) void qgemv_batched_kernel(const GemvBlock* __restrict__ blocks) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const GemvBlock blk = blocks[blockIdx.x];
-  gemv_block<BITS, LPR, UR, 1>(blk.p, blk.row0, blk.nrows, smem);
+  gemv_block<BITS, LPR, UR, 1, GS>(blk.p, blk.row0, blk.nrows, smem);
 }
 
 // ------------------------------------------------------------------ host --
@@ -428,88 +468,111 @@ GemvGeom gemv_choose(int n, int k, int bits) {
 }
 
 size_t gemv_lds_bytes(int max_groups, const GemvGeom& g) {
-  size_t bytes = (size_t)max_groups * (kXStride + sizeof(float2));
+  // per 64-code unit: paired x, and (C, X) once or (for groups of 32) twice
+  size_t bytes = (size_t)max_groups * (kXStride + sizeof(float4));
   if (g.wave_ksplit > 1) bytes += (size_t)g.rows_per_pass * g.wave_ksplit * sizeof(float);
   return bytes;
 }
 
-template <int BITS, int LPR, int UR, int WK>
+template <int BITS, int LPR, int UR, int WK, int GS>
 static hipError_t launch_one(const GemvProblem& p, const GemvGeom& g, hipStream_t st, size_t lds) {
   const int rows = GemvCfg<BITS, LPR, UR, WK>::ROWS * g.passes;
   const unsigned grid = (unsigned)((p.n + rows - 1) / rows);
-  hipLaunchKernelGGL((qgemv_kernel<BITS, LPR, UR, WK>), dim3(grid), dim3(kGemvThreads), lds, st, p,
+  hipLaunchKernelGGL((qgemv_kernel<BITS, LPR, UR, WK, GS>), dim3(grid), dim3(kGemvThreads), lds, st, p,
                      rows);
   return hipGetLastError();
 }
 
-template <int BITS, int LPR>
+template <int BITS, int LPR, int GS>
 static hipError_t launch_lpr(const GemvProblem& p, const GemvGeom& g, hipStream_t st, size_t lds) {
   constexpr int URB = gemv_ur(BITS);
-  if (g.row_unroll == URB && g.wave_ksplit == 1) return launch_one<BITS, LPR, URB, 1>(p, g, st, lds);
-  if (g.row_unroll == 1 && g.wave_ksplit == 1) return launch_one<BITS, LPR, 1, 1>(p, g, st, lds);
-  if (g.row_unroll == 1 && g.wave_ksplit == 4) return launch_one<BITS, LPR, 1, 4>(p, g, st, lds);
+  if (g.row_unroll == URB && g.wave_ksplit == 1) return launch_one<BITS, LPR, URB, 1, GS>(p, g, st, lds);
+  if (g.row_unroll == 1 && g.wave_ksplit == 1) return launch_one<BITS, LPR, 1, 1, GS>(p, g, st, lds);
+  if (g.row_unroll == 1 && g.wave_ksplit == 4) return launch_one<BITS, LPR, 1, 4, GS>(p, g, st, lds);
   return hipErrorInvalidValue;
 }
 
-template <int BITS>
+template <int BITS, int GS>
 static hipError_t launch_bits(const GemvProblem& p, const GemvGeom& g, hipStream_t st) {
   const size_t lds = gemv_lds_bytes(p.k / 64, g);
   switch (g.lanes_per_row) {
-    case 1: return launch_lpr<BITS, 1>(p, g, st, lds);
-    case 2: return launch_lpr<BITS, 2>(p, g, st, lds);
-    case 4: return launch_lpr<BITS, 4>(p, g, st, lds);
-    case 8: return launch_lpr<BITS, 8>(p, g, st, lds);
-    case 16: return launch_lpr<BITS, 16>(p, g, st, lds);
+    case 1: return launch_lpr<BITS, 1, GS>(p, g, st, lds);
+    case 2: return launch_lpr<BITS, 2, GS>(p, g, st, lds);
+    case 4: return launch_lpr<BITS, 4, GS>(p, g, st, lds);
+    case 8: return launch_lpr<BITS, 8, GS>(p, g, st, lds);
+    case 16: return launch_lpr<BITS, 16, GS>(p, g, st, lds);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_qgemv(const GemvProblem& p, int bits, const GemvGeom& g, hipStream_t st) {
+template <int GS>
+static hipError_t launch_gs(const GemvProblem& p, int bits, const GemvGeom& g, hipStream_t st) {
   switch (bits) {
-    case 2: return launch_bits<2>(p, g, st);
-    case 3: return launch_bits<3>(p, g, st);
-    case 4: return launch_bits<4>(p, g, st);
-    case 5: return launch_bits<5>(p, g, st);
-    case 6: return launch_bits<6>(p, g, st);
-    case 8: return launch_bits<8>(p, g, st);
+    case 2: return launch_bits<2, GS>(p, g, st);
+    case 3: return launch_bits<3, GS>(p, g, st);
+    case 4: return launch_bits<4, GS>(p, g, st);
+    case 5: return launch_bits<5, GS>(p, g, st);
+    case 6: return launch_bits<6, GS>(p, g, st);
+    case 8: return launch_bits<8, GS>(p, g, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int BITS, int LPR>
+hipError_t launch_qgemv(const GemvProblem& p, int bits, int group_size, const GemvGeom& g,
+                        hipStream_t st) {
+  switch (group_size) {
+    case 32: return launch_gs<32>(p, bits, g, st);
+    case 64: return launch_gs<64>(p, bits, g, st);
+    case 128: return launch_gs<128>(p, bits, g, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int BITS, int LPR, int GS>
 static hipError_t launch_batched_one(const GemvBlock* blocks, int num_blocks, size_t lds,
                                      hipStream_t st) {
   constexpr int URB = gemv_ur(BITS);
-  hipLaunchKernelGGL((qgemv_batched_kernel<BITS, LPR, URB>), dim3(num_blocks), dim3(kGemvThreads),
+  hipLaunchKernelGGL((qgemv_batched_kernel<BITS, LPR, URB, GS>), dim3(num_blocks), dim3(kGemvThreads),
                      lds, st, blocks);
   return hipGetLastError();
 }
 
-template <int BITS>
+template <int BITS, int GS>
 static hipError_t launch_batched_bits(const GemvBlock* blocks, int num_blocks, int lpr,
                                       size_t lds, hipStream_t st) {
   switch (lpr) {
-    case 1: return launch_batched_one<BITS, 1>(blocks, num_blocks, lds, st);
-    case 2: return launch_batched_one<BITS, 2>(blocks, num_blocks, lds, st);
-    case 4: return launch_batched_one<BITS, 4>(blocks, num_blocks, lds, st);
-    case 8: return launch_batched_one<BITS, 8>(blocks, num_blocks, lds, st);
-    case 16: return launch_batched_one<BITS, 16>(blocks, num_blocks, lds, st);
+    case 1: return launch_batched_one<BITS, 1, GS>(blocks, num_blocks, lds, st);
+    case 2: return launch_batched_one<BITS, 2, GS>(blocks, num_blocks, lds, st);
+    case 4: return launch_batched_one<BITS, 4, GS>(blocks, num_blocks, lds, st);
+    case 8: return launch_batched_one<BITS, 8, GS>(blocks, num_blocks, lds, st);
+    case 16: return launch_batched_one<BITS, 16, GS>(blocks, num_blocks, lds, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_qgemv_batched(const GemvBlock* blocks, int num_blocks, int bits,
+template <int GS>
+static hipError_t launch_batched_gs(const GemvBlock* blocks, int num_blocks, int bits, int lpr,
+                                    size_t lds, hipStream_t st) {
+  switch (bits) {
+    case 2: return launch_batched_bits<2, GS>(blocks, num_blocks, lpr, lds, st);
+    case 3: return launch_batched_bits<3, GS>(blocks, num_blocks, lpr, lds, st);
+    case 4: return launch_batched_bits<4, GS>(blocks, num_blocks, lpr, lds, st);
+    case 5: return launch_batched_bits<5, GS>(blocks, num_blocks, lpr, lds, st);
+    case 6: return launch_batched_bits<6, GS>(blocks, num_blocks, lpr, lds, st);
+    case 8: return launch_batched_bits<8, GS>(blocks, num_blocks, lpr, lds, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_qgemv_batched(const GemvBlock* blocks, int num_blocks, int bits, int group_size,
                                 int lanes_per_row, int max_groups, hipStream_t st) {
   GemvGeom g{lanes_per_row, gemv_row_unroll(bits), 1,
              gemv_rows_per_pass(lanes_per_row, gemv_row_unroll(bits), 1), 1};
   const size_t lds = gemv_lds_bytes(max_groups, g);
-  switch (bits) {
-    case 2: return launch_batched_bits<2>(blocks, num_blocks, lanes_per_row, lds, st);
-    case 3: return launch_batched_bits<3>(blocks, num_blocks, lanes_per_row, lds, st);
-    case 4: return launch_batched_bits<4>(blocks, num_blocks, lanes_per_row, lds, st);
-    case 5: return launch_batched_bits<5>(blocks, num_blocks, lanes_per_row, lds, st);
-    case 6: return launch_batched_bits<6>(blocks, num_blocks, lanes_per_row, lds, st);
-    case 8: return launch_batched_bits<8>(blocks, num_blocks, lanes_per_row, lds, st);
+  switch (group_size) {
+    case 32: return launch_batched_gs<32>(blocks, num_blocks, bits, lanes_per_row, lds, st);
+    case 64: return launch_batched_gs<64>(blocks, num_blocks, bits, lanes_per_row, lds, st);
+    case 128: return launch_batched_gs<128>(blocks, num_blocks, bits, lanes_per_row, lds, st);
     default: return hipErrorInvalidValue;
   }
 }

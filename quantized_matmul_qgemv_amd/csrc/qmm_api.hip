@@ -44,21 +44,23 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 constexpr int kGemvMaxK = 16384;
 constexpr int kMaxExperts = 1024;
 
-// Every entry point: 2, 3, 4, 5, 6 and 8 bits, groups of 64.
+// Every entry point: 2, 3, 4, 5, 6 and 8 bits, groups of 32, 64 or 128.
 int check_format(const char* fn, int bits, int group_size) {
   if (bits < 2 || bits > 8 || bits == 7)
     return fail(QMM_ERR_UNSUPPORTED, "%s: bits=%d not supported (2, 3, 4, 5, 6 or 8)", fn, bits);
-  if (group_size != 64)
-    return fail(QMM_ERR_UNSUPPORTED, "%s: group_size=%d not supported (64)", fn, group_size);
+  if (group_size != 32 && group_size != 64 && group_size != 128)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: group_size=%d not supported (32, 64 or 128)", fn, group_size);
   return QMM_OK;
 }
 
 
 
-int check_nk(const char* fn, int n, int k) {
+int check_nk(const char* fn, int n, int k, int group_size = 64) {
   if (n < 1) return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be >= 1", fn, n);
   if (k < 64 || k % 64 != 0)
-    return fail(QMM_ERR_INVALID_ARG, "%s: k=%d must be a positive multiple of group_size 64", fn, k);
+    return fail(QMM_ERR_INVALID_ARG, "%s: k=%d must be a positive multiple of 64", fn, k);
+  if (k % group_size != 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: k=%d must be a multiple of group_size %d", fn, k, group_size);
   return QMM_OK;
 }
 
@@ -76,7 +78,7 @@ int qmm_qgemv(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
   const char* fn = "qmm_qgemv";
   clear_error();
   if (int st = check_format(fn, bits, group_size)) return st;
-  if (int st = check_nk(fn, n, k)) return st;
+  if (int st = check_nk(fn, n, k, group_size)) return st;
   if (k > kGemvMaxK) return fail(QMM_ERR_INVALID_ARG, "%s: k=%d exceeds %d", fn, k, kGemvMaxK);
   CHECK_PTR(w, 16);
   CHECK_PTR(scales, 2);
@@ -85,7 +87,7 @@ int qmm_qgemv(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
   CHECK_PTR(y, 4);
   qmm::GemvProblem p{w, scales, biases, x, y, n, k};
   const qmm::GemvGeom g = qmm::gemv_choose(n, k, bits);
-  return hip_status(qmm::launch_qgemv(p, bits, g, (hipStream_t)stream), fn);
+  return hip_status(qmm::launch_qgemv(p, bits, group_size, g, (hipStream_t)stream), fn);
 }
 
 int qmm_qgemv_batched_plan(const qmm_gemv_problem* problems, int count, int bits,
@@ -99,7 +101,7 @@ int qmm_qgemv_batched_plan(const qmm_gemv_problem* problems, int count, int bits
   int lpr = 16, max_groups = 0;
   for (int i = 0; i < count; ++i) {
     const qmm_gemv_problem& q = problems[i];
-    if (check_nk(fn, q.n, q.k)) return fail(QMM_ERR_INVALID_ARG, "%s: problem %d: n=%d k=%d invalid", fn, i, q.n, q.k);
+    if (check_nk(fn, q.n, q.k, group_size)) return fail(QMM_ERR_INVALID_ARG, "%s: problem %d: n=%d k=%d invalid", fn, i, q.n, q.k);
     if (q.k > kGemvMaxK) return fail(QMM_ERR_INVALID_ARG, "%s: problem %d: k=%d exceeds %d", fn, i, q.k, kGemvMaxK);
     if (!q.w || !q.scales || !q.biases || !q.x || !q.y)
       return fail(QMM_ERR_INVALID_ARG, "%s: problem %d has a null pointer", fn, i);
@@ -185,13 +187,14 @@ int qmm_qgemv_batched(const void* plan_device, const void* plan_host, qmm_stream
     return fail(QMM_ERR_INVALID_ARG, "%s: corrupt plan header", fn);
   const qmm::GemvBlock* recs = reinterpret_cast<const qmm::GemvBlock*>(
       static_cast<const unsigned char*>(plan_device) + sizeof(qmm::GemvPlanHeader));
-  return hip_status(qmm::launch_qgemv_batched(recs, hdr.num_blocks, hdr.bits, hdr.lanes_per_row,
+  return hip_status(qmm::launch_qgemv_batched(recs, hdr.num_blocks, hdr.bits, hdr.group_size, hdr.lanes_per_row,
                                               hdr.max_groups, (hipStream_t)stream),
                     fn);
 }
 
 size_t qmm_qgemm_workspace_size(int m, int n, int k, int bits, int group_size) {
-  if (m < 1 || n < 1 || k < 64 || k % 64 != 0 || group_size != 64) return 0;
+  if (m < 1 || n < 1 || k < 64 || k % 64 != 0) return 0;
+  if ((group_size != 32 && group_size != 64 && group_size != 128) || k % group_size != 0) return 0;
   if (bits < 2 || bits > 8 || bits == 7) return 0;
   return qmm::gemm_workspace_bytes(m, n, k, bits);
 }
@@ -203,7 +206,7 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
   clear_error();
   if (int st = check_format(fn, bits, group_size)) return st;
   if (m < 0) return fail(QMM_ERR_INVALID_ARG, "%s: m=%d must be >= 0", fn, m);
-  if (int st = check_nk(fn, n, k)) return st;
+  if (int st = check_nk(fn, n, k, group_size)) return st;
   if (m == 0) return QMM_OK;
   CHECK_PTR(w, 16);
   CHECK_PTR(scales, 2);
@@ -216,7 +219,7 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
       return fail(QMM_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
     CHECK_PTR(workspace, 16);
   }
-  qmm::GemmArgs a{w, scales, biases, x, y, m, n, k};
+  qmm::GemmArgs a{w, scales, biases, x, y, m, n, k, group_size};
   return hip_status(qmm::launch_qgemm(a, bits, workspace, (hipStream_t)stream), fn);
 }
 
@@ -236,7 +239,7 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
     const qmm_gemm_problem& q = problems[i];
     int bad = 0;
     // an empty problem (m = 0) is never read or written: x and y may be null
-    if (q.m < 0 || check_nk(fn, q.n, q.k)) bad = 1;
+    if (q.m < 0 || check_nk(fn, q.n, q.k, group_size)) bad = 1;
     else if (!q.w || !q.scales || !q.biases || (q.m > 0 && (!q.x || !q.y))) bad = 2;
     else if (!aligned(q.w, 16) || !aligned(q.x, 16) || !aligned(q.y, 4) ||
              !aligned(q.scales, 2) || !aligned(q.biases, 2)) bad = 3;
@@ -254,7 +257,7 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
     probs[i].n = q.n;
     probs[i].k = q.k;
   }
-  const size_t need = qmm::gemm_batch_build(probs, count, bits, nullptr, 0);
+  const size_t need = qmm::gemm_batch_build(probs, count, bits, group_size, nullptr, 0);
   if (plan_bytes_needed) *plan_bytes_needed = need;
   if (plan == nullptr || plan_bytes < need) {
     free(probs);
@@ -264,7 +267,7 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
     free(probs);
     return fail(QMM_ERR_INVALID_ARG, "%s: plan is not 8-byte aligned", fn);
   }
-  qmm::gemm_batch_build(probs, count, bits, plan, plan_bytes);
+  qmm::gemm_batch_build(probs, count, bits, group_size, plan, plan_bytes);
   free(probs);
   qmm::GemmBatchHeader hdr;
   memcpy(&hdr, plan, sizeof hdr);
@@ -318,7 +321,7 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
     return fail(QMM_ERR_INVALID_ARG, "%s: e=%d must be in [1, %d]", fn, e, kMaxExperts);
   if (a_row_per_pair != 0 && a_row_per_pair != 1)
     return fail(QMM_ERR_INVALID_ARG, "%s: a_row_per_pair must be 0 or 1", fn);
-  if (int st = check_nk(fn, n, k)) return st;
+  if (int st = check_nk(fn, n, k, group_size)) return st;
   if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
   if (t == 0) return QMM_OK;
   CHECK_PTR(w, 16);
@@ -331,7 +334,7 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
   if (workspace == nullptr || workspace_bytes < need)
     return fail(QMM_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
   CHECK_PTR(workspace, 16);
-  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, expert_ids, y, t, top_k, e, n, k};
+  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, expert_ids, y, t, top_k, e, n, k, group_size};
   return hip_status(qmm::launch_qgemm_grouped(ga, bits, workspace, (hipStream_t)stream), fn);
 }
 
@@ -340,12 +343,12 @@ int qmm_quantize(const float* w_f32, uint32_t* words, uint16_t* scales, uint16_t
   const char* fn = "qmm_quantize";
   clear_error();
   if (int st = check_format(fn, bits, group_size)) return st;
-  if (int st = check_nk(fn, n, k)) return st;
+  if (int st = check_nk(fn, n, k, group_size)) return st;
   CHECK_PTR(w_f32, 16);
   CHECK_PTR(words, 4);
   CHECK_PTR(scales, 2);
   CHECK_PTR(biases, 2);
-  return hip_status(qmm::launch_quantize(w_f32, words, scales, biases, n, k, bits, (hipStream_t)stream), fn);
+  return hip_status(qmm::launch_quantize(w_f32, words, scales, biases, n, k, bits, group_size, (hipStream_t)stream), fn);
 }
 
 int qmm_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,
@@ -364,14 +367,14 @@ int qmm_dequant(const uint32_t* w, const uint16_t* scales, const uint16_t* biase
   const char* fn = "qmm_dequant";
   clear_error();
   if (int st = check_format(fn, bits, group_size)) return st;
-  if (int st = check_nk(fn, n, k)) return st;
+  if (int st = check_nk(fn, n, k, group_size)) return st;
   if (out_is_f16 != 0 && out_is_f16 != 1)
     return fail(QMM_ERR_INVALID_ARG, "%s: out_is_f16 must be 0 or 1", fn);
   CHECK_PTR(w, 4);
   CHECK_PTR(scales, 2);
   CHECK_PTR(biases, 2);
   CHECK_PTR(out, 4);
-  return hip_status(qmm::launch_dequant(w, scales, biases, out, out_is_f16, n, k, bits, (hipStream_t)stream), fn);
+  return hip_status(qmm::launch_dequant(w, scales, biases, out, out_is_f16, n, k, bits, group_size, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

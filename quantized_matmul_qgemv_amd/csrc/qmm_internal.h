@@ -60,8 +60,9 @@ int gemv_rows_per_pass(int lanes_per_row, int row_unroll, int wave_ksplit);
 int gemv_lanes_for_groups(int groups);
 size_t gemv_lds_bytes(int max_groups, const GemvGeom& g);
 
-hipError_t launch_qgemv(const GemvProblem& p, int bits, const GemvGeom& g, hipStream_t st);
-hipError_t launch_qgemv_batched(const GemvBlock* blocks, int num_blocks, int bits,
+hipError_t launch_qgemv(const GemvProblem& p, int bits, int group_size, const GemvGeom& g,
+                        hipStream_t st);
+hipError_t launch_qgemv_batched(const GemvBlock* blocks, int num_blocks, int bits, int group_size,
                                 int lanes_per_row, int max_groups, hipStream_t st);
 
 struct GemmArgs {
@@ -71,6 +72,7 @@ struct GemmArgs {
   const uint16_t* x;
   float* y;
   int m, n, k;
+  int group_size;  // codes per scale/bias group: 32, 64 or 128
 };
 size_t gemm_workspace_bytes(int m, int n, int k, int bits);
 hipError_t launch_qgemm(const GemmArgs& a, int bits, void* workspace, hipStream_t st);
@@ -130,8 +132,8 @@ void gemm_choose(int m, int n, int k, int* bm, int* nb, int* splits);
 
 // Choose the tile and split count for a batch and write the plan image.
 // Returns the image size; writes nothing when out is null or too small.
-size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, void* out,
-                        size_t out_bytes);
+size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, int group_size,
+                        void* out, size_t out_bytes);
 hipError_t launch_qgemm_batched(const void* plan_device, const GemmBatchHeader& hdr,
                                 void* workspace, hipStream_t st);
 
@@ -144,15 +146,16 @@ struct GroupedArgs {
   const int32_t* ids;
   float* y;
   int t, top_k, e, n, k;
+  int group_size;
 };
 size_t grouped_workspace_bytes(int t, int top_k, int e, int n);
 hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, hipStream_t st);
 
 hipError_t launch_quantize(const float* w, uint32_t* words, uint16_t* s, uint16_t* b, int n,
-                           int k, int bits, hipStream_t st);
+                           int k, int bits, int group_size, hipStream_t st);
 hipError_t launch_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,
                                hipStream_t st);
 hipError_t launch_dequant(const uint32_t* w, const uint16_t* s, const uint16_t* b, void* out,
-                          int out_is_f16, int n, int k, int bits, hipStream_t st);
+                          int out_is_f16, int n, int k, int bits, int group_size, hipStream_t st);
 
 }  // namespace qmm

@@ -1,6 +1,6 @@
 // Load-time quantization and the diagnostic unpack / dequant kernels.
 //
-// Quantization (asymmetric min/max per group of 64 along k): per group,
+// Quantization (asymmetric min/max per group of 32, 64 or 128 along k): per group,
 // s = fp16((max - min) / L), b = fp16(min), L = 2^bits - 1, in fp32 with IEEE
 // division and round-to-nearest-even; q = clamp(rint((w - b) / s), 0, L)
 // using the stored fp16 s and b; q = 0 everywhere when s == 0.  BaseRT
@@ -16,27 +16,27 @@
 
 namespace qmm {
 
-// One thread per (row, group).
-template <int BITS>
+// One thread per (row, group of GS codes).
+template <int BITS, int GS>
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w,
                                                        uint32_t* __restrict__ words,
                                                        uint16_t* __restrict__ s_out,
                                                        uint16_t* __restrict__ b_out,
                                                        int n, int groups) {
 #pragma clang fp contract(off)
-  using F = Fmt<BITS>;
+  constexpr int WPG = GS * BITS / 32;  // whole words: GS * BITS is a multiple of 32
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long)n * groups) return;
-  const float* src = w + gid * 64;  // row-major [n, k]: group gid starts at 64*gid
-  float v[64];
+  const float* src = w + gid * GS;  // row-major [n, k]: group gid starts at GS*gid
+  float v[GS];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < GS / 4; ++i) {
     const float4 f = reinterpret_cast<const float4*>(src)[i];
     v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
   }
   float mn = v[0], mx = v[0];
 #pragma unroll
-  for (int i = 1; i < 64; ++i) {
+  for (int i = 1; i < GS; ++i) {
     mn = fminf(mn, v[i]);
     mx = fmaxf(mx, v[i]);
   }
@@ -46,11 +46,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   const half_t b16 = (half_t)mn;
   const float sf = (float)s16;
   const float bf = (float)b16;
-  uint32_t out[F::WORDS_PER_GROUP];
+  uint32_t out[WPG];
 #pragma unroll
-  for (int j = 0; j < F::WORDS_PER_GROUP; ++j) out[j] = 0u;
+  for (int j = 0; j < WPG; ++j) out[j] = 0u;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
+  for (int i = 0; i < GS; ++i) {
     uint32_t q = 0;
     if (sf != 0.0f) {
       float t = __builtin_rintf(__fdiv_rn(v[i] - bf, sf));
@@ -61,9 +61,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     out[bit >> 5] |= q << (bit & 31);
     if ((bit & 31) + BITS > 32) out[(bit >> 5) + 1] |= q >> (32 - (bit & 31));  // straddles a word
   }
-  uint32_t* dst = words + gid * F::WORDS_PER_GROUP;
+  uint32_t* dst = words + gid * WPG;
 #pragma unroll
-  for (int j = 0; j < F::WORDS_PER_GROUP; ++j) dst[j] = out[j];
+  for (int j = 0; j < WPG; ++j) dst[j] = out[j];
   s_out[gid] = __builtin_bit_cast(uint16_t, s16);
   b_out[gid] = __builtin_bit_cast(uint16_t, b16);
 }
@@ -111,10 +111,10 @@ __global__ __launch_bounds__(256) void dequant_chunks_kernel(const uint32_t* __r
                                                              const uint16_t* __restrict__ s,
                                                              const uint16_t* __restrict__ b,
                                                              void* __restrict__ out, long words,
-                                                             long chunks) {
+                                                             long chunks, int gs) {
   const long c = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= chunks) return;
-  const long g = c >> 3;  // 8 chunks per 64-code group
+  const long g = c * 8 / gs;  // scale group of the chunk (a chunk never straddles one)
   uint32_t vlo, vhi, h[4];
   chunk_window_rt<BITS>(w, words, c, vlo, vhi);
   unpack_chunk<BITS>(vlo, vhi, h);
@@ -160,17 +160,17 @@ __global__ __launch_bounds__(256) void unpack_codes_kernel(const uint32_t* __res
   }
 }
 
-// One thread per packed word; every word lies in one group.
+// One thread per packed word; every word lies in one scale group.
 template <int BITS, bool F16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ w,
                                                       const uint16_t* __restrict__ s,
                                                       const uint16_t* __restrict__ b,
-                                                      void* __restrict__ out, long words) {
+                                                      void* __restrict__ out, long words, int gs) {
   using F = Fmt<BITS>;
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= words) return;
-  const long g = i / F::WORDS_PER_GROUP;  // global group index (row-major)
   const long k0 = i * F::CODES_PER_WORD;  // global code index
+  const long g = k0 / gs;                 // global scale-group index (row-major)
   if constexpr (F16) {
     const half_t sh = __builtin_bit_cast(half_t, s[g]);
     const half_t bh = __builtin_bit_cast(half_t, b[g]);
@@ -203,11 +203,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
 
 static unsigned blocks_for(long items) { return (unsigned)((items + 255) / 256); }
 
-hipError_t launch_quantize(const float* w, uint32_t* words, uint16_t* s, uint16_t* b, int n,
-                           int k, int bits, hipStream_t st) {
-  const int groups = k / 64;
+template <int GS>
+static hipError_t launch_quantize_gs(const float* w, uint32_t* words, uint16_t* s, uint16_t* b,
+                                     int n, int k, int bits, hipStream_t st) {
+  const int groups = k / GS;
   const unsigned grid = blocks_for((long)n * groups);
-#define QMM_Q(B) hipLaunchKernelGGL(quantize_kernel<B>, dim3(grid), dim3(256), 0, st, w, words, s, b, n, groups)
+#define QMM_Q(B) hipLaunchKernelGGL((quantize_kernel<B, GS>), dim3(grid), dim3(256), 0, st, w, words, s, b, n, groups)
   switch (bits) {
     case 2: QMM_Q(2); break;
     case 3: QMM_Q(3); break;
@@ -219,6 +220,16 @@ hipError_t launch_quantize(const float* w, uint32_t* words, uint16_t* s, uint16_
   }
 #undef QMM_Q
   return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float* w, uint32_t* words, uint16_t* s, uint16_t* b, int n,
+                           int k, int bits, int group_size, hipStream_t st) {
+  switch (group_size) {
+    case 32: return launch_quantize_gs<32>(w, words, s, b, n, k, bits, st);
+    case 64: return launch_quantize_gs<64>(w, words, s, b, n, k, bits, st);
+    case 128: return launch_quantize_gs<128>(w, words, s, b, n, k, bits, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,
@@ -242,13 +253,13 @@ hipError_t launch_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, 
 }
 
 hipError_t launch_dequant(const uint32_t* w, const uint16_t* s, const uint16_t* b, void* out,
-                          int out_is_f16, int n, int k, int bits, hipStream_t st) {
+                          int out_is_f16, int n, int k, int bits, int gs, hipStream_t st) {
   const long words = (long)n * k * bits / 32;
   const unsigned grid = blocks_for(words);
   const long chunks = (long)n * k / 8;
   const unsigned cgrid = blocks_for(chunks);
-#define QMM_DQ(B, H) hipLaunchKernelGGL((dequant_kernel<B, H>), dim3(grid), dim3(256), 0, st, w, s, b, out, words)
-#define QMM_DQC(B, H) hipLaunchKernelGGL((dequant_chunks_kernel<B, H>), dim3(cgrid), dim3(256), 0, st, w, s, b, out, words, chunks)
+#define QMM_DQ(B, H) hipLaunchKernelGGL((dequant_kernel<B, H>), dim3(grid), dim3(256), 0, st, w, s, b, out, words, gs)
+#define QMM_DQC(B, H) hipLaunchKernelGGL((dequant_chunks_kernel<B, H>), dim3(cgrid), dim3(256), 0, st, w, s, b, out, words, chunks, gs)
   if (out_is_f16) {
     switch (bits) {
       case 2: QMM_DQ(2, true); break;

@@ -358,9 +358,56 @@ def check_route(o, seed=8):
         assert np.allclose(ratio, np.exp(logits[i, ids[i, 1:]] - logits[i, ids[i, 0]]), rtol=1e-12)
 
 
+def check_group_sizes(o, seed=9):
+    """Groups of 32 and 128 codes.
+    * Per-group error bound (as check_quantize_error_bound) on rows whose
+      32-code slices have ranges a thousand times apart, so quantizing with
+      any other grouping breaks the bound on the narrow slices.
+    * Equivalence: when both halves of every 2*gs-code span share their min
+      and max, groups of gs and of 2*gs give the same codes, and the finer
+      scales and biases are the coarser ones repeated; the products agree.
+    * The matmul with groups of 32 equals the one with groups of 64 when the
+      two halves of each 64-group carry the same scale and bias."""
+    r = np.random.default_rng(seed)
+    for gs in (32, 128):
+        for bits in (2, 3, 4, 5, 6, 8):
+            levels = (1 << bits) - 1
+            w = (r.standard_normal((8, 256)) * 0.02).astype(np.float32)
+            w[:, 32:64] *= 1000.0  # slices of very different range
+            w[:, 160:192] *= 1000.0
+            q, s, b = o.quantize(w, bits, gs)
+            assert s.shape == (8, 256 // gs) and q.max() <= levels
+            w_hat = o.dequant_f64(q, s, b, gs)
+            wg = w.astype(np.float64).reshape(8, 256 // gs, gs)
+            mn, mx = wg.min(axis=2), wg.max(axis=2)
+            sv, bv = o.f16_value(s), o.f16_value(b)
+            bound = sv / 2 + np.abs(bv - mn) + levels * np.abs(sv - (mx - mn) / levels) \
+                + 2.0 ** -20 * (np.abs(mn) + np.abs(mx))
+            err = np.abs(w_hat - w.astype(np.float64)).reshape(8, 256 // gs, gs).max(axis=2)
+            assert np.all(err <= bound), (gs, bits)
+    for fine, coarse in ((32, 64), (64, 128)):
+        for bits in (3, 4, 8):
+            w = (r.standard_normal((4, 256)) * 0.02).astype(np.float32)
+            wc = w.reshape(4, 256 // coarse, 2, fine)
+            lo = np.minimum(wc[:, :, 0].min(axis=2), wc[:, :, 1].min(axis=2))
+            hi = np.maximum(wc[:, :, 0].max(axis=2), wc[:, :, 1].max(axis=2))
+            for half in (0, 1):  # both halves hold the span's min at 0 and max at 1
+                wc[:, :, half, 0] = lo
+                wc[:, :, half, 1] = hi
+            w = wc.reshape(4, 256)
+            qf, sf, bf = o.quantize(w, bits, fine)
+            qc, sc, bc = o.quantize(w, bits, coarse)
+            assert np.array_equal(qf, qc), (fine, bits)
+            assert np.array_equal(sf, np.repeat(sc, 2, axis=1)) and np.array_equal(bf, np.repeat(bc, 2, axis=1))
+            x = r.standard_normal((3, 256)).astype(np.float16)
+            yf = o.qmatmul_f64(o.pack(qf, bits), sf, bf, x, bits, fine)
+            yc = o.qmatmul_f64(o.pack(qc, bits), sc, bc, x, bits, coarse)
+            assert np.array_equal(yf, yc), (fine, bits)
+
+
 ALL_CHECKS = (
     check_f16_rounding, check_pack_golden, check_pack_roundtrip,
     check_quantize_golden, check_quantize_nearest_level, check_quantize_error_bound,
     check_dot_exact_rational, check_closed_forms, check_gemm_rows_are_gemvs,
-    check_grouped, check_route,
+    check_grouped, check_route, check_group_sizes,
 )

@@ -51,7 +51,9 @@ def test_gemv_errors(L):
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 7, 64, None), UNS, "bits=7")
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 1, 64, None), UNS, "bits=1")
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 16, 64, None), UNS, "bits=16")
-    expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 4, 32, None), UNS, "group_size=32")
+    expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 4, 16, None), UNS, "group_size=16")
+    expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 4, 256, None), UNS, "group_size=256")
+    expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 4, 128, None), INV, "multiple of group_size 128")
     expect(L.qmm_qgemv(A, A, A, A, A, 0, 64, 4, 64, None), INV, "n=0")
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 100, 4, 64, None), INV, "k=100")
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 0, 4, 64, None), INV, "k=0")
@@ -69,6 +71,8 @@ def test_gemm_errors(L):
     expect(L.qmm_qgemm(A, A, A, A, A, 4, 8, 64, 7, 64, None, 0, None), UNS, "bits=7")
     expect(L.qmm_qgemm(A, A, A, MIS, A, 4, 8, 64, 4, 64, None, 0, None), INV, "x is not")
     assert L.qmm_qgemm_workspace_size(2048, 9728, 2560, 4, 64) == 0
+    expect(L.qmm_qgemm(A, A, A, A, A, 4, 8, 192, 4, 128, None, 0, None), INV, "multiple of group_size 128")
+    expect(L.qmm_qgemm(A, A, A, A, A, 4, 8, 64, 4, 48, None, 0, None), UNS, "group_size=48")
 
 
 def test_grouped_errors(L):
@@ -137,7 +141,7 @@ def test_batched_plan_host_only(L):
     expect(L.qmm_qgemv_batched_plan(probs, 3, 4, 64, buf, need.value, C.byref(need)), INV, "misaligned")
 
 
-def gemm_batch_plan(L, shapes, bits=4, env=None):
+def gemm_batch_plan(L, shapes, bits=4, env=None, gs=64):
     """Build a batched-GEMM plan on the host for (m, n, k) shapes; decode it."""
     import struct
     old = os.environ.pop("QMM_GEMM_FORCE", None)
@@ -148,10 +152,10 @@ def gemm_batch_plan(L, shapes, bits=4, env=None):
         for i, (m, n, k) in enumerate(shapes):
             probs[i] = GemmProblem(A * (i + 1), A, A, A, A * (i + 1) + 0x1000, m, n, k)
         need, ws = C.c_size_t(0), C.c_size_t(0)
-        expect(L.qmm_qgemm_batched_plan(probs, len(shapes), bits, 64, None, 0, C.byref(need),
+        expect(L.qmm_qgemm_batched_plan(probs, len(shapes), bits, gs, None, 0, C.byref(need),
                                         C.byref(ws)), WSP, "plan buffer")
         buf = (C.c_uint8 * need.value)()
-        assert L.qmm_qgemm_batched_plan(probs, len(shapes), bits, 64, buf, need.value,
+        assert L.qmm_qgemm_batched_plan(probs, len(shapes), bits, gs, buf, need.value,
                                         C.byref(need), C.byref(ws)) == 0
     finally:
         os.environ.pop("QMM_GEMM_FORCE", None)
@@ -210,6 +214,13 @@ def test_batched_gemm_plan_covers_every_tile(L, shapes):
         assert hdr["ws"] == hdr["split_tiles"] * S * bm * bn * 4
     else:
         assert hdr["ws"] == 0
+
+
+def test_batched_gemm_plan_group_sizes(L):
+    """Quad scale loads (sbq) only for groups of 64; the header records the group size."""
+    for gs in (32, 64, 128):
+        hdr, _ = gemm_batch_plan(L, [(2048, 2560, 9728)], env="256,2,4", gs=gs)
+        assert hdr["gs"] == gs and hdr["sbq"] == (1 if gs == 64 else 0), (gs, hdr)
 
 
 def test_batched_gemm_plan_force_and_errors(L):

@@ -320,3 +320,101 @@ def test_grouped_edge_cases():
     # zero tokens: nothing launched, output untouched
     y = torch.full((0, 256), 1.0, device="cuda")
     qmm.qgemm_grouped(dev(words), dev(s), dev(b), dev(h[:0]), dev(ids[:0]), bits, True, y=y)
+
+
+# ----------------------------------------------------------- group sizes --
+
+GROUP_SIZES = (32, 128)
+
+
+def quantized_gs(key, n, k, bits, gs):
+    w = synth.draw_weight(key, n, k)
+    codes, s, b = oracle.quantize(w, bits, gs)
+    return w, codes, oracle.pack(codes, bits), s, b
+
+
+@pytest.mark.parametrize("gs", GROUP_SIZES)
+@pytest.mark.parametrize("bits", BITS)
+def test_group_size_quantize_dequant_bit_exact(bits, gs):
+    say("group size quantize/dequant", bits, gs)
+    w = synth.draw_weight((930, bits, gs, 0), 37, 512)
+    w[0, :gs] *= 1000.0   # a wide group next to narrow ones
+    w[1] = 0.25           # constant row: zero scale
+    codes, s, b = oracle.quantize(w, bits, gs)
+    words, gsc, gbi = qmm.quantize(dev(w), bits, group_size=gs)
+    assert np.array_equal(host(gsc, np.uint16), s)
+    assert np.array_equal(host(gbi, np.uint16), b)
+    assert np.array_equal(host(words, np.uint32), oracle.pack(codes, bits))
+    exact = oracle.dequant_f64(codes, s, b, gs)
+    got = host(qmm.dequant(words, dev(s), dev(b), 512, bits, out_f16=False, group_size=gs))
+    assert np.array_equal(got, oracle.round_to_f32(exact))
+    got = host(qmm.dequant(words, dev(s), dev(b), 512, bits, out_f16=True, group_size=gs))
+    assert np.array_equal(got.view(np.uint16), oracle.round_to_f16_bits(exact))
+
+
+@pytest.mark.parametrize("gs", GROUP_SIZES)
+@pytest.mark.parametrize("bits", BITS)
+def test_group_size_gemv_and_gemm(bits, gs):
+    say("group size gemv/gemm", bits, gs)
+    for n, k in ((1, 128), (300, 512), (1024, 1024), (64, 8192)):
+        _, _, words, s, b = quantized_gs((931, bits, gs, n), n, k, bits, gs)
+        x = synth.draw_act((931, bits, gs, n + 1), 1, k)
+        want = oracle.qmatmul_f64(words, s, b, x, bits, gs)[0]
+        y = qmm.qgemv(dev(words), dev(s), dev(b), dev(x[0]), bits, group_size=gs)
+        assert_close(host(y), want, f"gemv bits={bits} gs={gs} n={n} k={k}")
+    probs, wants = [], []
+    for i, (n, k) in enumerate(((2048, 1024), (999, 3072), (4096, 512))):
+        _, _, words, s, b = quantized_gs((932, bits, gs, i), n, k, bits, gs)
+        x = synth.draw_act((932, bits, gs, i + 10), 1, k)
+        probs.append((dev(words), dev(s), dev(b), dev(x[0]), torch.full((n,), float("nan"), device="cuda")))
+        wants.append(oracle.qmatmul_f64(words, s, b, x, bits, gs)[0])
+    qmm.qgemv_batched(qmm.qgemv_batched_plan(probs, bits, group_size=gs))
+    for t, want in zip(probs, wants):
+        assert_close(host(t[4]), want, f"batched gemv bits={bits} gs={gs}")
+    for m, n, k in ((1, 32, 128), (70, 520, 1024), (300, 1000, 1024), (16, 2048, 8192)):
+        _, _, words, s, b = quantized_gs((933, bits, gs, m), n, k, bits, gs)
+        x = synth.draw_act((933, bits, gs, m + 1), m, k)
+        want = oracle.qmatmul_f64(words, s, b, x, bits, gs)
+        y = qmm.qgemm(dev(words), dev(s), dev(b), dev(x), bits, group_size=gs)
+        assert_close(host(y), want, f"gemm bits={bits} gs={gs} m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("gs", GROUP_SIZES)
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_group_size_batched_gemm_every_tile(bits, gs, monkeypatch):
+    shapes = [(70, 520, 1024), (300, 200, 768 if gs == 32 else 896), (1, 64, 256)]
+    ins, wants = [], []
+    for i, (m, n, k) in enumerate(shapes):
+        _, _, words, s, b = quantized_gs((934, bits, gs, i), n, k, bits, gs)
+        x = synth.draw_act((934, bits, gs, i + 10), m, k)
+        wants.append(oracle.qmatmul_f64(words, s, b, x, bits, gs))
+        ins.append((dev(words), dev(s), dev(b), dev(x), torch.full((m, n), float("nan"), device="cuda")))
+    for bm, nb in BATCH_CFGS:
+        for splits in (1, 3):
+            say("group size batched", bits, gs, bm, nb, splits)
+            monkeypatch.setenv("QMM_GEMM_FORCE", f"{bm},{nb},{splits}")
+            plan = qmm.qgemm_batched_plan(ins, bits, group_size=gs)
+            monkeypatch.delenv("QMM_GEMM_FORCE")
+            assert (plan.header["bm"], plan.header["nb"], plan.header["splits"]) == (bm, nb, splits)
+            assert plan.header["sbq"] == 0
+            qmm.qgemm_batched(plan)
+            for (m, n, k), t, want in zip(shapes, ins, wants):
+                assert_close(host(t[4]), want, f"batched bits={bits} gs={gs} {bm}x{nb} S={splits} m={m}")
+                t[4].fill_(float("nan"))
+
+
+@pytest.mark.parametrize("gs", GROUP_SIZES)
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_group_size_grouped(bits, gs):
+    say("group size grouped", bits, gs)
+    e, n, k, t, top_k = 16, 300, 256, 100, 4
+    r = np.random.default_rng([935, bits, gs])
+    ws = [quantized_gs((935, bits, gs, ei), n, k, bits, gs) for ei in range(e)]
+    words = np.stack([q[2] for q in ws])
+    s = np.stack([q[3] for q in ws])
+    b = np.stack([q[4] for q in ws])
+    ids = np.ascontiguousarray(synth.topk_ids(r.standard_normal((t, e)), top_k), dtype=np.int32)
+    x = synth.draw_act((935, bits, gs, 1000), t, k)
+    want = oracle.grouped_f64(words, s, b, x, ids, bits, False, gs)
+    y = qmm.qgemm_grouped(dev(words), dev(s), dev(b), dev(x), dev(ids), bits, False, group_size=gs)
+    assert_close(host(y), want, f"grouped bits={bits} gs={gs}")

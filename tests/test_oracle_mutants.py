@@ -39,6 +39,17 @@ def m_dequant_wrong_group(o):
     o.dequant_f64 = dequant_f64
 
 
+def m_quantize_ignores_group_size(o):
+    real_quant = o.quantize
+
+    def quantize(w, bits, group_size=64):
+        q, s, b = real_quant(w, bits, 64)   # always groups of 64
+        f = 64 // group_size if group_size < 64 else 1
+        c = group_size // 64 if group_size > 64 else 1
+        return q, np.repeat(s, f, axis=1)[:, ::c], np.repeat(b, f, axis=1)[:, ::c]
+    o.quantize = quantize
+
+
 def m_pack_high_first(o):
     real_pack, real_unpack = o.pack, o.unpack
 
@@ -214,7 +225,7 @@ MUTANTS = [
     m_quantize_floor, m_quantize_ties_up, m_quantize_bias_max, m_quantize_unrounded_scale,
     m_quantize_no_clamp, m_quantize_levels_off_by_one, m_matmul_transposed, m_matmul_f32,
     m_grouped_wrong_row, m_grouped_expert_off_by_one, m_route_no_renorm, m_route_ascending,
-    m_f16_double_rounding, m_f16_truncate,
+    m_f16_double_rounding, m_f16_truncate, m_quantize_ignores_group_size,
 ]
 
 
