@@ -22,12 +22,13 @@ The same JSON line carries, measured in the same run:
                 M = 128 ... 2048, TFLOP/s against the fp16 matrix-core peak;
   moe           Qwen3-30B-A3B-shaped grouped GEMMs (128 experts, top-8) at
                 M = 512 and 2048 tokens, against their HBM roofline;
-  decode_context the lm_head alone, the decode pass as 197 sequential launches
+  decode_context the lm_head alone, q/k/v as three launches vs one launch over
+                the stacked weights, the decode pass as 197 sequential launches
                 replayed as one HIP graph, and that graph's per-launch floor;
   decode_q8     the Llama-3.2-3B-shaped 8-bit decode sweep (196 GEMVs);
   decode_formats the Qwen3-0.6B-shaped decode pass with 2-, 3-, 5- and 6-bit
-                weights (one batched launch each);
-  gemm_formats  one 2048 x 9728 x 2560 prefill GEMM per weight width;
+                and unquantized fp16 weights (one batched launch each);
+  gemm_formats  one 2048 x 9728 x 2560 prefill GEMM per weight width (and fp16);
   single_gemv   one 1x1024x1024 4-bit GEMV launch (latency).
 Inputs are seeded synthetic tensors with the models' shapes (weights
 N(0, 0.02) quantized on the GPU by qmm_quantize, activations N(0, 1) fp16).
@@ -59,12 +60,12 @@ METRIC = "Q4 decode GEMV HBM GB/s (% peak) + prefill qGEMM TFLOP/s (% MFMA peak)
 # on a copy of known size; valid only for the kernel sources it was taken on.
 TRAFFIC = {
     # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on `bench.py --only decode`
-    # (KiB per dispatch of qgemv_batched_kernel<4,16,4>) and on
+    # (KiB per dispatch of qgemv_batched_kernel<4,16,4,64>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 166803.5, "fetch_scale": 1073741824 / (524301.3 * 1024),
-    "write_kib": 1939.0, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "74cd8cc7fdbca88c2327974439554286c6b998dda6f59715095c3f8a9cda630b",
+    "fetch_kib": 166779.0, "fetch_scale": 1073741824 / (524301.3 * 1024),
+    "write_kib": 1939.1, "write_scale": 1073741824 / (1048576.0 * 1024),
+    "sources_sha256": "0146b8912eb0b264ccead8788d5964f6f610cee8a721b1928e13949c6f60251f",
 }
 
 
@@ -89,7 +90,10 @@ def prepare_dense(torch, qmm, w: synth.DenseWorkload, copies: int):
     for i, p in enumerate(w.projs + w.extra):
         layer = w.layers if i >= len(w.projs) else 0
         wf = torch.from_numpy(synth.draw_weight((w.wid, layer, i, synth.STREAM_W), p.n, p.k)).cuda()
-        words, s, b = qmm.quantize(wf, w.bits)
+        if w.bits == 16:  # unquantized fp16 weights: no scales or biases
+            words, s, b = wf.half().view(torch.int32), None, None
+        else:
+            words, s, b = qmm.quantize(wf, w.bits)
         del wf
         base[i] = (words, s, b)
     sets = []
@@ -98,7 +102,7 @@ def prepare_dense(torch, qmm, w: synth.DenseWorkload, copies: int):
         for layer, i, p in w.problems():
             words, s, b = base[i]
             if c > 0 or layer > 0 or (i >= len(w.projs)):
-                words, s, b = words.clone(), s.clone(), b.clone()
+                words, s, b = (None if t is None else t.clone() for t in (words, s, b))
             x = torch.from_numpy(synth.draw_act((w.wid, layer, i, synth.STREAM_X), 1, p.k)[0]).cuda()
             y = torch.empty(p.n, dtype=torch.float32, device="cuda")
             probs.append((words, s, b, x, y, p.n, p.k))
@@ -108,7 +112,8 @@ def prepare_dense(torch, qmm, w: synth.DenseWorkload, copies: int):
 
 
 def gemv_bytes(n, k, bits):
-    return n * k * bits // 8 + 2 * 2 * n * (k // 64) + 2 * k + 4 * n
+    scales = 0 if bits == 16 else 2 * 2 * n * (k // 64)   # fp16 scale + bias per group of 64
+    return n * k * bits // 8 + scales + 2 * k + 4 * n
 
 
 # ------------------------------------------------------------- measuring --
@@ -143,7 +148,7 @@ def bench_decode(torch, qmm, wl, steps, warmup, copies=2):
     return dict(sets=sets, plans=plans, step_bytes=step_bytes, ms_step=ms_step, wall=wall)
 
 
-def bench_decode_formats(torch, qmm, wl, bits_list=(2, 3, 5, 6), steps=20, warmup=3):
+def bench_decode_formats(torch, qmm, wl, bits_list=(2, 3, 5, 6, 16), steps=20, warmup=3):
     """The same decode pass (one batched launch of all its GEMVs) with the
     weights quantized to other widths: streaming rate per format."""
     out = {}
@@ -151,7 +156,7 @@ def bench_decode_formats(torch, qmm, wl, bits_list=(2, 3, 5, 6), steps=20, warmu
         w = dataclasses.replace(wl, bits=bits, name=f"{wl.name}@q{bits}")
         d = bench_decode(torch, qmm, w, steps, warmup)
         gbs = d["step_bytes"] / (d["ms_step"] * 1e-3) / 1e9
-        out[f"q{bits}"] = {"bytes_per_step": d["step_bytes"], "ms_per_step": round(d["ms_step"], 5),
+        out["f16" if bits == 16 else f"q{bits}"] = {"bytes_per_step": d["step_bytes"], "ms_per_step": round(d["ms_step"], 5),
                            "gb_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         del d
         torch.cuda.synchronize()
@@ -159,7 +164,7 @@ def bench_decode_formats(torch, qmm, wl, bits_list=(2, 3, 5, 6), steps=20, warmu
     return out
 
 
-def bench_gemm_formats(torch, qmm, m=2048, n=9728, k=2560, bits_list=(2, 3, 4, 5, 6, 8),
+def bench_gemm_formats(torch, qmm, m=2048, n=9728, k=2560, bits_list=(2, 3, 4, 5, 6, 8, 16),
                        steps=20, warmup=3):
     """One M x N x K prefill GEMM (the gate projection at M = 2048) per
     weight width, TFLOP/s against the fp16 matrix-core peak."""
@@ -169,12 +174,12 @@ def bench_gemm_formats(torch, qmm, m=2048, n=9728, k=2560, bits_list=(2, 3, 4, 5
     y = torch.empty((m, n), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     for bits in bits_list:
-        wq = qmm.quantize(wf, bits)
+        wq = (wf.half().view(torch.int32), None, None) if bits == 16 else qmm.quantize(wf, bits)
         ws = torch.empty(max(qmm.qgemm_workspace_size(m, n, k, bits), 16), dtype=torch.uint8, device="cuda")
         ms_call, _ = time_launches(torch, lambda i: qmm.qgemm(*wq, x, bits, y=y, workspace=ws),
                                    steps, warmup, stream)
         tfl = 2.0 * m * n * k / (ms_call * 1e-3) / 1e12
-        out[f"q{bits}"] = {"ms_per_call": round(ms_call, 4), "tflops": round(tfl, 1),
+        out["f16" if bits == 16 else f"q{bits}"] = {"ms_per_call": round(ms_call, 4), "tflops": round(tfl, 1),
                            "frac_of_fp16_peak": round(tfl / FP16_MFMA_PEAK_TFLOPS, 4)}
         del wq, ws
     del wf, x, y
@@ -209,6 +214,16 @@ def bench_decode_extras(torch, qmm, wl, sets, steps=20, warmup=3):
     nb = gemv_bytes(lm[0][5], lm[0][6], wl.bits)
     out["lm_head"] = {"n": lm[0][5], "k": lm[0][6], "us_per_launch": round(ms * 1e3, 2),
                       "gb_per_s": round(nb / (ms * 1e-3) / 1e9, 1)}
+    # q, k, v of layer 0 (same activations): three launches vs one launch over
+    # the weights stacked along n (2048 + 1024 + 1024 rows)
+    q, kk, v = sets[0][0], sets[0][1], sets[0][2]
+    ms3, _ = time_launches(torch, lambda i: [qmm.qgemv(*t[:4], wl.bits, y=t[4]) for t in (q, kk, v)],
+                           steps, warmup, stream)
+    cat = [torch.cat([t[j] for t in (q, kk, v)]) for j in range(3)]
+    ycat = torch.empty(cat[0].shape[0], dtype=torch.float32, device="cuda")
+    ms1, _ = time_launches(torch, lambda i: qmm.qgemv(*cat, q[3], wl.bits, y=ycat), steps, warmup, stream)
+    out["qkv"] = {"n": int(cat[0].shape[0]), "k": q[6], "us_three_launches": round(ms3 * 1e3, 2),
+                  "us_fused": round(ms1 * 1e3, 2)}
 
     def capture(body):
         g = torch.cuda.CUDAGraph()
@@ -465,7 +480,7 @@ def main():
                    "weight_copies_alternated": 2},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "qgemv_batched_kernel<4,16,4>",
+                     "traffic": traffic, "kernel": "qgemv_batched_kernel<4,16,4,64>",
                      "bytes_per_launch": d["step_bytes"],
                      "launch_ms_mean": round(d["ms_step"], 5)},
     }

@@ -25,7 +25,9 @@ follow the format fixed for the workloads (asymmetric min/max per group of
 nibbles per uint32 for 4-bit, 4 bytes per uint32 for 8-bit).  The pages
 name widths from 2 to 8 bits (BaseRT §3.3 and §4.1: Q2, Q3, Q4, Q5, Q6,
 Q8) without giving a layout; every width here uses the same little-endian
-bit stream.
+bit stream.  Scale groups of 32, 64 or 128 codes are supported.  The 16-bit
+format (unquantized fp16 weights, §4.1 FP16) is the plain matmul with each
+weight at its exact fp16 value (hmatmul_f64).
 
 Pins (all in the CPU test-suite): hand-worked packed words and quantizer
 cases, exhaustive pack/unpack round trips, brute-force code enumeration and
@@ -36,6 +38,6 @@ routing invariants.  No function here is "parity unpinned".
 """
 from .qmm_oracle import (  # noqa: F401
     f16_bits, f16_value, quantize, pack, unpack, dequant_f64, round_to_f32,
-    round_to_f16_bits, matmul_f64, qmatmul_f64, grouped_f64, route,
+    round_to_f16_bits, matmul_f64, qmatmul_f64, hmatmul_f64, grouped_f64, route,
     packed_words_per_row,
 )

@@ -156,6 +156,13 @@ def qmatmul_f64(words, s_bits, b_bits, x16, bits: int, group_size: int = 64):
     return matmul_f64(x16, w_hat)
 
 
+def hmatmul_f64(w_bits, x16) -> np.ndarray:
+    """Unquantized fp16 weights (the 16-bit format next to Q2..Q8): y[m, n] =
+    sum_k x[m, k] * W[n, k] with W given as fp16 bit patterns [n, k], each
+    taken at its exact value."""
+    return matmul_f64(np.atleast_2d(np.asarray(x16, dtype=np.float16)), f16_value(w_bits))
+
+
 def grouped_f64(words, s_bits, b_bits, a16, ids, bits: int, a_row_per_pair: bool,
                 group_size: int = 64) -> np.ndarray:
     """Mixture-of-experts grouped matmul.

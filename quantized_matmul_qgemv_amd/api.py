@@ -38,6 +38,13 @@ def _dev(t: torch.Tensor, name: str, dtypes) -> int:
     return t.data_ptr()
 
 
+def _sb(t, name: str, bits: int) -> int:
+    """Scale or bias array; fp16 weights (bits = 16) have none (None -> NULL)."""
+    if t is None and bits == 16:
+        return 0
+    return _dev(t, name, _SB)
+
+
 _W = (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
 _SB = (torch.int16, torch.float16) + ((torch.uint16,) if hasattr(torch, "uint16") else ())
 _X = (torch.float16,)
@@ -49,7 +56,7 @@ def qgemv(w, scales, biases, x, bits: int, y=None, group_size: int = GROUP, stre
     n, k = w.shape[0], x.shape[-1]
     if y is None:
         y = torch.empty(n, dtype=torch.float32, device=w.device)
-    check(lib().qmm_qgemv(_dev(w, "w", _W), _dev(scales, "scales", _SB), _dev(biases, "biases", _SB),
+    check(lib().qmm_qgemv(_dev(w, "w", _W), _sb(scales, "scales", bits), _sb(biases, "biases", bits),
                           _dev(x, "x", _X), _dev(y, "y", _Y), n, k, bits, group_size, _stream(stream)))
     return y
 
@@ -68,7 +75,7 @@ def qgemv_batched_plan(problems, bits: int, group_size: int = GROUP) -> GemvPlan
     """Build a batched-GEMV plan for a list of (w, scales, biases, x, y)."""
     arr = (GemvProblem * len(problems))()
     for i, (w, s, b, x, y) in enumerate(problems):
-        arr[i] = GemvProblem(_dev(w, "w", _W), _dev(s, "scales", _SB), _dev(b, "biases", _SB),
+        arr[i] = GemvProblem(_dev(w, "w", _W), _sb(s, "scales", bits), _sb(b, "biases", bits),
                              _dev(x, "x", _X), _dev(y, "y", _Y), w.shape[0], x.shape[-1])
     need = C.c_size_t(0)
     st = lib().qmm_qgemv_batched_plan(arr, len(problems), bits, group_size, None, 0, C.byref(need))
@@ -101,7 +108,7 @@ def qgemm(w, scales, biases, x, bits: int, y=None, group_size: int = GROUP, work
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=w.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    check(lib().qmm_qgemm(_dev(w, "w", _W), _dev(scales, "scales", _SB), _dev(biases, "biases", _SB),
+    check(lib().qmm_qgemm(_dev(w, "w", _W), _sb(scales, "scales", bits), _sb(biases, "biases", bits),
                           _dev(x, "x", _X), _dev(y, "y", _Y), m, n, k, bits, group_size,
                           ws_ptr, ws_len, _stream(stream)))
     return y
@@ -130,7 +137,7 @@ def qgemm_batched_plan(problems, bits: int, group_size: int = GROUP) -> GemmBatc
     """Plan one launch for a list of (w, scales, biases, x, y) GEMM problems."""
     arr = (GemmProblem * len(problems))()
     for i, (w, s, b, x, y) in enumerate(problems):
-        arr[i] = GemmProblem(_dev(w, "w", _W), _dev(s, "scales", _SB), _dev(b, "biases", _SB),
+        arr[i] = GemmProblem(_dev(w, "w", _W), _sb(s, "scales", bits), _sb(b, "biases", bits),
                              _dev(x, "x", _X), _dev(y, "y", _Y), x.shape[0], w.shape[0],
                              x.shape[1])
     need, ws = C.c_size_t(0), C.c_size_t(0)
@@ -169,8 +176,8 @@ def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: b
     ws_bytes = qgemm_grouped_workspace_size(t, top_k, e, n, k, bits, group_size)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=w.device)
-    check(lib().qmm_qgemm_grouped(_dev(w, "w", _W), _dev(scales, "scales", _SB),
-                                  _dev(biases, "biases", _SB), _dev(a, "a", _X),
+    check(lib().qmm_qgemm_grouped(_dev(w, "w", _W), _sb(scales, "scales", bits),
+                                  _sb(biases, "biases", bits), _dev(a, "a", _X),
                                   int(bool(a_row_per_pair)), _dev(expert_ids, "expert_ids", (torch.int32,)),
                                   _dev(y, "y", _Y), t, top_k, e, n, k, bits, group_size,
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),

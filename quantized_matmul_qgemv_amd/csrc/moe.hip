@@ -198,13 +198,20 @@ static hipError_t launch_grouped_sbq(const GroupedArgs& a, int32_t* ws, hipStrea
       nb = fn;
     }
   }
-  if (bm == 32) return nb == 2 ? launch_grouped_tile<BITS, 32, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 32, 1, SBQ>(a, ws, st);
-  if (bm == 64) return nb == 2 ? launch_grouped_tile<BITS, 64, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 64, 1, SBQ>(a, ws, st);
-  return nb == 2 ? launch_grouped_tile<BITS, 128, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 128, 1, SBQ>(a, ws, st);
+  if constexpr (BITS == 16) {  // fp16 weights: one column block per wave, no scales
+    if (bm == 32) return launch_grouped_tile<16, 32, 1, false>(a, ws, st);
+    if (bm == 64) return launch_grouped_tile<16, 64, 1, false>(a, ws, st);
+    return launch_grouped_tile<16, 128, 1, false>(a, ws, st);
+  } else {
+    if (bm == 32) return nb == 2 ? launch_grouped_tile<BITS, 32, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 32, 1, SBQ>(a, ws, st);
+    if (bm == 64) return nb == 2 ? launch_grouped_tile<BITS, 64, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 64, 1, SBQ>(a, ws, st);
+    return nb == 2 ? launch_grouped_tile<BITS, 128, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 128, 1, SBQ>(a, ws, st);
+  }
 }
 
 template <int BITS>
 static hipError_t launch_grouped_bits(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
+  if constexpr (BITS == 16) return launch_grouped_sbq<16, false>(a, ws, st);
   return (a.k / 64) % 4 == 0 && a.group_size == 64 ? launch_grouped_sbq<BITS, true>(a, ws, st)
                              : launch_grouped_sbq<BITS, false>(a, ws, st);
 }
@@ -218,6 +225,7 @@ hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, hipStr
     case 5: return launch_grouped_bits<5>(a, w, st);
     case 6: return launch_grouped_bits<6>(a, w, st);
     case 8: return launch_grouped_bits<8>(a, w, st);
+    case 16: return launch_grouped_bits<16>(a, w, st);
     default: return hipErrorInvalidValue;
   }
 }

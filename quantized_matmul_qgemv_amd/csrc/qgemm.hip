@@ -104,9 +104,8 @@ struct GemmPlan {
 static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 static GemmPlan gemm_plan(int m, int n, int k, int bits) {
-  (void)bits;
   GemmPlan p;
-  gemm_choose(m, n, k, &p.bm, &p.nb, &p.splits);
+  gemm_choose(m, n, k, bits, &p.bm, &p.nb, &p.splits);
   return p;
 }
 
@@ -166,13 +165,21 @@ static hipError_t launch_bm(const GemmArgs& a, const GemmPlan& p, float* ws, hip
 
 template <int BITS>
 static hipError_t launch_bits(const GemmArgs& a, const GemmPlan& p, float* ws, hipStream_t st) {
-  switch (p.bm) {
-    case 32: return launch_bm<BITS, 32>(a, p, ws, st);
-    case 64: return launch_bm<BITS, 64>(a, p, ws, st);
-    case 256:
-      return ((a.k / 64) / p.splits) % 4 == 0 && a.group_size == 64 ? launch_wide<BITS, true>(a, p, ws, st)
-                                              : launch_wide<BITS, false>(a, p, ws, st);
-    default: return launch_bm<BITS, 128>(a, p, ws, st);
+  if constexpr (BITS == 16) {  // fp16 weights: nb = 1 tiles, no scales (see gemm_choose)
+    switch (p.bm) {
+      case 32: return launch_tile<16, 32, 1, false>(a, p, ws, st);
+      case 64: return launch_tile<16, 64, 1, false>(a, p, ws, st);
+      default: return launch_tile<16, 128, 1, false>(a, p, ws, st);
+    }
+  } else {
+    switch (p.bm) {
+      case 32: return launch_bm<BITS, 32>(a, p, ws, st);
+      case 64: return launch_bm<BITS, 64>(a, p, ws, st);
+      case 256:
+        return ((a.k / 64) / p.splits) % 4 == 0 && a.group_size == 64 ? launch_wide<BITS, true>(a, p, ws, st)
+                                                : launch_wide<BITS, false>(a, p, ws, st);
+      default: return launch_bm<BITS, 128>(a, p, ws, st);
+    }
   }
 }
 
@@ -186,6 +193,7 @@ hipError_t launch_qgemm(const GemmArgs& a, int bits, void* workspace, hipStream_
     case 5: return launch_bits<5>(a, p, ws, st);
     case 6: return launch_bits<6>(a, p, ws, st);
     case 8: return launch_bits<8>(a, p, ws, st);
+    case 16: return launch_bits<16>(a, p, ws, st);
     default: return hipErrorInvalidValue;
   }
 }

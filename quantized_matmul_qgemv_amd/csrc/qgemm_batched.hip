@@ -161,10 +161,13 @@ bool splits_ok(const GemmBatchProblem* probs, int count, int S) {
 
 // divisible: only split counts that divide every problem's group count
 // (the single-GEMM kernel splits k evenly).
-Choice choose(const GemmBatchProblem* probs, int count, bool divisible) {
-  Choice best{1, 1, false, 1e300};
+// f16w: unquantized fp16 weights hold 4x the register bytes of a 4-bit
+// weight ring, so only the one-column-block tiles (nb = 1) are used.
+Choice choose(const GemmBatchProblem* probs, int count, bool divisible, bool f16w) {
+  Choice best{2, 1, false, 1e300};
   for (int ci = 0; ci < (int)(sizeof kCfgs / sizeof kCfgs[0]); ++ci) {
     const TileCfg& c = kCfgs[ci];
+    if (f16w && c.nb != 1) continue;
     const int bn = c.nb * 128;
     for (int S : kSplitChoices) {
       if (!splits_ok(probs, count, S)) continue;
@@ -197,7 +200,8 @@ Choice choose(const GemmBatchProblem* probs, int count, bool divisible) {
     for (int p = 0; parsed && p < count; ++p) even = even && (probs[p].k / 64) % sp == 0;
     if (parsed && splits_ok(probs, count, sp) && (even || !divisible)) {
       for (int ci = 0; ci < (int)(sizeof kCfgs / sizeof kCfgs[0]); ++ci)
-        if (kCfgs[ci].bm == bm && kCfgs[ci].nb == nb) best = Choice{ci, sp, sbq_ok(probs, count, sp), 0.0};
+        if (kCfgs[ci].bm == bm && kCfgs[ci].nb == nb && (!f16w || nb == 1))
+          best = Choice{ci, sp, sbq_ok(probs, count, sp), 0.0};
     }
   }
   return best;
@@ -205,13 +209,13 @@ Choice choose(const GemmBatchProblem* probs, int count, bool divisible) {
 
 }  // namespace
 
-void gemm_choose(int m, int n, int k, int* bm, int* nb, int* splits) {
+void gemm_choose(int m, int n, int k, int bits, int* bm, int* nb, int* splits) {
   GemmBatchProblem p;
   memset(&p, 0, sizeof p);
   p.m = m;
   p.n = n;
   p.k = k;
-  const Choice ch = choose(&p, 1, true);
+  const Choice ch = choose(&p, 1, true, bits == 16);
   *bm = kCfgs[ch.cfg].bm;
   *nb = kCfgs[ch.cfg].nb;
   *splits = ch.splits;
@@ -219,8 +223,8 @@ void gemm_choose(int m, int n, int k, int* bm, int* nb, int* splits) {
 
 size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, int group_size,
                         void* out, size_t out_bytes) {
-  Choice ch = choose(probs, count, false);
-  ch.sbq = ch.sbq && group_size == 64;  // quad scale loads: groups of 64 only
+  Choice ch = choose(probs, count, false, bits == 16);
+  ch.sbq = ch.sbq && group_size == 64 && bits != 16;  // quad scale loads: groups of 64 only
   const TileCfg& c = kCfgs[ch.cfg];
   const int bn = c.nb * 128;
   const int S = ch.splits;
@@ -304,22 +308,29 @@ static void launch_batched_cfg(const GemmBatchProblem* probs, const GemmTileRec*
 template <int BITS>
 static void launch_batched_bits(const GemmBatchProblem* probs, const GemmTileRec* tiles,
                                 const GemmBatchHeader& h, float* partials, hipStream_t st) {
-  if (h.bm == 256) {
-    if (h.sbq)
-      hipLaunchKernelGGL((qgemm_batched_wide_kernel<BITS, true>), dim3(h.num_tiles), dim3(kGemmThreads),
-                         0, st, probs, tiles, partials, h.group_size);
-    else
-      hipLaunchKernelGGL((qgemm_batched_wide_kernel<BITS, false>), dim3(h.num_tiles), dim3(kGemmThreads),
-                         0, st, probs, tiles, partials, h.group_size);
-  } else if (h.bm == 128) {
-    if (h.nb == 2) launch_batched_cfg<BITS, 128, 2>(probs, tiles, h, partials, st);
-    else launch_batched_cfg<BITS, 128, 1>(probs, tiles, h, partials, st);
-  } else if (h.bm == 64) {
-    if (h.nb == 2) launch_batched_cfg<BITS, 64, 2>(probs, tiles, h, partials, st);
-    else launch_batched_cfg<BITS, 64, 1>(probs, tiles, h, partials, st);
+  if constexpr (BITS == 16) {  // nb = 1 tiles only (see choose)
+    if (h.bm == 128) launch_batched_cfg<16, 128, 1>(probs, tiles, h, partials, st);
+    else if (h.bm == 64) launch_batched_cfg<16, 64, 1>(probs, tiles, h, partials, st);
+    else launch_batched_cfg<16, 32, 1>(probs, tiles, h, partials, st);
+    return;
   } else {
-    if (h.nb == 2) launch_batched_cfg<BITS, 32, 2>(probs, tiles, h, partials, st);
-    else launch_batched_cfg<BITS, 32, 1>(probs, tiles, h, partials, st);
+    if (h.bm == 256) {
+      if (h.sbq)
+        hipLaunchKernelGGL((qgemm_batched_wide_kernel<BITS, true>), dim3(h.num_tiles), dim3(kGemmThreads),
+                           0, st, probs, tiles, partials, h.group_size);
+      else
+        hipLaunchKernelGGL((qgemm_batched_wide_kernel<BITS, false>), dim3(h.num_tiles), dim3(kGemmThreads),
+                           0, st, probs, tiles, partials, h.group_size);
+    } else if (h.bm == 128) {
+      if (h.nb == 2) launch_batched_cfg<BITS, 128, 2>(probs, tiles, h, partials, st);
+      else launch_batched_cfg<BITS, 128, 1>(probs, tiles, h, partials, st);
+    } else if (h.bm == 64) {
+      if (h.nb == 2) launch_batched_cfg<BITS, 64, 2>(probs, tiles, h, partials, st);
+      else launch_batched_cfg<BITS, 64, 1>(probs, tiles, h, partials, st);
+    } else {
+      if (h.nb == 2) launch_batched_cfg<BITS, 32, 2>(probs, tiles, h, partials, st);
+      else launch_batched_cfg<BITS, 32, 1>(probs, tiles, h, partials, st);
+    }
   }
 }
 
@@ -338,6 +349,7 @@ hipError_t launch_qgemm_batched(const void* plan_device, const GemmBatchHeader& 
     case 5: launch_batched_bits<5>(probs, tiles, h, partials, st); break;
     case 6: launch_batched_bits<6>(probs, tiles, h, partials, st); break;
     case 8: launch_batched_bits<8>(probs, tiles, h, partials, st); break;
+    case 16: launch_batched_bits<16>(probs, tiles, h, partials, st); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

@@ -128,6 +128,9 @@ __device__ __forceinline__ half8_t b_operand(const BRaw<BITS>& r, int j) {
     dequant_word_f16<8>(r.w[2 * j], s2, b2, d0);
     dequant_word_f16<8>(r.w[2 * j + 1], s2, b2, d1);
     o = u32x4{as_u32(d0[0]), as_u32(d0[1]), as_u32(d1[0]), as_u32(d1[1])};
+  } else if constexpr (BITS == 16) {
+    // plain fp16 weights: words 4j .. 4j+3 of the lane's 32 k
+    o = u32x4{r.w[4 * j], r.w[4 * j + 1], r.w[4 * j + 2], r.w[4 * j + 3]};
   } else if constexpr (BITS == 2) {
     half2_t d[8];
     dequant_word_f16<2>(r.w[j >> 1], s2, b2, d);
@@ -261,7 +264,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
     for (int i = 0; i < SPT; ++i) {
       if (aon[i]) {
         uint32_t o[8];
-        if constexpr (Fmt<BITS>::CHUNKED) {
+        if constexpr (Fmt<BITS>::NATURAL) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] = src[i][e];
         } else {
@@ -276,7 +279,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   auto load_b = [&](BRaw<BITS> (&dst)[NB], int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      load_braw<BITS, !SBQ>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs);
+      load_braw<BITS, !SBQ && !Fmt<BITS>::F16W>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs);
   };
   // SBQ: scales and biases of four consecutive groups come in one 8-byte
   // load per column (a 2-byte load touches as many cache lines as a wide

@@ -101,7 +101,7 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       uint32_t o[8];
-      if constexpr (Fmt<BITS>::CHUNKED) {
+      if constexpr (Fmt<BITS>::NATURAL) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = src[i][e];
       } else {
@@ -115,7 +115,7 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
   auto load_b = [&](BRaw<BITS> (&dst)[NB], int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      load_braw<BITS, !SBQ>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs);
+      load_braw<BITS, !SBQ && !Fmt<BITS>::F16W>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs);
   };
   auto load_sbq = [&](u32x2 (&sq)[NB], u32x2 (&bq)[NB], int g4) {
 #pragma unroll

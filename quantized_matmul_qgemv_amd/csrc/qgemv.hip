@@ -81,7 +81,11 @@ __device__ __forceinline__ void stage_quarter(const uint32_t (&d)[8], int g, int
   using F = Fmt<BITS>;
   float csum = 0.0f, xsum = 0.0f;
   uint32_t out[8];
-  if constexpr (F::CHUNKED) {
+  if constexpr (F::F16W) {
+    // fp16 weights: x in natural order, no magic offsets (C = 0)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = d[i];
+  } else if constexpr (F::CHUNKED) {
     // chunk pairs are adjacent codes: x stays in natural order
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -250,11 +254,13 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
 #pragma unroll
         for (int v = 0; v < V4; ++v) bf.w[u][v] = src[v];
       }
+      if constexpr (!F::F16W) {
 #pragma unroll
-      for (int q = 0; q < SBN; ++q) {
-        const size_t si = (size_t)r * sgroups + (GS == 32 ? 2 * g + q : GS == 128 ? (g >> 1) : g);
-        bf.s[u][q] = S[si];
-        bf.b[u][q] = B[si];
+        for (int q = 0; q < SBN; ++q) {
+          const size_t si = (size_t)r * sgroups + (GS == 32 ? 2 * g + q : GS == 128 ? (g >> 1) : g);
+          bf.s[u][q] = S[si];
+          bf.b[u][q] = B[si];
+        }
       }
     }
     if (++it == tcount) { it = 0; ++ip; }
@@ -271,7 +277,21 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
     float a0[UR], a1[UR];
 #pragma unroll
     for (int u = 0; u < UR; ++u) a0[u] = a1[u] = 0.0f;
-    if constexpr (F::CHUNKED) {
+    if constexpr (F::F16W) {
+      // 16 bytes of weights (8 fp16) against 16 bytes of x at a time
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const u32x4 xv = reinterpret_cast<const u32x4*>(xg)[q];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          const u32x4 wv = bf.w[u][q];
+          a0[u] = dot2(wv.x, xv.x, a0[u]);
+          a1[u] = dot2(wv.y, xv.y, a1[u]);
+          a0[u] = dot2(wv.z, xv.z, a0[u]);
+          a1[u] = dot2(wv.w, xv.w, a1[u]);
+        }
+      }
+    } else if constexpr (F::CHUNKED) {
       // chunk-major: 8 codes = 4 natural pairs of x (16 bytes of LDS)
       auto chunk = [&](auto mc) {
         constexpr int m = decltype(mc)::value;
@@ -341,7 +361,10 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
       }
     }
     }
-    if constexpr (GS == 32) {
+    if constexpr (F::F16W) {
+#pragma unroll
+      for (int u = 0; u < UR; ++u) acc[u] += a0[u] + a1[u];
+    } else if constexpr (GS == 32) {
       const float4 c = reinterpret_cast<const float4*>(cx)[g];  // C_lo, X_lo, C_hi, X_hi
 #pragma unroll
       for (int u = 0; u < UR; ++u) {
@@ -436,7 +459,7 @@ __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4)
 // ------------------------------------------------------------------ host --
 
 // Rows in flight per lane: fewer for the wider formats (register budget).
-constexpr int gemv_ur(int bits) { return bits >= 5 ? 2 : 4; }
+constexpr int gemv_ur(int bits) { return bits == 16 ? 1 : bits >= 5 ? 2 : 4; }
 
 int gemv_row_unroll(int bits) { return gemv_ur(bits); }
 
@@ -520,6 +543,7 @@ static hipError_t launch_gs(const GemvProblem& p, int bits, const GemvGeom& g, h
 
 hipError_t launch_qgemv(const GemvProblem& p, int bits, int group_size, const GemvGeom& g,
                         hipStream_t st) {
+  if (bits == 16) return launch_bits<16, 64>(p, g, st);  // no scale groups
   switch (group_size) {
     case 32: return launch_gs<32>(p, bits, g, st);
     case 64: return launch_gs<64>(p, bits, g, st);
@@ -569,6 +593,7 @@ hipError_t launch_qgemv_batched(const GemvBlock* blocks, int num_blocks, int bit
   GemvGeom g{lanes_per_row, gemv_row_unroll(bits), 1,
              gemv_rows_per_pass(lanes_per_row, gemv_row_unroll(bits), 1), 1};
   const size_t lds = gemv_lds_bytes(max_groups, g);
+  if (bits == 16) return launch_batched_bits<16, 64>(blocks, num_blocks, lanes_per_row, lds, st);
   switch (group_size) {
     case 32: return launch_batched_gs<32>(blocks, num_blocks, bits, lanes_per_row, lds, st);
     case 64: return launch_batched_gs<64>(blocks, num_blocks, bits, lanes_per_row, lds, st);

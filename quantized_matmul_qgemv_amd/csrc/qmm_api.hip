@@ -44,10 +44,14 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 constexpr int kGemvMaxK = 16384;
 constexpr int kMaxExperts = 1024;
 
-// Every entry point: 2, 3, 4, 5, 6 and 8 bits, groups of 32, 64 or 128.
-int check_format(const char* fn, int bits, int group_size) {
-  if (bits < 2 || bits > 8 || bits == 7)
-    return fail(QMM_ERR_UNSUPPORTED, "%s: bits=%d not supported (2, 3, 4, 5, 6 or 8)", fn, bits);
+// Quantized weights: 2, 3, 4, 5, 6 and 8 bits, groups of 32, 64 or 128.
+// bits = 16 (unquantized fp16 weights) is accepted by the matmul entry
+// points only (allow16); it has no scales, and group_size must still be
+// one of the supported values (it is not used).
+int check_format(const char* fn, int bits, int group_size, bool allow16 = false) {
+  if (!(bits == 16 && allow16) && (bits < 2 || bits > 8 || bits == 7))
+    return fail(QMM_ERR_UNSUPPORTED, "%s: bits=%d not supported (2, 3, 4, 5, 6 or 8%s)", fn, bits,
+                allow16 ? "; 16 for fp16 weights" : "");
   if (group_size != 32 && group_size != 64 && group_size != 128)
     return fail(QMM_ERR_UNSUPPORTED, "%s: group_size=%d not supported (32, 64 or 128)", fn, group_size);
   return QMM_OK;
@@ -77,12 +81,14 @@ int qmm_qgemv(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
               qmm_stream stream) {
   const char* fn = "qmm_qgemv";
   clear_error();
-  if (int st = check_format(fn, bits, group_size)) return st;
+  if (int st = check_format(fn, bits, group_size, true)) return st;
   if (int st = check_nk(fn, n, k, group_size)) return st;
   if (k > kGemvMaxK) return fail(QMM_ERR_INVALID_ARG, "%s: k=%d exceeds %d", fn, k, kGemvMaxK);
   CHECK_PTR(w, 16);
-  CHECK_PTR(scales, 2);
-  CHECK_PTR(biases, 2);
+  if (bits != 16) {  // fp16 weights have no scales or biases
+    CHECK_PTR(scales, 2);
+    CHECK_PTR(biases, 2);
+  }
   CHECK_PTR(x, 16);
   CHECK_PTR(y, 4);
   qmm::GemvProblem p{w, scales, biases, x, y, n, k};
@@ -95,7 +101,7 @@ int qmm_qgemv_batched_plan(const qmm_gemv_problem* problems, int count, int bits
                            size_t* plan_bytes_needed) {
   const char* fn = "qmm_qgemv_batched_plan";
   clear_error();
-  if (int st = check_format(fn, bits, group_size)) return st;
+  if (int st = check_format(fn, bits, group_size, true)) return st;
   if (count < 1) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d must be >= 1", fn, count);
   if (problems == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: null problems", fn);
   int lpr = 16, max_groups = 0;
@@ -103,7 +109,7 @@ int qmm_qgemv_batched_plan(const qmm_gemv_problem* problems, int count, int bits
     const qmm_gemv_problem& q = problems[i];
     if (check_nk(fn, q.n, q.k, group_size)) return fail(QMM_ERR_INVALID_ARG, "%s: problem %d: n=%d k=%d invalid", fn, i, q.n, q.k);
     if (q.k > kGemvMaxK) return fail(QMM_ERR_INVALID_ARG, "%s: problem %d: k=%d exceeds %d", fn, i, q.k, kGemvMaxK);
-    if (!q.w || !q.scales || !q.biases || !q.x || !q.y)
+    if (!q.w || (bits != 16 && (!q.scales || !q.biases)) || !q.x || !q.y)
       return fail(QMM_ERR_INVALID_ARG, "%s: problem %d has a null pointer", fn, i);
     if (!aligned(q.w, 16) || !aligned(q.x, 16) || !aligned(q.y, 4) || !aligned(q.scales, 2) ||
         !aligned(q.biases, 2))
@@ -182,7 +188,7 @@ int qmm_qgemv_batched(const void* plan_device, const void* plan_host, qmm_stream
   memcpy(&hdr, plan_host, sizeof hdr);
   if (hdr.magic != qmm::kPlanMagic || hdr.version != qmm::kPlanVersion)
     return fail(QMM_ERR_INVALID_ARG, "%s: plan_host is not a plan image", fn);
-  if (int st = check_format(fn, hdr.bits, hdr.group_size)) return st;
+  if (int st = check_format(fn, hdr.bits, hdr.group_size, true)) return st;
   if (hdr.num_blocks < 1 || hdr.max_groups < 1 || hdr.max_groups > kGemvMaxK / 64)
     return fail(QMM_ERR_INVALID_ARG, "%s: corrupt plan header", fn);
   const qmm::GemvBlock* recs = reinterpret_cast<const qmm::GemvBlock*>(
@@ -195,7 +201,7 @@ int qmm_qgemv_batched(const void* plan_device, const void* plan_host, qmm_stream
 size_t qmm_qgemm_workspace_size(int m, int n, int k, int bits, int group_size) {
   if (m < 1 || n < 1 || k < 64 || k % 64 != 0) return 0;
   if ((group_size != 32 && group_size != 64 && group_size != 128) || k % group_size != 0) return 0;
-  if (bits < 2 || bits > 8 || bits == 7) return 0;
+  if ((bits < 2 || bits > 8 || bits == 7) && bits != 16) return 0;
   return qmm::gemm_workspace_bytes(m, n, k, bits);
 }
 
@@ -204,13 +210,15 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
               void* workspace, size_t workspace_bytes, qmm_stream stream) {
   const char* fn = "qmm_qgemm";
   clear_error();
-  if (int st = check_format(fn, bits, group_size)) return st;
+  if (int st = check_format(fn, bits, group_size, true)) return st;
   if (m < 0) return fail(QMM_ERR_INVALID_ARG, "%s: m=%d must be >= 0", fn, m);
   if (int st = check_nk(fn, n, k, group_size)) return st;
   if (m == 0) return QMM_OK;
   CHECK_PTR(w, 16);
-  CHECK_PTR(scales, 2);
-  CHECK_PTR(biases, 2);
+  if (bits != 16) {  // fp16 weights have no scales or biases
+    CHECK_PTR(scales, 2);
+    CHECK_PTR(biases, 2);
+  }
   CHECK_PTR(x, 16);
   CHECK_PTR(y, 4);
   const size_t need = qmm::gemm_workspace_bytes(m, n, k, bits);
@@ -228,7 +236,7 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
                            size_t* plan_bytes_needed, size_t* workspace_bytes_needed) {
   const char* fn = "qmm_qgemm_batched_plan";
   clear_error();
-  if (int st = check_format(fn, bits, group_size)) return st;
+  if (int st = check_format(fn, bits, group_size, true)) return st;
   if (count < 1) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d must be >= 1", fn, count);
   if (count > (1 << 20)) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d too large", fn, count);
   if (problems == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: null problems", fn);
@@ -240,7 +248,7 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
     int bad = 0;
     // an empty problem (m = 0) is never read or written: x and y may be null
     if (q.m < 0 || check_nk(fn, q.n, q.k, group_size)) bad = 1;
-    else if (!q.w || !q.scales || !q.biases || (q.m > 0 && (!q.x || !q.y))) bad = 2;
+    else if (!q.w || (bits != 16 && (!q.scales || !q.biases)) || (q.m > 0 && (!q.x || !q.y))) bad = 2;
     else if (!aligned(q.w, 16) || !aligned(q.x, 16) || !aligned(q.y, 4) ||
              !aligned(q.scales, 2) || !aligned(q.biases, 2)) bad = 3;
     if (bad) {
@@ -285,7 +293,7 @@ int qmm_qgemm_batched(const void* plan_device, const void* plan_host, void* work
   memcpy(&hdr, plan_host, sizeof hdr);
   if (hdr.magic != qmm::kBatchMagic || hdr.version != qmm::kBatchVersion)
     return fail(QMM_ERR_INVALID_ARG, "%s: plan_host is not a batched-GEMM plan image", fn);
-  if (int st = check_format(fn, hdr.bits, hdr.group_size)) return st;
+  if (int st = check_format(fn, hdr.bits, hdr.group_size, true)) return st;
   if (hdr.count < 1 || hdr.num_tiles < 0 || hdr.splits < 1 ||
       !(hdr.bm == 32 || hdr.bm == 64 || hdr.bm == 128 || hdr.bm == 256) ||
       !(hdr.nb == 1 || hdr.nb == 2) || (hdr.bm == 256 && hdr.nb != 2))
@@ -314,7 +322,7 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
                       qmm_stream stream) {
   const char* fn = "qmm_qgemm_grouped";
   clear_error();
-  if (int st = check_format(fn, bits, group_size)) return st;
+  if (int st = check_format(fn, bits, group_size, true)) return st;
   if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
   if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
   if (e < 1 || e > kMaxExperts)
@@ -325,8 +333,10 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
   if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
   if (t == 0) return QMM_OK;
   CHECK_PTR(w, 16);
-  CHECK_PTR(scales, 2);
-  CHECK_PTR(biases, 2);
+  if (bits != 16) {  // fp16 weights have no scales or biases
+    CHECK_PTR(scales, 2);
+    CHECK_PTR(biases, 2);
+  }
   CHECK_PTR(a, 16);
   CHECK_PTR(expert_ids, 4);
   CHECK_PTR(y, 4);

@@ -38,10 +38,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int BITS>
 struct Fmt {
-  static_assert(BITS >= 2 && BITS <= 8 && BITS != 7, "supported widths: 2, 3, 4, 5, 6, 8");
+  static_assert((BITS >= 2 && BITS <= 8 && BITS != 7) || BITS == 16,
+                "supported widths: 2, 3, 4, 5, 6, 8 and 16 (unquantized fp16 weights)");
   // 3-, 5- and 6-bit codes straddle word boundaries and are unpacked per
   // 8-code chunk (BITS bytes, see unpack_chunk); the others per word.
   static constexpr bool CHUNKED = (32 % BITS) != 0;
+  // 16: the weights are plain fp16 values (two per word, low half first);
+  // there are no codes, scales or biases.
+  static constexpr bool F16W = BITS == 16;
+  // weight pairs in natural k order (no activation permutation needed)
+  static constexpr bool NATURAL = CHUNKED || F16W;
   static constexpr int CODES_PER_WORD = CHUNKED ? 0 : 32 / BITS;
   static constexpr int PAIRS_PER_WORD = CODES_PER_WORD / 2;
   static constexpr int WORDS_PER_GROUP = 64 * BITS / 32;  // group of 64 codes
@@ -91,6 +97,8 @@ __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t (&h)[Fmt<BITS>:
     // bytes: D.b[i] = {S0:S1}.b[sel.b[i]], S1 = bytes 0..3, S0 = bytes 4..7
     h[0] = and_or(w, 0x00FF00FFu, 0x64006400u);
     h[1] = __builtin_amdgcn_perm(w, 0x64646464u, 0x00070005u);
+  } else if constexpr (BITS == 16) {
+    h[0] = w;  // already an fp16 pair
   } else {
     const uint32_t w8 = w >> 8;
     h[0] = and_or(w, 0x00030003u, 0x64006400u);

@@ -128,7 +128,7 @@ constexpr uint32_t kBatchVersion = 1;
 
 // Tile and split count for one GEMM (k split evenly), from the batch planner's
 // cost model; honours QMM_GEMM_FORCE.
-void gemm_choose(int m, int n, int k, int* bm, int* nb, int* splits);
+void gemm_choose(int m, int n, int k, int bits, int* bm, int* nb, int* splits);
 
 // Choose the tile and split count for a batch and write the plan image.
 // Returns the image size; writes nothing when out is null or too small.

@@ -405,9 +405,33 @@ def check_group_sizes(o, seed=9):
             assert np.array_equal(yf, yc), (fine, bits)
 
 
+def check_fp16_weights(o, seed=10):
+    """Unquantized fp16 weights: an identity weight returns x exactly; unit
+    scale, zero bias and integer codes (exact in fp16) give the same product
+    through the quantized path and through the fp16-weight path; a weight
+    matrix with one nonzero column picks that column of x times the weight."""
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((3, 64)).astype(np.float16)
+    eye = np.eye(64, dtype=np.float16).view(np.uint16)
+    assert np.array_equal(o.hmatmul_f64(eye, x), x.astype(np.float64))
+    for bits in (2, 4, 8):
+        codes = r.integers(0, 1 << bits, (5, 128), dtype=np.uint8)
+        s = np.full((5, 2), 0x3C00, dtype=np.uint16)
+        b = np.zeros((5, 2), dtype=np.uint16)
+        xx = r.standard_normal((2, 128)).astype(np.float16)
+        yq = o.qmatmul_f64(o.pack(codes, bits), s, b, xx, bits)
+        yh = o.hmatmul_f64(codes.astype(np.float16).view(np.uint16), xx)
+        assert np.array_equal(yq, yh), bits
+    w = np.zeros((4, 64), dtype=np.float16)
+    w[2, 17] = np.float16(-0.375)
+    y = o.hmatmul_f64(w.view(np.uint16), x)
+    assert np.array_equal(y[:, 2], -0.375 * x[:, 17].astype(np.float64))
+    assert not y[:, [0, 1, 3]].any()
+
+
 ALL_CHECKS = (
     check_f16_rounding, check_pack_golden, check_pack_roundtrip,
     check_quantize_golden, check_quantize_nearest_level, check_quantize_error_bound,
     check_dot_exact_rational, check_closed_forms, check_gemm_rows_are_gemvs,
-    check_grouped, check_route, check_group_sizes,
+    check_grouped, check_route, check_group_sizes, check_fp16_weights,
 )

@@ -50,7 +50,11 @@ def expect(status, code, fragment):
 def test_gemv_errors(L):
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 7, 64, None), UNS, "bits=7")
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 1, 64, None), UNS, "bits=1")
-    expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 16, 64, None), UNS, "bits=16")
+    expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 12, 64, None), UNS, "bits=12")
+    # 16 = unquantized fp16 weights: matmul entry points only, scales may be NULL
+    expect(L.qmm_qgemv(A, None, None, MIS, A, 8, 64, 16, 64, None), INV, "x is not 16-byte aligned")
+    expect(L.qmm_quantize(A, A, A, A, 8, 64, 16, 64, None), UNS, "bits=16")
+    expect(L.qmm_dequant(A, A, A, A, 1, 8, 64, 16, 64, None), UNS, "bits=16")
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 4, 16, None), UNS, "group_size=16")
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 4, 256, None), UNS, "group_size=256")
     expect(L.qmm_qgemv(A, A, A, A, A, 8, 64, 4, 128, None), INV, "multiple of group_size 128")

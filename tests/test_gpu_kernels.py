@@ -418,3 +418,100 @@ def test_group_size_grouped(bits, gs):
     want = oracle.grouped_f64(words, s, b, x, ids, bits, False, gs)
     y = qmm.qgemm_grouped(dev(words), dev(s), dev(b), dev(x), dev(ids), bits, False, group_size=gs)
     assert_close(host(y), want, f"grouped bits={bits} gs={gs}")
+
+
+# --------------------------------------------- unquantized fp16 weights --
+
+def fp16_weight(key, n, k):
+    """Seeded N(0, 0.02) weights rounded to fp16: (bit patterns [n, k] uint16,
+    packed words [n, k/2] uint32 with the lower-k half in the low bits)."""
+    w16 = synth.draw_weight(key, n, k).astype(np.float16).view(np.uint16)
+    return w16, np.ascontiguousarray(w16).view(np.uint32)
+
+
+def test_fp16_weights_gemv():
+    for n, k in ((1, 64), (37, 192), (1000, 1024), (300, 2048), (513, 3072), (64, 8192)):
+        say("fp16 gemv", n, k)
+        w16, words = fp16_weight((940, n, k), n, k)
+        x = synth.draw_act((940, n, k + 1), 1, k)
+        y = qmm.qgemv(dev(words), None, None, dev(x[0]), 16)
+        assert_close(host(y), oracle.hmatmul_f64(w16, x)[0], f"fp16 gemv n={n} k={k}")
+    say("fp16 gemv batched")
+    probs, wants = [], []
+    for i, (n, k) in enumerate(((2048, 1024), (1024, 3072), (999, 1024))):
+        w16, words = fp16_weight((941, i, n), n, k)
+        x = synth.draw_act((941, i, n + 1), 1, k)
+        probs.append((dev(words), None, None, dev(x[0]), torch.full((n,), float("nan"), device="cuda")))
+        wants.append(oracle.hmatmul_f64(w16, x)[0])
+    qmm.qgemv_batched(qmm.qgemv_batched_plan(probs, 16))
+    for t, want in zip(probs, wants):
+        assert_close(host(t[4]), want, "fp16 batched gemv")
+
+
+def test_fp16_weights_gemm(monkeypatch):
+    for m, n, k in ((1, 32, 64), (17, 300, 320), (128, 1024, 2560), (300, 1000, 1024), (16, 2048, 8192)):
+        say("fp16 gemm", m, n, k)
+        w16, words = fp16_weight((942, m, n), n, k)
+        x = synth.draw_act((942, m, n + 1), m, k)
+        y = qmm.qgemm(dev(words), None, None, dev(x), 16)
+        assert_close(host(y), oracle.hmatmul_f64(w16, x), f"fp16 gemm m={m} n={n} k={k}")
+    shapes = [(70, 520, 1024), (300, 200, 768), (1, 64, 256)]
+    ins, wants = [], []
+    for i, (m, n, k) in enumerate(shapes):
+        w16, words = fp16_weight((943, i, n), n, k)
+        x = synth.draw_act((943, i, n + 1), m, k)
+        wants.append(oracle.hmatmul_f64(w16, x))
+        ins.append((dev(words), None, None, dev(x), torch.full((m, n), float("nan"), device="cuda")))
+    plan = qmm.qgemm_batched_plan(ins, 16)
+    assert plan.header["nb"] == 1 and plan.header["sbq"] == 0
+    for bm in (128, 64, 32):
+        for splits in (1, 3):
+            say("fp16 gemm batched", bm, splits)
+            monkeypatch.setenv("QMM_GEMM_FORCE", f"{bm},1,{splits}")
+            plan = qmm.qgemm_batched_plan(ins, 16)
+            monkeypatch.delenv("QMM_GEMM_FORCE")
+            assert (plan.header["bm"], plan.header["nb"], plan.header["splits"]) == (bm, 1, splits)
+            qmm.qgemm_batched(plan)
+            for (m, n, k), t, want in zip(shapes, ins, wants):
+                assert_close(host(t[4]), want, f"fp16 batched {bm} S={splits} m={m}")
+                t[4].fill_(float("nan"))
+
+
+def test_fp16_weights_grouped():
+    e, n, k, t, top_k = 16, 300, 256, 100, 4
+    say("fp16 grouped")
+    r = np.random.default_rng(944)
+    w16s, wordss = zip(*[fp16_weight((944, ei, n), n, k) for ei in range(e)])
+    words = np.stack(wordss)
+    ids = np.ascontiguousarray(synth.topk_ids(r.standard_normal((t, e)), top_k), dtype=np.int32)
+    x = synth.draw_act((944, 1000), t, k)
+    h = synth.draw_act((944, 1001), t * top_k, k)
+    for per_pair, a in ((False, x), (True, h)):
+        want = np.zeros((t * top_k, n))
+        for p, ex in enumerate(ids.reshape(-1)):
+            want[p] = oracle.hmatmul_f64(w16s[ex], a[p if per_pair else p // top_k][None])[0]
+        y = qmm.qgemm_grouped(dev(words), None, None, dev(a), dev(ids), 16, per_pair)
+        assert_close(host(y), want, f"fp16 grouped per_pair={per_pair}")
+
+
+def test_fused_qkv_gemv_equals_separate():
+    """Decode q, k and v projections read the same activation vector; with
+    their weights stacked along n ([Wq; Wk; Wv], Qwen3-0.6B: 2048 + 1024 +
+    1024 rows over k = 1024) one GEMV launch gives exactly the three
+    separate results (rows are computed independently)."""
+    k = 1024
+    for bits in (4, 8, 16):
+        say("fused qkv", bits)
+        parts, sep = [], []
+        x = dev(synth.draw_act((945, bits), 1, k)[0])
+        for i, n in enumerate((2048, 1024, 1024)):
+            if bits == 16:
+                _, words = fp16_weight((945, bits, i), n, k)
+                s = b = None
+            else:
+                _, _, words, s, b = quantized((945, bits, i, 0), n, k, bits)
+            parts.append((words, s, b))
+            sep.append(qmm.qgemv(dev(words), None if s is None else dev(s), None if b is None else dev(b), x, bits))
+        cat = lambda j: None if parts[0][j] is None else dev(np.concatenate([p[j] for p in parts]))
+        fused = qmm.qgemv(cat(0), cat(1), cat(2), x, bits)
+        assert torch.equal(fused, torch.cat(sep)), bits
