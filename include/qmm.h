@@ -201,6 +201,29 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
                       int group_size, void* workspace, size_t workspace_bytes,
                       qmm_stream stream);
 
+/* Routing plan shared by the grouped products of one MoE layer.  Gate, up
+ * and down read the same expert ids, so the token-to-expert bucketing (the
+ * first launch of qmm_qgemm_grouped) can run once:
+ *   qmm_moe_route        buckets expert_ids [T, top_k] into `plan` (device
+ *                        memory of qmm_moe_route_size(T, top_k, E) bytes,
+ *                        16-byte aligned, caller-owned; contents on entry
+ *                        do not matter);
+ *   qmm_qgemm_grouped_routed  the grouped product of qmm_qgemm_grouped, with
+ *                        the same arguments except that `plan` replaces
+ *                        expert_ids and the workspace.
+ * The plan stays valid while expert_ids is unchanged, for any n, k, bits and
+ * group size, and may be read by several launches in flight.  A plan built
+ * for another (T, top_k, E) is detected on the device and the product is
+ * then not computed (y is left untouched).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (plan too small), HIP. */
+size_t qmm_moe_route_size(int t, int top_k, int e);
+int qmm_moe_route(const int32_t* expert_ids, int t, int top_k, int e, void* plan,
+                  size_t plan_bytes, qmm_stream stream);
+int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+                             const uint16_t* a, int a_row_per_pair, const void* plan, float* y,
+                             int t, int top_k, int e, int n, int k, int bits, int group_size,
+                             qmm_stream stream);
+
 /* ------------------------------------------------ load-time quantization
  * Asymmetric min/max quantization of a dense fp32 weight W[n, k] into the
  * packed format above: per group, s = fp16((max - min) / L) and

@@ -166,13 +166,21 @@ def qgemm_grouped_workspace_size(t, top_k, e, n, k, bits, group_size=GROUP) -> i
 
 
 def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: bool,
-                  y=None, group_size: int = GROUP, workspace=None, stream=None):
-    """Grouped MoE product via qmm_qgemm_grouped; returns y [T*top_k, n]."""
+                  y=None, group_size: int = GROUP, workspace=None, stream=None, plan=None):
+    """Grouped MoE product via qmm_qgemm_grouped; returns y [T*top_k, n].
+    With `plan` (from moe_route on the same expert_ids) it calls
+    qmm_qgemm_grouped_routed and skips the bucketing."""
     e, n = w.shape[0], w.shape[1]
     t, top_k = expert_ids.shape
     k = a.shape[1]
     if y is None:
         y = torch.empty((t * top_k, n), dtype=torch.float32, device=w.device)
+    if plan is not None:
+        check(lib().qmm_qgemm_grouped_routed(_dev(w, "w", _W), _sb(scales, "scales", bits),
+                                             _sb(biases, "biases", bits), _dev(a, "a", _X),
+                                             int(bool(a_row_per_pair)), plan.data_ptr(), _dev(y, "y", _Y),
+                                             t, top_k, e, n, k, bits, group_size, _stream(stream)))
+        return y
     ws_bytes = qgemm_grouped_workspace_size(t, top_k, e, n, k, bits, group_size)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=w.device)
@@ -183,6 +191,18 @@ def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: b
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   _stream(stream)))
     return y
+
+
+def moe_route(expert_ids, e: int, plan=None, stream=None):
+    """Bucket expert_ids [T, top_k] once (qmm_moe_route); returns the plan
+    tensor that qgemm_grouped(..., plan=...) reuses for every projection."""
+    t, top_k = expert_ids.shape
+    need = lib().qmm_moe_route_size(t, top_k, e)
+    if plan is None:
+        plan = torch.empty(max(need, 16), dtype=torch.uint8, device=expert_ids.device)
+    check(lib().qmm_moe_route(_dev(expert_ids, "expert_ids", (torch.int32,)), t, top_k, e,
+                              plan.data_ptr(), plan.numel() * plan.element_size(), _stream(stream)))
+    return plan
 
 
 def quantize(w_f32, bits: int, group_size: int = GROUP, stream=None):

@@ -35,7 +35,9 @@ struct MoeTile {
   int32_t rows;
 };
 
-// Workspace layout (int32 units): [num_tiles][sorted pairs: P][tiles: 3*max_tiles]
+// Workspace layout (int32 units): [num_tiles, row tile, pairs, experts][sorted pairs: P]
+// [tiles: 3*max_tiles].  The same image is the routing plan that one
+// bucketing pass builds for several grouped GEMMs on the same expert ids.
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 static int max_row_tiles(int pairs, int experts, int bm) {
@@ -137,6 +139,11 @@ __global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
       tiles[tstart + i] = MoeTile{tid, start + i * bm, rows};
     }
   }
+  if (tid == 0) {  // what the plan was built for (checked by grouped_kernel)
+    ws[1] = bm;
+    ws[2] = pairs;
+    ws[3] = experts;
+  }
 }
 
 template <int BITS, int BM, int NB, bool SBQ>
@@ -148,6 +155,9 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_kernel(GroupedArgs a, co
   const int pairs = a.t * a.top_k;
   const int tile = blockIdx.x / n_tiles;
   const int tn = blockIdx.x % n_tiles;
+  // a routing plan built for another row tile, pair count or expert count
+  // is not used (the output is left untouched)
+  if (ws[1] != BM || ws[2] != pairs || ws[3] != a.e) return;
   if (tile >= ws[0]) return;
   const MoeTile mt = reinterpret_cast<const MoeTile*>(ws + 4 + pairs)[tile];
   const int32_t* sorted = ws + 4;
@@ -167,30 +177,13 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_kernel(GroupedArgs a, co
                                a.n, tn * BN, a.n, 0, groups, lds, a.group_size);
 }
 
-template <int BITS, int BM, int NB, bool SBQ>
-static hipError_t launch_grouped_tile(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
-  constexpr int BN = 4 * NB * 32;
-  const int pairs = a.t * a.top_k;
-  hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(kBucketThreads), 0, st, a.ids, pairs, a.e,
-                     BM, ws);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int n_tiles = (a.n + BN - 1) / BN;
-  const int m_tiles = max_row_tiles(pairs, a.e, BM);
-  hipLaunchKernelGGL((grouped_kernel<BITS, BM, NB, SBQ>), dim3(m_tiles * n_tiles), dim3(kGemmThreads),
-                     0, st, a, ws, n_tiles);
-  return hipGetLastError();
-}
-
-template <int BITS, bool SBQ>
-static hipError_t launch_grouped_sbq(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
-  // Row tile from the mean number of pairs per expert (one row tile per
-  // expert keeps each expert's weights to a single pass over HBM); 128-wide
-  // column tiles double the workgroups per expert, which measured faster on
-  // the Qwen3-30B-A3B-shaped layers at 512 and 2048 tokens.
-  const int mean = (a.t * a.top_k + a.e - 1) / a.e;
+// Row tile from the mean number of pairs per expert (one row tile per
+// expert keeps each expert's weights to a single pass over HBM);
+// QMM_MOE_FORCE="bm,nb" overrides the tile (tuning sweeps).  The bucketing
+// and the grouped GEMM must agree on it, so both take it from here.
+static void moe_tile(int pairs, int experts, int* bm_out, int* nb_out) {
+  const int mean = (pairs + experts - 1) / experts;
   int bm = mean <= 16 ? 32 : mean <= 48 ? 64 : 128, nb = 1;
-  // QMM_MOE_FORCE="bm,nb" overrides the tile (tuning sweeps).
   if (const char* env = getenv("QMM_MOE_FORCE")) {
     int fb = 0, fn = 0;
     if (sscanf(env, "%d,%d", &fb, &fn) == 2 && (fb == 32 || fb == 64 || fb == 128) && (fn == 1 || fn == 2)) {
@@ -198,34 +191,69 @@ static hipError_t launch_grouped_sbq(const GroupedArgs& a, int32_t* ws, hipStrea
       nb = fn;
     }
   }
+  *bm_out = bm;
+  *nb_out = nb;
+}
+
+hipError_t launch_moe_route(const int32_t* ids, int t, int top_k, int e, void* plan, hipStream_t st) {
+  int bm, nb;
+  moe_tile(t * top_k, e, &bm, &nb);
+  hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(kBucketThreads), 0, st, ids, t * top_k, e, bm,
+                     reinterpret_cast<int32_t*>(plan));
+  return hipGetLastError();
+}
+
+template <int BITS, int BM, int NB, bool SBQ>
+static hipError_t launch_grouped_tile(const GroupedArgs& a, int32_t* ws, bool bucket, hipStream_t st) {
+  constexpr int BN = 4 * NB * 32;
+  const int pairs = a.t * a.top_k;
+  if (bucket) {
+    hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(kBucketThreads), 0, st, a.ids, pairs, a.e,
+                       BM, ws);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const int n_tiles = (a.n + BN - 1) / BN;
+  const int m_tiles = max_row_tiles(pairs, a.e, BM);
+  hipLaunchKernelGGL((grouped_kernel<BITS, BM, NB, SBQ>), dim3(m_tiles * n_tiles), dim3(kGemmThreads),
+                     0, st, a, ws, n_tiles);
+  return hipGetLastError();
+}
+
+// 128-wide column tiles (nb = 1) double the workgroups per expert, which
+// measured faster on the Qwen3-30B-A3B-shaped layers at 512 and 2048 tokens.
+template <int BITS, bool SBQ>
+static hipError_t launch_grouped_sbq(const GroupedArgs& a, int32_t* ws, bool bucket, hipStream_t st) {
+  int bm, nb;
+  moe_tile(a.t * a.top_k, a.e, &bm, &nb);
   if constexpr (BITS == 16) {  // fp16 weights: one column block per wave, no scales
-    if (bm == 32) return launch_grouped_tile<16, 32, 1, false>(a, ws, st);
-    if (bm == 64) return launch_grouped_tile<16, 64, 1, false>(a, ws, st);
-    return launch_grouped_tile<16, 128, 1, false>(a, ws, st);
+    if (bm == 32) return launch_grouped_tile<16, 32, 1, false>(a, ws, bucket, st);
+    if (bm == 64) return launch_grouped_tile<16, 64, 1, false>(a, ws, bucket, st);
+    return launch_grouped_tile<16, 128, 1, false>(a, ws, bucket, st);
   } else {
-    if (bm == 32) return nb == 2 ? launch_grouped_tile<BITS, 32, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 32, 1, SBQ>(a, ws, st);
-    if (bm == 64) return nb == 2 ? launch_grouped_tile<BITS, 64, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 64, 1, SBQ>(a, ws, st);
-    return nb == 2 ? launch_grouped_tile<BITS, 128, 2, SBQ>(a, ws, st) : launch_grouped_tile<BITS, 128, 1, SBQ>(a, ws, st);
+    if (bm == 32) return nb == 2 ? launch_grouped_tile<BITS, 32, 2, SBQ>(a, ws, bucket, st) : launch_grouped_tile<BITS, 32, 1, SBQ>(a, ws, bucket, st);
+    if (bm == 64) return nb == 2 ? launch_grouped_tile<BITS, 64, 2, SBQ>(a, ws, bucket, st) : launch_grouped_tile<BITS, 64, 1, SBQ>(a, ws, bucket, st);
+    return nb == 2 ? launch_grouped_tile<BITS, 128, 2, SBQ>(a, ws, bucket, st) : launch_grouped_tile<BITS, 128, 1, SBQ>(a, ws, bucket, st);
   }
 }
 
 template <int BITS>
-static hipError_t launch_grouped_bits(const GroupedArgs& a, int32_t* ws, hipStream_t st) {
-  if constexpr (BITS == 16) return launch_grouped_sbq<16, false>(a, ws, st);
-  return (a.k / 64) % 4 == 0 && a.group_size == 64 ? launch_grouped_sbq<BITS, true>(a, ws, st)
-                             : launch_grouped_sbq<BITS, false>(a, ws, st);
+static hipError_t launch_grouped_bits(const GroupedArgs& a, int32_t* ws, bool bucket, hipStream_t st) {
+  if constexpr (BITS == 16) return launch_grouped_sbq<16, false>(a, ws, bucket, st);
+  return (a.k / 64) % 4 == 0 && a.group_size == 64 ? launch_grouped_sbq<BITS, true>(a, ws, bucket, st)
+                             : launch_grouped_sbq<BITS, false>(a, ws, bucket, st);
 }
 
-hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, hipStream_t st) {
+hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, bool bucket, hipStream_t st) {
   int32_t* w = reinterpret_cast<int32_t*>(ws);
   switch (bits) {
-    case 2: return launch_grouped_bits<2>(a, w, st);
-    case 3: return launch_grouped_bits<3>(a, w, st);
-    case 4: return launch_grouped_bits<4>(a, w, st);
-    case 5: return launch_grouped_bits<5>(a, w, st);
-    case 6: return launch_grouped_bits<6>(a, w, st);
-    case 8: return launch_grouped_bits<8>(a, w, st);
-    case 16: return launch_grouped_bits<16>(a, w, st);
+    case 2: return launch_grouped_bits<2>(a, w, bucket, st);
+    case 3: return launch_grouped_bits<3>(a, w, bucket, st);
+    case 4: return launch_grouped_bits<4>(a, w, bucket, st);
+    case 5: return launch_grouped_bits<5>(a, w, bucket, st);
+    case 6: return launch_grouped_bits<6>(a, w, bucket, st);
+    case 8: return launch_grouped_bits<8>(a, w, bucket, st);
+    case 16: return launch_grouped_bits<16>(a, w, bucket, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -345,7 +345,60 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
     return fail(QMM_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
   CHECK_PTR(workspace, 16);
   qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, expert_ids, y, t, top_k, e, n, k, group_size};
-  return hip_status(qmm::launch_qgemm_grouped(ga, bits, workspace, (hipStream_t)stream), fn);
+  return hip_status(qmm::launch_qgemm_grouped(ga, bits, workspace, true, (hipStream_t)stream), fn);
+}
+
+size_t qmm_moe_route_size(int t, int top_k, int e) {
+  if (t < 0 || top_k < 1 || e < 1 || e > kMaxExperts) return 0;
+  if ((long)t * top_k > 0x7FFFFFFFL / 4) return 0;
+  return qmm::grouped_workspace_bytes(t, top_k, e, 0);
+}
+
+int qmm_moe_route(const int32_t* expert_ids, int t, int top_k, int e, void* plan,
+                  size_t plan_bytes, qmm_stream stream) {
+  const char* fn = "qmm_moe_route";
+  clear_error();
+  if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
+  if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
+  if (e < 1 || e > kMaxExperts)
+    return fail(QMM_ERR_INVALID_ARG, "%s: e=%d must be in [1, %d]", fn, e, kMaxExperts);
+  if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
+  if (t == 0) return QMM_OK;
+  CHECK_PTR(expert_ids, 4);
+  const size_t need = qmm::grouped_workspace_bytes(t, top_k, e, 0);
+  if (plan == nullptr || plan_bytes < need)
+    return fail(QMM_ERR_WORKSPACE, "%s: plan of %zu bytes, %zu needed", fn, plan_bytes, need);
+  CHECK_PTR(plan, 16);
+  return hip_status(qmm::launch_moe_route(expert_ids, t, top_k, e, plan, (hipStream_t)stream), fn);
+}
+
+int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+                             const uint16_t* a, int a_row_per_pair, const void* plan, float* y,
+                             int t, int top_k, int e, int n, int k, int bits, int group_size,
+                             qmm_stream stream) {
+  const char* fn = "qmm_qgemm_grouped_routed";
+  clear_error();
+  if (int st = check_format(fn, bits, group_size, true)) return st;
+  if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
+  if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
+  if (e < 1 || e > kMaxExperts)
+    return fail(QMM_ERR_INVALID_ARG, "%s: e=%d must be in [1, %d]", fn, e, kMaxExperts);
+  if (a_row_per_pair != 0 && a_row_per_pair != 1)
+    return fail(QMM_ERR_INVALID_ARG, "%s: a_row_per_pair must be 0 or 1", fn);
+  if (int st = check_nk(fn, n, k, group_size)) return st;
+  if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
+  if (t == 0) return QMM_OK;
+  CHECK_PTR(w, 16);
+  if (bits != 16) {
+    CHECK_PTR(scales, 2);
+    CHECK_PTR(biases, 2);
+  }
+  CHECK_PTR(a, 16);
+  CHECK_PTR(plan, 16);
+  CHECK_PTR(y, 4);
+  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, nullptr, y, t, top_k, e, n, k, group_size};
+  return hip_status(qmm::launch_qgemm_grouped(ga, bits, const_cast<void*>(plan), false,
+                                              (hipStream_t)stream), fn);
 }
 
 int qmm_quantize(const float* w_f32, uint32_t* words, uint16_t* scales, uint16_t* biases,

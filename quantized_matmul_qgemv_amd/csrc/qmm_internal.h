@@ -149,7 +149,9 @@ struct GroupedArgs {
   int group_size;
 };
 size_t grouped_workspace_bytes(int t, int top_k, int e, int n);
-hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, hipStream_t st);
+// bucket = false: ws already holds a routing plan for these ids (launch_moe_route).
+hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, bool bucket, hipStream_t st);
+hipError_t launch_moe_route(const int32_t* ids, int t, int top_k, int e, void* plan, hipStream_t st);
 
 hipError_t launch_quantize(const float* w, uint32_t* words, uint16_t* s, uint16_t* b, int n,
                            int k, int bits, int group_size, hipStream_t st);

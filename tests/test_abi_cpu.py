@@ -98,6 +98,23 @@ def test_grouped_errors(L):
            UNS, "bits=7")
 
 
+def test_route_errors(L):
+    need = L.qmm_moe_route_size(512, 8, 128)
+    assert need >= 4 * 512 * 8
+    assert L.qmm_moe_route_size(512, 0, 128) == 0 and L.qmm_moe_route_size(512, 8, 2000) == 0
+    expect(L.qmm_moe_route(A, 512, 8, 128, A, need - 1, None), WSP, "plan of")
+    expect(L.qmm_moe_route(A, 512, 8, 128, None, need, None), WSP, "plan of")
+    expect(L.qmm_moe_route(A + 2, 512, 8, 128, A, need, None), INV, "expert_ids is not 4-byte aligned")
+    expect(L.qmm_moe_route(A, 512, 8, 0, A, need, None), INV, "e=0")
+    assert L.qmm_moe_route(A, 0, 8, 128, None, 0, None) == 0            # no tokens: no-op
+    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 0, None, A, 512, 8, 128, 768, 2048, 4, 64, None),
+           INV, "null pointer plan")
+    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 3, A, A, 512, 8, 128, 768, 2048, 4, 64, None),
+           INV, "a_row_per_pair")
+    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 0, A, A, 512, 8, 128, 768, 2048, 7, 64, None),
+           UNS, "bits=7")
+
+
 def test_other_errors(L):
     expect(L.qmm_quantize(MIS, A, A, A, 8, 64, 4, 64, None), INV, "w_f32 is not 16-byte aligned")
     expect(L.qmm_unpack_codes(A, A, 8, 65, 4, None), INV, "k=65")

@@ -515,3 +515,34 @@ def test_fused_qkv_gemv_equals_separate():
         cat = lambda j: None if parts[0][j] is None else dev(np.concatenate([p[j] for p in parts]))
         fused = qmm.qgemv(cat(0), cat(1), cat(2), x, bits)
         assert torch.equal(fused, torch.cat(sep)), bits
+
+
+def test_routed_grouped_equals_grouped():
+    """One routing plan serves gate, up and down (and any width or group
+    size); results are bit-identical to the self-bucketing call.  A plan
+    built for other expert counts is refused on the device (y untouched)."""
+    t, top_k, e, hidden, inter = 96, 4, 16, 384, 256
+    r = np.random.default_rng(946)
+    ids = np.ascontiguousarray(synth.topk_ids(r.standard_normal((t, e)), top_k), dtype=np.int32)
+    I = dev(ids)
+    plan = qmm.moe_route(I, e)
+    x = dev(synth.draw_act((946, 1), t, hidden))
+    h = dev(synth.draw_act((946, 2), t * top_k, inter))
+    for bits, gs in ((4, 64), (3, 32), (8, 128)):
+        for (k, n, per_pair, a) in ((hidden, inter, False, x), (inter, hidden, True, h)):
+            say("routed grouped", bits, gs, k, n)
+            words, s_, b_, *_ = grouped_inputs((946, bits, k, n), e, n, k, bits, t, top_k, ids=ids)
+            if gs != 64:
+                qs = [quantized_gs((946, bits, gs, ei), n, k, bits, gs) for ei in range(e)]
+                words = np.stack([q[2] for q in qs]); s_ = np.stack([q[3] for q in qs]); b_ = np.stack([q[4] for q in qs])
+            W, S, B = dev(words), dev(s_), dev(b_)
+            y0 = qmm.qgemm_grouped(W, S, B, a, I, bits, per_pair, group_size=gs)
+            y1 = qmm.qgemm_grouped(W, S, B, a, I, bits, per_pair, group_size=gs, plan=plan)
+            assert torch.equal(y0, y1), (bits, gs, per_pair)
+    say("routed grouped: foreign plan")
+    other = qmm.moe_route(I, e + 1)
+    y = torch.full((t * top_k, inter), 7.0, device="cuda")
+    words, s_, b_, *_ = grouped_inputs((947, 4, 0, 0), e, inter, hidden, 4, t, top_k, ids=ids)
+    qmm.qgemm_grouped(dev(words), dev(s_), dev(b_), x, I, 4, False, y=y, plan=other)
+    torch.cuda.synchronize()
+    assert bool((y == 7.0).all())
