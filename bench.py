@@ -362,6 +362,34 @@ def bench_moe(torch, qmm, steps=10, warmup=2):
                        "tflops": round(flops / t / 1e12, 2), "frac_of_roofline": round(roof / t, 4),
                        "launches": "1 routing + 3 grouped GEMMs",
                        "ms_per_step_bucketing_each_gemm": round(ms_unshared, 4)}
+        # the whole FFN block: routing, fused gate+up with SwiGLU (fp16 h),
+        # down from h, routing-weighted combine into y [M, hidden]
+        (Wg, Sg, Bg, X, _, _, _, _), (Wu, Su, Bu, _, _, _, _, _), (Wd, Sd, Bd, _, _, _, Yd, _) = calls
+        pairs = m * wl.top_k
+        H = torch.empty((pairs, wl.inter), dtype=torch.float16, device="cuda")
+        logits = synth.draw_logits((wl.wid, m, 0, synth.STREAM_LOGITS), m, wl.experts)
+        p_ = np.exp(logits - logits.max(axis=1, keepdims=True))
+        p_ = p_ / p_.sum(axis=1, keepdims=True)
+        wts = np.take_along_axis(p_, calls[0][4].cpu().numpy().astype(np.int64), axis=1)
+        Wts = torch.from_numpy((wts / wts.sum(axis=1, keepdims=True)).astype(np.float32)).cuda()
+        Yout = torch.empty((m, wl.hidden), dtype=torch.float32, device="cuda")
+
+        def block(_):
+            qmm.moe_route(ids0, wl.experts, plan=plan)
+            qmm.moe_gate_up_swiglu((Wg, Sg, Bg), (Wu, Su, Bu), X, ids0, plan, wl.bits, h=H)
+            qmm.qgemm_grouped(Wd, Sd, Bd, H, ids0, wl.bits, True, y=Yd, plan=plan)
+            qmm.moe_combine(Yd, Wts, y=Yout)
+        ms_block, _ = time_launches(torch, block, steps, warmup, stream)
+        used = np.unique(calls[0][4].cpu().numpy()).size
+        wbytes = sum(used * (n * k * wl.bits // 8 + 4 * n * (k // 64)) for (_, k, n, _) in synth.moe_projs(wl))
+        bbytes = wbytes + m * wl.hidden * 2 + 2 * pairs * wl.inter * 2 + 2 * pairs * wl.hidden * 4 \
+            + m * wl.hidden * 4 + m * wl.top_k * 8
+        tb = ms_block * 1e-3
+        broof = max(bbytes / (HBM_PEAK_GBS * 1e9), flops / (FP16_MFMA_PEAK_TFLOPS * 1e12))
+        out[str(m)]["ffn_block"] = {
+            "launches": "routing + fused gate/up SwiGLU + down + combine",
+            "ms_per_block": round(ms_block, 4), "bytes": int(bbytes),
+            "tflops": round(flops / tb / 1e12, 2), "frac_of_roofline": round(broof / tb, 4)}
         del calls
     del weights
     torch.cuda.synchronize()

@@ -224,6 +224,27 @@ int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const ui
                              int t, int top_k, int e, int n, int k, int bits, int group_size,
                              qmm_stream stream);
 
+/* Mixture-of-experts FFN block around the grouped products.
+ *   qmm_moe_gate_up_swiglu  for every pair p (token row p / top_k of x
+ *       [T, k] fp16), with e = the pair's expert from `plan` (qmm_moe_route):
+ *           h[p, c] = fp16( silu(g) * u ),  silu(g) = g / (1 + exp(-g)),
+ *           g = sum_k x[row, k] W_gate_e[c, k],  u = likewise with W_up_e
+ *       (g, u and the SwiGLU in fp32; one rounding to fp16).  w_gate, w_up
+ *       [E, n, k*bits/32] with their scales and biases as in
+ *       qmm_qgemm_grouped; h [T*top_k, n] fp16 bits (overwritten) is the
+ *       down projection's A (a_row_per_pair = 1).  bits = 16: fp16 weights.
+ *   qmm_moe_combine  y[t, c] = sum_{j < top_k} weights[t, j] * y_pairs[t*top_k + j, c]
+ *       with the slots added in order j = 0, 1, ... (fp32 fma), so the result
+ *       does not depend on scheduling.  y_pairs [T*top_k, n] fp32 (the down
+ *       projection's output), weights [T, top_k] fp32, y [T, n] fp32.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int qmm_moe_gate_up_swiglu(const uint32_t* w_gate, const uint16_t* s_gate, const uint16_t* b_gate,
+                           const uint32_t* w_up, const uint16_t* s_up, const uint16_t* b_up,
+                           const uint16_t* x, const void* plan, uint16_t* h, int t, int top_k,
+                           int e, int n, int k, int bits, int group_size, qmm_stream stream);
+int qmm_moe_combine(const float* y_pairs, const float* weights, float* y, int t, int top_k, int n,
+                    qmm_stream stream);
+
 /* ------------------------------------------------ load-time quantization
  * Asymmetric min/max quantization of a dense fp32 weight W[n, k] into the
  * packed format above: per group, s = fp16((max - min) / L) and

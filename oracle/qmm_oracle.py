@@ -189,6 +189,33 @@ def grouped_f64(words, s_bits, b_bits, a16, ids, bits: int, a_row_per_pair: bool
     return y
 
 
+# ------------------------------------------------------- MoE FFN block --
+
+def silu_f64(g) -> np.ndarray:
+    """silu(g) = g * sigmoid(g) = g / (1 + exp(-g)), in float64."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def moe_swiglu_f64(gate, up, x16, ids, bits: int, group_size: int = 64) -> np.ndarray:
+    """SwiGLU input of the down projection, per pair p (token row p // top_k):
+        h[p, c] = silu(g[p, c]) * u[p, c]
+    where g and u are the grouped products of the token row with the pair's
+    expert's gate and up weights (each given as (words, s_bits, b_bits))."""
+    g = grouped_f64(*gate, x16, ids, bits, False, group_size)
+    u = grouped_f64(*up, x16, ids, bits, False, group_size)
+    return silu_f64(g) * u
+
+
+def moe_combine_f64(y_pairs, weights) -> np.ndarray:
+    """y[t, c] = sum_j weights[t, j] * y_pairs[t * top_k + j, c] in float64."""
+    w = np.asarray(weights, dtype=np.float64)
+    t, top_k = w.shape
+    yp = np.asarray(y_pairs, dtype=np.float64).reshape(t, top_k, -1)
+    return np.einsum("tj,tjc->tc", w, yp)
+
+
 # --------------------------------------------------------------- routing --
 
 def route(logits, top_k: int):

@@ -56,6 +56,8 @@ SIGNATURES = {
     "qmm_moe_route_size": (SZ, [I, I, I]),
     "qmm_moe_route": (I, [P, I, I, I, P, SZ, P]),
     "qmm_qgemm_grouped_routed": (I, [P, P, P, P, I, P, P, I, I, I, I, I, I, I, P]),
+    "qmm_moe_gate_up_swiglu": (I, [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]),
+    "qmm_moe_combine": (I, [P, P, P, I, I, I, P]),
     "qmm_quantize": (I, [P, P, P, P, I, I, I, I, P]),
     "qmm_unpack_codes": (I, [P, P, I, I, I, P]),
     "qmm_dequant": (I, [P, P, P, P, I, I, I, I, I, P]),

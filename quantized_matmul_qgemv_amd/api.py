@@ -205,6 +205,35 @@ def moe_route(expert_ids, e: int, plan=None, stream=None):
     return plan
 
 
+def moe_gate_up_swiglu(gate, up, x, expert_ids, plan, bits: int, h=None, group_size: int = GROUP,
+                       stream=None):
+    """h [T*top_k, n] fp16 = silu(x W_gate^T) * (x W_up^T) per pair, via
+    qmm_moe_gate_up_swiglu; gate and up are (words, scales, biases)."""
+    wg, sg, bg = gate
+    wu, su, bu = up
+    e, n = wg.shape[0], wg.shape[1]
+    t, top_k = expert_ids.shape
+    k = x.shape[1]
+    if h is None:
+        h = torch.empty((t * top_k, n), dtype=torch.float16, device=wg.device)
+    check(lib().qmm_moe_gate_up_swiglu(_dev(wg, "w_gate", _W), _sb(sg, "s_gate", bits), _sb(bg, "b_gate", bits),
+                                       _dev(wu, "w_up", _W), _sb(su, "s_up", bits), _sb(bu, "b_up", bits),
+                                       _dev(x, "x", _X), plan.data_ptr(), _dev(h, "h", _X),
+                                       t, top_k, e, n, k, bits, group_size, _stream(stream)))
+    return h
+
+
+def moe_combine(y_pairs, weights, y=None, stream=None):
+    """y [T, n] = sum_j weights[t, j] * y_pairs[t*top_k + j] (slot order), via qmm_moe_combine."""
+    t, top_k = weights.shape
+    n = y_pairs.shape[1]
+    if y is None:
+        y = torch.empty((t, n), dtype=torch.float32, device=y_pairs.device)
+    check(lib().qmm_moe_combine(_dev(y_pairs, "y_pairs", _Y), _dev(weights, "weights", _Y),
+                                _dev(y, "y", _Y), t, top_k, n, _stream(stream)))
+    return y
+
+
 def quantize(w_f32, bits: int, group_size: int = GROUP, stream=None):
     """Quantize fp32 W [n, k] on the device -> (words int32, scales int16, biases int16)."""
     n, k = w_f32.shape

@@ -177,6 +177,77 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_kernel(GroupedArgs a, co
                                a.n, tn * BN, a.n, 0, groups, lds, a.group_size);
 }
 
+// Fused gate + up with the SwiGLU epilogue: one workgroup computes, for
+// its row tile and 128 columns, both products of the token rows with the
+// expert's gate and up weights and writes h = silu(gate) * up in fp16 (the
+// down projection's input), so neither fp32 product goes to memory.
+static void moe_tile(int pairs, int experts, int* bm_out, int* nb_out);
+
+struct SwigluArgs {
+  const uint32_t* wg;
+  const uint16_t* sg;
+  const uint16_t* bg;
+  const uint32_t* wu;
+  const uint16_t* su;
+  const uint16_t* bu;
+  const uint16_t* x;
+  uint16_t* h;
+  int t, top_k, e, n, k, group_size;
+};
+
+template <int BITS, int BM, bool SBQ>
+__global__ __launch_bounds__(kGemmThreads) void swiglu_kernel(SwigluArgs a, const int32_t* __restrict__ ws,
+                                                              int n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * kAStride];
+  __shared__ int32_t pair_of[BM];
+  const int pairs = a.t * a.top_k;
+  const int tile = blockIdx.x / n_tiles;
+  const int tn = blockIdx.x % n_tiles;
+  if (ws[1] != BM || ws[2] != pairs || ws[3] != a.e) return;
+  if (tile >= ws[0]) return;
+  const MoeTile mt = reinterpret_cast<const MoeTile*>(ws + 4 + pairs)[tile];
+  const int32_t* sorted = ws + 4;
+  for (int i = threadIdx.x; i < BM; i += blockDim.x)
+    pair_of[i] = sorted[mt.start + (i < mt.rows ? i : mt.rows - 1)];
+  __syncthreads();
+  const int top_k = a.top_k;
+  const int rows = mt.rows;
+  auto a_row = [&](int i) { return pair_of[i] / top_k; };
+  auto c_row = [&](int i) { return i < rows ? pair_of[i] : -1; };
+  const int groups = a.k >> 6;
+  const size_t wstride = (size_t)a.n * groups * Fmt<BITS>::WORDS_PER_GROUP;
+  const size_t sstride = (size_t)a.n * (a.k / a.group_size);
+  const size_t eo = (size_t)mt.expert;
+  gemm_tile<BITS, BM, 2, SBQ, true>(ARows{a.x, a.k}, a_row, c_row, a.wg + eo * wstride,
+                                    a.sg + eo * sstride, a.bg + eo * sstride, nullptr, a.n,
+                                    tn * 128, a.n, 0, groups, lds, a.group_size,
+                                    a.wu + eo * wstride, a.su + eo * sstride, a.bu + eo * sstride,
+                                    a.h + tn * 128);
+}
+
+template <int BITS, bool SBQ>
+static hipError_t launch_swiglu_sbq(const SwigluArgs& a, const int32_t* plan, hipStream_t st) {
+  int bm, nb;
+  moe_tile(a.t * a.top_k, a.e, &bm, &nb);
+  const int n_tiles = (a.n + 127) / 128;
+  const int m_tiles = max_row_tiles(a.t * a.top_k, a.e, bm);
+  const dim3 grid(m_tiles * n_tiles);
+  if (bm == 32) hipLaunchKernelGGL((swiglu_kernel<BITS, 32, SBQ>), grid, dim3(kGemmThreads), 0, st, a, plan, n_tiles);
+  else if (bm == 64) hipLaunchKernelGGL((swiglu_kernel<BITS, 64, SBQ>), grid, dim3(kGemmThreads), 0, st, a, plan, n_tiles);
+  else hipLaunchKernelGGL((swiglu_kernel<BITS, 128, SBQ>), grid, dim3(kGemmThreads), 0, st, a, plan, n_tiles);
+  return hipGetLastError();
+}
+
+template <int BITS>
+static hipError_t launch_swiglu_bits(const SwigluArgs& a, const int32_t* plan, hipStream_t st) {
+  if constexpr (BITS == 16) {
+    return launch_swiglu_sbq<16, false>(a, plan, st);
+  } else {
+    return (a.k / 64) % 4 == 0 && a.group_size == 64 ? launch_swiglu_sbq<BITS, true>(a, plan, st)
+                                                     : launch_swiglu_sbq<BITS, false>(a, plan, st);
+  }
+}
+
 // Row tile from the mean number of pairs per expert (one row tile per
 // expert keeps each expert's weights to a single pass over HBM);
 // QMM_MOE_FORCE="bm,nb" overrides the tile (tuning sweeps).  The bucketing
@@ -256,6 +327,49 @@ hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, bool b
     case 16: return launch_grouped_bits<16>(a, w, bucket, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_moe_swiglu(const uint32_t* wg, const uint16_t* sg, const uint16_t* bg,
+                             const uint32_t* wu, const uint16_t* su, const uint16_t* bu,
+                             const uint16_t* x, const void* plan, uint16_t* h, int t, int top_k,
+                             int e, int n, int k, int bits, int group_size, hipStream_t st) {
+  const SwigluArgs a{wg, sg, bg, wu, su, bu, x, h, t, top_k, e, n, k, group_size};
+  const int32_t* p = static_cast<const int32_t*>(plan);
+  switch (bits) {
+    case 2: return launch_swiglu_bits<2>(a, p, st);
+    case 3: return launch_swiglu_bits<3>(a, p, st);
+    case 4: return launch_swiglu_bits<4>(a, p, st);
+    case 5: return launch_swiglu_bits<5>(a, p, st);
+    case 6: return launch_swiglu_bits<6>(a, p, st);
+    case 8: return launch_swiglu_bits<8>(a, p, st);
+    case 16: return launch_swiglu_bits<16>(a, p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// y[t, :] = sum over j of weights[t, j] * y_pairs[t * top_k + j, :], the
+// slots added in order j = 0 .. top_k-1 (fp32 fma): the routing-weighted
+// combine of the down projection's per-pair rows, independent of scheduling.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ y_pairs,
+                                                          const float* __restrict__ weights,
+                                                          float* __restrict__ y, int t, int top_k,
+                                                          int n) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)t * n) return;
+  const long tok = i / n;
+  const long col = i % n;
+  float acc = 0.0f;
+  for (int j = 0; j < top_k; ++j)
+    acc = fmaf(weights[tok * top_k + j], y_pairs[(tok * top_k + j) * n + col], acc);
+  y[i] = acc;
+}
+
+hipError_t launch_moe_combine(const float* y_pairs, const float* weights, float* y, int t, int top_k,
+                              int n, hipStream_t st) {
+  const long count = (long)t * n;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
+                     y_pairs, weights, y, t, top_k, n);
+  return hipGetLastError();
 }
 
 }  // namespace qmm

@@ -183,13 +183,23 @@ struct ARows {
 // lds holds 2 * BM * AST halves.
 constexpr int kAStride = 72;  // LDS row stride in halves: 64 + 8 pad (144 B)
 
-template <int BITS, int BM, int NB, bool SBQ, typename ARowFn, typename CRowFn>
+//
+// SWIGLU (NB = 2): the two column blocks of a wave are the SAME 32 columns of
+// two weight sets, gate (w_, s_, b_) and up (w2_, s2_, b2_); the epilogue
+// writes h = silu(gate) * up, rounded to fp16, to h_tile[row * ldy + c] for
+// the tile's 128 columns (y_tile is unused).
+template <int BITS, int BM, int NB, bool SBQ, bool SWIGLU = false, typename ARowFn, typename CRowFn>
 __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_row,
                                           const uint32_t* __restrict__ w_,
                                           const uint16_t* __restrict__ s_,
                                           const uint16_t* __restrict__ b_, float* __restrict__ y_tile,
                                           int ldy, int n0, int n, int g_begin, int g_end,
-                                          uint16_t* lds, int gs = 64) {
+                                          uint16_t* lds, int gs = 64,
+                                          const uint32_t* __restrict__ w2_ = nullptr,
+                                          const uint16_t* __restrict__ s2_ = nullptr,
+                                          const uint16_t* __restrict__ b2_ = nullptr,
+                                          uint16_t* __restrict__ h_tile = nullptr) {
+  static_assert(!SWIGLU || NB == 2, "SwiGLU pairs a gate and an up column block");
   constexpr int MB = BM / 32;
   constexpr int SPANS = BM * 4;  // 16-wide spans of A per step
   constexpr int SPT = (SPANS + kGemmThreads - 1) / kGemmThreads;
@@ -212,11 +222,12 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   gptr<uint16_t> bcol[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    int col = n0 + (wave * NB + nb) * 32 + l32;
+    int col = SWIGLU ? n0 + wave * 32 + l32 : n0 + (wave * NB + nb) * 32 + l32;
     col = col < n ? col : n - 1;
-    wcol[nb] = w + (size_t)col * groups * WPG;
-    scol[nb] = s + (size_t)col * sgroups;
-    bcol[nb] = b + (size_t)col * sgroups;
+    const bool second = SWIGLU && nb == 1;
+    wcol[nb] = (second ? to_global(w2_) : w) + (size_t)col * groups * WPG;
+    scol[nb] = (second ? to_global(s2_) : s) + (size_t)col * sgroups;
+    bcol[nb] = (second ? to_global(b2_) : b) + (size_t)col * sgroups;
   }
 
   gptr<uint16_t> asrc[SPT];
@@ -382,6 +393,27 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
 #undef QMM_GEMM_STEP
   }
 
+  // epilogue: D[i][j] of a 32x32 block sits in lane (j + 32*((i/4)%2)),
+  // register (i/8)*4 + i%4.
+  if constexpr (SWIGLU) {
+    const gptr_mut<uint16_t> hp = to_global_mut(h_tile);
+    const int lc = wave * 32 + l32;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = mb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+        const int row = c_row(i);
+        if (row >= 0 && n0 + lc < n) {
+          const float g = acc[mb][0][r];
+          const float u = acc[mb][1][r];
+          const float hv = g / (1.0f + expf(-g)) * u;  // silu(gate) * up
+          hp[(size_t)row * ldy + lc] = __builtin_bit_cast(uint16_t, (half_t)hv);
+        }
+      }
+    }
+    return;
+  }
   // epilogue: D[i][j] of a 32x32 block sits in lane (j + 32*((i/4)%2)),
   // register (i/8)*4 + i%4.
 #pragma unroll

@@ -401,6 +401,51 @@ int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const ui
                                               (hipStream_t)stream), fn);
 }
 
+int qmm_moe_gate_up_swiglu(const uint32_t* w_gate, const uint16_t* s_gate, const uint16_t* b_gate,
+                           const uint32_t* w_up, const uint16_t* s_up, const uint16_t* b_up,
+                           const uint16_t* x, const void* plan, uint16_t* h, int t, int top_k,
+                           int e, int n, int k, int bits, int group_size, qmm_stream stream) {
+  const char* fn = "qmm_moe_gate_up_swiglu";
+  clear_error();
+  if (int st = check_format(fn, bits, group_size, true)) return st;
+  if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
+  if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
+  if (e < 1 || e > kMaxExperts)
+    return fail(QMM_ERR_INVALID_ARG, "%s: e=%d must be in [1, %d]", fn, e, kMaxExperts);
+  if (int st = check_nk(fn, n, k, group_size)) return st;
+  if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
+  if (t == 0) return QMM_OK;
+  CHECK_PTR(w_gate, 16);
+  CHECK_PTR(w_up, 16);
+  if (bits != 16) {
+    CHECK_PTR(s_gate, 2);
+    CHECK_PTR(b_gate, 2);
+    CHECK_PTR(s_up, 2);
+    CHECK_PTR(b_up, 2);
+  }
+  CHECK_PTR(x, 16);
+  CHECK_PTR(plan, 16);
+  CHECK_PTR(h, 2);
+  return hip_status(qmm::launch_moe_swiglu(w_gate, s_gate, b_gate, w_up, s_up, b_up, x, plan, h, t,
+                                           top_k, e, n, k, bits, group_size, (hipStream_t)stream),
+                    fn);
+}
+
+int qmm_moe_combine(const float* y_pairs, const float* weights, float* y, int t, int top_k, int n,
+                    qmm_stream stream) {
+  const char* fn = "qmm_moe_combine";
+  clear_error();
+  if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
+  if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
+  if (n < 1) return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be >= 1", fn, n);
+  if ((long)t * top_k * n > 0x7FFFFFFFFFL) return fail(QMM_ERR_INVALID_ARG, "%s: too large", fn);
+  if (t == 0) return QMM_OK;
+  CHECK_PTR(y_pairs, 4);
+  CHECK_PTR(weights, 4);
+  CHECK_PTR(y, 4);
+  return hip_status(qmm::launch_moe_combine(y_pairs, weights, y, t, top_k, n, (hipStream_t)stream), fn);
+}
+
 int qmm_quantize(const float* w_f32, uint32_t* words, uint16_t* scales, uint16_t* biases,
                  int n, int k, int bits, int group_size, qmm_stream stream) {
   const char* fn = "qmm_quantize";

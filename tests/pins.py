@@ -429,9 +429,47 @@ def check_fp16_weights(o, seed=10):
     assert not y[:, [0, 1, 3]].any()
 
 
+def check_moe_ffn(o, seed=11):
+    """SwiGLU and the weighted combine.
+    * silu: silu(0) = 0; silu(1) = 1/(1 + e^-1) = 0.7310585786300049 (the
+      textbook logistic value); silu(x) - silu(-x) = x; silu(40) = 40 and
+      silu(-40) = -40 e^-40 to double precision.
+    * one-hot activation (x = e_j): g and u are column j of the expert's
+      dequantized gate and up weights, so h = silu(W_g[:, j]) * W_u[:, j].
+    * combine: one-hot routing weights pick one pair row; weights summing to
+      one over identical rows return that row; the slot order matters."""
+    assert o.silu_f64(0.0) == 0.0
+    assert abs(o.silu_f64(1.0) - 0.7310585786300049) < 1e-15
+    xs = np.linspace(-6, 6, 25)
+    assert np.allclose(o.silu_f64(xs) - o.silu_f64(-xs), xs, rtol=0, atol=1e-14)
+    assert abs(o.silu_f64(40.0) - 40.0) < 1e-12 and abs(o.silu_f64(-40.0) + 40.0 * np.exp(-40.0)) < 1e-28
+    r = np.random.default_rng(seed)
+    e, n, k, t, top_k = 3, 5, 64, 4, 2
+    ids = np.array([[0, 2], [1, 0], [2, 1], [0, 1]], dtype=np.int32)
+    mats = []
+    for which in range(2):
+        ws = [o.quantize((r.standard_normal((n, k)) * 0.5).astype(np.float32), 4) for _ in range(e)]
+        mats.append((np.stack([o.pack(q, 4) for q, _, _ in ws]), np.stack([s_ for _, s_, _ in ws]),
+                     np.stack([b_ for _, _, b_ in ws]), [o.dequant_f64(q, s_, b_) for q, s_, b_ in ws]))
+    for j in (0, 17, 63):
+        x = np.zeros((t, k), dtype=np.float16)
+        x[:, j] = 1.0
+        h = o.moe_swiglu_f64(mats[0][:3], mats[1][:3], x, ids, 4)
+        for p_ in range(t * top_k):
+            ex = ids.reshape(-1)[p_]
+            g = mats[0][3][ex][:, j]
+            u = mats[1][3][ex][:, j]
+            assert np.allclose(h[p_], g / (1 + np.exp(-g)) * u, rtol=1e-15, atol=0)
+    yp = r.standard_normal((t * top_k, 7))
+    w1 = np.zeros((t, top_k)); w1[:, 1] = 1.0
+    assert np.array_equal(o.moe_combine_f64(yp, w1), yp[1::top_k])
+    same = np.repeat(r.standard_normal((t, 1, 7)), top_k, axis=1).reshape(t * top_k, 7)
+    assert np.allclose(o.moe_combine_f64(same, np.full((t, top_k), 1.0 / top_k)), same[::top_k], rtol=1e-15)
+
+
 ALL_CHECKS = (
     check_f16_rounding, check_pack_golden, check_pack_roundtrip,
     check_quantize_golden, check_quantize_nearest_level, check_quantize_error_bound,
     check_dot_exact_rational, check_closed_forms, check_gemm_rows_are_gemvs,
-    check_grouped, check_route, check_group_sizes, check_fp16_weights,
+    check_grouped, check_route, check_group_sizes, check_fp16_weights, check_moe_ffn,
 )

@@ -50,6 +50,15 @@ def m_quantize_ignores_group_size(o):
     o.quantize = quantize
 
 
+def m_silu_is_sigmoid(o):
+    o.silu_f64 = lambda g: 1.0 / (1.0 + np.exp(-np.asarray(g, dtype=np.float64)))
+
+
+def m_combine_slots_reversed(o):
+    real = o.moe_combine_f64
+    o.moe_combine_f64 = lambda y_pairs, weights: real(y_pairs, np.asarray(weights)[:, ::-1])
+
+
 def m_pack_high_first(o):
     real_pack, real_unpack = o.pack, o.unpack
 
@@ -225,7 +234,8 @@ MUTANTS = [
     m_quantize_floor, m_quantize_ties_up, m_quantize_bias_max, m_quantize_unrounded_scale,
     m_quantize_no_clamp, m_quantize_levels_off_by_one, m_matmul_transposed, m_matmul_f32,
     m_grouped_wrong_row, m_grouped_expert_off_by_one, m_route_no_renorm, m_route_ascending,
-    m_f16_double_rounding, m_f16_truncate, m_quantize_ignores_group_size,
+    m_f16_double_rounding, m_f16_truncate, m_quantize_ignores_group_size, m_silu_is_sigmoid,
+    m_combine_slots_reversed,
 ]
 
 
