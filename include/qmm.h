@@ -257,6 +257,16 @@ int qmm_moe_combine(const float* y_pairs, const float* weights, float* y, int t,
 int qmm_quantize(const float* w_f32, uint32_t* words, uint16_t* scales, uint16_t* biases,
                  int n, int k, int bits, int group_size, qmm_stream stream);
 
+/* bf16 weights (load time).  The matrix cores multiply fp16 by fp16 or bf16
+ * by bf16, not fp16 activations by bf16 weights, so bf16 weights are
+ * converted once to fp16 and then used as bits = 16:
+ *   dst[i] = fp16(bf16 src[i]), round to nearest even; exact for every bf16
+ *   whose magnitude lies in fp16's normal range, +-inf beyond 65504.
+ *   src, dst: count uint16 bit patterns (count even, 4-byte aligned; dst may
+ *   equal src for an in-place conversion).
+ * Errors: INVALID_ARG, HIP. */
+int qmm_convert_bf16(const uint16_t* src, uint16_t* dst, size_t count, qmm_stream stream);
+
 /* ------------------------------------------------------------- diagnostics
  * Expose the device-side stages of the hot path for bit-exact checking.
  * qmm_unpack_codes: codes[n, k] (uint8) = the codes of `w`, decoded with

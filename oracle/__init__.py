@@ -27,7 +27,8 @@ name widths from 2 to 8 bits (BaseRT §3.3 and §4.1: Q2, Q3, Q4, Q5, Q6,
 Q8) without giving a layout; every width here uses the same little-endian
 bit stream.  Scale groups of 32, 64 or 128 codes are supported.  The 16-bit
 format (unquantized fp16 weights, §4.1 FP16) is the plain matmul with each
-weight at its exact fp16 value (hmatmul_f64).  Around the grouped products
+weight at its exact fp16 value (hmatmul_f64); bf16 weights enter it through
+their fp16 rounding (bf16_to_f16_bits).  Around the grouped products
 of a mixture-of-experts FFN block: the SwiGLU input of the down projection,
 silu(gate) * up per pair (moe_swiglu_f64), and the routing-weighted sum of
 each token's pair rows (moe_combine_f64).
@@ -42,5 +43,5 @@ routing invariants.  No function here is "parity unpinned".
 from .qmm_oracle import (  # noqa: F401
     f16_bits, f16_value, quantize, pack, unpack, dequant_f64, round_to_f32,
     round_to_f16_bits, matmul_f64, qmatmul_f64, hmatmul_f64, grouped_f64, route,
-    packed_words_per_row, silu_f64, moe_swiglu_f64, moe_combine_f64,
+    packed_words_per_row, silu_f64, moe_swiglu_f64, moe_combine_f64, bf16_to_f16_bits,
 )

@@ -156,6 +156,15 @@ def qmatmul_f64(words, s_bits, b_bits, x16, bits: int, group_size: int = 64):
     return matmul_f64(x16, w_hat)
 
 
+def bf16_to_f16_bits(b_bits) -> np.ndarray:
+    """bf16 bit patterns -> fp16 bit patterns of the same value, rounded to
+    nearest even (the bf16 value is exact in float32; numpy converts float32
+    to float16 with one rounding).  Beyond fp16's range: +-inf; NaN stays NaN."""
+    f32 = (np.asarray(b_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(over="ignore"):
+        return f32.astype(np.float16).view(np.uint16)
+
+
 def hmatmul_f64(w_bits, x16) -> np.ndarray:
     """Unquantized fp16 weights (the 16-bit format next to Q2..Q8): y[m, n] =
     sum_k x[m, k] * W[n, k] with W given as fp16 bit patterns [n, k], each

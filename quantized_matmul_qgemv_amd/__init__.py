@@ -5,7 +5,7 @@ include/qmm.h); this package only marshals torch device tensors into it.
 """
 from ._lib import QmmError, lib, last_error  # noqa: F401
 from .api import (  # noqa: F401
-    GemmBatchPlan, GemvPlan, dequant, moe_combine, moe_gate_up_swiglu, moe_route, qgemm, qgemm_batched, qgemm_batched_plan,
+    GemmBatchPlan, GemvPlan, convert_bf16, dequant, moe_combine, moe_gate_up_swiglu, moe_route, qgemm, qgemm_batched, qgemm_batched_plan,
     qgemm_grouped, qgemm_grouped_workspace_size,
     qgemm_workspace_size, qgemv, qgemv_batched, qgemv_batched_plan, quantize,
     unpack_codes,
@@ -13,7 +13,7 @@ from .api import (  # noqa: F401
 
 __all__ = [
     "QmmError", "lib", "last_error", "GemmBatchPlan", "GemvPlan", "dequant", "qgemm",
-    "moe_combine", "moe_gate_up_swiglu", "moe_route", "qgemm_batched", "qgemm_batched_plan", "qgemm_grouped",
+    "convert_bf16", "moe_combine", "moe_gate_up_swiglu", "moe_route", "qgemm_batched", "qgemm_batched_plan", "qgemm_grouped",
     "qgemm_grouped_workspace_size", "qgemm_workspace_size", "qgemv", "qgemv_batched",
     "qgemv_batched_plan", "quantize", "unpack_codes",
 ]

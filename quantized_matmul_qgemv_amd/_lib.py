@@ -58,6 +58,7 @@ SIGNATURES = {
     "qmm_qgemm_grouped_routed": (I, [P, P, P, P, I, P, P, I, I, I, I, I, I, I, P]),
     "qmm_moe_gate_up_swiglu": (I, [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]),
     "qmm_moe_combine": (I, [P, P, P, I, I, I, P]),
+    "qmm_convert_bf16": (I, [P, P, SZ, P]),
     "qmm_quantize": (I, [P, P, P, P, I, I, I, I, P]),
     "qmm_unpack_codes": (I, [P, P, I, I, I, P]),
     "qmm_dequant": (I, [P, P, P, P, I, I, I, I, I, P]),

@@ -234,6 +234,18 @@ def moe_combine(y_pairs, weights, y=None, stream=None):
     return y
 
 
+def convert_bf16(w_bf16, out=None, stream=None):
+    """bf16 weights (torch.bfloat16, or int16 bit patterns) -> fp16 weights as
+    int32 words [.., k/2] for bits = 16, via qmm_convert_bf16."""
+    src = w_bf16.view(torch.int16) if w_bf16.dtype == torch.bfloat16 else w_bf16
+    if not src.is_contiguous() or src.shape[-1] % 2:
+        raise ValueError("w_bf16 must be contiguous with an even last dimension")
+    if out is None:
+        out = torch.empty(src.shape[:-1] + (src.shape[-1] // 2,), dtype=torch.int32, device=src.device)
+    check(lib().qmm_convert_bf16(_dev(src, "w_bf16", _SB), out.data_ptr(), src.numel(), _stream(stream)))
+    return out
+
+
 def quantize(w_f32, bits: int, group_size: int = GROUP, stream=None):
     """Quantize fp32 W [n, k] on the device -> (words int32, scales int16, biases int16)."""
     n, k = w_f32.shape

@@ -459,6 +459,17 @@ int qmm_quantize(const float* w_f32, uint32_t* words, uint16_t* scales, uint16_t
   return hip_status(qmm::launch_quantize(w_f32, words, scales, biases, n, k, bits, group_size, (hipStream_t)stream), fn);
 }
 
+int qmm_convert_bf16(const uint16_t* src, uint16_t* dst, size_t count, qmm_stream stream) {
+  const char* fn = "qmm_convert_bf16";
+  clear_error();
+  if (count == 0) return QMM_OK;
+  if (count % 2 != 0) return fail(QMM_ERR_INVALID_ARG, "%s: count=%zu must be even", fn, count);
+  if (count > ((size_t)1 << 40)) return fail(QMM_ERR_INVALID_ARG, "%s: count=%zu too large", fn, count);
+  CHECK_PTR(src, 4);
+  CHECK_PTR(dst, 4);
+  return hip_status(qmm::launch_convert_bf16(src, dst, (long)count, (hipStream_t)stream), fn);
+}
+
 int qmm_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,
                      qmm_stream stream) {
   const char* fn = "qmm_unpack_codes";

@@ -161,6 +161,7 @@ hipError_t launch_moe_combine(const float* y_pairs, const float* weights, float*
 
 hipError_t launch_quantize(const float* w, uint32_t* words, uint16_t* s, uint16_t* b, int n,
                            int k, int bits, int group_size, hipStream_t st);
+hipError_t launch_convert_bf16(const uint16_t* src, uint16_t* dst, long count, hipStream_t st);
 hipError_t launch_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,
                                hipStream_t st);
 hipError_t launch_dequant(const uint32_t* w, const uint16_t* s, const uint16_t* b, void* out,

@@ -203,6 +203,29 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
 
 static unsigned blocks_for(long items) { return (unsigned)((items + 255) / 256); }
 
+// bf16 weights -> fp16 (load time): the bf16 value widened to fp32 (exact),
+// then rounded to fp16 (round to nearest even; beyond fp16's range: +-inf).
+// Every bf16 inside fp16's normal range converts exactly (8 significant bits
+// into 11).  Two values per thread.
+__global__ __launch_bounds__(256) void convert_bf16_kernel(const uint32_t* __restrict__ src,
+                                                           uint32_t* __restrict__ dst, long pairs) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= pairs) return;
+  const uint32_t v = src[i];
+  const float lo = __builtin_bit_cast(float, v << 16);
+  const float hi = __builtin_bit_cast(float, v & 0xFFFF0000u);
+  const uint32_t l16 = __builtin_bit_cast(uint16_t, (half_t)lo);
+  const uint32_t h16 = __builtin_bit_cast(uint16_t, (half_t)hi);
+  dst[i] = l16 | (h16 << 16);
+}
+
+hipError_t launch_convert_bf16(const uint16_t* src, uint16_t* dst, long count, hipStream_t st) {
+  const long pairs = count / 2;
+  hipLaunchKernelGGL(convert_bf16_kernel, dim3(blocks_for(pairs)), dim3(256), 0, st,
+                     reinterpret_cast<const uint32_t*>(src), reinterpret_cast<uint32_t*>(dst), pairs);
+  return hipGetLastError();
+}
+
 template <int GS>
 static hipError_t launch_quantize_gs(const float* w, uint32_t* words, uint16_t* s, uint16_t* b,
                                      int n, int k, int bits, hipStream_t st) {

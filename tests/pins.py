@@ -467,9 +467,30 @@ def check_moe_ffn(o, seed=11):
     assert np.allclose(o.moe_combine_f64(same, np.full((t, top_k), 1.0 / top_k)), same[::top_k], rtol=1e-15)
 
 
+def check_bf16_to_f16(o):
+    """bf16 -> fp16 conversion of weights: hand-worked patterns (1.0, -2.0,
+    0.125, 65280 = largest bf16 below fp16's max, 65536 -> inf, NaN), the
+    two subnormal rounding cases at 2^-25 (a tie, to even: 0) and 1.5 * 2^-25
+    (up to the smallest subnormal 2^-24), and exactness of every bf16 whose
+    magnitude lies in fp16's normal range."""
+    cases = {0x3F80: 0x3C00, 0xC000: 0xC000, 0x3E00: 0x3000, 0x477F: 0x7BF8, 0x4780: 0x7C00,
+             0xC780: 0xFC00, 0x3300: 0x0000, 0x3340: 0x0001, 0x0000: 0x0000, 0x8000: 0x8000}
+    got = o.bf16_to_f16_bits(np.array(list(cases), dtype=np.uint16))
+    assert [int(v) for v in got] == list(cases.values()), [hex(v) for v in got]
+    nan = int(o.bf16_to_f16_bits(np.array([0x7FC0], dtype=np.uint16))[0])
+    assert (nan & 0x7C00) == 0x7C00 and (nan & 0x03FF) != 0
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # NaN patterns
+        val = (allb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    normal = np.isfinite(val) & (np.abs(val) >= 2.0 ** -14) & (np.abs(val) <= 65504.0)
+    out = o.f16_value(o.bf16_to_f16_bits(allb[normal]))
+    assert np.array_equal(out, val[normal])
+
+
 ALL_CHECKS = (
     check_f16_rounding, check_pack_golden, check_pack_roundtrip,
     check_quantize_golden, check_quantize_nearest_level, check_quantize_error_bound,
     check_dot_exact_rational, check_closed_forms, check_gemm_rows_are_gemvs,
     check_grouped, check_route, check_group_sizes, check_fp16_weights, check_moe_ffn,
+    check_bf16_to_f16,
 )

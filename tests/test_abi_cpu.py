@@ -115,6 +115,13 @@ def test_route_errors(L):
            UNS, "bits=7")
 
 
+def test_convert_bf16_errors(L):
+    expect(L.qmm_convert_bf16(A, A, 7, None), INV, "must be even")
+    expect(L.qmm_convert_bf16(A + 2, A, 8, None), INV, "src is not 4-byte aligned")
+    expect(L.qmm_convert_bf16(A, None, 8, None), INV, "null pointer dst")
+    assert L.qmm_convert_bf16(None, None, 0, None) == 0
+
+
 def test_other_errors(L):
     expect(L.qmm_quantize(MIS, A, A, A, 8, 64, 4, 64, None), INV, "w_f32 is not 16-byte aligned")
     expect(L.qmm_unpack_codes(A, A, 8, 65, 4, None), INV, "k=65")

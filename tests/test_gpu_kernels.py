@@ -610,3 +610,24 @@ def test_moe_ffn_block_chain():
     yp = r.standard_normal((t * top_k, 333)).astype(np.float32)
     got = qmm.moe_combine(torch.from_numpy(yp).cuda(), W)
     assert_close(host(got), oracle.moe_combine_f64(yp, wts.astype(np.float32)), "combine")
+
+
+
+def test_convert_bf16_bit_exact_all_patterns():
+    """Every one of the 65536 bf16 bit patterns converts to the oracle's fp16
+    (NaN payloads compared as NaN); then a GEMV over converted bf16 weights
+    matches the float64 product of the bf16 values (exact in fp16 here)."""
+    say("bf16 -> fp16")
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = host(qmm.convert_bf16(dev(allb.view(np.int16))), np.uint32).view(np.uint16)
+    want = oracle.bf16_to_f16_bits(allb)
+    nan = (want & 0x7C00) == 0x7C00
+    nan &= (want & 0x03FF) != 0
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.all(((got[nan] & 0x7C00) == 0x7C00) & ((got[nan] & 0x03FF) != 0))
+    n, k = 300, 1024
+    wb = torch.from_numpy(synth.draw_weight((960, n, k), n, k)).to(torch.bfloat16)
+    w16 = oracle.bf16_to_f16_bits(wb.view(torch.int16).numpy().view(np.uint16))
+    x = synth.draw_act((960, 1), 1, k)
+    y = qmm.qgemv(qmm.convert_bf16(wb.cuda()), None, None, dev(x[0]), 16)
+    assert_close(host(y), oracle.hmatmul_f64(w16, x)[0], "bf16 weights via fp16")
