@@ -64,9 +64,9 @@ TRAFFIC = {
     # (KiB per dispatch of qgemv_batched_kernel<4,16,4,64>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 166779.0, "fetch_scale": 1073741824 / (524301.3 * 1024),
-    "write_kib": 1939.1, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "0146b8912eb0b264ccead8788d5964f6f610cee8a721b1928e13949c6f60251f",
+    "fetch_kib": 166771.0, "fetch_scale": 1073741824 / (524301.3 * 1024),
+    "write_kib": 1939.3, "write_scale": 1073741824 / (1048576.0 * 1024),
+    "sources_sha256": "fbb57fbe7cd5c41c6fff7702febe9a199f2c3db515388034a088467486015fe3",
 }
 
 
@@ -197,6 +197,24 @@ def bench_single_gemv(torch, qmm, steps=200, warmup=20):
         torch, lambda i: qmm.qgemv(words, s, b, x, wl.bits, y=y), steps, warmup, stream)
     return {"workload": wl.name, "us_per_launch": round(ms * 1e3, 2),
             "gb_per_s": round(gemv_bytes(n, k, 4) / (ms * 1e-3) / 1e9, 1)}
+
+
+def bench_projections(torch, qmm, wl, sets, launches=20):
+    """Each distinct projection of the decode pass (layer 0's q, k, v, o,
+    gate, up, down and the lm_head) as `launches` back-to-back single GEMV
+    launches, in that order (a kernel trace of this run gives each
+    projection's kernel duration; the event time here includes the launch
+    gaps, which dominate the small projections)."""
+    stream = torch.cuda.current_stream()
+    names = [p.name for p in wl.projs] + [p.name for p in wl.extra]
+    picks = list(range(len(wl.projs))) + [len(sets[0]) - 1]
+    out = {}
+    for name, idx in zip(names, picks):
+        words, s_, b_, x, y, n, k = sets[0][idx]
+        ms, _ = time_launches(torch, lambda i: qmm.qgemv(words, s_, b_, x, wl.bits, y=y), launches, 3, stream)
+        out[name] = {"n": n, "k": k, "us_per_launch": round(ms * 1e3, 2),
+                     "gb_per_s": round(gemv_bytes(n, k, wl.bits) / (ms * 1e-3) / 1e9, 1)}
+    return out
 
 
 def bench_decode_extras(torch, qmm, wl, sets, steps=20, warmup=3):
@@ -437,7 +455,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["all", "decode", "prefill", "moe"], default="all",
+    ap.add_argument("--only", choices=["all", "decode", "decode_extras", "projections", "prefill", "moe"],
+                    default="all",
                     help="run one workload only (for profiling); prefill and moe print "
                          "their own section as the JSON line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -525,9 +544,11 @@ def main():
                      "bytes_per_launch": d["step_bytes"],
                      "launch_ms_mean": round(d["ms_step"], 5)},
     }
-    if args.only == "all":
+    if args.only in ("all", "decode_extras"):
         log("decode extras")
         result["decode_context"] = bench_decode_extras(torch, qmm, wl, d["sets"])
+    if args.only == "projections":
+        result["projections"] = bench_projections(torch, qmm, wl, d["sets"])
     del d
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
