@@ -146,9 +146,14 @@ __global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
   }
 }
 
+// Waves per SIMD the register allocator is held to: two, except for the
+// 128-row, 256-column tiles of the 5- to 16-bit formats, which would spill
+// at two and keep the whole register file at one.
+constexpr int moe_waves(int bits, int bm, int nb) { return (bm == 128 && nb == 2 && bits >= 5) ? 1 : 2; }
+
 template <int BITS, int BM, int NB, bool SBQ>
-__global__ __launch_bounds__(kGemmThreads) void grouped_kernel(GroupedArgs a, const int32_t* __restrict__ ws,
-                                                               int n_tiles) {
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(moe_waves(BITS, BM, NB))))
+void grouped_kernel(GroupedArgs a, const int32_t* __restrict__ ws, int n_tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * kAStride];
   __shared__ int32_t pair_of[BM];
   constexpr int BN = 4 * NB * 32;
@@ -196,8 +201,8 @@ struct SwigluArgs {
 };
 
 template <int BITS, int BM, bool SBQ>
-__global__ __launch_bounds__(kGemmThreads) void swiglu_kernel(SwigluArgs a, const int32_t* __restrict__ ws,
-                                                              int n_tiles) {
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(moe_waves(BITS, BM, 2))))
+void swiglu_kernel(SwigluArgs a, const int32_t* __restrict__ ws, int n_tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * kAStride];
   __shared__ int32_t pair_of[BM];
   const int pairs = a.t * a.top_k;
