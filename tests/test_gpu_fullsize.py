@@ -116,3 +116,60 @@ def test_moe_sampled(m):
         ids_o, _ = oracle.route(logits[:64], wl.top_k)
         assert np.array_equal(ids_o, ids[:64])
         del W, S, B, q
+
+
+_MOE_DEV = {}
+
+
+def _moe_device_weights(wl):
+    """Every expert of gate, up and down quantized on the GPU, as bench.py
+    holds them (drawn once per test module)."""
+    if not _MOE_DEV:
+        for pi, (name, k, n, _) in enumerate(synth.moe_projs(wl)):
+            ws, ss, bs = [], [], []
+            for e in range(wl.experts):
+                wf = torch.from_numpy(synth.draw_weight((wl.wid, e, pi, synth.STREAM_W), n, k)).cuda()
+                w_, s_, b_ = qmm.quantize(wf, wl.bits)
+                ws.append(w_); ss.append(s_); bs.append(b_)
+            _MOE_DEV[name] = (torch.stack(ws), torch.stack(ss), torch.stack(bs))
+    return _MOE_DEV
+
+
+@pytest.mark.parametrize("m", synth.QWEN3_30B_A3B_Q4_MOE.ms)
+def test_moe_ffn_block_sampled(m):
+    """The FFN block as bench.py times it (routing plan, fused gate/up with
+    SwiGLU to fp16 h, routed down from h, routing-weighted combine) on
+    sampled tokens: h over all intermediate columns of each of the token's
+    pairs, and the combined output on sampled hidden columns."""
+    wl = synth.QWEN3_30B_A3B_Q4_MOE
+    dw = _moe_device_weights(wl)
+    x, ids, logits = synth.draw_moe_inputs(wl, m, 0)
+    ids_o, wts = oracle.route(logits, wl.top_k)
+    assert np.array_equal(ids_o, ids)
+    say("full moe ffn block", m)
+    I = torch.from_numpy(ids).cuda()
+    plan = qmm.moe_route(I, wl.experts)
+    h = qmm.moe_gate_up_swiglu(dw["gate"], dw["up"], torch.from_numpy(x).cuda(), I, plan, wl.bits)
+    yd = qmm.qgemm_grouped(*dw["down"], h, I, wl.bits, True, plan=plan)
+    y = qmm.moe_combine(yd, torch.from_numpy(wts.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    hh, yh = host(h), host(y)
+    tokens = sorted({0, m - 1, int(np.random.default_rng(m).integers(1, m - 1))})
+    cols = sample_rows(wl.hidden, 32, 5 * m)
+    for t in tokens:
+        y_pairs = np.zeros((wl.top_k, cols.size))
+        for slot in range(wl.top_k):
+            p, e = t * wl.top_k + slot, int(ids[t, slot])
+            proj = {}
+            for pi, name in ((0, "gate"), (1, "up")):
+                wf = synth.draw_weight((wl.wid, e, pi, synth.STREAM_W), wl.inter, wl.hidden)
+                codes, s, b = oracle.quantize(wf, wl.bits)
+                proj[name] = oracle.qmatmul_f64(oracle.pack(codes, wl.bits), s, b, x[t][None, :], wl.bits)[0]
+            h_want = oracle.silu_f64(proj["gate"]) * proj["up"]
+            assert_close(hh[p].astype(np.float64), h_want, f"moe ffn m={m} h of pair {p}")
+            wd = synth.draw_weight((wl.wid, e, 2, synth.STREAM_W), wl.hidden, wl.inter)[cols]
+            codes, s, b = oracle.quantize(wd, wl.bits)
+            y_pairs[slot] = oracle.qmatmul_f64(oracle.pack(codes, wl.bits), s, b,
+                                               h_want.astype(np.float16)[None, :], wl.bits)[0]
+        want = oracle.moe_combine_f64(y_pairs, wts[t:t + 1].astype(np.float32))[0]
+        assert_close(yh[t, cols], want, f"moe ffn m={m} token {t}")
