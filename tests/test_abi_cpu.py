@@ -129,6 +129,32 @@ def test_other_errors(L):
     expect(L.qmm_dequant(A, A, A, A, 1, 8, 64, 7, 64, None), UNS, "bits=7")
 
 
+def check_gemv_plan_covers(buf, shapes):
+    """Block records of a GEMV plan image: pointers and row ranges tile every
+    problem (problem i has w = A * (i + 1)) exactly once, in whole passes
+    except for each problem's last block."""
+    hdr = (C.c_int32 * 16).from_buffer(buf)
+    lpr, rows, blocks, max_groups = hdr[4], hdr[5], hdr[6], hdr[7]
+    assert max_groups == max(k for _, k in shapes) // 64
+    assert all((k // 64) % lpr == 0 for _, k in shapes)
+    rec = (C.c_int64 * (8 * blocks)).from_buffer(buf, 64)
+    seen = {}
+    for bi in range(blocks):
+        r = rec[8 * bi: 8 * bi + 8]
+        n_k = r[5] & 0xFFFFFFFFFFFFFFFF
+        n, k = n_k & 0xFFFFFFFF, n_k >> 32
+        rr = r[6] & 0xFFFFFFFFFFFFFFFF
+        row0, nrows = rr & 0xFFFFFFFF, rr >> 32
+        seen.setdefault(r[0], []).append((row0, nrows, n, k))
+    assert len(seen) == len(shapes)
+    for i, (n, k) in enumerate(shapes):
+        recs = sorted(seen[A * (i + 1)])
+        assert all(x[2] == n and x[3] == k and x[1] > 0 for x in recs)
+        assert recs[0][0] == 0 and all(a[0] + a[1] == b[0] for a, b in zip(recs, recs[1:]))
+        assert recs[-1][0] + recs[-1][1] == n
+        assert all(x[1] % rows == 0 for x in recs[:-1])
+
+
 def test_batched_plan_host_only(L):
     probs = (GemvProblem * 3)()
     shapes = [(2048, 1024), (1024, 3072), (151936, 1024)]
@@ -144,22 +170,7 @@ def test_batched_plan_host_only(L):
     lpr, rows, blocks, max_groups, count = hdr[4], hdr[5], hdr[6], hdr[7], hdr[8]
     assert lpr == 16 and max_groups == 48 and count == 3 and rows == 64
     assert need.value == 64 + 64 * blocks
-    # block records: pointers and row ranges tile every problem exactly once
-    rec = (C.c_int64 * (8 * blocks)).from_buffer(buf, 64)
-    seen = {}
-    for bi in range(blocks):
-        r = rec[8 * bi: 8 * bi + 8]
-        n_k = r[5] & 0xFFFFFFFFFFFFFFFF
-        n, k = n_k & 0xFFFFFFFF, n_k >> 32
-        rr = r[6] & 0xFFFFFFFFFFFFFFFF
-        row0, nrows = rr & 0xFFFFFFFF, rr >> 32
-        seen.setdefault(r[0], []).append((row0, nrows, n, k))
-    for i, (n, k) in enumerate(shapes):
-        recs = sorted(seen[A * (i + 1)])
-        assert all(x[2] == n and x[3] == k for x in recs)
-        assert recs[0][0] == 0 and all(a[0] + a[1] == b[0] for a, b in zip(recs, recs[1:]))
-        assert recs[-1][0] + recs[-1][1] == n
-        assert all(x[1] % rows == 0 for x in recs[:-1])
+    check_gemv_plan_covers(buf, shapes)
     # corrupt header / bad problem
     bad = (C.c_uint8 * 64)()
     expect(L.qmm_qgemv_batched(A, bad, None), INV, "not a plan image")
@@ -201,15 +212,10 @@ def gemm_batch_plan(L, shapes, bits=4, env=None, gs=64):
     return hdr, recs
 
 
-@pytest.mark.parametrize("shapes", [
-    [(2048, 4096, 2560), (2048, 1024, 2560), (2048, 1024, 2560)],   # q, k, v
-    [(2048, 9728, 2560), (2048, 9728, 2560)],                         # gate, up
-    [(128, 2560, 9728)],                                              # down at M=128
-    [(128, 4096, 2560), (128, 1024, 2560), (128, 1024, 2560)],
-    [(70, 520, 1024), (1, 64, 64), (0, 128, 128), (300, 200, 192)],   # ragged, m=0, k=3 groups
-])
-def test_batched_gemm_plan_covers_every_tile(L, shapes):
-    hdr, recs = gemm_batch_plan(L, shapes)
+def check_gemm_plan_covers(hdr, recs, shapes):
+    """Every output tile of every problem is covered by S records whose k
+    ranges split [0, G) in order; split tiles have one GemmSplitTile each;
+    the workspace holds every partial tile."""
     assert hdr["magic"] == 0x424D4D51 and hdr["count"] == len(shapes)
     bm, bn, S = hdr["bm"], hdr["nb"] * 128, hdr["splits"]
     assert bm in (32, 64, 128, 256) and hdr["num_tiles"] % 8 == 0
@@ -242,6 +248,58 @@ def test_batched_gemm_plan_covers_every_tile(L, shapes):
         assert hdr["ws"] == hdr["split_tiles"] * S * bm * bn * 4
     else:
         assert hdr["ws"] == 0
+
+
+@pytest.mark.parametrize("shapes", [
+    [(2048, 4096, 2560), (2048, 1024, 2560), (2048, 1024, 2560)],   # q, k, v
+    [(2048, 9728, 2560), (2048, 9728, 2560)],                         # gate, up
+    [(128, 2560, 9728)],                                              # down at M=128
+    [(128, 4096, 2560), (128, 1024, 2560), (128, 1024, 2560)],
+    [(70, 520, 1024), (1, 64, 64), (0, 128, 128), (300, 200, 192)],   # ragged, m=0, k=3 groups
+])
+def test_batched_gemm_plan_covers_every_tile(L, shapes):
+    hdr, recs = gemm_batch_plan(L, shapes)
+    check_gemm_plan_covers(hdr, recs, shapes)
+
+
+def test_batched_plans_random(L):
+    """Seeded random problem lists (ragged and empty problems, every width
+    and group size, planner choices and forced tiles and splits): both plan
+    builders cover every output exactly once."""
+    import numpy as np
+    r = np.random.default_rng(2024)
+    cfgs = [(256, 2), (128, 2), (128, 1), (64, 2), (64, 1), (32, 2), (32, 1)]
+    for trial in range(60):
+        bits = int(r.choice([2, 3, 4, 5, 6, 8, 16]))
+        gs = 64 if bits == 16 else int(r.choice([32, 64, 128]))
+        step = max(64, gs)
+        count = int(r.integers(1, 5))
+        shapes = []
+        for _ in range(count):
+            m = int(r.choice([0, 1, int(r.integers(2, 700))]))
+            shapes.append((m, int(r.integers(1, 1500)), step * int(r.integers(1, 40))))
+        env = None
+        if trial % 2:
+            bm, nb = cfgs[int(r.integers(len(cfgs)))]
+            env = f"{bm},{nb},{int(r.choice([1, 2, 3, 4, 5, 8]))}"
+        hdr, recs = gemm_batch_plan(L, shapes, bits=bits, env=env, gs=gs)
+        assert hdr["bits"] == bits and hdr["gs"] == gs
+        check_gemm_plan_covers(hdr, recs, shapes)
+
+        vshapes = [(int(r.integers(1, 5000)), step * int(r.integers(1, 4096 // step + 1)))
+                   for _ in range(int(r.integers(1, 7)))]
+        probs = (GemvProblem * len(vshapes))()
+        for i, (n, k) in enumerate(vshapes):
+            probs[i] = GemvProblem(A * (i + 1), A, A, A, A, n, k)
+        need = C.c_size_t(0)
+        expect(L.qmm_qgemv_batched_plan(probs, len(vshapes), bits, gs, None, 0, C.byref(need)), WSP,
+               "plan buffer")
+        buf = (C.c_uint8 * need.value)()
+        assert L.qmm_qgemv_batched_plan(probs, len(vshapes), bits, gs, buf, need.value, C.byref(need)) == 0
+        hv = (C.c_int32 * 16).from_buffer(buf)
+        assert hv[2] == bits and hv[3] == gs and hv[8] == len(vshapes)
+        assert need.value == 64 + 64 * hv[6]
+        check_gemv_plan_covers(buf, vshapes)
 
 
 def test_batched_gemm_plan_group_sizes(L):
