@@ -583,6 +583,34 @@ def test_moe_gate_up_swiglu(bits, gs):
     assert_close(host(h).astype(np.float64), want, f"swiglu bits={bits} gs={gs}")
 
 
+@pytest.mark.parametrize("bits", [4, 3, 8])
+@pytest.mark.parametrize("bm,nb", [(32, 1), (32, 2), (64, 1), (64, 2), (128, 1), (128, 2), (160, 1)])
+def test_moe_forced_tiles(bits, bm, nb, monkeypatch):
+    """Every MoE row tile and column width, forced: self-bucketing and
+    routed grouped GEMMs and the fused gate/up SwiGLU on ragged shapes
+    (experts with more pairs than one row tile, columns past the last
+    full 128- or 256-wide tile)."""
+    say("moe forced tile", bits, bm, nb)
+    e, hidden, inter, t, top_k = 6, 192, 300, 150, 4   # 100 pairs per expert on average
+    r = np.random.default_rng([957, bits])
+    ids = np.ascontiguousarray(synth.topk_ids(r.standard_normal((t, e)), top_k), dtype=np.int32)
+    x = synth.draw_act((957, bits, 1), t, hidden)
+    gate, _ = _expert_set((958, bits), e, inter, hidden, bits)
+    up, _ = _expert_set((959, bits), e, inter, hidden, bits)
+    monkeypatch.setenv("QMM_MOE_FORCE", f"{bm},{nb}")
+    I = dev(ids)
+    plan = qmm.moe_route(I, e)
+    y0 = qmm.qgemm_grouped(*_to_dev(gate), dev(x), I, bits, False)
+    y1 = qmm.qgemm_grouped(*_to_dev(gate), dev(x), I, bits, False, plan=plan)
+    h = qmm.moe_gate_up_swiglu(_to_dev(gate), _to_dev(up), dev(x), I, plan, bits)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("QMM_MOE_FORCE")
+    assert_close(host(y0), oracle.grouped_f64(*gate, x, ids, bits, False), f"grouped {bm}x{nb}")
+    assert torch.equal(y0, y1), "routed differs from self-bucketing"
+    assert_close(host(h).astype(np.float64), oracle.moe_swiglu_f64(gate, up, x, ids, bits),
+                 f"swiglu {bm}x{nb}")
+
+
 def test_moe_ffn_block_chain():
     """route -> fused gate/up SwiGLU -> routed down -> weighted combine equals
     the float64 chain; the combine alone is checked on random rows too."""
