@@ -147,8 +147,9 @@ __global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
 }
 
 // Waves per SIMD the register allocator is held to: two, except for the
-// 128-row, 256-column tiles of the 5- to 16-bit formats, which would spill
-// at two and keep the whole register file at one.
+// 128-row, 256-column tiles of the 5- to 16-bit formats and the 160-row
+// fused gate/up tiles (160 accumulators per lane), which would spill at two
+// and keep the whole register file at one.
 constexpr int moe_waves(int bits, int bm, int nb) {
   return (nb == 2 && ((bm == 128 && bits >= 5) || bm == 160)) ? 1 : 2;
 }
@@ -259,8 +260,8 @@ static hipError_t launch_swiglu_bits(const SwigluArgs& a, const int32_t* plan, h
 // Row tile from the mean number of pairs per expert (one row tile per
 // expert keeps each expert's weights to a single pass over HBM).  Around a
 // mean of 128 the per-expert counts straddle 128 (100 to 159 for 2048
-// tokens, top-8 of 128 experts), so 160-row tiles take almost every expert
-// in one tile where 128-row tiles need a second, mostly empty one (194
+// tokens, top-8 of 128 experts), so 160-row tiles take every expert in one
+// tile where 128-row tiles need a second, mostly empty one (194
 // against 128 row tiles; measured 8-11 % faster for the three grouped GEMMs).
 // QMM_MOE_FORCE="bm,nb" overrides the tile (tuning sweeps).  The bucketing
 // and the grouped GEMM must agree on it, so both take it from here.
