@@ -122,7 +122,7 @@ struct TileCfg {
 };
 constexpr TileCfg kCfgs[] = {
     {256, 2, 256, 2.487, 0.300}, {128, 2, 512, 1.532, 0.321}, {128, 1, 768, 1.329, 0.234},
-    {64, 2, 512, 1.400, 0.345},  {64, 1, 1024, 1.283, 0.481}, {32, 2, 768, 1.509, 0.300},
+    {64, 2, 768, 1.400, 0.345},  {64, 1, 1024, 1.283, 0.481}, {32, 2, 768, 1.509, 0.300},
     {32, 1, 1280, 1.631, 0.300},
 };
 constexpr int kSplitChoices[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16};
