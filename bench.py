@@ -283,14 +283,20 @@ def bench_decode_extras(torch, qmm, wl, sets, steps=20, warmup=3):
 PREFILL_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 
 
+PREFILL_WEIGHTS = "tile-interleaved copy (qmm_repack_tiled, once at load)"
+
+
 def bench_prefill(torch, qmm, ms, steps=3, warmup=1, batched=True):
     wl = synth.QWEN3_4B_Q4_PREFILL
     out = {}
     base = {}
     for i, p in enumerate(wl.projs):
         wf = torch.from_numpy(synth.draw_weight((wl.wid, 0, i, synth.STREAM_W), p.n, p.k)).cuda()
-        base[i] = qmm.quantize(wf, wl.bits)
-        del wf
+        words, s_, b_ = qmm.quantize(wf, wl.bits)
+        # the batched launches read the tile-interleaved copy (repacked once,
+        # as a model would at load time); the per-projection path row-major
+        base[i] = (qmm.repack_tiled(words, wl.bits), s_, b_) if batched else (words, s_, b_)
+        del wf, words
     layers = [[tuple(t.clone() for t in base[i]) if layer else base[i]
                for i in range(len(wl.projs))] for layer in range(wl.layers)]
     torch.cuda.synchronize()
@@ -303,7 +309,7 @@ def bench_prefill(torch, qmm, ms, steps=3, warmup=1, batched=True):
             names = [p.name for p in wl.projs]
             plans = [[qmm.qgemm_batched_plan(
                 [(*L[names.index(nm)], xs[names.index(nm)], ys[names.index(nm)]) for nm in grp],
-                wl.bits) for grp in PREFILL_GROUPS] for L in layers]
+                wl.bits, tiled=True) for grp in PREFILL_GROUPS] for L in layers]
 
             def step(_):
                 for lp in plans:
@@ -502,6 +508,7 @@ def main():
     if args.only in ("prefill", "moe"):
         if args.only == "prefill":
             out = {"workload": synth.QWEN3_4B_Q4_PREFILL.name, "peak_tflops": FP16_MFMA_PEAK_TFLOPS,
+                   "weights": PREFILL_WEIGHTS,
                    "by_m": bench_prefill(torch, qmm, synth.QWEN3_4B_Q4_PREFILL.ms)}
         else:
             out = {"workload": synth.QWEN3_30B_A3B_Q4_MOE.name, "by_m": bench_moe(torch, qmm)}
@@ -567,7 +574,7 @@ def main():
         result["decode_formats"] = {"workload": wl.name + " shapes", **bench_decode_formats(torch, qmm, wl)}
         log("prefill")
         result["prefill"] = {"workload": synth.QWEN3_4B_Q4_PREFILL.name,
-                             "peak_tflops": FP16_MFMA_PEAK_TFLOPS,
+                             "peak_tflops": FP16_MFMA_PEAK_TFLOPS, "weights": PREFILL_WEIGHTS,
                              "by_m": bench_prefill(torch, qmm, synth.QWEN3_4B_Q4_PREFILL.ms)}
         torch.cuda.empty_cache()
         log("gemm formats")

@@ -160,8 +160,14 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
  * writes an fp32 partial tile there and a second, short kernel adds the
  * partials of every tile in split order, so results are identical from run
  * to run.  Calls that share a workspace must not run concurrently.
- * Problems must not write overlapping y ranges.  Errors: INVALID_ARG,
- * UNSUPPORTED, WORKSPACE, HIP. */
+ * Problems must not write overlapping y ranges.
+ * Weight layout: `bits` alone means every w is row-major [n, k*bits/32] as
+ * everywhere else; `bits | QMM_WEIGHTS_TILED` means every w was produced by
+ * qmm_repack_tiled (then every n must be a multiple of 32), which the
+ * prefill tiles read with fewer, fully contiguous loads.  Scales and biases
+ * stay row-major either way.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE,
+ * HIP. */
+#define QMM_WEIGHTS_TILED 0x100
 typedef struct {
   const uint32_t* w;
   const uint16_t* scales;
@@ -266,6 +272,19 @@ int qmm_quantize(const float* w_f32, uint32_t* words, uint16_t* scales, uint16_t
  *   equal src for an in-place conversion).
  * Errors: INVALID_ARG, HIP. */
 int qmm_convert_bf16(const uint16_t* src, uint16_t* dst, size_t count, qmm_stream stream);
+
+/* Tile-interleaved weights for the batched prefill GEMM (load time; a
+ * layout of this library's own, not from the pages): out holds the same
+ * words as the row-major w [n, k*bits/32], each 64-code group moved whole:
+ *   group g of column c: w word (c * G + g) * WPG
+ *                     -> out word ((c / 32) * G * 32 + g * 32 + c % 32) * WPG
+ *   with G = k / 64 and WPG = 2 * bits words per group (32 for bits = 16),
+ * so the 32 columns of one matrix-core column block are contiguous for each
+ * group.  n must be a multiple of 32 and k of 64; w and out are device
+ * buffers of n * k * bits / 8 bytes (16-byte aligned, not overlapping); out
+ * is used with QMM_WEIGHTS_TILED.  The decode GEMV keeps reading row-major
+ * weights.  Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int qmm_repack_tiled(const uint32_t* w, uint32_t* out, int n, int k, int bits, qmm_stream stream);
 
 /* ------------------------------------------------------------- diagnostics
  * Expose the device-side stages of the hot path for bit-exact checking.

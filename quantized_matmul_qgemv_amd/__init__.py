@@ -7,7 +7,7 @@ from ._lib import QmmError, lib, last_error  # noqa: F401
 from .api import (  # noqa: F401
     GemmBatchPlan, GemvPlan, convert_bf16, dequant, moe_combine, moe_gate_up_swiglu, moe_route, qgemm, qgemm_batched, qgemm_batched_plan,
     qgemm_grouped, qgemm_grouped_workspace_size,
-    qgemm_workspace_size, qgemv, qgemv_batched, qgemv_batched_plan, quantize,
+    qgemm_workspace_size, qgemv, qgemv_batched, qgemv_batched_plan, quantize, repack_tiled,
     unpack_codes,
 )
 
@@ -15,5 +15,5 @@ __all__ = [
     "QmmError", "lib", "last_error", "GemmBatchPlan", "GemvPlan", "dequant", "qgemm",
     "convert_bf16", "moe_combine", "moe_gate_up_swiglu", "moe_route", "qgemm_batched", "qgemm_batched_plan", "qgemm_grouped",
     "qgemm_grouped_workspace_size", "qgemm_workspace_size", "qgemv", "qgemv_batched",
-    "qgemv_batched_plan", "quantize", "unpack_codes",
+    "qgemv_batched_plan", "quantize", "repack_tiled", "unpack_codes",
 ]

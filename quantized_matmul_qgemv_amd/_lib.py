@@ -16,6 +16,7 @@ QMM_ERR_INVALID_ARG = 1
 QMM_ERR_UNSUPPORTED = 2
 QMM_ERR_WORKSPACE = 3
 QMM_ERR_HIP = 4
+QMM_WEIGHTS_TILED = 0x100  # bits flag: weights from qmm_repack_tiled
 
 STATUS_NAMES = {0: "QMM_OK", 1: "QMM_ERR_INVALID_ARG", 2: "QMM_ERR_UNSUPPORTED",
                 3: "QMM_ERR_WORKSPACE", 4: "QMM_ERR_HIP"}
@@ -59,6 +60,7 @@ SIGNATURES = {
     "qmm_moe_gate_up_swiglu": (I, [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]),
     "qmm_moe_combine": (I, [P, P, P, I, I, I, P]),
     "qmm_convert_bf16": (I, [P, P, SZ, P]),
+    "qmm_repack_tiled": (I, [P, P, I, I, I, P]),
     "qmm_quantize": (I, [P, P, P, P, I, I, I, I, P]),
     "qmm_unpack_codes": (I, [P, P, I, I, I, P]),
     "qmm_dequant": (I, [P, P, P, P, I, I, I, I, I, P]),

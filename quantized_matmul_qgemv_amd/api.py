@@ -130,23 +130,25 @@ class GemmBatchPlan:
         raw = bytes(self.host)[:48]
         f = __import__("struct").unpack("<IIiiiiiiiiii", raw)
         return {"bits": f[2], "bm": f[4], "nb": f[5], "sbq": f[6], "count": f[7],
-                "num_tiles": f[8], "split_tiles": f[9], "splits": f[10]}
+                "num_tiles": f[8], "split_tiles": f[9], "splits": f[10], "wtiled": f[11]}
 
 
-def qgemm_batched_plan(problems, bits: int, group_size: int = GROUP) -> GemmBatchPlan:
-    """Plan one launch for a list of (w, scales, biases, x, y) GEMM problems."""
+def qgemm_batched_plan(problems, bits: int, group_size: int = GROUP, tiled: bool = False) -> GemmBatchPlan:
+    """Plan one launch for a list of (w, scales, biases, x, y) GEMM problems;
+    tiled=True when every w comes from repack_tiled."""
+    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0)
     arr = (GemmProblem * len(problems))()
     for i, (w, s, b, x, y) in enumerate(problems):
         arr[i] = GemmProblem(_dev(w, "w", _W), _sb(s, "scales", bits), _sb(b, "biases", bits),
                              _dev(x, "x", _X), _dev(y, "y", _Y), x.shape[0], w.shape[0],
                              x.shape[1])
     need, ws = C.c_size_t(0), C.c_size_t(0)
-    st = lib().qmm_qgemm_batched_plan(arr, len(problems), bits, group_size, None, 0,
+    st = lib().qmm_qgemm_batched_plan(arr, len(problems), flag_bits, group_size, None, 0,
                                       C.byref(need), C.byref(ws))
     if st not in (_lib.QMM_OK, _lib.QMM_ERR_WORKSPACE):
         check(st)
     host = (C.c_uint8 * need.value)()
-    check(lib().qmm_qgemm_batched_plan(arr, len(problems), bits, group_size, host, need.value,
+    check(lib().qmm_qgemm_batched_plan(arr, len(problems), flag_bits, group_size, host, need.value,
                                        C.byref(need), C.byref(ws)))
     dev_ = problems[0][0].device
     device = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(dev_)
@@ -243,6 +245,17 @@ def convert_bf16(w_bf16, out=None, stream=None):
     if out is None:
         out = torch.empty(src.shape[:-1] + (src.shape[-1] // 2,), dtype=torch.int32, device=src.device)
     check(lib().qmm_convert_bf16(_dev(src, "w_bf16", _SB), out.data_ptr(), src.numel(), _stream(stream)))
+    return out
+
+
+def repack_tiled(w, bits: int, out=None, stream=None):
+    """Tile-interleaved copy of packed weights w [n, k*bits/32] (int32) for
+    the batched prefill GEMM with tiled=True, via qmm_repack_tiled."""
+    n = w.shape[0]
+    k = w.shape[1] * 32 // bits
+    if out is None:
+        out = torch.empty_like(w)
+    check(lib().qmm_repack_tiled(_dev(w, "w", _W), _dev(out, "out", _W), n, k, bits, _stream(stream)))
     return out
 
 

@@ -76,11 +76,21 @@ __device__ __forceinline__ int sb_index(int g, int h, int gs) {
   return gs == 64 ? g : gs == 32 ? 2 * g + h : (g >> 1);
 }
 
+// Weight layouts.  Row-major (wtiled = 0): column c's groups follow each
+// other, group g of column c at word (c * G + g) * WPG.  Tile-interleaved
+// (wtiled = 1, qmm_repack_tiled): for each block of 32 columns and each
+// group, the 32 columns' groups are contiguous, group g of column c at
+// word ((c / 32) * G * 32 + g * 32 + c % 32) * WPG, so the 32 columns of a
+// wave's weight load are one contiguous run of 32 * WPG words.
+__device__ __forceinline__ size_t weight_column_offset(int col, int groups, int wpg, int wtiled) {
+  return wtiled ? ((size_t)(col >> 5) * groups * 32 + (col & 31)) * wpg : (size_t)col * groups * wpg;
+}
+
 template <int BITS, bool WITH_SB = true>
 __device__ __forceinline__ void load_braw(BRaw<BITS>& r, gptr<uint32_t> wcol, gptr<uint16_t> scol,
-                                          gptr<uint16_t> bcol, int g, int h, int gs) {
+                                          gptr<uint16_t> bcol, int g, int h, int gs, int gstride) {
   constexpr int WPG = Fmt<BITS>::WORDS_PER_GROUP;
-  gptr<uint32_t> p = wcol + (size_t)g * WPG + h * (WPG / 2);
+  gptr<uint32_t> p = wcol + (size_t)g * gstride + h * (WPG / 2);
   if constexpr (BITS == 6) {
     // half a 48-byte group: 8-byte aligned
 #pragma unroll
@@ -198,12 +208,14 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
                                           const uint32_t* __restrict__ w2_ = nullptr,
                                           const uint16_t* __restrict__ s2_ = nullptr,
                                           const uint16_t* __restrict__ b2_ = nullptr,
-                                          uint16_t* __restrict__ h_tile = nullptr) {
+                                          uint16_t* __restrict__ h_tile = nullptr,
+                                          int wtiled = 0) {
   static_assert(!SWIGLU || NB == 2, "SwiGLU pairs a gate and an up column block");
   constexpr int MB = BM / 32;
   constexpr int SPANS = BM * 4;  // 16-wide spans of A per step
   constexpr int SPT = (SPANS + kGemmThreads - 1) / kGemmThreads;
   constexpr int WPG = Fmt<BITS>::WORDS_PER_GROUP;
+  const int gstride = wtiled ? 32 * WPG : WPG;  // words from one group of a column to the next
   const gptr<uint32_t> w = to_global(w_);
   const gptr<uint16_t> s = to_global(s_);
   const gptr<uint16_t> b = to_global(b_);
@@ -225,7 +237,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
     int col = SWIGLU ? n0 + wave * 32 + l32 : n0 + (wave * NB + nb) * 32 + l32;
     col = col < n ? col : n - 1;
     const bool second = SWIGLU && nb == 1;
-    wcol[nb] = (second ? to_global(w2_) : w) + (size_t)col * groups * WPG;
+    wcol[nb] = (second ? to_global(w2_) : w) + weight_column_offset(col, groups, WPG, wtiled);
     scol[nb] = (second ? to_global(s2_) : s) + (size_t)col * sgroups;
     bcol[nb] = (second ? to_global(b2_) : b) + (size_t)col * sgroups;
   }
@@ -290,7 +302,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   auto load_b = [&](BRaw<BITS> (&dst)[NB], int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      load_braw<BITS, !SBQ && !Fmt<BITS>::F16W>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs);
+      load_braw<BITS, !SBQ && !Fmt<BITS>::F16W>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs, gstride);
   };
   // SBQ: scales and biases of four consecutive groups come in one 8-byte
   // load per column (a 2-byte load touches as many cache lines as a wide

@@ -33,13 +33,15 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
                                                const uint16_t* __restrict__ s_,
                                                const uint16_t* __restrict__ b_,
                                                float* __restrict__ y_tile, int ldy, int n0, int n,
-                                               int g_begin, int g_end, uint16_t* lds, int gs = 64) {
+                                               int g_begin, int g_end, uint16_t* lds, int gs = 64,
+                                               int wtiled = 0) {
   constexpr int BM = kWideBM;
   constexpr int MB = BM / 32;
   constexpr int NB = 2;
   constexpr int SPT = BM * 4 / kGemmThreads;  // 16-wide spans of A per thread per step
   constexpr int WPG = Fmt<BITS>::WORDS_PER_GROUP;
   constexpr int SLOT = BM * kAStride;
+  const int gstride = wtiled ? 32 * WPG : WPG;
   const gptr<uint32_t> w = to_global(w_);
   const gptr<uint16_t> s = to_global(s_);
   const gptr<uint16_t> b = to_global(b_);
@@ -60,7 +62,7 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
   for (int nb = 0; nb < NB; ++nb) {
     int col = n0 + (wave * NB + nb) * 32 + l32;
     col = col < n ? col : n - 1;
-    wcol[nb] = w + (size_t)col * groups * WPG;
+    wcol[nb] = w + weight_column_offset(col, groups, WPG, wtiled);
     scol[nb] = s + (size_t)col * sgroups;
     bcol[nb] = b + (size_t)col * sgroups;
   }
@@ -115,7 +117,7 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
   auto load_b = [&](BRaw<BITS> (&dst)[NB], int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      load_braw<BITS, !SBQ && !Fmt<BITS>::F16W>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs);
+      load_braw<BITS, !SBQ && !Fmt<BITS>::F16W>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs, gstride);
   };
   auto load_sbq = [&](u32x2 (&sq)[NB], u32x2 (&bq)[NB], int g4) {
 #pragma unroll

@@ -236,6 +236,8 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
                            size_t* plan_bytes_needed, size_t* workspace_bytes_needed) {
   const char* fn = "qmm_qgemm_batched_plan";
   clear_error();
+  const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
+  bits &= ~QMM_WEIGHTS_TILED;
   if (int st = check_format(fn, bits, group_size, true)) return st;
   if (count < 1) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d must be >= 1", fn, count);
   if (count > (1 << 20)) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d too large", fn, count);
@@ -247,14 +249,16 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
     const qmm_gemm_problem& q = problems[i];
     int bad = 0;
     // an empty problem (m = 0) is never read or written: x and y may be null
-    if (q.m < 0 || check_nk(fn, q.n, q.k, group_size)) bad = 1;
+    if (q.m < 0 || check_nk(fn, q.n, q.k, group_size) || (wtiled && q.n % 32 != 0)) bad = 1;
     else if (!q.w || (bits != 16 && (!q.scales || !q.biases)) || (q.m > 0 && (!q.x || !q.y))) bad = 2;
     else if (!aligned(q.w, 16) || !aligned(q.x, 16) || !aligned(q.y, 4) ||
              !aligned(q.scales, 2) || !aligned(q.biases, 2)) bad = 3;
     if (bad) {
       free(probs);
       return fail(QMM_ERR_INVALID_ARG, "%s: problem %d: %s", fn, i,
-                  bad == 1 ? "bad m, n or k" : bad == 2 ? "null pointer" : "misaligned pointer");
+                  bad == 1 ? (wtiled ? "bad m, n or k (tile-interleaved weights need n % 32 == 0)"
+                                     : "bad m, n or k")
+                           : bad == 2 ? "null pointer" : "misaligned pointer");
     }
     probs[i].w = q.w;
     probs[i].s = q.scales;
@@ -265,7 +269,7 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
     probs[i].n = q.n;
     probs[i].k = q.k;
   }
-  const size_t need = qmm::gemm_batch_build(probs, count, bits, group_size, nullptr, 0);
+  const size_t need = qmm::gemm_batch_build(probs, count, bits, group_size, wtiled, nullptr, 0);
   if (plan_bytes_needed) *plan_bytes_needed = need;
   if (plan == nullptr || plan_bytes < need) {
     free(probs);
@@ -275,7 +279,7 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
     free(probs);
     return fail(QMM_ERR_INVALID_ARG, "%s: plan is not 8-byte aligned", fn);
   }
-  qmm::gemm_batch_build(probs, count, bits, group_size, plan, plan_bytes);
+  qmm::gemm_batch_build(probs, count, bits, group_size, wtiled, plan, plan_bytes);
   free(probs);
   qmm::GemmBatchHeader hdr;
   memcpy(&hdr, plan, sizeof hdr);
@@ -294,7 +298,7 @@ int qmm_qgemm_batched(const void* plan_device, const void* plan_host, void* work
   if (hdr.magic != qmm::kBatchMagic || hdr.version != qmm::kBatchVersion)
     return fail(QMM_ERR_INVALID_ARG, "%s: plan_host is not a batched-GEMM plan image", fn);
   if (int st = check_format(fn, hdr.bits, hdr.group_size, true)) return st;
-  if (hdr.count < 1 || hdr.num_tiles < 0 || hdr.splits < 1 ||
+  if (hdr.count < 1 || hdr.num_tiles < 0 || hdr.splits < 1 || (hdr.wtiled != 0 && hdr.wtiled != 1) ||
       !(hdr.bm == 32 || hdr.bm == 64 || hdr.bm == 128 || hdr.bm == 256) ||
       !(hdr.nb == 1 || hdr.nb == 2) || (hdr.bm == 256 && hdr.nb != 2))
     return fail(QMM_ERR_INVALID_ARG, "%s: corrupt plan header", fn);
@@ -468,6 +472,20 @@ int qmm_convert_bf16(const uint16_t* src, uint16_t* dst, size_t count, qmm_strea
   CHECK_PTR(src, 4);
   CHECK_PTR(dst, 4);
   return hip_status(qmm::launch_convert_bf16(src, dst, (long)count, (hipStream_t)stream), fn);
+}
+
+int qmm_repack_tiled(const uint32_t* w, uint32_t* out, int n, int k, int bits, qmm_stream stream) {
+  const char* fn = "qmm_repack_tiled";
+  clear_error();
+  if (int st = check_format(fn, bits, 64, true)) return st;
+  if (int st = check_nk(fn, n, k)) return st;
+  if (n % 32 != 0) return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32", fn, n);
+  CHECK_PTR(w, 16);
+  CHECK_PTR(out, 16);
+  const size_t bytes = (size_t)n * (size_t)(k / 64) * (size_t)bits * 8;
+  const uintptr_t a = (uintptr_t)w, b = (uintptr_t)out;
+  if (a < b + bytes && b < a + bytes) return fail(QMM_ERR_INVALID_ARG, "%s: w and out overlap", fn);
+  return hip_status(qmm::launch_repack_tiled(w, out, n, k, bits, (hipStream_t)stream), fn);
 }
 
 int qmm_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,

@@ -118,7 +118,7 @@ struct alignas(64) GemmBatchHeader {
   int32_t num_tiles;     // tile records (grid size)
   int32_t split_tiles;   // tiles whose k is split (GemmSplitTile records after the tiles)
   int32_t splits;
-  int32_t pad0;
+  int32_t wtiled;        // weights in the tile-interleaved layout (qmm_repack_tiled)
   uint64_t workspace_bytes;
   uint64_t pad1;
 };
@@ -133,7 +133,7 @@ void gemm_choose(int m, int n, int k, int bits, int* bm, int* nb, int* splits);
 // Choose the tile and split count for a batch and write the plan image.
 // Returns the image size; writes nothing when out is null or too small.
 size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, int group_size,
-                        void* out, size_t out_bytes);
+                        int wtiled, void* out, size_t out_bytes);
 hipError_t launch_qgemm_batched(const void* plan_device, const GemmBatchHeader& hdr,
                                 void* workspace, hipStream_t st);
 
@@ -162,6 +162,7 @@ hipError_t launch_moe_combine(const float* y_pairs, const float* weights, float*
 hipError_t launch_quantize(const float* w, uint32_t* words, uint16_t* s, uint16_t* b, int n,
                            int k, int bits, int group_size, hipStream_t st);
 hipError_t launch_convert_bf16(const uint16_t* src, uint16_t* dst, long count, hipStream_t st);
+hipError_t launch_repack_tiled(const uint32_t* w, uint32_t* out, int n, int k, int bits, hipStream_t st);
 hipError_t launch_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,
                                hipStream_t st);
 hipError_t launch_dequant(const uint32_t* w, const uint16_t* s, const uint16_t* b, void* out,

@@ -226,6 +226,31 @@ hipError_t launch_convert_bf16(const uint16_t* src, uint16_t* dst, long count, h
   return hipGetLastError();
 }
 
+// Tile-interleaved copy of packed weights (one thread per word): group g
+// of column c moves from word (c * G + g) * WPG to
+// ((c / 32) * G * 32 + g * 32 + c % 32) * WPG.  The GEMM tile core then
+// reads the 32 columns of a wave's weight load as one contiguous run.
+__global__ __launch_bounds__(256) void repack_tiled_kernel(const uint32_t* __restrict__ src,
+                                                           uint32_t* __restrict__ dst, long words,
+                                                           int groups, int wpg) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= words) return;
+  const long per_col = (long)groups * wpg;
+  const long col = i / per_col;
+  const long rem = i - col * per_col;
+  const long g = rem / wpg;
+  const long e = rem - g * wpg;
+  dst[(((col >> 5) * groups + g) * 32 + (col & 31)) * wpg + e] = src[i];
+}
+
+hipError_t launch_repack_tiled(const uint32_t* w, uint32_t* out, int n, int k, int bits, hipStream_t st) {
+  const int wpg = bits * 2;  // words per 64-code group (fp16 weights: 32)
+  const long words = (long)n * (k / 64) * wpg;
+  hipLaunchKernelGGL(repack_tiled_kernel, dim3(blocks_for(words)), dim3(256), 0, st, w, out, words,
+                     k / 64, wpg);
+  return hipGetLastError();
+}
+
 template <int GS>
 static hipError_t launch_quantize_gs(const float* w, uint32_t* words, uint16_t* s, uint16_t* b,
                                      int n, int k, int bits, hipStream_t st) {

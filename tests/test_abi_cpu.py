@@ -203,7 +203,7 @@ def gemm_batch_plan(L, shapes, bits=4, env=None, gs=64):
     raw = bytes(buf)
     f = struct.unpack_from("<IIiiiiiiiiiiQ", raw, 0)
     hdr = dict(zip(["magic", "version", "bits", "gs", "bm", "nb", "sbq", "count", "num_tiles",
-                    "split_tiles", "splits", "pad", "ws"], f))
+                    "split_tiles", "splits", "wtiled", "ws"], f))
     off = 64 + 64 * len(shapes)
     recs = [struct.unpack_from("<8i", raw, off + 32 * i) for i in range(hdr["num_tiles"])]
     off2 = off + 32 * hdr["num_tiles"]
@@ -300,6 +300,29 @@ def test_batched_plans_random(L):
         assert hv[2] == bits and hv[3] == gs and hv[8] == len(vshapes)
         assert need.value == 64 + 64 * hv[6]
         check_gemv_plan_covers(buf, vshapes)
+
+
+def test_repack_tiled_errors_and_plan_flag(L):
+    """qmm_repack_tiled checks shapes, width and overlap on the host; a
+    batched plan with QMM_WEIGHTS_TILED records the flag and needs n % 32 == 0."""
+    B = A + (1 << 24)
+    expect(L.qmm_repack_tiled(A, B, 48, 128, 4, None), INV, "multiple of 32")
+    expect(L.qmm_repack_tiled(A, B, 64, 100, 4, None), INV, "k=100")
+    expect(L.qmm_repack_tiled(A, B, 64, 128, 7, None), UNS, "bits=7")
+    expect(L.qmm_repack_tiled(None, B, 64, 128, 4, None), INV, "null pointer")
+    expect(L.qmm_repack_tiled(A, MIS, 64, 128, 4, None), INV, "aligned")
+    expect(L.qmm_repack_tiled(A, A + 64, 64, 128, 4, None), INV, "overlap")
+    tiled = _lib.QMM_WEIGHTS_TILED
+    hdr, recs = gemm_batch_plan(L, [(70, 512, 1024), (300, 224, 768)], bits=4 | tiled)
+    assert hdr["bits"] == 4 and hdr["wtiled"] == 1
+    check_gemm_plan_covers(hdr, recs, [(70, 512, 1024), (300, 224, 768)])
+    hdr, _ = gemm_batch_plan(L, [(70, 512, 1024)], bits=4)
+    assert hdr["wtiled"] == 0
+    probs = (GemmProblem * 1)()
+    probs[0] = GemmProblem(A, A, A, A, A, 64, 200, 128)
+    need, ws = C.c_size_t(0), C.c_size_t(0)
+    expect(L.qmm_qgemm_batched_plan(probs, 1, 4 | tiled, 64, None, 0, C.byref(need), C.byref(ws)), INV,
+           "n % 32")
 
 
 def test_batched_gemm_plan_group_sizes(L):

@@ -74,7 +74,18 @@ def test_prefill_layer_sampled(m):
         plan = qmm.qgemm_batched_plan(
             [(*dev_w[names.index(nm)], xd[names.index(nm)], ys[names.index(nm)]) for nm in grp], wl.bits)
         qmm.qgemm_batched(plan)
+    # as bench.py runs it: tile-interleaved weights, bit-identical outputs
+    yt = [torch.full_like(y, float("nan")) for y in ys]
+    wt = [qmm.repack_tiled(w[0], wl.bits) for w in dev_w]
+    for grp in bench.PREFILL_GROUPS:
+        say("full prefill batched tiled", m, "+".join(grp))
+        idx = [names.index(nm) for nm in grp]
+        plan = qmm.qgemm_batched_plan([(wt[i], dev_w[i][1], dev_w[i][2], xd[i], yt[i]) for i in idx],
+                                      wl.bits, tiled=True)
+        qmm.qgemm_batched(plan)
     torch.cuda.synchronize()
+    for i, p in enumerate(wl.projs):
+        assert torch.equal(yt[i], ys[i]), f"prefill m={m} {p.name}: tiled weights differ"
     for i, p in enumerate(wl.projs):
         say("full prefill single", m, p.name)
         y1 = qmm.qgemm(*dev_w[i], xd[i], wl.bits)
