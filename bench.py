@@ -345,7 +345,9 @@ def bench_moe(torch, qmm, steps=10, warmup=2):
             wf = torch.from_numpy(synth.draw_weight((wl.wid, e, pi, synth.STREAM_W), n, k)).cuda()
             w_, s_, b_ = qmm.quantize(wf, wl.bits)
             ws.append(w_); ss.append(s_); bs.append(b_)
-        weights.append((torch.stack(ws), torch.stack(ss), torch.stack(bs), n, k, per_pair))
+        # tile-interleaved copy of the stacked expert words (once, at load)
+        weights.append((qmm.repack_tiled(torch.stack(ws), wl.bits), torch.stack(ss), torch.stack(bs),
+                        n, k, per_pair))
         del ws, ss, bs
     stream = torch.cuda.current_stream()
     for m in wl.ms:
@@ -373,11 +375,11 @@ def bench_moe(torch, qmm, steps=10, warmup=2):
         def step(_):
             qmm.moe_route(ids0, wl.experts, plan=plan)
             for (W, S, B, A, I, per_pair, Y, WS) in calls:
-                qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, plan=plan)
+                qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, plan=plan, tiled=True)
 
         def step_unshared(_):
             for (W, S, B, A, I, per_pair, Y, WS) in calls:
-                qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, workspace=WS)
+                qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, workspace=WS, tiled=True)
         ms_step, _ = time_launches(torch, step, steps, warmup, stream)
         ms_unshared, _ = time_launches(torch, step_unshared, steps, warmup, stream)
         t = ms_step * 1e-3
@@ -400,8 +402,8 @@ def bench_moe(torch, qmm, steps=10, warmup=2):
 
         def block(_):
             qmm.moe_route(ids0, wl.experts, plan=plan)
-            qmm.moe_gate_up_swiglu((Wg, Sg, Bg), (Wu, Su, Bu), X, ids0, plan, wl.bits, h=H)
-            qmm.qgemm_grouped(Wd, Sd, Bd, H, ids0, wl.bits, True, y=Yd, plan=plan)
+            qmm.moe_gate_up_swiglu((Wg, Sg, Bg), (Wu, Su, Bu), X, ids0, plan, wl.bits, h=H, tiled=True)
+            qmm.qgemm_grouped(Wd, Sd, Bd, H, ids0, wl.bits, True, y=Yd, plan=plan, tiled=True)
             qmm.moe_combine(Yd, Wts, y=Yout)
         ms_block, _ = time_launches(torch, block, steps, warmup, stream)
         used = np.unique(calls[0][4].cpu().numpy()).size
@@ -511,7 +513,8 @@ def main():
                    "weights": PREFILL_WEIGHTS,
                    "by_m": bench_prefill(torch, qmm, synth.QWEN3_4B_Q4_PREFILL.ms)}
         else:
-            out = {"workload": synth.QWEN3_30B_A3B_Q4_MOE.name, "by_m": bench_moe(torch, qmm)}
+            out = {"workload": synth.QWEN3_30B_A3B_Q4_MOE.name, "weights": PREFILL_WEIGHTS,
+                   "by_m": bench_moe(torch, qmm)}
         print(json.dumps(out), flush=True)
         return
 
@@ -580,7 +583,8 @@ def main():
         log("gemm formats")
         result["gemm_formats"] = {"shape": [2048, 9728, 2560], **bench_gemm_formats(torch, qmm)}
         log("moe")
-        result["moe"] = {"workload": synth.QWEN3_30B_A3B_Q4_MOE.name, "by_m": bench_moe(torch, qmm)}
+        result["moe"] = {"workload": synth.QWEN3_30B_A3B_Q4_MOE.name, "weights": PREFILL_WEIGHTS,
+                         "by_m": bench_moe(torch, qmm)}
     if not args.no_cpu:
         log("cpu baseline")
         result["cpu_baseline"] = cpu_baseline(wl)

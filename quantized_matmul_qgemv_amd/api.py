@@ -168,10 +168,13 @@ def qgemm_grouped_workspace_size(t, top_k, e, n, k, bits, group_size=GROUP) -> i
 
 
 def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: bool,
-                  y=None, group_size: int = GROUP, workspace=None, stream=None, plan=None):
+                  y=None, group_size: int = GROUP, workspace=None, stream=None, plan=None,
+                  tiled: bool = False):
     """Grouped MoE product via qmm_qgemm_grouped; returns y [T*top_k, n].
     With `plan` (from moe_route on the same expert_ids) it calls
-    qmm_qgemm_grouped_routed and skips the bucketing."""
+    qmm_qgemm_grouped_routed and skips the bucketing.  tiled=True when w
+    comes from repack_tiled (of the stacked [E*n, ...] words)."""
+    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0)
     e, n = w.shape[0], w.shape[1]
     t, top_k = expert_ids.shape
     k = a.shape[1]
@@ -181,7 +184,7 @@ def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: b
         check(lib().qmm_qgemm_grouped_routed(_dev(w, "w", _W), _sb(scales, "scales", bits),
                                              _sb(biases, "biases", bits), _dev(a, "a", _X),
                                              int(bool(a_row_per_pair)), plan.data_ptr(), _dev(y, "y", _Y),
-                                             t, top_k, e, n, k, bits, group_size, _stream(stream)))
+                                             t, top_k, e, n, k, flag_bits, group_size, _stream(stream)))
         return y
     ws_bytes = qgemm_grouped_workspace_size(t, top_k, e, n, k, bits, group_size)
     if workspace is None:
@@ -189,7 +192,7 @@ def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: b
     check(lib().qmm_qgemm_grouped(_dev(w, "w", _W), _sb(scales, "scales", bits),
                                   _sb(biases, "biases", bits), _dev(a, "a", _X),
                                   int(bool(a_row_per_pair)), _dev(expert_ids, "expert_ids", (torch.int32,)),
-                                  _dev(y, "y", _Y), t, top_k, e, n, k, bits, group_size,
+                                  _dev(y, "y", _Y), t, top_k, e, n, k, flag_bits, group_size,
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   _stream(stream)))
     return y
@@ -208,9 +211,11 @@ def moe_route(expert_ids, e: int, plan=None, stream=None):
 
 
 def moe_gate_up_swiglu(gate, up, x, expert_ids, plan, bits: int, h=None, group_size: int = GROUP,
-                       stream=None):
+                       stream=None, tiled: bool = False):
     """h [T*top_k, n] fp16 = silu(x W_gate^T) * (x W_up^T) per pair, via
-    qmm_moe_gate_up_swiglu; gate and up are (words, scales, biases)."""
+    qmm_moe_gate_up_swiglu; gate and up are (words, scales, biases), both
+    from repack_tiled when tiled=True."""
+    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0)
     wg, sg, bg = gate
     wu, su, bu = up
     e, n = wg.shape[0], wg.shape[1]
@@ -221,7 +226,7 @@ def moe_gate_up_swiglu(gate, up, x, expert_ids, plan, bits: int, h=None, group_s
     check(lib().qmm_moe_gate_up_swiglu(_dev(wg, "w_gate", _W), _sb(sg, "s_gate", bits), _sb(bg, "b_gate", bits),
                                        _dev(wu, "w_up", _W), _sb(su, "s_up", bits), _sb(bu, "b_up", bits),
                                        _dev(x, "x", _X), plan.data_ptr(), _dev(h, "h", _X),
-                                       t, top_k, e, n, k, bits, group_size, _stream(stream)))
+                                       t, top_k, e, n, k, flag_bits, group_size, _stream(stream)))
     return h
 
 
@@ -251,8 +256,8 @@ def convert_bf16(w_bf16, out=None, stream=None):
 def repack_tiled(w, bits: int, out=None, stream=None):
     """Tile-interleaved copy of packed weights w [n, k*bits/32] (int32) for
     the batched prefill GEMM with tiled=True, via qmm_repack_tiled."""
-    n = w.shape[0]
-    k = w.shape[1] * 32 // bits
+    n = w.numel() // w.shape[-1]  # stacked experts [E, n, words] repack as one [E*n, words]
+    k = w.shape[-1] * 32 // bits
     if out is None:
         out = torch.empty_like(w)
     check(lib().qmm_repack_tiled(_dev(w, "w", _W), _dev(out, "out", _W), n, k, bits, _stream(stream)))

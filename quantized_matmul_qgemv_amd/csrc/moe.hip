@@ -182,7 +182,8 @@ void grouped_kernel(GroupedArgs a, const int32_t* __restrict__ ws, int n_tiles) 
   const size_t sstride = (size_t)a.n * (a.k / a.group_size);
   gemm_tile<BITS, BM, NB, SBQ>(ARows{a.a, a.k}, a_row, c_row, a.w + mt.expert * wstride,
                                a.s + mt.expert * sstride, a.b + mt.expert * sstride, a.y + tn * BN,
-                               a.n, tn * BN, a.n, 0, groups, lds, a.group_size);
+                               a.n, tn * BN, a.n, 0, groups, lds, a.group_size, nullptr, nullptr, nullptr,
+                               nullptr, a.wtiled);
 }
 
 // Fused gate + up with the SwiGLU epilogue: one workgroup computes, for
@@ -201,6 +202,7 @@ struct SwigluArgs {
   const uint16_t* x;
   uint16_t* h;
   int t, top_k, e, n, k, group_size;
+  int wtiled;  // weights in the tile-interleaved layout (qmm_repack_tiled)
 };
 
 template <int BITS, int BM, bool SBQ>
@@ -230,7 +232,7 @@ void swiglu_kernel(SwigluArgs a, const int32_t* __restrict__ ws, int n_tiles) {
                                     a.sg + eo * sstride, a.bg + eo * sstride, nullptr, a.n,
                                     tn * 128, a.n, 0, groups, lds, a.group_size,
                                     a.wu + eo * wstride, a.su + eo * sstride, a.bu + eo * sstride,
-                                    a.h + tn * 128);
+                                    a.h + tn * 128, a.wtiled);
 }
 
 template <int BITS, bool SBQ>
@@ -348,8 +350,8 @@ hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, bool b
 hipError_t launch_moe_swiglu(const uint32_t* wg, const uint16_t* sg, const uint16_t* bg,
                              const uint32_t* wu, const uint16_t* su, const uint16_t* bu,
                              const uint16_t* x, const void* plan, uint16_t* h, int t, int top_k,
-                             int e, int n, int k, int bits, int group_size, hipStream_t st) {
-  const SwigluArgs a{wg, sg, bg, wu, su, bu, x, h, t, top_k, e, n, k, group_size};
+                             int e, int n, int k, int bits, int group_size, int wtiled, hipStream_t st) {
+  const SwigluArgs a{wg, sg, bg, wu, su, bu, x, h, t, top_k, e, n, k, group_size, wtiled};
   const int32_t* p = static_cast<const int32_t*>(plan);
   switch (bits) {
     case 2: return launch_swiglu_bits<2>(a, p, st);

@@ -326,6 +326,8 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
                       qmm_stream stream) {
   const char* fn = "qmm_qgemm_grouped";
   clear_error();
+  const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
+  bits &= ~QMM_WEIGHTS_TILED;
   if (int st = check_format(fn, bits, group_size, true)) return st;
   if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
   if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
@@ -334,6 +336,8 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
   if (a_row_per_pair != 0 && a_row_per_pair != 1)
     return fail(QMM_ERR_INVALID_ARG, "%s: a_row_per_pair must be 0 or 1", fn);
   if (int st = check_nk(fn, n, k, group_size)) return st;
+  if (wtiled && n % 32 != 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32 for tile-interleaved weights", fn, n);
   if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
   if (t == 0) return QMM_OK;
   CHECK_PTR(w, 16);
@@ -348,7 +352,7 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
   if (workspace == nullptr || workspace_bytes < need)
     return fail(QMM_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
   CHECK_PTR(workspace, 16);
-  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, expert_ids, y, t, top_k, e, n, k, group_size};
+  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, expert_ids, y, t, top_k, e, n, k, group_size, wtiled};
   return hip_status(qmm::launch_qgemm_grouped(ga, bits, workspace, true, (hipStream_t)stream), fn);
 }
 
@@ -382,6 +386,8 @@ int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const ui
                              qmm_stream stream) {
   const char* fn = "qmm_qgemm_grouped_routed";
   clear_error();
+  const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
+  bits &= ~QMM_WEIGHTS_TILED;
   if (int st = check_format(fn, bits, group_size, true)) return st;
   if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
   if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
@@ -390,6 +396,8 @@ int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const ui
   if (a_row_per_pair != 0 && a_row_per_pair != 1)
     return fail(QMM_ERR_INVALID_ARG, "%s: a_row_per_pair must be 0 or 1", fn);
   if (int st = check_nk(fn, n, k, group_size)) return st;
+  if (wtiled && n % 32 != 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32 for tile-interleaved weights", fn, n);
   if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
   if (t == 0) return QMM_OK;
   CHECK_PTR(w, 16);
@@ -400,7 +408,7 @@ int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const ui
   CHECK_PTR(a, 16);
   CHECK_PTR(plan, 16);
   CHECK_PTR(y, 4);
-  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, nullptr, y, t, top_k, e, n, k, group_size};
+  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, nullptr, y, t, top_k, e, n, k, group_size, wtiled};
   return hip_status(qmm::launch_qgemm_grouped(ga, bits, const_cast<void*>(plan), false,
                                               (hipStream_t)stream), fn);
 }
@@ -411,12 +419,16 @@ int qmm_moe_gate_up_swiglu(const uint32_t* w_gate, const uint16_t* s_gate, const
                            int e, int n, int k, int bits, int group_size, qmm_stream stream) {
   const char* fn = "qmm_moe_gate_up_swiglu";
   clear_error();
+  const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
+  bits &= ~QMM_WEIGHTS_TILED;
   if (int st = check_format(fn, bits, group_size, true)) return st;
   if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
   if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
   if (e < 1 || e > kMaxExperts)
     return fail(QMM_ERR_INVALID_ARG, "%s: e=%d must be in [1, %d]", fn, e, kMaxExperts);
   if (int st = check_nk(fn, n, k, group_size)) return st;
+  if (wtiled && n % 32 != 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32 for tile-interleaved weights", fn, n);
   if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
   if (t == 0) return QMM_OK;
   CHECK_PTR(w_gate, 16);
@@ -431,7 +443,7 @@ int qmm_moe_gate_up_swiglu(const uint32_t* w_gate, const uint16_t* s_gate, const
   CHECK_PTR(plan, 16);
   CHECK_PTR(h, 2);
   return hip_status(qmm::launch_moe_swiglu(w_gate, s_gate, b_gate, w_up, s_up, b_up, x, plan, h, t,
-                                           top_k, e, n, k, bits, group_size, (hipStream_t)stream),
+                                           top_k, e, n, k, bits, group_size, wtiled, (hipStream_t)stream),
                     fn);
 }
 

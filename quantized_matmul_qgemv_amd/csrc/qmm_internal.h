@@ -147,6 +147,7 @@ struct GroupedArgs {
   float* y;
   int t, top_k, e, n, k;
   int group_size;
+  int wtiled;  // weights in the tile-interleaved layout (qmm_repack_tiled)
 };
 size_t grouped_workspace_bytes(int t, int top_k, int e, int n);
 // bucket = false: ws already holds a routing plan for these ids (launch_moe_route).
@@ -155,7 +156,7 @@ hipError_t launch_moe_route(const int32_t* ids, int t, int top_k, int e, void* p
 hipError_t launch_moe_swiglu(const uint32_t* wg, const uint16_t* sg, const uint16_t* bg,
                              const uint32_t* wu, const uint16_t* su, const uint16_t* bu,
                              const uint16_t* x, const void* plan, uint16_t* h, int t, int top_k,
-                             int e, int n, int k, int bits, int group_size, hipStream_t st);
+                             int e, int n, int k, int bits, int group_size, int wtiled, hipStream_t st);
 hipError_t launch_moe_combine(const float* y_pairs, const float* weights, float* y, int t, int top_k,
                               int n, hipStream_t st);
 

@@ -163,7 +163,14 @@ def test_moe_ffn_block_sampled(m):
     h = qmm.moe_gate_up_swiglu(dw["gate"], dw["up"], torch.from_numpy(x).cuda(), I, plan, wl.bits)
     yd = qmm.qgemm_grouped(*dw["down"], h, I, wl.bits, True, plan=plan)
     y = qmm.moe_combine(yd, torch.from_numpy(wts.astype(np.float32)).cuda())
+    # as bench.py runs it: tile-interleaved expert weights, bit-identical
+    tw = {nm: (qmm.repack_tiled(dw[nm][0], wl.bits), dw[nm][1], dw[nm][2]) for nm in dw}
+    h_t = qmm.moe_gate_up_swiglu(tw["gate"], tw["up"], torch.from_numpy(x).cuda(), I, plan, wl.bits,
+                                 tiled=True)
+    yd_t = qmm.qgemm_grouped(*tw["down"], h_t, I, wl.bits, True, plan=plan, tiled=True)
     torch.cuda.synchronize()
+    assert torch.equal(h_t, h) and torch.equal(yd_t, yd), f"moe ffn m={m}: tiled weights differ"
+    del tw, h_t, yd_t
     hh, yh = host(h), host(y)
     tokens = sorted({0, m - 1, int(np.random.default_rng(m).integers(1, m - 1))})
     cols = sample_rows(wl.hidden, 32, 5 * m)

@@ -655,6 +655,34 @@ def test_moe_forced_tiles(bits, bm, nb, monkeypatch):
                  f"swiglu {bm}x{nb}")
 
 
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("bm,nb", [(32, 1), (64, 2), (128, 1), (160, 1)])
+def test_moe_tiled_weights(bits, bm, nb, monkeypatch):
+    """Grouped GEMMs (self-bucketing and routed) and the fused SwiGLU over
+    tile-interleaved expert weights are bit-identical to the row-major run."""
+    say("moe tiled", bits, bm, nb)
+    e, hidden, inter, t, top_k = 6, 192, 320, 150, 4
+    r = np.random.default_rng([962, bits])
+    ids = np.ascontiguousarray(synth.topk_ids(r.standard_normal((t, e)), top_k), dtype=np.int32)
+    x = dev(synth.draw_act((962, bits, 1), t, hidden))
+    gate = _to_dev(_expert_set((963, bits), e, inter, hidden, bits)[0])
+    up = _to_dev(_expert_set((964, bits), e, inter, hidden, bits)[0])
+    gate_t = (qmm.repack_tiled(gate[0], bits), gate[1], gate[2])
+    up_t = (qmm.repack_tiled(up[0], bits), up[1], up[2])
+    monkeypatch.setenv("QMM_MOE_FORCE", f"{bm},{nb}")
+    I = dev(ids)
+    plan = qmm.moe_route(I, e)
+    y0 = qmm.qgemm_grouped(*gate, x, I, bits, False)
+    y1 = qmm.qgemm_grouped(*gate_t, x, I, bits, False, tiled=True)
+    y2 = qmm.qgemm_grouped(*gate_t, x, I, bits, False, plan=plan, tiled=True)
+    h0 = qmm.moe_gate_up_swiglu(gate, up, x, I, plan, bits)
+    h1 = qmm.moe_gate_up_swiglu(gate_t, up_t, x, I, plan, bits, tiled=True)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("QMM_MOE_FORCE")
+    assert torch.equal(y0, y1) and torch.equal(y0, y2), f"grouped tiled differs {bm}x{nb}"
+    assert torch.equal(h0, h1), f"swiglu tiled differs {bm}x{nb}"
+
+
 def test_moe_ffn_block_chain():
     """route -> fused gate/up SwiGLU -> routed down -> weighted combine equals
     the float64 chain; the combine alone is checked on random rows too."""
