@@ -64,9 +64,9 @@ TRAFFIC = {
     # (KiB per dispatch of qgemv_batched_kernel<4,16,4,64>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 166749.3, "fetch_scale": 1073741824 / (524301.3 * 1024),
-    "write_kib": 1939.4, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "714fdc05d53643b7fd87ba246ad6f4c97c6a303a17a457bfe7013e366ce67703",
+    "fetch_kib": 166780.9, "fetch_scale": 1073741824 / (524301.3 * 1024),
+    "write_kib": 1938.9, "write_scale": 1073741824 / (1048576.0 * 1024),
+    "sources_sha256": "90cdbfc6cf75d5c9e5a945150a77a5ad8e71487e10a15aac95757551109acd01",
 }
 
 
