@@ -64,9 +64,9 @@ TRAFFIC = {
     # (KiB per dispatch of qgemv_batched_kernel<4,16,4,64>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 166780.9, "fetch_scale": 1073741824 / (524301.3 * 1024),
-    "write_kib": 1938.9, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "90cdbfc6cf75d5c9e5a945150a77a5ad8e71487e10a15aac95757551109acd01",
+    "fetch_kib": 166755.8, "fetch_scale": 1073741824 / (524301.3 * 1024),
+    "write_kib": 1938.6, "write_scale": 1073741824 / (1048576.0 * 1024),
+    "sources_sha256": "930899746c41ab2d2905f5f5fa9d8b2f56ec7e532b18d36df56b54d6a11fff14",
 }
 
 
@@ -176,8 +176,9 @@ def bench_gemm_formats(torch, qmm, m=2048, n=9728, k=2560, bits_list=(2, 3, 4, 5
     stream = torch.cuda.current_stream()
     for bits in bits_list:
         wq = (wf.half().view(torch.int32), None, None) if bits == 16 else qmm.quantize(wf, bits)
+        wq = (qmm.repack_tiled(wq[0], bits), wq[1], wq[2])  # tile-interleaved copy, once
         ws = torch.empty(max(qmm.qgemm_workspace_size(m, n, k, bits), 16), dtype=torch.uint8, device="cuda")
-        ms_call, _ = time_launches(torch, lambda i: qmm.qgemm(*wq, x, bits, y=y, workspace=ws),
+        ms_call, _ = time_launches(torch, lambda i: qmm.qgemm(*wq, x, bits, y=y, workspace=ws, tiled=True),
                                    steps, warmup, stream)
         tfl = 2.0 * m * n * k / (ms_call * 1e-3) / 1e12
         out["f16" if bits == 16 else f"q{bits}"] = {"ms_per_call": round(ms_call, 4), "tflops": round(tfl, 1),
@@ -581,7 +582,8 @@ def main():
                              "by_m": bench_prefill(torch, qmm, synth.QWEN3_4B_Q4_PREFILL.ms)}
         torch.cuda.empty_cache()
         log("gemm formats")
-        result["gemm_formats"] = {"shape": [2048, 9728, 2560], **bench_gemm_formats(torch, qmm)}
+        result["gemm_formats"] = {"shape": [2048, 9728, 2560], "weights": PREFILL_WEIGHTS,
+                                  **bench_gemm_formats(torch, qmm)}
         log("moe")
         result["moe"] = {"workload": synth.QWEN3_30B_A3B_Q4_MOE.name, "weights": PREFILL_WEIGHTS,
                          "by_m": bench_moe(torch, qmm)}

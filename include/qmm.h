@@ -282,12 +282,12 @@ int qmm_convert_bf16(const uint16_t* src, uint16_t* dst, size_t count, qmm_strea
  * so the 32 columns of one matrix-core column block are contiguous for each
  * group.  n must be a multiple of 32 and k of 64; w and out are device
  * buffers of n * k * bits / 8 bytes (16-byte aligned, not overlapping); out
- * is used with QMM_WEIGHTS_TILED: on a batched plan's bits, or on the bits
- * of qmm_qgemm_grouped, qmm_qgemm_grouped_routed and qmm_moe_gate_up_swiglu
- * (stacked experts [E, n, ...] repack as one [E*n, ...] matrix, which keeps
- * each expert's block whole when n is a multiple of 32).  The decode GEMV
- * and qmm_qgemm keep reading row-major weights.  Errors: INVALID_ARG,
- * UNSUPPORTED, HIP. */
+ * is used with QMM_WEIGHTS_TILED: on the bits of qmm_qgemm, of a batched
+ * plan, of qmm_qgemm_grouped, qmm_qgemm_grouped_routed and
+ * qmm_moe_gate_up_swiglu (stacked experts [E, n, ...] repack as one
+ * [E*n, ...] matrix, which keeps each expert's block whole when n is a
+ * multiple of 32).  The decode GEMV keeps reading row-major weights.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
 int qmm_repack_tiled(const uint32_t* w, uint32_t* out, int n, int k, int bits, qmm_stream stream);
 
 /* ------------------------------------------------------------- diagnostics

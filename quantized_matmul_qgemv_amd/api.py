@@ -97,8 +97,9 @@ def qgemm_workspace_size(m, n, k, bits, group_size=GROUP) -> int:
 
 
 def qgemm(w, scales, biases, x, bits: int, y=None, group_size: int = GROUP, workspace=None,
-          stream=None):
-    """y[m, n] = sum_k x[m, k] * W_hat[n, k] via qmm_qgemm."""
+          stream=None, tiled: bool = False):
+    """y[m, n] = sum_k x[m, k] * W_hat[n, k] via qmm_qgemm (tiled=True when w
+    comes from repack_tiled)."""
     m, k = x.shape
     n = w.shape[0]
     if y is None:
@@ -109,7 +110,8 @@ def qgemm(w, scales, biases, x, bits: int, y=None, group_size: int = GROUP, work
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check(lib().qmm_qgemm(_dev(w, "w", _W), _sb(scales, "scales", bits), _sb(biases, "biases", bits),
-                          _dev(x, "x", _X), _dev(y, "y", _Y), m, n, k, bits, group_size,
+                          _dev(x, "x", _X), _dev(y, "y", _Y), m, n, k,
+                          bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0), group_size,
                           ws_ptr, ws_len, _stream(stream)))
     return y
 

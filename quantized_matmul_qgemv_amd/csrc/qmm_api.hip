@@ -210,9 +210,13 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
               void* workspace, size_t workspace_bytes, qmm_stream stream) {
   const char* fn = "qmm_qgemm";
   clear_error();
+  const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
+  bits &= ~QMM_WEIGHTS_TILED;
   if (int st = check_format(fn, bits, group_size, true)) return st;
   if (m < 0) return fail(QMM_ERR_INVALID_ARG, "%s: m=%d must be >= 0", fn, m);
   if (int st = check_nk(fn, n, k, group_size)) return st;
+  if (wtiled && n % 32 != 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32 for tile-interleaved weights", fn, n);
   if (m == 0) return QMM_OK;
   CHECK_PTR(w, 16);
   if (bits != 16) {  // fp16 weights have no scales or biases
@@ -227,7 +231,7 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
       return fail(QMM_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
     CHECK_PTR(workspace, 16);
   }
-  qmm::GemmArgs a{w, scales, biases, x, y, m, n, k, group_size};
+  qmm::GemmArgs a{w, scales, biases, x, y, m, n, k, group_size, wtiled};
   return hip_status(qmm::launch_qgemm(a, bits, workspace, (hipStream_t)stream), fn);
 }
 

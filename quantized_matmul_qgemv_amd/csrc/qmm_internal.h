@@ -73,6 +73,7 @@ struct GemmArgs {
   float* y;
   int m, n, k;
   int group_size;  // codes per scale/bias group: 32, 64 or 128
+  int wtiled;      // weights in the tile-interleaved layout (qmm_repack_tiled)
 };
 size_t gemm_workspace_bytes(int m, int n, int k, int bits);
 hipError_t launch_qgemm(const GemmArgs& a, int bits, void* workspace, hipStream_t st);

@@ -323,6 +323,7 @@ def test_repack_tiled_errors_and_plan_flag(L):
     need, ws = C.c_size_t(0), C.c_size_t(0)
     expect(L.qmm_qgemm_batched_plan(probs, 1, 4 | tiled, 64, None, 0, C.byref(need), C.byref(ws)), INV,
            "n % 32")
+    expect(L.qmm_qgemm(A, A, A, A, A, 8, 200, 128, 4 | tiled, 64, A, 1 << 20, None), INV, "multiple of 32")
     expect(L.qmm_qgemm_grouped(A, A, A, A, 0, A, A, 8, 2, 4, 200, 128, 4 | tiled, 64, A, 1 << 20, None),
            INV, "multiple of 32")
     expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 0, A, A, 8, 2, 4, 200, 128, 4 | tiled, 64, None),

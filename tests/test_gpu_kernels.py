@@ -295,6 +295,29 @@ def test_gemm_batched_tiled_weights(bits, bm, nb, splits, monkeypatch):
         assert_close(host(t1[4]), want, f"tiled {bm}x{nb} S={splits} m={m} n={n} k={k}")
 
 
+@pytest.mark.parametrize("bits", [4, 16])
+@pytest.mark.parametrize("force", ["256,2,2", "128,2,1", "128,1,4", "64,1,1", "32,2,2"])
+def test_gemm_tiled_weights(bits, force, monkeypatch):
+    """qmm_qgemm over tile-interleaved weights is bit-identical to the
+    row-major call (every tile family, with and without k split)."""
+    say("gemm tiled", bits, force)
+    m, n, k = 300, 224, 1024
+    if bits == 16:
+        w = dev(fp16_weight((965, 0), n, k)[1])
+        s_ = b_ = None
+    else:
+        _, _, words, s16, b16 = quantized((965, bits), n, k, bits)
+        w, s_, b_ = dev(words), dev(s16), dev(b16)
+    x = dev(synth.draw_act((965, 1), m, k))
+    wt = qmm.repack_tiled(w, bits)
+    monkeypatch.setenv("QMM_GEMM_FORCE", force)
+    y0 = qmm.qgemm(w, s_, b_, x, bits)
+    y1 = qmm.qgemm(wt, s_, b_, x, bits, tiled=True)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("QMM_GEMM_FORCE")
+    assert torch.equal(y0, y1), force
+
+
 def test_gemm_rows_equal_gemv_and_deterministic():
     say("gemm rows")
     m, n, k, bits = 70, 520, 1024, 4
