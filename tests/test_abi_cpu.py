@@ -330,6 +330,10 @@ def test_repack_tiled_errors_and_plan_flag(L):
            INV, "multiple of 32")
     expect(L.qmm_moe_gate_up_swiglu(A, A, A, A, A, A, A, A, A, 8, 2, 4, 200, 128, 4 | tiled, 64, None),
            INV, "multiple of 32")
+    # entry points that read row-major weights only refuse the flag
+    expect(L.qmm_qgemv(A, A, A, A, A, 64, 128, 4 | tiled, 64, None), UNS, "bits")
+    expect(L.qmm_dequant(A, A, A, A, 0, 64, 128, 4 | tiled, 64, None), UNS, "bits")
+    expect(L.qmm_repack_tiled(A, B, 64, 128, 4 | tiled, None), UNS, "bits")
 
 
 def test_batched_gemm_plan_group_sizes(L):
