@@ -27,7 +27,9 @@
  *            word, low nibble first; for bits = 8, 4 bytes per word, low byte
  *            first; 3-, 5- and 6-bit codes straddle word boundaries (every 8
  *            codes fill exactly `bits` bytes).  Row stride: k * bits / 32
- *            words; a 64-code group is 8 * bits bytes.
+ *            words; a 64-code group is 8 * bits bytes.  The GEMM entry points
+ *            also read a tile-interleaved copy of these words (see
+ *            qmm_repack_tiled and QMM_WEIGHTS_TILED).
  *   scales,  fp16 bit patterns (uint16) [n, k / group_size]: the per-group
  *   biases   step s and offset b (asymmetric min/max quantization: b is the
  *            group minimum, s = (max - min) / (2^bits - 1)).
