@@ -40,8 +40,12 @@
  * ------------
  *   * Supported: bits in {2, 3, 4, 5, 6, 8}; group_size in {32, 64, 128}; k a positive
  *     multiple of 64 and of group_size; n, m >= 1 (m = 0 / t = 0 is accepted and does nothing).
- *   * Every tensor pointer is a DEVICE pointer owned by the caller, 16-byte
- *     aligned, and must stay valid until the stream reaches the launch.
+ *   * Every tensor pointer is a DEVICE pointer owned by the caller and must
+ *     stay valid until the stream reaches the launch.  Weights, activations,
+ *     plans and workspaces must be 16-byte aligned; scales and biases 2-byte
+ *     aligned (8-byte aligned arrays let the GEMM kernels load the scales of
+ *     four groups at once; others take a slower per-group path); outputs
+ *     4-byte (fp32) or 2-byte (fp16) aligned.
  *     Output buffers must not overlap inputs.
  *   * `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue
  *     work and return; results are valid once the stream is synchronized.
@@ -188,18 +192,34 @@ int qmm_qgemm_batched(const void* plan_device, const void* plan_host, void* work
                       size_t workspace_bytes, qmm_stream stream);
 
 /* --------------------------------------------- mixture-of-experts grouped
+ * BaseRT (native-Metal LLM inference on Apple Silicon), abstract and Fig. 1:
+ * the mixture-of-experts prefill (Qwen3-30B-A3B, 4-bit) is where the pages
+ * report their larger advantage; they give no mechanism, so the one here is
+ * token-to-expert bucketing with one tile schedule per expert.  §3.3 applies
+ * as for the GEMM (dequantization inside the inner loop).
+ *
  * Pair p = t * top_k + j routes token t to expert e = expert_ids[t, j]:
  *     y[p, n] = sum_k A[row(p), k] * W_hat_e[n, k]
  *   w       [E, n, k*bits/32]; scales, biases [E, n, k/group_size]
  *   a       fp16 bits; a_row_per_pair = 0: A is [T, k] and row(p) = p / top_k
  *           (gate / up projections read the token); 1: A is [T*top_k, k] and
  *           row(p) = p (the down projection reads the pair's own row)
- *   expert_ids [T, top_k] int32, each in [0, E) (not checked on the device;
- *           an id outside the range is undefined behaviour)
+ *   expert_ids [T, top_k] int32, each in [0, E).  A pair whose id lies outside
+ *           that range is not computed: its output row is NaN, and the count
+ *           of such pairs is recorded in the plan header (below).
  *   y       [T*top_k, n] fp32 (overwritten)
  * Device-side token-to-expert bucketing (histogram, scan, scatter) builds
  * one tile list per expert in the workspace; the grouped GEMM then gathers
  * A rows, dequantizes that expert's weight tiles and scatters output rows.
+ * The workspace size depends only on (T, top_k, E); n, k, bits and
+ * group_size are accepted so that a caller can size it from the same
+ * arguments as the product.
+ *
+ * Routing plan / workspace image (device memory, int32 words):
+ *   word 0  row tiles in the list     word 1  rows per row tile
+ *   word 2  pairs (T * top_k)         word 3  experts E
+ *   word 4  pairs whose expert id was outside [0, E)  (byte offset 16)
+ *   words 5..7 zero; then the bucketed pair list and the row-tile list.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
 size_t qmm_qgemm_grouped_workspace_size(int t, int top_k, int e, int n, int k, int bits,
                                         int group_size);
@@ -209,47 +229,55 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
                       int group_size, void* workspace, size_t workspace_bytes,
                       qmm_stream stream);
 
-/* Routing plan shared by the grouped products of one MoE layer.  Gate, up
- * and down read the same expert ids, so the token-to-expert bucketing (the
- * first launch of qmm_qgemm_grouped) can run once:
+/* Routing plan shared by the grouped products of one MoE layer (BaseRT,
+ * abstract and Fig. 1: MoE prefill; §3 amortized dispatch).  Gate, up and
+ * down read the same expert ids, so the token-to-expert bucketing (the first
+ * launch of qmm_qgemm_grouped) can run once:
  *   qmm_moe_route        buckets expert_ids [T, top_k] into `plan` (device
  *                        memory of qmm_moe_route_size(T, top_k, E) bytes,
  *                        16-byte aligned, caller-owned; contents on entry
  *                        do not matter);
  *   qmm_qgemm_grouped_routed  the grouped product of qmm_qgemm_grouped, with
- *                        the same arguments except that `plan` replaces
- *                        expert_ids and the workspace.
+ *                        the same arguments except that `plan` and its size
+ *                        `plan_bytes` replace expert_ids and the workspace.
  * The plan stays valid while expert_ids is unchanged, for any n, k, bits and
- * group size, and may be read by several launches in flight.  A plan built
- * for another (T, top_k, E) is detected on the device and the product is
- * then not computed (y is left untouched).
- * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (plan too small), HIP. */
+ * group size, and may be read by several launches in flight.  plan_bytes
+ * below qmm_moe_route_size(T, top_k, E) is refused on the host (WORKSPACE);
+ * a plan built for another (T, top_k, E) or another row tile is detected on
+ * the device and the whole output is then written as NaN.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
 size_t qmm_moe_route_size(int t, int top_k, int e);
 int qmm_moe_route(const int32_t* expert_ids, int t, int top_k, int e, void* plan,
                   size_t plan_bytes, qmm_stream stream);
 int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
-                             const uint16_t* a, int a_row_per_pair, const void* plan, float* y,
-                             int t, int top_k, int e, int n, int k, int bits, int group_size,
-                             qmm_stream stream);
+                             const uint16_t* a, int a_row_per_pair, const void* plan,
+                             size_t plan_bytes, float* y, int t, int top_k, int e, int n, int k,
+                             int bits, int group_size, qmm_stream stream);
 
-/* Mixture-of-experts FFN block around the grouped products.
+/* Mixture-of-experts FFN block around the grouped products (BaseRT §3.3:
+ * the FFN's matmuls and activation fused into fewer kernels; abstract and
+ * Fig. 1: MoE prefill).
  *   qmm_moe_gate_up_swiglu  for every pair p (token row p / top_k of x
- *       [T, k] fp16), with e = the pair's expert from `plan` (qmm_moe_route):
+ *       [T, k] fp16), with e = the pair's expert from `plan` (qmm_moe_route,
+ *       plan_bytes as for qmm_qgemm_grouped_routed):
  *           h[p, c] = fp16( silu(g) * u ),  silu(g) = g / (1 + exp(-g)),
  *           g = sum_k x[row, k] W_gate_e[c, k],  u = likewise with W_up_e
  *       (g, u and the SwiGLU in fp32; one rounding to fp16).  w_gate, w_up
  *       [E, n, k*bits/32] with their scales and biases as in
  *       qmm_qgemm_grouped; h [T*top_k, n] fp16 bits (overwritten) is the
  *       down projection's A (a_row_per_pair = 1).  bits = 16: fp16 weights.
+ *       Rows of pairs with an out-of-range expert id, and all of h when the
+ *       plan was built for other counts, are written as fp16 NaN.
  *   qmm_moe_combine  y[t, c] = sum_{j < top_k} weights[t, j] * y_pairs[t*top_k + j, c]
  *       with the slots added in order j = 0, 1, ... (fp32 fma), so the result
  *       does not depend on scheduling.  y_pairs [T*top_k, n] fp32 (the down
  *       projection's output), weights [T, top_k] fp32, y [T, n] fp32.
- * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (plan too small), HIP. */
 int qmm_moe_gate_up_swiglu(const uint32_t* w_gate, const uint16_t* s_gate, const uint16_t* b_gate,
                            const uint32_t* w_up, const uint16_t* s_up, const uint16_t* b_up,
-                           const uint16_t* x, const void* plan, uint16_t* h, int t, int top_k,
-                           int e, int n, int k, int bits, int group_size, qmm_stream stream);
+                           const uint16_t* x, const void* plan, size_t plan_bytes, uint16_t* h,
+                           int t, int top_k, int e, int n, int k, int bits, int group_size,
+                           qmm_stream stream);
 int qmm_moe_combine(const float* y_pairs, const float* weights, float* y, int t, int top_k, int n,
                     qmm_stream stream);
 

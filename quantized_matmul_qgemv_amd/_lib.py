@@ -9,7 +9,10 @@ from __future__ import annotations
 import ctypes as C
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
+# QMM_LIBRARY names another build of the same library (the host-sanitizer
+# build of the CPU tests); by default the in-tree libqmm.so.
+LIB_PATH = os.environ.get("QMM_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libqmm.so")
 
 QMM_OK = 0
 QMM_ERR_INVALID_ARG = 1
@@ -56,8 +59,8 @@ SIGNATURES = {
     "qmm_qgemm_grouped": (I, [P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, SZ, P]),
     "qmm_moe_route_size": (SZ, [I, I, I]),
     "qmm_moe_route": (I, [P, I, I, I, P, SZ, P]),
-    "qmm_qgemm_grouped_routed": (I, [P, P, P, P, I, P, P, I, I, I, I, I, I, I, P]),
-    "qmm_moe_gate_up_swiglu": (I, [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]),
+    "qmm_qgemm_grouped_routed": (I, [P, P, P, P, I, P, SZ, P, I, I, I, I, I, I, I, P]),
+    "qmm_moe_gate_up_swiglu": (I, [P, P, P, P, P, P, P, P, SZ, P, I, I, I, I, I, I, I, P]),
     "qmm_moe_combine": (I, [P, P, P, I, I, I, P]),
     "qmm_convert_bf16": (I, [P, P, SZ, P]),
     "qmm_repack_tiled": (I, [P, P, I, I, I, P]),

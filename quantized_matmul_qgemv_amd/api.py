@@ -45,6 +45,17 @@ def _sb(t, name: str, bits: int) -> int:
     return _dev(t, name, _SB)
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def moe_plan_dropped(plan: torch.Tensor) -> int:
+    """Pairs whose expert id lay outside [0, E) when `plan` was built (the
+    int32 at byte offset 16 of a routing plan or grouped workspace); their
+    output rows are NaN.  Reads device memory, so it synchronizes."""
+    return int(plan[16:20].view(torch.int32).item())
+
+
 _W = (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
 _SB = (torch.int16, torch.float16) + ((torch.uint16,) if hasattr(torch, "uint16") else ())
 _X = (torch.float16,)
@@ -185,7 +196,8 @@ def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: b
     if plan is not None:
         check(lib().qmm_qgemm_grouped_routed(_dev(w, "w", _W), _sb(scales, "scales", bits),
                                              _sb(biases, "biases", bits), _dev(a, "a", _X),
-                                             int(bool(a_row_per_pair)), plan.data_ptr(), _dev(y, "y", _Y),
+                                             int(bool(a_row_per_pair)), plan.data_ptr(), _nbytes(plan),
+                                             _dev(y, "y", _Y),
                                              t, top_k, e, n, k, flag_bits, group_size, _stream(stream)))
         return y
     ws_bytes = qgemm_grouped_workspace_size(t, top_k, e, n, k, bits, group_size)
@@ -198,6 +210,11 @@ def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: b
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   _stream(stream)))
     return y
+
+
+def moe_route_size(t: int, top_k: int, e: int) -> int:
+    """Bytes of the routing plan qmm_moe_route writes for (t, top_k, e)."""
+    return lib().qmm_moe_route_size(t, top_k, e)
 
 
 def moe_route(expert_ids, e: int, plan=None, stream=None):
@@ -227,7 +244,7 @@ def moe_gate_up_swiglu(gate, up, x, expert_ids, plan, bits: int, h=None, group_s
         h = torch.empty((t * top_k, n), dtype=torch.float16, device=wg.device)
     check(lib().qmm_moe_gate_up_swiglu(_dev(wg, "w_gate", _W), _sb(sg, "s_gate", bits), _sb(bg, "b_gate", bits),
                                        _dev(wu, "w_up", _W), _sb(su, "s_up", bits), _sb(bu, "b_up", bits),
-                                       _dev(x, "x", _X), plan.data_ptr(), _dev(h, "h", _X),
+                                       _dev(x, "x", _X), plan.data_ptr(), _nbytes(plan), _dev(h, "h", _X),
                                        t, top_k, e, n, k, flag_bits, group_size, _stream(stream)))
     return h
 
@@ -266,28 +283,36 @@ def repack_tiled(w, bits: int, out=None, stream=None):
     return out
 
 
-def quantize(w_f32, bits: int, group_size: int = GROUP, stream=None):
-    """Quantize fp32 W [n, k] on the device -> (words int32, scales int16, biases int16)."""
+def quantize(w_f32, bits: int, group_size: int = GROUP, stream=None, out=None):
+    """Quantize fp32 W [n, k] on the device -> (words int32, scales int16, biases int16);
+    `out` = (words, scales, biases) writes into given tensors."""
     n, k = w_f32.shape
-    words = torch.empty((n, k * bits // 32), dtype=torch.int32, device=w_f32.device)
-    s = torch.empty((n, k // group_size), dtype=torch.int16, device=w_f32.device)
-    b = torch.empty_like(s)
-    check(lib().qmm_quantize(_dev(w_f32, "w_f32", (torch.float32,)), words.data_ptr(), s.data_ptr(),
-                             b.data_ptr(), n, k, bits, group_size, _stream(stream)))
+    if out is None:
+        words = torch.empty((n, k * bits // 32), dtype=torch.int32, device=w_f32.device)
+        s = torch.empty((n, k // group_size), dtype=torch.int16, device=w_f32.device)
+        b = torch.empty_like(s)
+    else:
+        words, s, b = out
+    check(lib().qmm_quantize(_dev(w_f32, "w_f32", (torch.float32,)), _dev(words, "words", _W),
+                             _dev(s, "scales", _SB), _dev(b, "biases", _SB), n, k, bits, group_size,
+                             _stream(stream)))
     return words, s, b
 
 
-def unpack_codes(w, k: int, bits: int, stream=None):
+def unpack_codes(w, k: int, bits: int, stream=None, out=None):
     n = w.shape[0]
-    codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
-    check(lib().qmm_unpack_codes(_dev(w, "w", _W), codes.data_ptr(), n, k, bits, _stream(stream)))
+    codes = torch.empty((n, k), dtype=torch.uint8, device=w.device) if out is None else out
+    check(lib().qmm_unpack_codes(_dev(w, "w", _W), _dev(codes, "codes", (torch.uint8,)), n, k, bits,
+                                 _stream(stream)))
     return codes
 
 
 def dequant(w, scales, biases, k: int, bits: int, out_f16: bool, group_size: int = GROUP,
-            stream=None):
+            stream=None, out=None):
     n = w.shape[0]
-    out = torch.empty((n, k), dtype=torch.int16 if out_f16 else torch.float32, device=w.device)
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.int16 if out_f16 else torch.float32, device=w.device)
     check(lib().qmm_dequant(_dev(w, "w", _W), _dev(scales, "scales", _SB), _dev(biases, "biases", _SB),
-                            out.data_ptr(), int(out_f16), n, k, bits, group_size, _stream(stream)))
+                            _dev(out, "out", (torch.int16,) if out_f16 else (torch.float32,)), int(out_f16),
+                            n, k, bits, group_size, _stream(stream)))
     return out

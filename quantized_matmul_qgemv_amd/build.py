@@ -58,6 +58,63 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-sanitizer build (AddressSanitizer + UndefinedBehaviorSanitizer on the
+# host code only; the device code is built as usual).  Used by the CPU tests,
+# which load it into a Python whose ASan runtime is preloaded.
+SAN_BUILD = os.path.join(PKG, "_build_hostsan")
+SAN_LIB = os.path.join(SAN_BUILD, "libqmm_hostsan.so")
+SAN_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime that the sanitized build links against."""
+    r = subprocess.run([os.path.join(os.path.dirname(HIPCC), "..", "llvm", "bin", "clang"),
+                        "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang's libclang_rt.asan-x86_64.so was not found")
+    return path
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Build libqmm_hostsan.so (rebuilt only when a source or flag changed)."""
+    import hashlib
+    h = hashlib.sha256(" ".join(CFLAGS + SAN_FLAGS).encode())
+    for d in (CSRC, INCLUDE):
+        for f in sorted(os.listdir(d)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    stamp = os.path.join(SAN_BUILD, "sources.sha256")
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    if os.path.exists(SAN_LIB) and os.path.exists(stamp) and open(stamp).read() == h.hexdigest():
+        return SAN_LIB
+
+    def one(src):
+        obj = os.path.join(SAN_BUILD, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *CFLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stderr}")
+        return obj
+    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(one, SOURCES))
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", SAN_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
+    with open(stamp, "w") as fh:
+        fh.write(h.hexdigest())
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -30,26 +30,33 @@ constexpr int kBucketThreads = 1024;
 constexpr int kMaxExperts = 1024;
 
 struct MoeTile {
-  int32_t expert;
-  int32_t start;  // first slot in the sorted pair list
+  int32_t expert;  // -1: the pairs whose expert id lies outside [0, E)
+  int32_t start;   // first slot in the sorted pair list
   int32_t rows;
 };
 
-// Workspace layout (int32 units): [num_tiles, row tile, pairs, experts][sorted pairs: P]
-// [tiles: 3*max_tiles].  The same image is the routing plan that one
-// bucketing pass builds for several grouped GEMMs on the same expert ids.
+// Workspace layout (int32 units): a header of kPlanHeaderInts words
+//   [0] row tiles in the list   [1] row tile (rows)   [2] pairs   [3] experts
+//   [4] pairs whose expert id is outside [0, E) (their output rows are NaN)
+//   [5..7] zero
+// then the sorted pairs (P words) and the tile list (3 words per tile).  The
+// same image is the routing plan that one bucketing pass builds for several
+// grouped GEMMs on the same expert ids.  Pairs with an out-of-range id sit
+// after every valid bucket and get row tiles of their own (expert -1), so
+// the bound on row tiles counts E + 1 buckets.
+constexpr int kPlanHeaderInts = 8;
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 static int max_row_tiles(int pairs, int experts, int bm) {
-  const int by_pairs = (pairs + bm - 1) / bm + experts;
-  return by_pairs < pairs ? by_pairs : (pairs > 0 ? pairs : 1);
+  const long by_pairs = (long)(pairs + bm - 1) / bm + experts + 1;
+  return by_pairs < pairs ? (int)by_pairs : (pairs > 0 ? pairs : 1);
 }
 
 size_t grouped_workspace_bytes(int t, int top_k, int e, int n) {
   (void)n;
   const long pairs = (long)t * top_k;
   const long tiles = max_row_tiles((int)pairs, e, 32);
-  return align_up((size_t)(4 + pairs + 3 * tiles) * sizeof(int32_t), 256);
+  return align_up((size_t)(kPlanHeaderInts + pairs + 3 * tiles) * sizeof(int32_t), 256);
 }
 
 // Inclusive sum over the 64 lanes of a wave.
@@ -73,29 +80,35 @@ __global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
   __shared__ int32_t cnt[kMaxExperts];
   __shared__ int32_t cursor[kMaxExperts];
   __shared__ int32_t wtot[2][kWaves];
+  __shared__ int32_t bad_count;   // pairs with an id outside [0, experts)
+  __shared__ int32_t bad_cursor;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  int32_t* num_tiles = ws;
-  int32_t* sorted = ws + 4;
-  MoeTile* tiles = reinterpret_cast<MoeTile*>(ws + 4 + pairs);
+  int32_t* sorted = ws + kPlanHeaderInts;
+  MoeTile* tiles = reinterpret_cast<MoeTile*>(ws + kPlanHeaderInts + pairs);
 
   cnt[tid] = 0;
+  if (tid == 0) bad_count = 0;
   int myid[kBucketIdsPerThread];
 #pragma unroll
   for (int i = 0; i < kBucketIdsPerThread; ++i) {
     const int p = tid + i * kBucketThreads;
     const int e = p < pairs ? ids[p] : -1;
-    myid[i] = (e >= 0 && e < experts) ? e : -1;
+    // -1: no pair; -2: a pair whose id is out of range
+    myid[i] = p >= pairs ? -1 : (e >= 0 && e < experts) ? e : -2;
   }
   __syncthreads();
-  // histogram of expert ids (invalid ids are skipped)
+  // histogram of expert ids; out-of-range ids are counted apart
 #pragma unroll
-  for (int i = 0; i < kBucketIdsPerThread; ++i)
+  for (int i = 0; i < kBucketIdsPerThread; ++i) {
     if (myid[i] >= 0) atomicAdd(&cnt[myid[i]], 1);
+    else if (myid[i] == -2) atomicAdd(&bad_count, 1);
+  }
   for (int p = tid + kBucketIdsPerThread * kBucketThreads; p < pairs; p += kBucketThreads) {
     const int e = ids[p];
     if (e >= 0 && e < experts) atomicAdd(&cnt[e], 1);
+    else atomicAdd(&bad_count, 1);
   }
   __syncthreads();
   // exclusive scans of the pair counts and of the row-tile counts:
@@ -118,7 +131,16 @@ __global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
       wtot[0][lane] = s0 - a0;  // exclusive prefix of the wave totals
       wtot[1][lane] = s1 - a1;
     }
-    if (lane == kWaves - 1) num_tiles[0] = s1;
+    if (lane == kWaves - 1) {
+      // the out-of-range pairs follow every valid bucket, with tiles of their own
+      const int bad = bad_count;
+      const int bad_tiles = (bad + bm - 1) / bm;
+      bad_cursor = s0;
+      for (int i = 0; i < bad_tiles; ++i)
+        tiles[s1 + i] = MoeTile{-1, s0 + i * bm, bad - i * bm < bm ? bad - i * bm : bm};
+      ws[0] = s1 + bad_tiles;
+      ws[4] = bad;
+    }
   }
   __syncthreads();
   const int start = wtot[0][wave] + ic - c;
@@ -127,11 +149,14 @@ __global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
   __syncthreads();
   // scatter pair indices into their expert's bucket
 #pragma unroll
-  for (int i = 0; i < kBucketIdsPerThread; ++i)
+  for (int i = 0; i < kBucketIdsPerThread; ++i) {
     if (myid[i] >= 0) sorted[atomicAdd(&cursor[myid[i]], 1)] = tid + i * kBucketThreads;
+    else if (myid[i] == -2) sorted[atomicAdd(&bad_cursor, 1)] = tid + i * kBucketThreads;
+  }
   for (int p = tid + kBucketIdsPerThread * kBucketThreads; p < pairs; p += kBucketThreads) {
     const int e = ids[p];
     if (e >= 0 && e < experts) sorted[atomicAdd(&cursor[e], 1)] = p;
+    else sorted[atomicAdd(&bad_cursor, 1)] = p;
   }
   if (tid < experts) {
     for (int i = 0; i < tl; ++i) {
@@ -139,10 +164,37 @@ __global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
       tiles[tstart + i] = MoeTile{tid, start + i * bm, rows};
     }
   }
-  if (tid == 0) {  // what the plan was built for (checked by grouped_kernel)
+  if (tid == 0) {  // what the plan was built for (checked by every grouped kernel)
     ws[1] = bm;
     ws[2] = pairs;
     ws[3] = experts;
+    ws[5] = 0;
+    ws[6] = 0;
+    ws[7] = 0;
+  }
+}
+
+// Output of a grouped launch that cannot be computed: a plan built for
+// another row tile, pair count or expert count.  The whole output
+// (rows x cols elements, row stride ld) is filled with NaN by the launch's
+// workgroups together, so the failure shows in every result.
+template <typename T>
+__device__ void fill_nan_all(T* out, long rows, int cols, int ld, T nan) {
+  const long total = rows * cols;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride)
+    out[(i / cols) * ld + i % cols] = nan;
+}
+
+// Rows of the pairs of an out-of-range row tile (expert -1): NaN in the
+// tile's columns [c0, c0 + bn) (bounded by n).
+template <typename T>
+__device__ void fill_nan_rows(T* out, const int32_t* sorted, const MoeTile& mt, int c0, int bn, int n,
+                              T nan) {
+  const int cols = n - c0 < bn ? n - c0 : bn;
+  for (int i = threadIdx.x; i < mt.rows * cols; i += blockDim.x) {
+    const long row = sorted[mt.start + i / cols];
+    out[row * n + c0 + i % cols] = nan;
   }
 }
 
@@ -164,11 +216,18 @@ void grouped_kernel(GroupedArgs a, const int32_t* __restrict__ ws, int n_tiles) 
   const int tile = blockIdx.x / n_tiles;
   const int tn = blockIdx.x % n_tiles;
   // a routing plan built for another row tile, pair count or expert count
-  // is not used (the output is left untouched)
-  if (ws[1] != BM || ws[2] != pairs || ws[3] != a.e) return;
+  // is not used: the whole output becomes NaN
+  if (ws[1] != BM || ws[2] != pairs || ws[3] != a.e) {
+    fill_nan_all(a.y, pairs, a.n, a.n, __builtin_nanf(""));
+    return;
+  }
   if (tile >= ws[0]) return;
-  const MoeTile mt = reinterpret_cast<const MoeTile*>(ws + 4 + pairs)[tile];
-  const int32_t* sorted = ws + 4;
+  const MoeTile mt = reinterpret_cast<const MoeTile*>(ws + kPlanHeaderInts + pairs)[tile];
+  const int32_t* sorted = ws + kPlanHeaderInts;
+  if (mt.expert < 0) {  // pairs with an out-of-range expert id
+    fill_nan_rows(a.y, sorted, mt, tn * BN, BN, a.n, __builtin_nanf(""));
+    return;
+  }
   for (int i = threadIdx.x; i < BM; i += blockDim.x)
     pair_of[i] = sorted[mt.start + (i < mt.rows ? i : mt.rows - 1)];
   __syncthreads();
@@ -213,10 +272,18 @@ void swiglu_kernel(SwigluArgs a, const int32_t* __restrict__ ws, int n_tiles) {
   const int pairs = a.t * a.top_k;
   const int tile = blockIdx.x / n_tiles;
   const int tn = blockIdx.x % n_tiles;
-  if (ws[1] != BM || ws[2] != pairs || ws[3] != a.e) return;
+  const uint16_t nan16 = 0x7E00;  // fp16 quiet NaN
+  if (ws[1] != BM || ws[2] != pairs || ws[3] != a.e) {  // foreign plan: h is all NaN
+    fill_nan_all(a.h, pairs, a.n, a.n, nan16);
+    return;
+  }
   if (tile >= ws[0]) return;
-  const MoeTile mt = reinterpret_cast<const MoeTile*>(ws + 4 + pairs)[tile];
-  const int32_t* sorted = ws + 4;
+  const MoeTile mt = reinterpret_cast<const MoeTile*>(ws + kPlanHeaderInts + pairs)[tile];
+  const int32_t* sorted = ws + kPlanHeaderInts;
+  if (mt.expert < 0) {  // pairs with an out-of-range expert id
+    fill_nan_rows(a.h, sorted, mt, tn * 128, 128, a.n, nan16);
+    return;
+  }
   for (int i = threadIdx.x; i < BM; i += blockDim.x)
     pair_of[i] = sorted[mt.start + (i < mt.rows ? i : mt.rows - 1)];
   __syncthreads();
@@ -249,13 +316,21 @@ static hipError_t launch_swiglu_sbq(const SwigluArgs& a, const int32_t* plan, hi
   return hipGetLastError();
 }
 
+// Quad scale loads (8 bytes per column, four groups of 64): the expert and
+// column offsets of the scales are multiples of 8 bytes when k / 64 is a
+// multiple of 4, so only the arrays' own alignment is checked.
+static bool sbq_ok(int k, int group_size, const void* s, const void* b) {
+  return (k / 64) % 4 == 0 && group_size == 64 && ((uintptr_t)s & 7) == 0 && ((uintptr_t)b & 7) == 0;
+}
+
 template <int BITS>
 static hipError_t launch_swiglu_bits(const SwigluArgs& a, const int32_t* plan, hipStream_t st) {
   if constexpr (BITS == 16) {
     return launch_swiglu_sbq<16, false>(a, plan, st);
   } else {
-    return (a.k / 64) % 4 == 0 && a.group_size == 64 ? launch_swiglu_sbq<BITS, true>(a, plan, st)
-                                                     : launch_swiglu_sbq<BITS, false>(a, plan, st);
+    return sbq_ok(a.k, a.group_size, a.sg, a.bg) && sbq_ok(a.k, a.group_size, a.su, a.bu)
+               ? launch_swiglu_sbq<BITS, true>(a, plan, st)
+               : launch_swiglu_sbq<BITS, false>(a, plan, st);
   }
 }
 
@@ -267,6 +342,9 @@ static hipError_t launch_swiglu_bits(const SwigluArgs& a, const int32_t* plan, h
 // against 128 row tiles; measured 8-11 % faster for the three grouped GEMMs).
 // QMM_MOE_FORCE="bm,nb" overrides the tile (tuning sweeps).  The bucketing
 // and the grouped GEMM must agree on it, so both take it from here.
+// QMM_MOE_FORCE is read on every call (tuning sweeps change it between
+// calls); a routing plan built under one value and used under another is
+// caught on the device by the plan-header check (the output becomes NaN).
 static void moe_tile(int pairs, int experts, int* bm_out, int* nb_out) {
   const int mean = (pairs + experts - 1) / experts;
   int bm = mean <= 16 ? 32 : mean <= 48 ? 64 : (mean >= 112 && mean <= 144) ? 160 : 128, nb = 1;
@@ -329,8 +407,8 @@ static hipError_t launch_grouped_sbq(const GroupedArgs& a, int32_t* ws, bool buc
 template <int BITS>
 static hipError_t launch_grouped_bits(const GroupedArgs& a, int32_t* ws, bool bucket, hipStream_t st) {
   if constexpr (BITS == 16) return launch_grouped_sbq<16, false>(a, ws, bucket, st);
-  return (a.k / 64) % 4 == 0 && a.group_size == 64 ? launch_grouped_sbq<BITS, true>(a, ws, bucket, st)
-                             : launch_grouped_sbq<BITS, false>(a, ws, bucket, st);
+  return sbq_ok(a.k, a.group_size, a.s, a.b) ? launch_grouped_sbq<BITS, true>(a, ws, bucket, st)
+                                             : launch_grouped_sbq<BITS, false>(a, ws, bucket, st);
 }
 
 hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, bool bucket, hipStream_t st) {

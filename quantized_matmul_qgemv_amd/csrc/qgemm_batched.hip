@@ -224,7 +224,12 @@ void gemm_choose(int m, int n, int k, int bits, int* bm, int* nb, int* splits) {
 size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, int group_size,
                         int wtiled, void* out, size_t out_bytes) {
   Choice ch = choose(probs, count, false, bits == 16);
-  ch.sbq = ch.sbq && group_size == 64 && bits != 16;  // quad scale loads: groups of 64 only
+  // quad scale loads (8 bytes per column): groups of 64 with 8-byte aligned
+  // scale and bias arrays only
+  bool sb_aligned = true;
+  for (int p = 0; p < count; ++p)
+    sb_aligned = sb_aligned && ((uintptr_t)probs[p].s & 7) == 0 && ((uintptr_t)probs[p].b & 7) == 0;
+  ch.sbq = ch.sbq && group_size == 64 && bits != 16 && sb_aligned;
   const TileCfg& c = kCfgs[ch.cfg];
   const int bn = c.nb * 128;
   const int S = ch.splits;

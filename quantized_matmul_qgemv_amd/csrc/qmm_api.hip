@@ -68,6 +68,18 @@ int check_nk(const char* fn, int n, int k, int group_size = 64) {
   return QMM_OK;
 }
 
+// A routing plan must be at least as large as the one qmm_moe_route writes
+// for (t, top_k, e); one built for other counts is also detected on the
+// device (the output becomes NaN), but a buffer too small for these counts
+// would be read past its end, so it is refused here.
+int check_plan_size(const char* fn, size_t plan_bytes, int t, int top_k, int e) {
+  const size_t need = qmm::grouped_workspace_bytes(t, top_k, e, 0);
+  if (plan_bytes < need)
+    return fail(QMM_ERR_WORKSPACE, "%s: plan of %zu bytes, a routing plan for t=%d top_k=%d e=%d has %zu",
+                fn, plan_bytes, t, top_k, e, need);
+  return QMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,9 +172,11 @@ int qmm_qgemv_batched_plan(const qmm_gemv_problem* problems, int count, int bits
   hdr.num_blocks = (int32_t)blocks;
   hdr.max_groups = max_groups;
   hdr.count = count;
+  // The caller's buffer is only 8-byte aligned, so the 64-byte-aligned
+  // records are copied in byte-wise rather than stored as structures.
   unsigned char* out = static_cast<unsigned char*>(plan);
   memcpy(out, &hdr, sizeof hdr);
-  qmm::GemvBlock* recs = reinterpret_cast<qmm::GemvBlock*>(out + sizeof hdr);
+  unsigned char* recs = out + sizeof hdr;
   long bi = 0;
   for (int i = 0; i < count; ++i) {
     const qmm_gemv_problem& q = problems[i];
@@ -173,7 +187,7 @@ int qmm_qgemv_batched_plan(const qmm_gemv_problem* problems, int count, int bits
       blk.p = qmm::GemvProblem{q.w, q.scales, q.biases, q.x, q.y, q.n, q.k};
       blk.row0 = r;
       blk.nrows = q.n - r < chunk ? q.n - r : chunk;
-      recs[bi++] = blk;
+      memcpy(recs + (size_t)bi++ * sizeof blk, &blk, sizeof blk);
     }
   }
   return QMM_OK;
@@ -199,6 +213,7 @@ int qmm_qgemv_batched(const void* plan_device, const void* plan_host, qmm_stream
 }
 
 size_t qmm_qgemm_workspace_size(int m, int n, int k, int bits, int group_size) {
+  bits &= ~QMM_WEIGHTS_TILED;  // the layout does not change the split-k workspace
   if (m < 1 || n < 1 || k < 64 || k % 64 != 0) return 0;
   if ((group_size != 32 && group_size != 64 && group_size != 128) || k % group_size != 0) return 0;
   if ((bits < 2 || bits > 8 || bits == 7) && bits != 16) return 0;
@@ -246,9 +261,13 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
   if (count < 1) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d must be >= 1", fn, count);
   if (count > (1 << 20)) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d too large", fn, count);
   if (problems == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: null problems", fn);
-  qmm::GemmBatchProblem* probs = static_cast<qmm::GemmBatchProblem*>(
-      calloc((size_t)count, sizeof(qmm::GemmBatchProblem)));
+  // GemmBatchProblem is 64-byte aligned (one device cache line per record);
+  // calloc guarantees only 16, so the host copy is allocated aligned.
+  const size_t probs_bytes = (size_t)count * sizeof(qmm::GemmBatchProblem);
+  qmm::GemmBatchProblem* probs =
+      static_cast<qmm::GemmBatchProblem*>(aligned_alloc(alignof(qmm::GemmBatchProblem), probs_bytes));
   if (probs == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: out of host memory", fn);
+  memset(probs, 0, probs_bytes);
   for (int i = 0; i < count; ++i) {
     const qmm_gemm_problem& q = problems[i];
     int bad = 0;
@@ -385,9 +404,9 @@ int qmm_moe_route(const int32_t* expert_ids, int t, int top_k, int e, void* plan
 }
 
 int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
-                             const uint16_t* a, int a_row_per_pair, const void* plan, float* y,
-                             int t, int top_k, int e, int n, int k, int bits, int group_size,
-                             qmm_stream stream) {
+                             const uint16_t* a, int a_row_per_pair, const void* plan,
+                             size_t plan_bytes, float* y, int t, int top_k, int e, int n, int k,
+                             int bits, int group_size, qmm_stream stream) {
   const char* fn = "qmm_qgemm_grouped_routed";
   clear_error();
   const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
@@ -412,6 +431,7 @@ int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const ui
   CHECK_PTR(a, 16);
   CHECK_PTR(plan, 16);
   CHECK_PTR(y, 4);
+  if (int st = check_plan_size(fn, plan_bytes, t, top_k, e)) return st;
   qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, nullptr, y, t, top_k, e, n, k, group_size, wtiled};
   return hip_status(qmm::launch_qgemm_grouped(ga, bits, const_cast<void*>(plan), false,
                                               (hipStream_t)stream), fn);
@@ -419,8 +439,9 @@ int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const ui
 
 int qmm_moe_gate_up_swiglu(const uint32_t* w_gate, const uint16_t* s_gate, const uint16_t* b_gate,
                            const uint32_t* w_up, const uint16_t* s_up, const uint16_t* b_up,
-                           const uint16_t* x, const void* plan, uint16_t* h, int t, int top_k,
-                           int e, int n, int k, int bits, int group_size, qmm_stream stream) {
+                           const uint16_t* x, const void* plan, size_t plan_bytes, uint16_t* h,
+                           int t, int top_k, int e, int n, int k, int bits, int group_size,
+                           qmm_stream stream) {
   const char* fn = "qmm_moe_gate_up_swiglu";
   clear_error();
   const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
@@ -446,6 +467,7 @@ int qmm_moe_gate_up_swiglu(const uint32_t* w_gate, const uint16_t* s_gate, const
   CHECK_PTR(x, 16);
   CHECK_PTR(plan, 16);
   CHECK_PTR(h, 2);
+  if (int st = check_plan_size(fn, plan_bytes, t, top_k, e)) return st;
   return hip_status(qmm::launch_moe_swiglu(w_gate, s_gate, b_gate, w_up, s_up, b_up, x, plan, h, t,
                                            top_k, e, n, k, bits, group_size, wtiled, (hipStream_t)stream),
                     fn);

@@ -64,3 +64,39 @@ def assert_close(got, want, what=""):
     m = float(np.max(np.abs(got - want))) if got.size else 0.0
     assert r <= REL_L2 and m <= MAX_ABS, f"{what}: rel_l2={r:.3e} max_abs={m:.3e}"
     return r, m
+
+
+# Guard bands: an output written into the middle of a larger buffer whose
+# every byte (the output region included) starts as a sentinel.  A kernel
+# that writes past either end of its output changes a sentinel byte.
+GUARD_BYTES = 4096
+SENTINEL = 0xA5
+
+
+class Guarded:
+    """A device tensor of `shape` and `dtype` with GUARD_BYTES of sentinel
+    bytes on either side (the tensor itself starts filled with sentinels
+    too, so a kernel that leaves part of it unwritten is also caught by the
+    parity check that follows)."""
+
+    def __init__(self, shape, dtype):
+        import torch
+        self.shape = tuple(shape)
+        numel = 1
+        for d in self.shape:
+            numel *= d
+        esz = torch.empty((), dtype=dtype).element_size()
+        self.pad = GUARD_BYTES // esz
+        self.nbytes = numel * esz
+        self.buf = torch.empty(2 * self.pad + numel, dtype=dtype, device="cuda")
+        self.buf.view(torch.uint8).fill_(SENTINEL)
+        self.t = self.buf[self.pad:self.pad + numel].view(self.shape)
+
+    def intact(self) -> bool:
+        u8 = self.buf.view(-1).view(__import__("torch").uint8)
+        head = u8[:GUARD_BYTES]
+        tail = u8[GUARD_BYTES + self.nbytes:]
+        return bool((head == SENTINEL).all()) and bool((tail == SENTINEL).all())
+
+    def check(self, what=""):
+        assert self.intact(), f"{what}: a write landed outside the output's {self.shape} region"

@@ -107,12 +107,46 @@ def test_route_errors(L):
     expect(L.qmm_moe_route(A + 2, 512, 8, 128, A, need, None), INV, "expert_ids is not 4-byte aligned")
     expect(L.qmm_moe_route(A, 512, 8, 0, A, need, None), INV, "e=0")
     assert L.qmm_moe_route(A, 0, 8, 128, None, 0, None) == 0            # no tokens: no-op
-    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 0, None, A, 512, 8, 128, 768, 2048, 4, 64, None),
+    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 0, None, need, A, 512, 8, 128, 768, 2048, 4, 64, None),
            INV, "null pointer plan")
-    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 3, A, A, 512, 8, 128, 768, 2048, 4, 64, None),
+    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 3, A, need, A, 512, 8, 128, 768, 2048, 4, 64, None),
            INV, "a_row_per_pair")
-    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 0, A, A, 512, 8, 128, 768, 2048, 7, 64, None),
+    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 0, A, need, A, 512, 8, 128, 768, 2048, 7, 64, None),
            UNS, "bits=7")
+    # a plan buffer smaller than the routing plan for these counts is refused
+    # on the host (a plan for other counts of the same size is caught on the
+    # device, where the output becomes NaN)
+    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 0, A, need - 1, A, 512, 8, 128, 768, 2048, 4, 64, None),
+           WSP, "routing plan for t=512")
+    expect(L.qmm_moe_gate_up_swiglu(A, A, A, A, A, A, A, A, need - 1, A, 512, 8, 128, 768, 2048, 4, 64, None),
+           WSP, "routing plan for t=512")
+    small = L.qmm_moe_route_size(256, 8, 128)
+    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 0, A, small, A, 512, 8, 128, 768, 2048, 4, 64, None),
+           WSP, "plan of")
+
+
+def test_route_size_counts_out_of_range_bucket(L):
+    """The plan has an 8-word header, one word per pair and three per row
+    tile; the row-tile bound counts the E valid buckets plus one for pairs
+    whose expert id is out of range (every tile holds at least one pair, so
+    never more tiles than pairs)."""
+    for t, top_k, e in ((512, 8, 128), (2048, 8, 128), (1, 1, 1), (3, 2, 1000), (5, 8, 4)):
+        pairs = t * top_k
+        tiles = min((pairs + 31) // 32 + e + 1, pairs)
+        want = -(-(8 + pairs + 3 * tiles) * 4 // 256) * 256
+        assert L.qmm_moe_route_size(t, top_k, e) == want, (t, top_k, e)
+        assert L.qmm_qgemm_grouped_workspace_size(t, top_k, e, 768, 2048, 4, 64) == want
+
+
+def test_workspace_size_ignores_layout_flag(L):
+    """The split-k workspace does not depend on the weight layout: the size
+    query gives the same answer with QMM_WEIGHTS_TILED on the bits."""
+    tiled = _lib.QMM_WEIGHTS_TILED
+    for (m, n, k) in ((128, 2560, 9728), (64, 512, 4096), (2048, 9728, 2560), (1, 64, 64)):
+        for bits in (2, 3, 4, 5, 6, 8, 16):
+            plain = L.qmm_qgemm_workspace_size(m, n, k, bits, 64)
+            assert L.qmm_qgemm_workspace_size(m, n, k, bits | tiled, 64) == plain, (m, n, k, bits)
+    assert L.qmm_qgemm_workspace_size(128, 2560, 9728, 4, 64) > 0
 
 
 def test_convert_bf16_errors(L):
@@ -326,9 +360,10 @@ def test_repack_tiled_errors_and_plan_flag(L):
     expect(L.qmm_qgemm(A, A, A, A, A, 8, 200, 128, 4 | tiled, 64, A, 1 << 20, None), INV, "multiple of 32")
     expect(L.qmm_qgemm_grouped(A, A, A, A, 0, A, A, 8, 2, 4, 200, 128, 4 | tiled, 64, A, 1 << 20, None),
            INV, "multiple of 32")
-    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 0, A, A, 8, 2, 4, 200, 128, 4 | tiled, 64, None),
+    expect(L.qmm_qgemm_grouped_routed(A, A, A, A, 0, A, 1 << 20, A, 8, 2, 4, 200, 128, 4 | tiled, 64, None),
            INV, "multiple of 32")
-    expect(L.qmm_moe_gate_up_swiglu(A, A, A, A, A, A, A, A, A, 8, 2, 4, 200, 128, 4 | tiled, 64, None),
+    expect(L.qmm_moe_gate_up_swiglu(A, A, A, A, A, A, A, A, 1 << 20, A, 8, 2, 4, 200, 128, 4 | tiled, 64,
+                                    None),
            INV, "multiple of 32")
     # entry points that read row-major weights only refuse the flag
     expect(L.qmm_qgemv(A, A, A, A, A, 64, 128, 4 | tiled, 64, None), UNS, "bits")
@@ -341,6 +376,25 @@ def test_batched_gemm_plan_group_sizes(L):
     for gs in (32, 64, 128):
         hdr, _ = gemm_batch_plan(L, [(2048, 2560, 9728)], env="256,2,4", gs=gs)
         assert hdr["gs"] == gs and hdr["sbq"] == (1 if gs == 64 else 0), (gs, hdr)
+
+
+def test_batched_gemm_plan_sbq_needs_aligned_scales(L):
+    """Quad scale loads are 8-byte loads: a plan whose scales or biases are
+    only 2- or 4-byte aligned takes the per-group path (sbq = 0)."""
+    for s_ptr, b_ptr, want in ((A, A, 1), (A + 2, A, 0), (A, A + 4, 0), (A + 8, A + 16, 1)):
+        probs = (GemmProblem * 2)()
+        probs[0] = GemmProblem(A, A, A, A, A, 2048, 2560, 9728)
+        probs[1] = GemmProblem(A, s_ptr, b_ptr, A, A, 2048, 2560, 9728)
+        need, ws = C.c_size_t(0), C.c_size_t(0)
+        os.environ["QMM_GEMM_FORCE"] = "128,2,1"
+        try:
+            assert L.qmm_qgemm_batched_plan(probs, 2, 4, 64, None, 0, C.byref(need), C.byref(ws)) == WSP
+            buf = (C.c_uint8 * need.value)()
+            assert L.qmm_qgemm_batched_plan(probs, 2, 4, 64, buf, need.value, C.byref(need),
+                                            C.byref(ws)) == 0
+        finally:
+            os.environ.pop("QMM_GEMM_FORCE", None)
+        assert C.cast(buf, C.POINTER(C.c_int32))[6] == want, (s_ptr, b_ptr)
 
 
 def test_batched_gemm_plan_force_and_errors(L):

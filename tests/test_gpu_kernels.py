@@ -318,6 +318,74 @@ def test_gemm_tiled_weights(bits, force, monkeypatch):
     assert torch.equal(y0, y1), force
 
 
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("gs", [32, 64, 128])
+def test_gemm_tiled_every_format(bits, gs, monkeypatch):
+    """Tile-interleaved weights for every width and scale-group size (the
+    6-bit 8-byte and 8-bit 32-byte half-group loads, and the scale index of
+    groups of 32 and 128 under the tiled group stride): qmm_qgemm and a
+    batched plan over the repacked words are bit-identical to the row-major
+    calls with the same tile and split, and within tolerance of the oracle."""
+    m, n, k = 150, 224, 1024
+    w32, _, words, s16, b16 = quantized_gs((966, bits, gs), n, k, bits, gs)
+    x = synth.draw_act((966, bits, gs, 1), m, k)
+    want = oracle.qmatmul_f64(words, s16, b16, x, bits, gs)
+    W, S, B, X = dev(words), dev(s16), dev(b16), dev(x)
+    Wt = qmm.repack_tiled(W, bits)
+    for force in ("128,2,1", "64,1,4", "256,2,2", "32,2,1"):
+        say("gemm tiled format", bits, gs, force)
+        monkeypatch.setenv("QMM_GEMM_FORCE", force)
+        y0 = qmm.qgemm(W, S, B, X, bits, group_size=gs)
+        y1 = qmm.qgemm(Wt, S, B, X, bits, group_size=gs, tiled=True)
+        yb0 = torch.full((m, n), float("nan"), device="cuda")
+        yb1 = torch.full((m, n), float("nan"), device="cuda")
+        p0 = qmm.qgemm_batched_plan([(W, S, B, X, yb0)], bits, group_size=gs)
+        p1 = qmm.qgemm_batched_plan([(Wt, S, B, X, yb1)], bits, group_size=gs, tiled=True)
+        monkeypatch.delenv("QMM_GEMM_FORCE")
+        qmm.qgemm_batched(p0)
+        qmm.qgemm_batched(p1)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1), f"qgemm tiled differs: bits={bits} gs={gs} {force}"
+        assert torch.equal(yb0, yb1), f"batched tiled differs: bits={bits} gs={gs} {force}"
+        assert_close(host(y1), want, f"qgemm tiled bits={bits} gs={gs} {force}")
+        assert_close(host(yb1), want, f"batched tiled bits={bits} gs={gs} {force}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_unaligned_scales_take_per_group_path(bits, monkeypatch):
+    """Scales and biases that are 2-byte but not 8-byte aligned (a slice at
+    an odd fp16 offset) make the GEMMs load the scales group by group: the
+    plan records sbq = 0 and the products equal the aligned run bit for bit."""
+    say("gemm unaligned scales", bits)
+    m, n, k = 200, 256, 2048
+    _, _, words, s16, b16 = quantized((967, bits), n, k, bits)
+    x = dev(synth.draw_act((967, bits, 1), m, k))
+    W = dev(words)
+    S, B = dev(s16), dev(b16)
+    flat_s = torch.empty(S.numel() + 1, dtype=S.dtype, device="cuda")
+    flat_b = torch.empty(B.numel() + 3, dtype=B.dtype, device="cuda")
+    Su = flat_s[1:].view(S.shape)
+    Bu = flat_b[3:].view(B.shape)
+    Su.copy_(S)
+    Bu.copy_(B)
+    assert Su.data_ptr() % 8 and Bu.data_ptr() % 8
+    y0 = qmm.qgemm(W, S, B, x, bits)
+    y1 = qmm.qgemm(W, Su, Bu, x, bits)
+    ya = torch.empty((m, n), device="cuda")
+    yu = torch.empty((m, n), device="cuda")
+    monkeypatch.setenv("QMM_GEMM_FORCE", "128,2,1")
+    pa = qmm.qgemm_batched_plan([(W, S, B, x, ya)], bits)
+    pu = qmm.qgemm_batched_plan([(W, Su, Bu, x, yu)], bits)
+    monkeypatch.delenv("QMM_GEMM_FORCE")
+    assert pa.header["sbq"] == 1 and pu.header["sbq"] == 0
+    qmm.qgemm_batched(pa)
+    qmm.qgemm_batched(pu)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    assert torch.equal(ya, yu)
+    assert_close(host(y1), oracle.qmatmul_f64(words, s16, b16, host(x), bits), "unaligned scales")
+
+
 def test_gemm_rows_equal_gemv_and_deterministic():
     say("gemm rows")
     m, n, k, bits = 70, 520, 1024, 4
@@ -587,7 +655,8 @@ def test_fused_qkv_gemv_equals_separate():
 def test_routed_grouped_equals_grouped():
     """One routing plan serves gate, up and down (and any width or group
     size); results are bit-identical to the self-bucketing call.  A plan
-    built for other expert counts is refused on the device (y untouched)."""
+    built for other expert counts is refused on the device: the whole
+    output becomes NaN."""
     t, top_k, e, hidden, inter = 96, 4, 16, 384, 256
     r = np.random.default_rng(946)
     ids = np.ascontiguousarray(synth.topk_ids(r.standard_normal((t, e)), top_k), dtype=np.int32)
@@ -611,8 +680,52 @@ def test_routed_grouped_equals_grouped():
     y = torch.full((t * top_k, inter), 7.0, device="cuda")
     words, s_, b_, *_ = grouped_inputs((947, 4, 0, 0), e, inter, hidden, 4, t, top_k, ids=ids)
     qmm.qgemm_grouped(dev(words), dev(s_), dev(b_), x, I, 4, False, y=y, plan=other)
+    hh = torch.zeros((t * top_k, inter), dtype=torch.float16, device="cuda")
+    qmm.moe_gate_up_swiglu((dev(words), dev(s_), dev(b_)), (dev(words), dev(s_), dev(b_)), x, I, other, 4, h=hh)
     torch.cuda.synchronize()
-    assert bool((y == 7.0).all())
+    assert bool(torch.isnan(y).all()), "grouped output over a foreign plan must be all NaN"
+    assert bool(torch.isnan(hh).all()), "SwiGLU output over a foreign plan must be all NaN"
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_moe_out_of_range_ids_nan_and_counted(bits):
+    """Pairs whose expert id lies outside [0, E) (here -1, E, E + 100 and a
+    large negative id) are not computed: their output rows are NaN in the
+    self-bucketing, routed and fused SwiGLU products, every other row matches
+    the oracle, and the plan header (byte offset 16) counts them."""
+    say("moe out-of-range ids", bits)
+    t, top_k, e, hidden, inter = 40, 4, 8, 128, 160
+    r = np.random.default_rng([948, bits])
+    ids = np.ascontiguousarray(synth.topk_ids(r.standard_normal((t, e)), top_k), dtype=np.int32)
+    flat = ids.reshape(-1)
+    bad_at = [0, 5, 6, 17, 63, t * top_k - 1]
+    for i, v in zip(bad_at, (-1, e, e + 100, -(1 << 30), e, -1)):
+        flat[i] = v
+    bad = np.zeros(t * top_k, dtype=bool)
+    bad[bad_at] = True
+    ok_ids = np.where(bad.reshape(ids.shape), 0, ids)   # oracle rows for the valid pairs
+    x = synth.draw_act((948, bits, 1), t, hidden)
+    gate, _ = _expert_set((948, bits, 2), e, inter, hidden, bits)
+    up, _ = _expert_set((948, bits, 3), e, inter, hidden, bits)
+    I = dev(ids)
+    ws = torch.empty(qmm.qgemm_grouped_workspace_size(t, top_k, e, inter, hidden, bits), dtype=torch.uint8,
+                     device="cuda")
+    y0 = qmm.qgemm_grouped(*_to_dev(gate), dev(x), I, bits, False, workspace=ws)
+    plan = qmm.moe_route(I, e)
+    y1 = qmm.qgemm_grouped(*_to_dev(gate), dev(x), I, bits, False, plan=plan)
+    h = qmm.moe_gate_up_swiglu(_to_dev(gate), _to_dev(up), dev(x), I, plan, bits)
+    torch.cuda.synchronize()
+    assert qmm.moe_plan_dropped(ws) == len(bad_at)
+    assert qmm.moe_plan_dropped(plan) == len(bad_at)
+    want = oracle.grouped_f64(*gate, x, ok_ids, bits, False)
+    hw = oracle.moe_swiglu_f64(gate, up, x, ok_ids, bits)
+    for name, got in (("self-bucketing", host(y0)), ("routed", host(y1)),
+                      ("swiglu", host(h).astype(np.float64))):
+        assert np.isnan(got[bad]).all(), f"{name}: rows of out-of-range pairs must be NaN"
+        assert not np.isnan(got[~bad]).any(), f"{name}: valid rows must be finite"
+        assert_close(got[~bad], (hw if name == "swiglu" else want)[~bad], f"{name} valid rows")
+    assert torch.equal(torch.nan_to_num(y0, nan=-7.0), torch.nan_to_num(y1, nan=-7.0)), \
+        "routed differs from self-bucketing"
 
 
 # ---------------------------------------------------- MoE FFN block (fused) --
