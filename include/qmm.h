@@ -229,6 +229,28 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
                       int group_size, void* workspace, size_t workspace_bytes,
                       qmm_stream stream);
 
+/* Allocation-free grouped product, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): qmm_qgemm_grouped with the same arguments minus the
+ * workspace.  Its bucket lists and tile list live in a static device array
+ * of QMM_GROUPED_SCRATCH_BYTES (1 MiB) that each GPU holds from the first
+ * call on it until the process ends; the call allocates nothing, frees
+ * nothing and calls no allocating library routine.  The scratch serves
+ * every (t, top_k, e) whose qmm_qgemm_grouped_workspace_size is at most
+ * 1 MiB (up to about 239,000 pairs, e.g. 29,900 tokens at top-8, with
+ * E = 128); larger problems are refused with QMM_ERR_WORKSPACE before any
+ * launch.  Every call on one GPU shares that GPU's array, so calls that
+ * overlap on one GPU (several streams, several host threads) race and must
+ * be serialized by the caller; the array is never cleared (each call
+ * rewrites every word it reads).  Pairs with an out-of-range expert id get
+ * NaN rows as in qmm_qgemm_grouped; their count stays in the scratch and is
+ * not reported.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+#define QMM_GROUPED_SCRATCH_BYTES (1u << 20)
+int qmm_qgemm_grouped_noalloc(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+                              const uint16_t* a, int a_row_per_pair, const int32_t* expert_ids,
+                              float* y, int t, int top_k, int e, int n, int k, int bits,
+                              int group_size, qmm_stream stream);
+
 /* Routing plan shared by the grouped products of one MoE layer (BaseRT,
  * abstract and Fig. 1: MoE prefill; §3 amortized dispatch).  Gate, up and
  * down read the same expert ids, so the token-to-expert bucketing (the first

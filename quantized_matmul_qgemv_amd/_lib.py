@@ -20,6 +20,7 @@ QMM_ERR_UNSUPPORTED = 2
 QMM_ERR_WORKSPACE = 3
 QMM_ERR_HIP = 4
 QMM_WEIGHTS_TILED = 0x100  # bits flag: weights from qmm_repack_tiled
+QMM_GROUPED_SCRATCH_BYTES = 1 << 20  # static scratch of qmm_qgemm_grouped_noalloc
 
 STATUS_NAMES = {0: "QMM_OK", 1: "QMM_ERR_INVALID_ARG", 2: "QMM_ERR_UNSUPPORTED",
                 3: "QMM_ERR_WORKSPACE", 4: "QMM_ERR_HIP"}
@@ -57,6 +58,7 @@ SIGNATURES = {
     "qmm_qgemm_batched": (I, [P, P, P, SZ, P]),
     "qmm_qgemm_grouped_workspace_size": (SZ, [I, I, I, I, I, I, I]),
     "qmm_qgemm_grouped": (I, [P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, SZ, P]),
+    "qmm_qgemm_grouped_noalloc": (I, [P, P, P, P, I, P, P, I, I, I, I, I, I, I, P]),
     "qmm_moe_route_size": (SZ, [I, I, I]),
     "qmm_moe_route": (I, [P, I, I, I, P, SZ, P]),
     "qmm_qgemm_grouped_routed": (I, [P, P, P, P, I, P, SZ, P, I, I, I, I, I, I, I, P]),

@@ -212,6 +212,24 @@ def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: b
     return y
 
 
+def qgemm_grouped_noalloc(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: bool, y,
+                          group_size: int = GROUP, stream=None, tiled: bool = False):
+    """qmm_qgemm_grouped_noalloc: the grouped product into a caller-given y
+    [T*top_k, n] with the library's static device scratch instead of a
+    workspace (nothing is allocated; calls on one GPU must not overlap)."""
+    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0)
+    e, n = w.shape[0], w.shape[1]
+    t, top_k = expert_ids.shape
+    k = a.shape[1]
+    check(lib().qmm_qgemm_grouped_noalloc(_dev(w, "w", _W), _sb(scales, "scales", bits),
+                                          _sb(biases, "biases", bits), _dev(a, "a", _X),
+                                          int(bool(a_row_per_pair)),
+                                          _dev(expert_ids, "expert_ids", (torch.int32,)),
+                                          _dev(y, "y", _Y), t, top_k, e, n, k, flag_bits, group_size,
+                                          _stream(stream)))
+    return y
+
+
 def moe_route_size(t: int, top_k: int, e: int) -> int:
     """Bytes of the routing plan qmm_moe_route writes for (t, top_k, e)."""
     return lib().qmm_moe_route_size(t, top_k, e)

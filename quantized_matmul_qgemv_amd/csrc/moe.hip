@@ -21,6 +21,9 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "qgemm_core.h"
 #include "qmm_internal.h"
 
@@ -358,6 +361,44 @@ static void moe_tile(int pairs, int experts, int* bm_out, int* nb_out) {
   }
   *bm_out = bm;
   *nb_out = nb;
+}
+
+// ---------------------------------------------------------------------------
+// Static device scratch of the allocation-free grouped GEMM
+// (qmm_qgemm_grouped_noalloc): the bucket lists and tile list that
+// qmm_qgemm_grouped keeps in its caller's workspace live here instead.  Each
+// GPU the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: its
+// device address is looked up once per device with hipGetSymbolAddress and
+// only that address is passed to kernels.  Every call on one GPU shares the
+// array, so calls that overlap on one GPU race; nothing in it needs to start
+// at zero (the bucketing writes every word the GEMM reads).
+static __device__ __align__(256) unsigned char scratch[kGroupedScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t grouped_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_moe_route(const int32_t* ids, int t, int top_k, int e, void* plan, hipStream_t st) {

@@ -379,6 +379,46 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
   return hip_status(qmm::launch_qgemm_grouped(ga, bits, workspace, true, (hipStream_t)stream), fn);
 }
 
+int qmm_qgemm_grouped_noalloc(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
+                              const uint16_t* a, int a_row_per_pair, const int32_t* expert_ids,
+                              float* y, int t, int top_k, int e, int n, int k, int bits,
+                              int group_size, qmm_stream stream) {
+  const char* fn = "qmm_qgemm_grouped_noalloc";
+  clear_error();
+  const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
+  bits &= ~QMM_WEIGHTS_TILED;
+  if (int st = check_format(fn, bits, group_size, true)) return st;
+  if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
+  if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
+  if (e < 1 || e > kMaxExperts)
+    return fail(QMM_ERR_INVALID_ARG, "%s: e=%d must be in [1, %d]", fn, e, kMaxExperts);
+  if (a_row_per_pair != 0 && a_row_per_pair != 1)
+    return fail(QMM_ERR_INVALID_ARG, "%s: a_row_per_pair must be 0 or 1", fn);
+  if (int st = check_nk(fn, n, k, group_size)) return st;
+  if (wtiled && n % 32 != 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32 for tile-interleaved weights", fn, n);
+  if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
+  if (t == 0) return QMM_OK;
+  CHECK_PTR(w, 16);
+  if (bits != 16) {
+    CHECK_PTR(scales, 2);
+    CHECK_PTR(biases, 2);
+  }
+  CHECK_PTR(a, 16);
+  CHECK_PTR(expert_ids, 4);
+  CHECK_PTR(y, 4);
+  const size_t need = qmm::grouped_workspace_bytes(t, top_k, e, n);
+  if (need > qmm::kGroupedScratchBytes)
+    return fail(QMM_ERR_WORKSPACE,
+                "%s: t=%d top_k=%d e=%d needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use qmm_qgemm_grouped with a workspace)",
+                fn, t, top_k, e, need, qmm::kGroupedScratchBytes);
+  void* scratch = nullptr;
+  if (int st = hip_status(qmm::grouped_scratch(&scratch), fn)) return st;
+  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, expert_ids, y, t, top_k, e, n, k, group_size, wtiled};
+  return hip_status(qmm::launch_qgemm_grouped(ga, bits, scratch, true, (hipStream_t)stream), fn);
+}
+
 size_t qmm_moe_route_size(int t, int top_k, int e) {
   if (t < 0 || top_k < 1 || e < 1 || e > kMaxExperts) return 0;
   if ((long)t * top_k > 0x7FFFFFFFL / 4) return 0;

@@ -151,6 +151,10 @@ struct GroupedArgs {
   int wtiled;  // weights in the tile-interleaved layout (qmm_repack_tiled)
 };
 size_t grouped_workspace_bytes(int t, int top_k, int e, int n);
+// Static device scratch of the allocation-free grouped GEMM: its size, and
+// its device address on the current device (looked up once per device).
+constexpr size_t kGroupedScratchBytes = 1u << 20;
+hipError_t grouped_scratch(void** ptr);
 // bucket = false: ws already holds a routing plan for these ids (launch_moe_route).
 hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, bool bucket, hipStream_t st);
 hipError_t launch_moe_route(const int32_t* ids, int t, int top_k, int e, void* plan, hipStream_t st);

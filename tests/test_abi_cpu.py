@@ -125,6 +125,28 @@ def test_route_errors(L):
            WSP, "plan of")
 
 
+def test_grouped_noalloc_errors(L):
+    """The allocation-free grouped call validates like qmm_qgemm_grouped and
+    refuses, before any HIP call, a problem whose bucket lists exceed its
+    1 MiB static scratch."""
+    assert _lib.QMM_GROUPED_SCRATCH_BYTES == 1 << 20
+    ok = L.qmm_qgemm_grouped_workspace_size(29000, 8, 128, 768, 2048, 4, 64)
+    assert ok <= _lib.QMM_GROUPED_SCRATCH_BYTES
+    big = L.qmm_qgemm_grouped_workspace_size(40000, 8, 128, 768, 2048, 4, 64)
+    assert big > _lib.QMM_GROUPED_SCRATCH_BYTES
+    expect(L.qmm_qgemm_grouped_noalloc(A, A, A, A, 0, A, A, 40000, 8, 128, 768, 2048, 4, 64, None),
+           WSP, "static scratch holds 1048576")
+    expect(L.qmm_qgemm_grouped_noalloc(A, A, A, A, 0, None, A, 512, 8, 128, 768, 2048, 4, 64, None),
+           INV, "null pointer expert_ids")
+    expect(L.qmm_qgemm_grouped_noalloc(A, A, A, A, 2, A, A, 512, 8, 128, 768, 2048, 4, 64, None),
+           INV, "a_row_per_pair")
+    expect(L.qmm_qgemm_grouped_noalloc(A, A, A, A, 0, A, A, 512, 8, 128, 768, 2048, 7, 64, None),
+           UNS, "bits=7")
+    expect(L.qmm_qgemm_grouped_noalloc(A, A, A, A, 0, A, A, 8, 2, 4, 200, 128, 4 | _lib.QMM_WEIGHTS_TILED,
+                                       64, None), INV, "multiple of 32")
+    assert L.qmm_qgemm_grouped_noalloc(A, A, A, A, 0, A, A, 0, 8, 128, 768, 2048, 4, 64, None) == 0
+
+
 def test_route_size_counts_out_of_range_bucket(L):
     """The plan has an 8-word header, one word per pair and three per row
     tile; the row-tile bound counts the E valid buckets plus one for pairs
