@@ -52,6 +52,7 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+LLC_EVICT_BYTES = 320 << 20     # more than the 256 MB last-level cache (MALL)
 FP16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 matrix cores (256 CU x 2.4 GHz x 4096 flop/clk)
 
 METRIC = "Q4 decode GEMV HBM GB/s (% peak) + prefill qGEMM TFLOP/s (% MFMA peak)"
@@ -139,6 +140,30 @@ def time_launches(torch, launch, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps, wall
 
 
+def time_steps(torch, step, steps, warmup, stream):
+    """Warm up, then time each of `steps` calls between its own pair of HIP
+    events on the launch stream (a step here is a whole prefill or MoE pass,
+    milliseconds long, so per-step events cost nothing measurable).  Returns
+    the per-step times in ms."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(warmup + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def step_stats(ms):
+    a = np.asarray(ms, dtype=np.float64)
+    return {"ms_per_step_median": round(float(np.median(a)), 4), "ms_per_step_min": round(float(a.min()), 4),
+            "ms_per_step_mean": round(float(a.mean()), 4), "steps_timed": int(a.size)}
+
+
 def bench_decode(torch, qmm, wl, steps, warmup, copies=2):
     sets = prepare_dense(torch, qmm, wl, copies)
     plans = [qmm.qgemv_batched_plan([p[:5] for p in s], wl.bits) for s in sets]
@@ -168,7 +193,9 @@ def bench_decode_formats(torch, qmm, wl, bits_list=(2, 3, 5, 6, 16), steps=20, w
 def bench_gemm_formats(torch, qmm, m=2048, n=9728, k=2560, bits_list=(2, 3, 4, 5, 6, 8, 16),
                        steps=20, warmup=3):
     """One M x N x K prefill GEMM (the gate projection at M = 2048) per
-    weight width, TFLOP/s against the fp16 matrix-core peak."""
+    weight width, TFLOP/s against the fp16 matrix-core peak.  Consecutive
+    calls rotate over enough device copies of the weights (more than the
+    256 MB last-level cache holds) that no call finds its weights cached."""
     out = {}
     wf = torch.from_numpy(synth.draw_weight((9, m, n, k), n, k)).cuda()
     x = torch.from_numpy(synth.draw_act((9, m, n, k + 1), m, k)).cuda()
@@ -177,13 +204,19 @@ def bench_gemm_formats(torch, qmm, m=2048, n=9728, k=2560, bits_list=(2, 3, 4, 5
     for bits in bits_list:
         wq = (wf.half().view(torch.int32), None, None) if bits == 16 else qmm.quantize(wf, bits)
         wq = (qmm.repack_tiled(wq[0], bits), wq[1], wq[2])  # tile-interleaved copy, once
+        wbytes = sum(t.numel() * t.element_size() for t in wq if t is not None)
+        copies = max(2, -(-LLC_EVICT_BYTES // wbytes))
+        sets = [wq] + [tuple(None if t is None else t.clone() for t in wq) for _ in range(copies - 1)]
         ws = torch.empty(max(qmm.qgemm_workspace_size(m, n, k, bits), 16), dtype=torch.uint8, device="cuda")
-        ms_call, _ = time_launches(torch, lambda i: qmm.qgemm(*wq, x, bits, y=y, workspace=ws, tiled=True),
-                                   steps, warmup, stream)
+        ms_call, _ = time_launches(
+            torch, lambda i: qmm.qgemm(*sets[i % copies], x, bits, y=y, workspace=ws, tiled=True),
+            steps, warmup, stream)
         tfl = 2.0 * m * n * k / (ms_call * 1e-3) / 1e12
         out["f16" if bits == 16 else f"q{bits}"] = {"ms_per_call": round(ms_call, 4), "tflops": round(tfl, 1),
-                           "frac_of_fp16_peak": round(tfl / FP16_MFMA_PEAK_TFLOPS, 4)}
-        del wq, ws
+                           "frac_of_fp16_peak": round(tfl / FP16_MFMA_PEAK_TFLOPS, 4),
+                           "weight_copies_rotated": copies}
+        del wq, ws, sets
+        torch.cuda.empty_cache()
     del wf, x, y
     torch.cuda.empty_cache()
     return out
@@ -287,30 +320,59 @@ PREFILL_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 PREFILL_WEIGHTS = "tile-interleaved copy (qmm_repack_tiled, once at load)"
 
 
-def bench_prefill(torch, qmm, ms, steps=3, warmup=1, batched=True):
-    wl = synth.QWEN3_4B_Q4_PREFILL
-    out = {}
+def prefill_layers(torch, qmm, wl, batched=True):
+    """Per-layer weights of the prefill workload: each distinct projection
+    quantized once on the GPU, then device copies for every layer (36 x 57 MB
+    at 4 bits, far more than the last-level cache).  Batched launches read
+    the tile-interleaved copy (repacked once, as a model would at load time);
+    the per-projection path reads row-major words."""
     base = {}
     for i, p in enumerate(wl.projs):
         wf = torch.from_numpy(synth.draw_weight((wl.wid, 0, i, synth.STREAM_W), p.n, p.k)).cuda()
         words, s_, b_ = qmm.quantize(wf, wl.bits)
-        # the batched launches read the tile-interleaved copy (repacked once,
-        # as a model would at load time); the per-projection path row-major
         base[i] = (qmm.repack_tiled(words, wl.bits), s_, b_) if batched else (words, s_, b_)
         del wf, words
     layers = [[tuple(t.clone() for t in base[i]) if layer else base[i]
                for i in range(len(wl.projs))] for layer in range(wl.layers)]
     torch.cuda.synchronize()
+    return layers
+
+
+def prefill_io(torch, wl, m):
+    xs = [torch.from_numpy(synth.draw_act((wl.wid, m, i, synth.STREAM_X), m, p.k)).cuda()
+          for i, p in enumerate(wl.projs)]
+    ys = [torch.empty((m, p.n), dtype=torch.float32, device="cuda") for p in wl.projs]
+    return xs, ys
+
+
+def prefill_plans(qmm, wl, layers, xs, ys, groups=PREFILL_GROUPS):
+    names = [p.name for p in wl.projs]
+    return [[qmm.qgemm_batched_plan(
+        [(*L[names.index(nm)], xs[names.index(nm)], ys[names.index(nm)]) for nm in grp],
+        wl.bits, tiled=True) for grp in groups] for L in layers]
+
+
+def prefill_work(wl, m):
+    """Algorithmic bytes (x, packed codes, fp16 scales and biases, y, each
+    once) and flops of one prefill step (all layers) at m rows."""
+    per_layer = sum(m * p.k * 2 + p.n * p.k * wl.bits // 8 + 4 * p.n * (p.k // 64) + 4 * m * p.n
+                    for p in wl.projs)
+    flops = 2.0 * m * sum(p.n * p.k for p in wl.projs) * wl.layers
+    return per_layer * wl.layers, flops
+
+
+def bench_prefill(torch, qmm, ms, steps=20, warmup=3, batched=True):
+    """Each step: 36 layers x 4 batched launches (q+k+v, o, gate+up, down).
+    Per-step HIP events; median and minimum over `steps` timed steps.
+    Roofline per M: min(fp16 matrix-core peak, intensity x HBM bandwidth)."""
+    wl = synth.QWEN3_4B_Q4_PREFILL
+    out = {}
+    layers = prefill_layers(torch, qmm, wl, batched)
     stream = torch.cuda.current_stream()
     for m in ms:
-        xs = [torch.from_numpy(synth.draw_act((wl.wid, m, i, synth.STREAM_X), m, p.k)).cuda()
-              for i, p in enumerate(wl.projs)]
-        ys = [torch.empty((m, p.n), dtype=torch.float32, device="cuda") for p in wl.projs]
+        xs, ys = prefill_io(torch, wl, m)
         if batched:
-            names = [p.name for p in wl.projs]
-            plans = [[qmm.qgemm_batched_plan(
-                [(*L[names.index(nm)], xs[names.index(nm)], ys[names.index(nm)]) for nm in grp],
-                wl.bits, tiled=True) for grp in PREFILL_GROUPS] for L in layers]
+            plans = prefill_plans(qmm, wl, layers, xs, ys)
 
             def step(_):
                 for lp in plans:
@@ -321,45 +383,73 @@ def bench_prefill(torch, qmm, ms, steps=3, warmup=1, batched=True):
                 for L in layers:
                     for i, (words, s, b) in enumerate(L):
                         qmm.qgemm(words, s, b, xs[i], wl.bits, y=ys[i])
-        ms_step, _ = time_launches(torch, step, steps, warmup, stream)
-        flops = 2.0 * m * sum(p.n * p.k for p in wl.projs) * wl.layers
-        tfl = flops / (ms_step * 1e-3) / 1e12
-        out[str(m)] = {"ms_per_step": round(ms_step, 3), "tflops": round(tfl, 1),
-                       "frac_of_fp16_peak": round(tfl / FP16_MFMA_PEAK_TFLOPS, 4)}
+        st = step_stats(time_steps(torch, step, steps, warmup, stream))
+        nbytes, flops = prefill_work(wl, m)
+        roof_s = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (FP16_MFMA_PEAK_TFLOPS * 1e12))
+        roof_tfl = flops / roof_s / 1e12
+        tfl = flops / (st["ms_per_step_median"] * 1e-3) / 1e12
+        out[str(m)] = {**st, "tflops": round(tfl, 1),
+                       "tflops_at_min": round(flops / (st["ms_per_step_min"] * 1e-3) / 1e12, 1),
+                       "frac_of_fp16_peak": round(tfl / FP16_MFMA_PEAK_TFLOPS, 4),
+                       "bytes_per_step": int(nbytes), "flops_per_step": flops,
+                       "roofline_tflops": round(roof_tfl, 1),
+                       "roofline_bound": "mfma" if roof_tfl >= FP16_MFMA_PEAK_TFLOPS - 1e-6 else "hbm",
+                       "frac_of_roofline": round(tfl / roof_tfl, 4)}
         if batched:
             out[str(m)]["tiles"] = {"+".join(g): "{bm}x{n}/S{splits}".format(n=pl.header["nb"] * 128, **pl.header)
                                     for g, pl in zip(PREFILL_GROUPS, plans[0])}
             del plans
         del xs, ys
-    del layers, base
+    del layers
     torch.cuda.synchronize()
     return out
 
 
-def bench_moe(torch, qmm, steps=10, warmup=2):
-    wl = synth.QWEN3_30B_A3B_Q4_MOE
-    out = {}
-    weights = []
+def prefill_roofline_block(by_m):
+    """The prefill half of the metric: achieved TFLOP/s (median step) against
+    min(fp16 matrix-core peak, arithmetic intensity x HBM bandwidth) per M."""
+    return {"unit": "TFLOP/s", "peak": FP16_MFMA_PEAK_TFLOPS, "hbm_peak_gbs": HBM_PEAK_GBS,
+            "kernel": "qgemm_batched_kernel (4 launches per layer)",
+            "by_m": {m: {"achieved": v["tflops"], "roofline": v["roofline_tflops"], "bound": v["roofline_bound"],
+                         "frac": v["frac_of_roofline"], "frac_of_peak": v["frac_of_fp16_peak"],
+                         "ms_per_step_median": v["ms_per_step_median"], "ms_per_step_min": v["ms_per_step_min"]}
+                     for m, v in by_m.items()}}
+
+
+def moe_weights(torch, qmm, wl, copies=2):
+    """Expert weights of gate, up and down (quantized once on the GPU, then
+    repacked to the tile-interleaved layout), `copies` device copies so that
+    consecutive steps never find them in the last-level cache (340 MB each)."""
+    sets = [[] for _ in range(copies)]
     for pi, (name, k, n, per_pair) in enumerate(synth.moe_projs(wl)):
         ws, ss, bs = [], [], []
         for e in range(wl.experts):
             wf = torch.from_numpy(synth.draw_weight((wl.wid, e, pi, synth.STREAM_W), n, k)).cuda()
             w_, s_, b_ = qmm.quantize(wf, wl.bits)
             ws.append(w_); ss.append(s_); bs.append(b_)
-        # tile-interleaved copy of the stacked expert words (once, at load)
-        weights.append((qmm.repack_tiled(torch.stack(ws), wl.bits), torch.stack(ss), torch.stack(bs),
-                        n, k, per_pair))
+        W = qmm.repack_tiled(torch.stack(ws), wl.bits)
+        S, B = torch.stack(ss), torch.stack(bs)
         del ws, ss, bs
+        for c in range(copies):
+            sets[c].append((W, S, B, n, k, per_pair) if c == 0 else (W.clone(), S.clone(), B.clone(), n, k, per_pair))
+    torch.cuda.synchronize()
+    return sets
+
+
+def bench_moe(torch, qmm, steps=20, warmup=3, copies=2):
+    wl = synth.QWEN3_30B_A3B_Q4_MOE
+    out = {}
+    wsets = moe_weights(torch, qmm, wl, copies)
     stream = torch.cuda.current_stream()
     for m in wl.ms:
-        calls = []
+        ins = []
         step_bytes = 0
         flops = 0
-        for pi, (W, S, B, n, k, per_pair) in enumerate(weights):
+        pairs = m * wl.top_k
+        for pi, (W, S, B, n, k, per_pair) in enumerate(wsets[0]):
             a, ids, _ = synth.draw_moe_inputs(wl, m, pi)
             A = torch.from_numpy(a).cuda()
             I = torch.from_numpy(ids).cuda()
-            pairs = m * wl.top_k
             Y = torch.empty((pairs, n), dtype=torch.float32, device="cuda")
             wsz = qmm.qgemm_grouped_workspace_size(m, wl.top_k, wl.experts, n, k, wl.bits)
             WS = torch.empty(wsz, dtype=torch.uint8, device="cuda")
@@ -367,72 +457,105 @@ def bench_moe(torch, qmm, steps=10, warmup=2):
             step_bytes += used * (n * k * wl.bits // 8 + 4 * n * (k // 64)) + A.numel() * 2 \
                 + pairs * n * 4 + ids.size * 4
             flops += 2 * pairs * n * k
-            calls.append((W, S, B, A, I, per_pair, Y, WS))
-
+            ins.append((A, I, per_pair, Y, WS))
         # the three projections share the routing: bucket once per step
-        ids0 = calls[0][4]
+        ids0 = ins[0][1]
         plan = qmm.moe_route(ids0, wl.experts)
 
-        def step(_):
+        def step(i):
+            ws = wsets[i % copies]
             qmm.moe_route(ids0, wl.experts, plan=plan)
-            for (W, S, B, A, I, per_pair, Y, WS) in calls:
+            for (W, S, B, n, k, _), (A, I, per_pair, Y, WS) in zip(ws, ins):
                 qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, plan=plan, tiled=True)
 
-        def step_unshared(_):
-            for (W, S, B, A, I, per_pair, Y, WS) in calls:
+        def step_unshared(i):
+            ws = wsets[i % copies]
+            for (W, S, B, n, k, _), (A, I, per_pair, Y, WS) in zip(ws, ins):
                 qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, workspace=WS, tiled=True)
-        ms_step, _ = time_launches(torch, step, steps, warmup, stream)
-        ms_unshared, _ = time_launches(torch, step_unshared, steps, warmup, stream)
-        t = ms_step * 1e-3
+        st = step_stats(time_steps(torch, step, steps, warmup, stream))
+        st_un = step_stats(time_steps(torch, step_unshared, steps, warmup, stream))
+        t = st["ms_per_step_median"] * 1e-3
         roof = max(step_bytes / (HBM_PEAK_GBS * 1e9), flops / (FP16_MFMA_PEAK_TFLOPS * 1e12))
-        out[str(m)] = {"ms_per_step": round(ms_step, 4), "gb_per_s": round(step_bytes / t / 1e9, 1),
-                       "tflops": round(flops / t / 1e12, 2), "frac_of_roofline": round(roof / t, 4),
+        out[str(m)] = {**st, "gb_per_s": round(step_bytes / t / 1e9, 1),
+                       "tflops": round(flops / t / 1e12, 2), "bytes_per_step": int(step_bytes),
+                       "flops_per_step": int(flops), "roofline_ms": round(roof * 1e3, 4),
+                       "frac_of_roofline": round(roof / t, 4),
                        "launches": "1 routing + 3 grouped GEMMs",
-                       "ms_per_step_bucketing_each_gemm": round(ms_unshared, 4)}
+                       "ms_per_step_bucketing_each_gemm": st_un["ms_per_step_median"]}
         # the whole FFN block: routing, fused gate+up with SwiGLU (fp16 h),
         # down from h, routing-weighted combine into y [M, hidden]
-        (Wg, Sg, Bg, X, _, _, _, _), (Wu, Su, Bu, _, _, _, _, _), (Wd, Sd, Bd, _, _, _, Yd, _) = calls
-        pairs = m * wl.top_k
+        (A, _, _, _, _), _, (_, _, _, Yd, _) = ins
         H = torch.empty((pairs, wl.inter), dtype=torch.float16, device="cuda")
         logits = synth.draw_logits((wl.wid, m, 0, synth.STREAM_LOGITS), m, wl.experts)
         p_ = np.exp(logits - logits.max(axis=1, keepdims=True))
         p_ = p_ / p_.sum(axis=1, keepdims=True)
-        wts = np.take_along_axis(p_, calls[0][4].cpu().numpy().astype(np.int64), axis=1)
+        wts = np.take_along_axis(p_, ids0.cpu().numpy().astype(np.int64), axis=1)
         Wts = torch.from_numpy((wts / wts.sum(axis=1, keepdims=True)).astype(np.float32)).cuda()
         Yout = torch.empty((m, wl.hidden), dtype=torch.float32, device="cuda")
 
-        def block(_):
+        def block(i):
+            (Wg, Sg, Bg, *_), (Wu, Su, Bu, *_), (Wd, Sd, Bd, *_) = wsets[i % copies]
             qmm.moe_route(ids0, wl.experts, plan=plan)
-            qmm.moe_gate_up_swiglu((Wg, Sg, Bg), (Wu, Su, Bu), X, ids0, plan, wl.bits, h=H, tiled=True)
+            qmm.moe_gate_up_swiglu((Wg, Sg, Bg), (Wu, Su, Bu), A, ids0, plan, wl.bits, h=H, tiled=True)
             qmm.qgemm_grouped(Wd, Sd, Bd, H, ids0, wl.bits, True, y=Yd, plan=plan, tiled=True)
             qmm.moe_combine(Yd, Wts, y=Yout)
-        ms_block, _ = time_launches(torch, block, steps, warmup, stream)
-        used = np.unique(calls[0][4].cpu().numpy()).size
+        stb = step_stats(time_steps(torch, block, steps, warmup, stream))
+        used = np.unique(ids0.cpu().numpy()).size
         wbytes = sum(used * (n * k * wl.bits // 8 + 4 * n * (k // 64)) for (_, k, n, _) in synth.moe_projs(wl))
         bbytes = wbytes + m * wl.hidden * 2 + 2 * pairs * wl.inter * 2 + 2 * pairs * wl.hidden * 4 \
             + m * wl.hidden * 4 + m * wl.top_k * 8
-        tb = ms_block * 1e-3
+        tb = stb["ms_per_step_median"] * 1e-3
         broof = max(bbytes / (HBM_PEAK_GBS * 1e9), flops / (FP16_MFMA_PEAK_TFLOPS * 1e12))
         out[str(m)]["ffn_block"] = {
             "launches": "routing + fused gate/up SwiGLU + down + combine",
-            "ms_per_block": round(ms_block, 4), "bytes": int(bbytes),
-            "tflops": round(flops / tb / 1e12, 2), "frac_of_roofline": round(broof / tb, 4)}
-        del calls
-    del weights
+            "ms_per_block_median": stb["ms_per_step_median"], "ms_per_block_min": stb["ms_per_step_min"],
+            "bytes": int(bbytes), "tflops": round(flops / tb / 1e12, 2),
+            "frac_of_roofline": round(broof / tb, 4)}
+        del ins
+    del wsets
     torch.cuda.synchronize()
     return out
 
 
-def cpu_baseline(wl, budget_s=15.0):
-    """The float64 oracle (unpack -> dequantize -> matmul) on a bounded
-    sample of the decode workload: whole layers in order, then lm_head row
-    slices, until about `budget_s` seconds of oracle time."""
-    import oracle
+def host_info():
+    """Cores and CPU of the host the oracle runs on."""
     try:
         import threadpoolctl
-        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        threads = 1
+        blas = 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "nproc": len(os.sched_getaffinity(0)),
+            "blas_threads": int(blas), "cpu_model": model}
+
+
+def _oracle_gemm(oracle, wl, layer, i, p, m, rows=None):
+    """Inputs of one projection (quantized by the oracle, not timed) and the
+    timed oracle call; rows limits the output rows (a row slice)."""
+    n = p.n if rows is None else min(rows, p.n)
+    w = synth.draw_weight((wl.wid, layer, i, synth.STREAM_W), n, p.k)
+    codes, s, b = oracle.quantize(w, wl.bits)
+    words = oracle.pack(codes, wl.bits)
+    x = synth.draw_act((wl.wid, m, i, synth.STREAM_X), m, p.k)
+    t0 = time.perf_counter()
+    oracle.qmatmul_f64(words, s, b, x, wl.bits)
+    return time.perf_counter() - t0, n
+
+
+def cpu_baseline(wl, budget_s=8.0):
+    """The float64 oracle (unpack -> dequantize -> matmul, numpy: the unpack
+    and dequantize steps run on one thread, the matmul on the BLAS threads)
+    on a bounded sample of the decode workload: whole layers in order, then
+    lm_head row slices, until about `budget_s` seconds of oracle time."""
+    import oracle
     done_bytes = 0
     spent = 0.0
     items = 0
@@ -451,10 +574,177 @@ def cpu_baseline(wl, budget_s=15.0):
         spent += time.perf_counter() - t0
         done_bytes += gemv_bytes(p.n, p.k, wl.bits)
         items += 1
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+    info = host_info()
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": info["blas_threads"],
+            "kind": "oracle", **info,
             "sample": f"{items} GEMVs of the decode workload ({done_bytes / 1e6:.1f} MB algorithmic, "
                       f"{spent:.1f} s of float64 unpack+dequant+matmul; lm_head as 4096-row slices)"}
+
+
+def cpu_baseline_configs(rows=2048, experts=16):
+    """The oracle on bounded samples of the other workloads, each scaled to
+    the whole workload and labelled as such:
+      single GEMV 1x1024x1024 (timed in full, best of 3);
+      Llama-3.2-3B Q8 decode: layer 0, the first `rows` output rows of each
+        projection, scaled by weight count to the 196-GEMV pass (every layer
+        has the same shapes);
+      Qwen3-4B Q4 prefill at each M: layer 0, the first `rows` output rows of
+        each projection, scaled by weight count to 36 layers;
+      Qwen3-30B-A3B MoE at each M: gate, up and down for the pairs of the
+        first `experts` experts, scaled by the number of experts (the
+        oracle's time is dominated by unpacking and dequantizing each
+        expert's weights once)."""
+    import oracle
+    out = {}
+    single = synth.SINGLE_Q4
+    p = single.projs[0]
+    best = min(_oracle_gemm(oracle, single, 0, 0, p, 1)[0] for _ in range(3))
+    out["q4-gemv-1x1024x1024"] = {"ms": round(best * 1e3, 3),
+                                  "gb_per_s": round(gemv_bytes(p.n, p.k, 4) / best / 1e9, 4),
+                                  "sample": "whole GEMV, best of 3"}
+    q8 = synth.LLAMA32_3B_Q8_DECODE
+    spent, wsample, bsample = 0.0, 0, 0
+    for i, p in enumerate(q8.projs):
+        dt, n = _oracle_gemm(oracle, q8, 0, i, p, 1, rows)
+        spent += dt
+        wsample += n * p.k
+        bsample += gemv_bytes(n, p.k, q8.bits)
+    scale = q8.weight_count() / wsample
+    out[q8.name] = {"ms_per_step_extrapolated": round(spent * scale * 1e3, 1),
+                    "gb_per_s": round(bsample / spent / 1e9, 4),
+                    "sample": f"layer 0, first {rows} rows of each projection ({spent:.1f} s); "
+                              f"x{scale:.1f} by weight count, extrapolated (identical shapes per layer)"}
+    pf = synth.QWEN3_4B_Q4_PREFILL
+    by_m = {}
+    for m in pf.ms:
+        spent, wsample, fl = 0.0, 0, 0.0
+        for i, p in enumerate(pf.projs):
+            dt, n = _oracle_gemm(oracle, pf, 0, i, p, m, rows)
+            spent += dt
+            wsample += n * p.k
+        scale = pf.weight_count() / wsample
+        _, flops = prefill_work(pf, m)
+        t_full = spent * scale
+        by_m[str(m)] = {"ms_per_step_extrapolated": round(t_full * 1e3, 1),
+                        "tflops": round(flops / t_full / 1e12, 5),
+                        "sample_s": round(spent, 2)}
+    out[pf.name] = {"by_m": by_m, "sample": f"layer 0, first {rows} rows of each projection at each M; "
+                                            "scaled by weight count to 36 layers, extrapolated"}
+    moe = synth.QWEN3_30B_A3B_Q4_MOE
+    by_m = {}
+    for m in moe.ms:
+        spent, fl = 0.0, 0.0
+        for pi, (name, k, n, per_pair) in enumerate(synth.moe_projs(moe)):
+            a, ids, _ = synth.draw_moe_inputs(moe, m, pi)
+            ws = [oracle.quantize(synth.draw_weight((moe.wid, e, pi, synth.STREAM_W), n, k), moe.bits)
+                  for e in range(experts)]
+            words = np.stack([oracle.pack(c, moe.bits) for c, _, _ in ws])
+            s_ = np.stack([s for _, s, _ in ws])
+            b_ = np.stack([b for _, _, b in ws])
+            # exactly the pairs routed to the sampled experts, each as its
+            # own one-slot token (row(p) = p), with its A row
+            flat = ids.reshape(-1)
+            sel = np.nonzero(flat < experts)[0]
+            a_sub = a[sel] if per_pair else a[sel // moe.top_k]
+            t0 = time.perf_counter()
+            oracle.grouped_f64(words, s_, b_, a_sub, flat[sel][:, None].astype(np.int32), moe.bits, True)
+            spent += time.perf_counter() - t0
+            fl += 2.0 * m * moe.top_k * n * k
+        t_full = spent * moe.experts / experts
+        by_m[str(m)] = {"ms_per_step_extrapolated": round(t_full * 1e3, 1),
+                        "tflops": round(fl / t_full / 1e12, 5), "sample_s": round(spent, 2)}
+    out[moe.name] = {"by_m": by_m, "sample": f"gate, up and down over experts 0..{experts - 1} and the tokens "
+                                             f"routed to them; x{moe.experts // experts} by expert count, "
+                                             "extrapolated"}
+    return {"kind": "oracle", **host_info(), "by_workload": out}
+
+
+def dispatch_cost():
+    """Host microseconds per call of each entry point, from the C++ harness
+    (no Python in the loop); None if it was not built."""
+    import subprocess
+    exe = os.path.join(ROOT, "quantized_matmul_qgemv_amd", "qmm_dispatch_cost")
+    if not os.path.exists(exe):
+        return None
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        log("dispatch harness failed:", r.stderr.strip()[-500:])
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def python_dispatch_cost(torch, qmm, calls=200):
+    """Host microseconds per call through the Python binding (ctypes
+    marshalling + the C call) for qgemv and a batched GEMM launch."""
+    wl = synth.SINGLE_Q4
+    words, s, b, x, y, n, k = prepare_dense(torch, qmm, wl, 1)[0][0]
+    X = torch.zeros((64, k), dtype=torch.float16, device="cuda")
+    Y = torch.empty((64, n), dtype=torch.float32, device="cuda")
+    plan = qmm.qgemm_batched_plan([(words, s, b, X, Y)], 4)
+    out = {}
+    for name, fn in (("qgemv", lambda: qmm.qgemv(words, s, b, x, 4, y=y)),
+                     ("qgemm_batched", lambda: qmm.qgemm_batched(plan))):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        reps = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            for _ in range(calls):
+                fn()
+            reps.append((time.perf_counter() - t0) / calls * 1e6)
+            torch.cuda.synchronize()
+        out[name] = round(float(np.median(reps)), 3)
+    return {"unit": "us host time per call", **out}
+
+
+_PROFILE_CACHE = {}
+
+
+def profile_launch(torch, qmm, spec, reps):
+    """One launch of the benchmark, repeated `reps` times, for profilers:
+    spec = "prefill:M:GROUP" (GROUP = qkv, o, gateup or down; layer 0's
+    batched launch over tile-interleaved weights) or "moe:M:PROJ" (PROJ =
+    gate, up, down or swiglu; routed, over tile-interleaved weights)."""
+    kind, m, what = spec.split(":")
+    m = int(m)
+    stream = torch.cuda.current_stream()
+    if kind == "prefill":
+        wl = synth.QWEN3_4B_Q4_PREFILL
+        wl1 = dataclasses.replace(wl, layers=1)
+        if "prefill" not in _PROFILE_CACHE:
+            _PROFILE_CACHE["prefill"] = prefill_layers(torch, qmm, wl1)
+        layers = _PROFILE_CACHE["prefill"]
+        if ("io", m) not in _PROFILE_CACHE:
+            _PROFILE_CACHE[("io", m)] = prefill_io(torch, wl1, m)
+        xs, ys = _PROFILE_CACHE[("io", m)]
+        gi = {"qkv": 0, "o": 1, "gateup": 2, "down": 3}[what]
+        plan = prefill_plans(qmm, wl1, layers, xs, ys, (PREFILL_GROUPS[gi],))[0][0]
+        ms, _ = time_launches(torch, lambda i: qmm.qgemm_batched(plan), reps, 2, stream)
+        _, flops1 = prefill_work(dataclasses.replace(wl1, projs=tuple(
+            p for p in wl.projs if p.name in PREFILL_GROUPS[gi])), m)
+        return {"launch": spec, "ms_per_launch": round(ms, 5), "tflops": round(flops1 / (ms * 1e-3) / 1e12, 1),
+                "tiles": "{bm}x{n}/S{splits}".format(n=plan.header["nb"] * 128, **plan.header)}
+    wl = synth.QWEN3_30B_A3B_Q4_MOE
+    if "moe" not in _PROFILE_CACHE:
+        _PROFILE_CACHE["moe"] = moe_weights(torch, qmm, wl, 1)[0]
+    wset = _PROFILE_CACHE["moe"]
+    pi = {"gate": 0, "up": 1, "down": 2, "swiglu": 0}[what]
+    a, ids, _ = synth.draw_moe_inputs(wl, m, pi)
+    A, I = torch.from_numpy(a).cuda(), torch.from_numpy(ids).cuda()
+    plan = qmm.moe_route(I, wl.experts)
+    W, S, B, n, k, per_pair = wset[pi]
+    if what == "swiglu":
+        (Wu, Su, Bu, *_) = wset[1]
+        H = torch.empty((m * wl.top_k, n), dtype=torch.float16, device="cuda")
+        fn = lambda i: qmm.moe_gate_up_swiglu((W, S, B), (Wu, Su, Bu), A, I, plan, wl.bits, h=H, tiled=True)
+        flops = 2 * 2.0 * m * wl.top_k * n * k
+    else:
+        Y = torch.empty((m * wl.top_k, n), dtype=torch.float32, device="cuda")
+        fn = lambda i: qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, plan=plan, tiled=True)
+        flops = 2.0 * m * wl.top_k * n * k
+    ms, _ = time_launches(torch, fn, reps, 2, stream)
+    return {"launch": spec, "ms_per_launch": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
 
 
 # ------------------------------------------------------------------- main --
@@ -473,6 +763,13 @@ def main():
                     help="run only a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--gemm", metavar="M,N,K",
                     help="run only qmm_qgemm on one 4-bit shape, --steps times (for counters), and exit")
+    ap.add_argument("--launch", metavar="SPEC",
+                    help="run benchmark launches --steps times each and exit (for profilers): a "
+                         "comma-separated list of prefill:M:{qkv,o,gateup,down} and moe:M:{gate,up,down,swiglu}")
+    ap.add_argument("--ms", metavar="M[,M...]", help="prefill/moe: only these M")
+    ap.add_argument("--forces", metavar="F;F...",
+                    help="with --launch: time every launch under each QMM_GEMM_FORCE value "
+                         "(bm,nb,splits; empty = the planner's choice)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -508,11 +805,27 @@ def main():
                           "tflops": round(2.0 * m * n * k / (ms_call * 1e-3) / 1e12, 1)}), flush=True)
         return
 
+    if args.launch:
+        forces = args.forces.split(";") if args.forces else [None]
+        for spec in args.launch.split(","):
+            for f in forces:
+                if f is not None:
+                    if f:
+                        os.environ["QMM_GEMM_FORCE"] = f
+                    else:
+                        os.environ.pop("QMM_GEMM_FORCE", None)
+                r = profile_launch(torch, qmm, spec, args.steps)
+                if f is not None:
+                    r["force"] = f
+                print(json.dumps(r), flush=True)
+        return
+
     if args.only in ("prefill", "moe"):
         if args.only == "prefill":
+            ms = tuple(int(v) for v in args.ms.split(",")) if args.ms else synth.QWEN3_4B_Q4_PREFILL.ms
+            by_m = bench_prefill(torch, qmm, ms)
             out = {"workload": synth.QWEN3_4B_Q4_PREFILL.name, "peak_tflops": FP16_MFMA_PEAK_TFLOPS,
-                   "weights": PREFILL_WEIGHTS,
-                   "by_m": bench_prefill(torch, qmm, synth.QWEN3_4B_Q4_PREFILL.ms)}
+                   "weights": PREFILL_WEIGHTS, "by_m": by_m, "prefill_roofline": prefill_roofline_block(by_m)}
         else:
             out = {"workload": synth.QWEN3_30B_A3B_Q4_MOE.name, "weights": PREFILL_WEIGHTS,
                    "by_m": bench_moe(torch, qmm)}
@@ -558,6 +871,8 @@ def main():
     if args.only in ("all", "decode_extras"):
         log("decode extras")
         result["decode_context"] = bench_decode_extras(torch, qmm, wl, d["sets"])
+        result["decode_context"]["host_dispatch_c"] = dispatch_cost()
+        result["decode_context"]["host_dispatch_python"] = python_dispatch_cost(torch, qmm)
     if args.only == "projections":
         result["projections"] = bench_projections(torch, qmm, wl, d["sets"])
     del d
@@ -577,9 +892,11 @@ def main():
         log("decode formats")
         result["decode_formats"] = {"workload": wl.name + " shapes", **bench_decode_formats(torch, qmm, wl)}
         log("prefill")
+        by_m = bench_prefill(torch, qmm, synth.QWEN3_4B_Q4_PREFILL.ms)
+        result["prefill_roofline"] = prefill_roofline_block(by_m)
         result["prefill"] = {"workload": synth.QWEN3_4B_Q4_PREFILL.name,
                              "peak_tflops": FP16_MFMA_PEAK_TFLOPS, "weights": PREFILL_WEIGHTS,
-                             "by_m": bench_prefill(torch, qmm, synth.QWEN3_4B_Q4_PREFILL.ms)}
+                             "by_m": by_m}
         torch.cuda.empty_cache()
         log("gemm formats")
         result["gemm_formats"] = {"shape": [2048, 9728, 2560], "weights": PREFILL_WEIGHTS,
@@ -590,6 +907,9 @@ def main():
     if not args.no_cpu:
         log("cpu baseline")
         result["cpu_baseline"] = cpu_baseline(wl)
+        if args.only == "all":
+            log("cpu baseline, other workloads")
+            result["cpu_baseline"]["other_workloads"] = cpu_baseline_configs()
     print(json.dumps(result), flush=True)
 
 

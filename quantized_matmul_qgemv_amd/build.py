@@ -55,7 +55,25 @@ def build(verbose: bool = False) -> str:
     shutil.move(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_dispatch_cost(verbose)
     return LIB
+
+
+# Host dispatch-cost harness (dispatch_cost.hip): a C++ program linked
+# against libqmm.so, run by bench.py.
+DISPATCH_SRC = os.path.join(PKG, "dispatch_cost.hip")
+DISPATCH_BIN = os.path.join(PKG, "qmm_dispatch_cost")
+
+
+def build_dispatch_cost(verbose: bool = False) -> str:
+    cmd = [HIPCC, *CFLAGS, "-O2", DISPATCH_SRC, f"-L{PKG}", "-lqmm", "-Wl,-rpath,$ORIGIN",
+           "-o", DISPATCH_BIN]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on dispatch_cost.hip:\n{' '.join(cmd)}\n{r.stderr}")
+    if verbose:
+        print(f"built {DISPATCH_BIN}")
+    return DISPATCH_BIN
 
 
 # Host-sanitizer build (AddressSanitizer + UndefinedBehaviorSanitizer on the
