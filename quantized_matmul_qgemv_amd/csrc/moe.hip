@@ -201,6 +201,27 @@ __device__ void fill_nan_rows(T* out, const int32_t* sorted, const MoeTile& mt, 
   }
 }
 
+// Workgroup -> (row tile, column tile).  Workgroups are dealt round-robin
+// to the 8 XCDs (workgroup b runs on XCD b % 8), each with its own L2.  All
+// column tiles of one row tile gather the same A rows (the expert's tokens),
+// so they are placed on one XCD, next to each other in its dispatch order,
+// and the row tiles are dealt round-robin across the XCDs:
+//   b -> xcd = b % 8, i = b / 8;  row tile = (i / n_tiles) * 8 + xcd,
+//   column tile = i % n_tiles.
+// The grid is ceil(row tiles / 8) * 8 * n_tiles workgroups.
+constexpr int kMoeXcds = 8;
+
+__device__ __forceinline__ void moe_tile_of(int n_tiles, int& tile, int& tn) {
+  const int xcd = blockIdx.x % kMoeXcds;
+  const int i = blockIdx.x / kMoeXcds;
+  tile = (i / n_tiles) * kMoeXcds + xcd;
+  tn = i % n_tiles;
+}
+
+static unsigned moe_grid(int m_tiles, int n_tiles) {
+  return (unsigned)((m_tiles + kMoeXcds - 1) / kMoeXcds) * kMoeXcds * n_tiles;
+}
+
 // Waves per SIMD the register allocator is held to: two, except for the
 // 128-row, 256-column tiles of the 5- to 16-bit formats and the 160-row
 // fused gate/up tiles (160 accumulators per lane), which would spill at two
@@ -216,8 +237,8 @@ void grouped_kernel(GroupedArgs a, const int32_t* __restrict__ ws, int n_tiles) 
   __shared__ int32_t pair_of[BM];
   constexpr int BN = 4 * NB * 32;
   const int pairs = a.t * a.top_k;
-  const int tile = blockIdx.x / n_tiles;
-  const int tn = blockIdx.x % n_tiles;
+  int tile, tn;
+  moe_tile_of(n_tiles, tile, tn);
   // a routing plan built for another row tile, pair count or expert count
   // is not used: the whole output becomes NaN
   if (ws[1] != BM || ws[2] != pairs || ws[3] != a.e) {
@@ -273,8 +294,8 @@ void swiglu_kernel(SwigluArgs a, const int32_t* __restrict__ ws, int n_tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * kAStride];
   __shared__ int32_t pair_of[BM];
   const int pairs = a.t * a.top_k;
-  const int tile = blockIdx.x / n_tiles;
-  const int tn = blockIdx.x % n_tiles;
+  int tile, tn;
+  moe_tile_of(n_tiles, tile, tn);
   const uint16_t nan16 = 0x7E00;  // fp16 quiet NaN
   if (ws[1] != BM || ws[2] != pairs || ws[3] != a.e) {  // foreign plan: h is all NaN
     fill_nan_all(a.h, pairs, a.n, a.n, nan16);
@@ -311,7 +332,7 @@ static hipError_t launch_swiglu_sbq(const SwigluArgs& a, const int32_t* plan, hi
   moe_tile(a.t * a.top_k, a.e, &bm, &nb);
   const int n_tiles = (a.n + 127) / 128;
   const int m_tiles = max_row_tiles(a.t * a.top_k, a.e, bm);
-  const dim3 grid(m_tiles * n_tiles);
+  const dim3 grid(moe_grid(m_tiles, n_tiles));
   if (bm == 32) hipLaunchKernelGGL((swiglu_kernel<BITS, 32, SBQ>), grid, dim3(kGemmThreads), 0, st, a, plan, n_tiles);
   else if (bm == 64) hipLaunchKernelGGL((swiglu_kernel<BITS, 64, SBQ>), grid, dim3(kGemmThreads), 0, st, a, plan, n_tiles);
   else if (bm == 160) hipLaunchKernelGGL((swiglu_kernel<BITS, 160, SBQ>), grid, dim3(kGemmThreads), 0, st, a, plan, n_tiles);
@@ -337,12 +358,16 @@ static hipError_t launch_swiglu_bits(const SwigluArgs& a, const int32_t* plan, h
   }
 }
 
-// Row tile from the mean number of pairs per expert (one row tile per
-// expert keeps each expert's weights to a single pass over HBM).  Around a
-// mean of 128 the per-expert counts straddle 128 (100 to 159 for 2048
-// tokens, top-8 of 128 experts), so 160-row tiles take every expert in one
-// tile where 128-row tiles need a second, mostly empty one (194
-// against 128 row tiles; measured 8-11 % faster for the three grouped GEMMs).
+// Row tile from the mean number of pairs per expert.  Measured on the
+// Qwen3-30B-A3B-shaped layers (128 experts, top-8) with the XCD-aware
+// workgroup order above: at 2048 tokens (128 pairs per expert on average,
+// 100 to 159) 64-row tiles beat 160-row ones for gate (92.7 vs 94.3 us),
+// down (103.5 vs 113.2) and the fused gate/up (193.1 vs 197.8): two or
+// three row tiles per expert give the chip more workgroups than one
+// 160-row tile, and the repeated weight columns mostly come from L2 or the
+// last-level cache.  At 512 tokens (32 per expert) 64 rows are best too;
+// 32 rows below 16 per expert, 128 above 160 per expert (each expert's
+// weights then stream once per 128 pairs).
 // QMM_MOE_FORCE="bm,nb" overrides the tile (tuning sweeps).  The bucketing
 // and the grouped GEMM must agree on it, so both take it from here.
 // QMM_MOE_FORCE is read on every call (tuning sweeps change it between
@@ -350,7 +375,7 @@ static hipError_t launch_swiglu_bits(const SwigluArgs& a, const int32_t* plan, h
 // caught on the device by the plan-header check (the output becomes NaN).
 static void moe_tile(int pairs, int experts, int* bm_out, int* nb_out) {
   const int mean = (pairs + experts - 1) / experts;
-  int bm = mean <= 16 ? 32 : mean <= 48 ? 64 : (mean >= 112 && mean <= 144) ? 160 : 128, nb = 1;
+  int bm = mean <= 16 ? 32 : mean <= 160 ? 64 : 128, nb = 1;
   if (const char* env = getenv("QMM_MOE_FORCE")) {
     int fb = 0, fn = 0;
     if (sscanf(env, "%d,%d", &fb, &fn) == 2 && (fb == 32 || fb == 64 || fb == 128 || (fb == 160 && fn == 1)) &&
@@ -421,7 +446,7 @@ static hipError_t launch_grouped_tile(const GroupedArgs& a, int32_t* ws, bool bu
   }
   const int n_tiles = (a.n + BN - 1) / BN;
   const int m_tiles = max_row_tiles(pairs, a.e, BM);
-  hipLaunchKernelGGL((grouped_kernel<BITS, BM, NB, SBQ>), dim3(m_tiles * n_tiles), dim3(kGemmThreads),
+  hipLaunchKernelGGL((grouped_kernel<BITS, BM, NB, SBQ>), dim3(moe_grid(m_tiles, n_tiles)), dim3(kGemmThreads),
                      0, st, a, ws, n_tiles);
   return hipGetLastError();
 }
