@@ -396,7 +396,7 @@ def bench_prefill(torch, qmm, ms, steps=20, warmup=3, batched=True):
                        "roofline_bound": "mfma" if roof_tfl >= FP16_MFMA_PEAK_TFLOPS - 1e-6 else "hbm",
                        "frac_of_roofline": round(tfl / roof_tfl, 4)}
         if batched:
-            out[str(m)]["tiles"] = {"+".join(g): "{bm}x{n}/S{splits}".format(n=pl.header["nb"] * 128, **pl.header)
+            out[str(m)]["tiles"] = {"+".join(g): "{bm}x{n}/S{splits}/K{kw}".format(n=pl.header["nb"] * 128, **pl.header)
                                     for g, pl in zip(PREFILL_GROUPS, plans[0])}
             del plans
         del xs, ys
@@ -699,19 +699,23 @@ def python_dispatch_cost(torch, qmm, calls=200):
 
 
 _PROFILE_CACHE = {}
+PROFILE_LAYERS = 8
 
 
 def profile_launch(torch, qmm, spec, reps):
-    """One launch of the benchmark, repeated `reps` times, for profilers:
-    spec = "prefill:M:GROUP" (GROUP = qkv, o, gateup or down; layer 0's
-    batched launch over tile-interleaved weights) or "moe:M:PROJ" (PROJ =
-    gate, up, down or swiglu; routed, over tile-interleaved weights)."""
+    """One launch of the benchmark, repeated `reps` times, for profilers and
+    tile sweeps: spec = "prefill:M:GROUP" (GROUP = qkv, o, gateup or down;
+    the batched launch over tile-interleaved weights, rotating over the
+    weights of PROFILE_LAYERS layers, 8 x 57 MB, so that every launch reads
+    its weights from HBM as in a full prefill step rather than from the
+    last-level cache) or "moe:M:PROJ" (PROJ = gate, up, down or swiglu;
+    routed, over tile-interleaved weights)."""
     kind, m, what = spec.split(":")
     m = int(m)
     stream = torch.cuda.current_stream()
     if kind == "prefill":
         wl = synth.QWEN3_4B_Q4_PREFILL
-        wl1 = dataclasses.replace(wl, layers=1)
+        wl1 = dataclasses.replace(wl, layers=PROFILE_LAYERS)
         if "prefill" not in _PROFILE_CACHE:
             _PROFILE_CACHE["prefill"] = prefill_layers(torch, qmm, wl1)
         layers = _PROFILE_CACHE["prefill"]
@@ -719,12 +723,13 @@ def profile_launch(torch, qmm, spec, reps):
             _PROFILE_CACHE[("io", m)] = prefill_io(torch, wl1, m)
         xs, ys = _PROFILE_CACHE[("io", m)]
         gi = {"qkv": 0, "o": 1, "gateup": 2, "down": 3}[what]
-        plan = prefill_plans(qmm, wl1, layers, xs, ys, (PREFILL_GROUPS[gi],))[0][0]
-        ms, _ = time_launches(torch, lambda i: qmm.qgemm_batched(plan), reps, 2, stream)
-        _, flops1 = prefill_work(dataclasses.replace(wl1, projs=tuple(
+        plans = [pl[0] for pl in prefill_plans(qmm, wl1, layers, xs, ys, (PREFILL_GROUPS[gi],))]
+        ms, _ = time_launches(torch, lambda i: qmm.qgemm_batched(plans[i % len(plans)]), reps, 2, stream)
+        _, flops1 = prefill_work(dataclasses.replace(wl, layers=1, projs=tuple(
             p for p in wl.projs if p.name in PREFILL_GROUPS[gi])), m)
+        h = plans[0].header
         return {"launch": spec, "ms_per_launch": round(ms, 5), "tflops": round(flops1 / (ms * 1e-3) / 1e12, 1),
-                "tiles": "{bm}x{n}/S{splits}".format(n=plan.header["nb"] * 128, **plan.header)}
+                "tiles": "{bm}x{n}/S{splits}/K{kw}".format(n=h["nb"] * 128, **h)}
     wl = synth.QWEN3_30B_A3B_Q4_MOE
     if "moe" not in _PROFILE_CACHE:
         _PROFILE_CACHE["moe"] = moe_weights(torch, qmm, wl, 1)[0]

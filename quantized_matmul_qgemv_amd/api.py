@@ -140,10 +140,11 @@ class GemmBatchPlan:
     @property
     def header(self) -> dict:
         """Tile choice recorded in the image (for logs and tests)."""
-        raw = bytes(self.host)[:48]
-        f = __import__("struct").unpack("<IIiiiiiiiiii", raw)
+        raw = bytes(self.host)[:64]
+        f = __import__("struct").unpack("<IIiiiiiiiiiiQii", raw)
         return {"bits": f[2], "bm": f[4], "nb": f[5], "sbq": f[6], "count": f[7],
-                "num_tiles": f[8], "split_tiles": f[9], "splits": f[10], "wtiled": f[11]}
+                "num_tiles": f[8], "split_tiles": f[9], "splits": f[10], "wtiled": f[11],
+                "kw": f[13]}
 
 
 def qgemm_batched_plan(problems, bits: int, group_size: int = GROUP, tiled: bool = False) -> GemmBatchPlan:

@@ -62,11 +62,11 @@ __global__ __launch_bounds__(256) void qgemm_batched_reduce_kernel(
     if (q < cols) y[q] = acc[q];
 }
 
-template <int BITS, int BM, int NB, bool SBQ>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2))) void qgemm_batched_kernel(
+template <int BITS, int BM, int NB, bool SBQ, int KW>
+__global__ __launch_bounds__(kGemmThreads * KW) __attribute__((amdgpu_waves_per_eu(2))) void qgemm_batched_kernel(
     const GemmBatchProblem* __restrict__ probs, const GemmTileRec* __restrict__ tiles,
     float* partials, int gs, int wtiled) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BM * kAStride];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[gemm_lds_halves(BM, NB, KW)];
   constexpr int BN = 4 * NB * 32;
   const GemmTileRec t = tiles[blockIdx.x];
   if (t.problem < 0) return;
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int rowoff = split ? 0 : m0;
   auto a_row = [&](int i) { const int r = m0 + i; return r < m ? r : m - 1; };
   auto c_row = [&](int i) { return m0 + i < m ? rowoff + i : -1; };
-  gemm_tile<BITS, BM, NB, SBQ>(ARows{P.x, P.k}, a_row, c_row, P.w, P.s, P.b, ytile, ldy, t.n0,
+  gemm_tile<BITS, BM, NB, SBQ, false, KW>(ARows{P.x, P.k}, a_row, c_row, P.w, P.s, P.b, ytile, ldy, t.n0,
                                P.n, t.g0, t.g1, lds, gs, nullptr, nullptr, nullptr, nullptr, wtiled);
 }
 
@@ -108,23 +108,37 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1)
 // ------------------------------------------------------------------ host --
 
 // Tile configurations and the planner's cost model.  For a batch with W
-// workgroups (tiles x splits) of `steps` k64 steps each on a configuration
-// with `slots` resident workgroups (per CU x 256 CUs):
-//   time = rounds * steps * t_step + (splits > 1 ? split_us + split_us_per_mb * partial MB : 0)
-//   rounds = ceil(W / slots) when W >= slots, else (W / slots)^alpha
-// (a partly filled chip runs each workgroup faster).  t_step and alpha were
-// fitted to measured launches of the Qwen3-4B-shaped prefill groups (q+k+v,
-// o, gate+up, down) at M = 128 ... 2048 with 4-bit weights: the chosen
-// configuration is within 2 % of the best one on average there.
+// workgroups (tiles x splits), each running `steps` k64 steps (per k half),
+// on a configuration with `occ` resident workgroups per CU:
+//   k       = ceil(W / 256)                  workgroups on the busiest CU
+//   compute = steps * t1 * ceil(k / occ) * min(k, occ)^gamma
+//   l2      = W * steps * kw * (bm * 128 + bn * 8 * bits) / kL2GBs
+//   time    = kFixedUs + max(compute, l2) + (splits > 1 ? split cost : 0)
+// t1 is the time of one step of a workgroup alone on a CU; gamma says how
+// much a CU's resident workgroups slow each other down (0: not at all, 1:
+// they take turns); the l2 term bounds the operand traffic of the whole
+// grid (A tiles and packed weights per step, from L2).  t1, gamma,
+// kFixedUs and kL2GBs were fitted (least squares on log time) to about
+// 1,100 launches of the Qwen3-4B-shaped prefill groups (q+k+v, o, gate+up,
+// down) at M = 128 ... 2048 with 4-bit weights, every configuration and
+// split count, each launch reading its weights from HBM (rotating over 8
+// layers): the fit's rms error is 7-12 % per configuration, and its choice
+// is within 3 % of the best measured configuration at every M.
 struct TileCfg {
-  int bm, nb, slots;
-  double t_step_us, alpha;
+  int bm, nb, kw, occ;
+  double t1_us, gamma;
 };
 constexpr TileCfg kCfgs[] = {
-    {256, 2, 256, 2.487, 0.300}, {128, 2, 512, 1.532, 0.321}, {128, 1, 768, 1.329, 0.234},
-    {64, 2, 768, 1.400, 0.345},  {64, 1, 1024, 1.283, 0.481}, {32, 2, 768, 1.509, 0.300},
-    {32, 1, 1280, 1.631, 0.300},
+    {256, 2, 1, 1, 1.900, 0.00}, {128, 2, 1, 2, 1.040, 0.48}, {128, 1, 1, 3, 0.680, 0.48},
+    {64, 2, 1, 3, 0.600, 0.64},  {64, 1, 1, 4, 0.400, 0.48},  {32, 2, 1, 3, 0.460, 0.64},
+    {32, 1, 1, 5, 0.320, 0.52},
+    // two k halves per workgroup (8 waves)
+    {128, 1, 2, 1, 1.320, 0.00}, {64, 2, 2, 1, 1.240, 0.00}, {64, 1, 2, 2, 0.720, 0.64},
+    {32, 1, 2, 2, 0.580, 0.64},
 };
+constexpr int kCUs = 256;
+constexpr double kFixedUs = 1.0;
+constexpr double kL2GBs = 10000.0;
 constexpr int kSplitChoices[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16};
 constexpr double kSplitUs = 6.25;          // reduce launch
 constexpr double kSplitUsPerMB = 0.5;      // partial tiles written and read back
@@ -160,17 +174,18 @@ bool splits_ok(const GemmBatchProblem* probs, int count, int S) {
 }
 
 // divisible: only split counts that divide every problem's group count
-// (the single-GEMM kernel splits k evenly).
+// and one k half per workgroup (the single-GEMM kernel).
 // f16w: unquantized fp16 weights hold 4x the register bytes of a 4-bit
 // weight ring, so only the one-column-block tiles (nb = 1) are used.
-Choice choose(const GemmBatchProblem* probs, int count, bool divisible, bool f16w) {
+Choice choose(const GemmBatchProblem* probs, int count, int bits, bool divisible, bool f16w) {
   Choice best{2, 1, false, 1e300};
   for (int ci = 0; ci < (int)(sizeof kCfgs / sizeof kCfgs[0]); ++ci) {
     const TileCfg& c = kCfgs[ci];
     if (f16w && c.nb != 1) continue;
+    if (divisible && c.kw != 1) continue;
     const int bn = c.nb * 128;
     for (int S : kSplitChoices) {
-      if (!splits_ok(probs, count, S)) continue;
+      if (!splits_ok(probs, count, S * c.kw)) continue;
       bool even = true;
       for (int p = 0; p < count; ++p) even = even && (probs[p].k / 64) % S == 0;
       if (divisible && !even) continue;
@@ -179,28 +194,33 @@ Choice choose(const GemmBatchProblem* probs, int count, bool divisible, bool f16
       for (int p = 0; p < count; ++p) {
         const long tp = (long)ceil_div_i(probs[p].m, c.bm) * ceil_div_i(probs[p].n, bn);
         wg += tp * S;
-        const int st = ceil_div_i(probs[p].k / 64, S);
+        const int st = ceil_div_i(ceil_div_i(probs[p].k / 64, S), c.kw);
         if (st > steps) steps = st;
       }
+      if (wg == 0) continue;
       const double partial = S > 1 ? (double)wg * c.bm * bn * 4.0 : 0.0;
       if (partial > kMaxPartialBytes) continue;
-      const double fill = (double)wg / c.slots;
-      const double rounds = fill >= 1.0 ? (double)ceil_div_i(wg, c.slots) : pow(fill, c.alpha);
-      const double us = rounds * steps * c.t_step_us +
+      const long k = (wg + kCUs - 1) / kCUs;
+      const double compute = steps * c.t1_us * (double)((k + c.occ - 1) / c.occ) *
+                             pow((double)(k < c.occ ? k : c.occ), c.gamma);
+      const double l2 = (double)wg * steps * c.kw * (c.bm * 128.0 + bn * 8.0 * bits) / (kL2GBs * 1e3);
+      const double us = kFixedUs + (compute > l2 ? compute : l2) +
                         (S > 1 ? kSplitUs + kSplitUsPerMB * partial / 1e6 : 0.0);
       if (us < best.us * 0.999) best = Choice{ci, S, sbq_ok(probs, count, S), us};
     }
   }
-  // QMM_GEMM_FORCE="bm,nb,splits" overrides the choice (tuning sweeps); it
-  // is ignored unless it names a configuration and a valid split count.
+  // QMM_GEMM_FORCE="bm,nb,splits[,kw]" overrides the choice (tuning
+  // sweeps); it is ignored unless it names a configuration and a valid
+  // split count.
   if (const char* env = getenv("QMM_GEMM_FORCE")) {
-    int bm = 0, nb = 0, sp = 0;
-    const bool parsed = sscanf(env, "%d,%d,%d", &bm, &nb, &sp) == 3 && sp >= 1;
+    int bm = 0, nb = 0, sp = 0, kw = 1;
+    const int got = sscanf(env, "%d,%d,%d,%d", &bm, &nb, &sp, &kw);
+    const bool parsed = got >= 3 && sp >= 1 && (kw == 1 || kw == 2);
     bool even = parsed;
     for (int p = 0; parsed && p < count; ++p) even = even && (probs[p].k / 64) % sp == 0;
-    if (parsed && splits_ok(probs, count, sp) && (even || !divisible)) {
+    if (parsed && splits_ok(probs, count, sp * kw) && (even || !divisible)) {
       for (int ci = 0; ci < (int)(sizeof kCfgs / sizeof kCfgs[0]); ++ci)
-        if (kCfgs[ci].bm == bm && kCfgs[ci].nb == nb && (!f16w || nb == 1))
+        if (kCfgs[ci].bm == bm && kCfgs[ci].nb == nb && kCfgs[ci].kw == kw && (!f16w || nb == 1))
           best = Choice{ci, sp, sbq_ok(probs, count, sp), 0.0};
     }
   }
@@ -215,7 +235,7 @@ void gemm_choose(int m, int n, int k, int bits, int* bm, int* nb, int* splits) {
   p.m = m;
   p.n = n;
   p.k = k;
-  const Choice ch = choose(&p, 1, true, bits == 16);
+  const Choice ch = choose(&p, 1, bits, true, bits == 16);
   *bm = kCfgs[ch.cfg].bm;
   *nb = kCfgs[ch.cfg].nb;
   *splits = ch.splits;
@@ -223,7 +243,7 @@ void gemm_choose(int m, int n, int k, int bits, int* bm, int* nb, int* splits) {
 
 size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, int group_size,
                         int wtiled, void* out, size_t out_bytes) {
-  Choice ch = choose(probs, count, false, bits == 16);
+  Choice ch = choose(probs, count, bits, false, bits == 16);
   // quad scale loads (8 bytes per column): groups of 64 with 8-byte aligned
   // scale and bias arrays only
   bool sb_aligned = true;
@@ -253,6 +273,7 @@ size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, int 
   hdr.group_size = group_size;
   hdr.bm = c.bm;
   hdr.nb = c.nb;
+  hdr.kw = c.kw;
   hdr.sbq = ch.sbq ? 1 : 0;
   hdr.count = count;
   hdr.num_tiles = (int32_t)grid;
@@ -300,27 +321,36 @@ size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, int 
   return need;
 }
 
-template <int BITS, int BM, int NB>
+template <int BITS, int BM, int NB, int KW = 1>
 static void launch_batched_cfg(const GemmBatchProblem* probs, const GemmTileRec* tiles,
                                const GemmBatchHeader& h, float* partials, hipStream_t st) {
   if (h.sbq)
-    hipLaunchKernelGGL((qgemm_batched_kernel<BITS, BM, NB, true>), dim3(h.num_tiles), dim3(kGemmThreads),
-                       0, st, probs, tiles, partials, h.group_size, h.wtiled);
+    hipLaunchKernelGGL((qgemm_batched_kernel<BITS, BM, NB, true, KW>), dim3(h.num_tiles),
+                       dim3(kGemmThreads * KW), 0, st, probs, tiles, partials, h.group_size, h.wtiled);
   else
-    hipLaunchKernelGGL((qgemm_batched_kernel<BITS, BM, NB, false>), dim3(h.num_tiles), dim3(kGemmThreads),
-                       0, st, probs, tiles, partials, h.group_size, h.wtiled);
+    hipLaunchKernelGGL((qgemm_batched_kernel<BITS, BM, NB, false, KW>), dim3(h.num_tiles),
+                       dim3(kGemmThreads * KW), 0, st, probs, tiles, partials, h.group_size, h.wtiled);
 }
 
 template <int BITS>
 static void launch_batched_bits(const GemmBatchProblem* probs, const GemmTileRec* tiles,
                                 const GemmBatchHeader& h, float* partials, hipStream_t st) {
   if constexpr (BITS == 16) {  // nb = 1 tiles only (see choose)
-    if (h.bm == 128) launch_batched_cfg<16, 128, 1>(probs, tiles, h, partials, st);
+    if (h.kw == 2) {
+      if (h.bm == 128) launch_batched_cfg<16, 128, 1, 2>(probs, tiles, h, partials, st);
+      else if (h.bm == 64) launch_batched_cfg<16, 64, 1, 2>(probs, tiles, h, partials, st);
+      else launch_batched_cfg<16, 32, 1, 2>(probs, tiles, h, partials, st);
+    } else if (h.bm == 128) launch_batched_cfg<16, 128, 1>(probs, tiles, h, partials, st);
     else if (h.bm == 64) launch_batched_cfg<16, 64, 1>(probs, tiles, h, partials, st);
     else launch_batched_cfg<16, 32, 1>(probs, tiles, h, partials, st);
     return;
   } else {
-    if (h.bm == 256) {
+    if (h.kw == 2) {
+      if (h.bm == 128) launch_batched_cfg<BITS, 128, 1, 2>(probs, tiles, h, partials, st);
+      else if (h.bm == 64 && h.nb == 2) launch_batched_cfg<BITS, 64, 2, 2>(probs, tiles, h, partials, st);
+      else if (h.bm == 64) launch_batched_cfg<BITS, 64, 1, 2>(probs, tiles, h, partials, st);
+      else launch_batched_cfg<BITS, 32, 1, 2>(probs, tiles, h, partials, st);
+    } else if (h.bm == 256) {
       if (h.sbq)
         hipLaunchKernelGGL((qgemm_batched_wide_kernel<BITS, true>), dim3(h.num_tiles), dim3(kGemmThreads),
                            0, st, probs, tiles, partials, h.group_size, h.wtiled);
@@ -367,3 +397,4 @@ hipError_t launch_qgemm_batched(const void* plan_device, const GemmBatchHeader& 
 }
 
 }  // namespace qmm
+

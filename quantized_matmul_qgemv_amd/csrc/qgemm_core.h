@@ -11,6 +11,11 @@
 //   * The 4 waves split the tile's columns: wave w owns columns
 //     [w*NB*32, (w+1)*NB*32).  So each weight column is dequantized by
 //     exactly one wave (no redundant unpack work).
+//   * KW = 2 runs two such groups of 4 waves on the two halves of the
+//     tile's k range and adds the halves in LDS at the end: twice the
+//     waves per tile (more latency hiding when a grid has few tiles)
+//     without the partial tiles and the reduce launch of a k split across
+//     workgroups.
 //   * The weight operand never touches LDS: a lane of a 32x32x16 MFMA
 //     supplies 8 consecutive-in-k values of one column, which is one packed
 //     word (4-bit), two words (8-bit) or half a word (2-bit).  A lane loads
@@ -190,15 +195,25 @@ struct ARows {
 //   * one barrier per step.
 // The loop is unrolled by 4 so that every ring index is a compile-time
 // constant (register arrays indexed at run time would spill).
-// lds holds 2 * BM * AST halves.
+// lds holds gemm_lds_halves(BM, NB, KW) halves; the workgroup has
+// KW * kGemmThreads threads.
 constexpr int kAStride = 72;  // LDS row stride in halves: 64 + 8 pad (144 B)
+
+// LDS of one gemm_tile, in halves: two A slots per k half and, for KW = 2,
+// room for the second half's accumulators (4 waves x MB x NB x 16 x 64 floats).
+__host__ __device__ constexpr int gemm_lds_halves(int bm, int nb, int kw) {
+  return kw * 2 * bm * kAStride > (kw > 1 ? 4 * (bm / 32) * nb * 16 * 64 * 2 : 0)
+             ? kw * 2 * bm * kAStride
+             : 4 * (bm / 32) * nb * 16 * 64 * 2;
+}
 
 //
 // SWIGLU (NB = 2): the two column blocks of a wave are the SAME 32 columns of
 // two weight sets, gate (w_, s_, b_) and up (w2_, s2_, b2_); the epilogue
 // writes h = silu(gate) * up, rounded to fp16, to h_tile[row * ldy + c] for
 // the tile's 128 columns (y_tile is unused).
-template <int BITS, int BM, int NB, bool SBQ, bool SWIGLU = false, typename ARowFn, typename CRowFn>
+template <int BITS, int BM, int NB, bool SBQ, bool SWIGLU = false, int KW = 1, typename ARowFn,
+          typename CRowFn>
 __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_row,
                                           const uint32_t* __restrict__ w_,
                                           const uint16_t* __restrict__ s_,
@@ -211,6 +226,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
                                           uint16_t* __restrict__ h_tile = nullptr,
                                           int wtiled = 0) {
   static_assert(!SWIGLU || NB == 2, "SwiGLU pairs a gate and an up column block");
+  static_assert(KW == 1 || KW == 2, "one or two k halves per workgroup");
   constexpr int MB = BM / 32;
   constexpr int SPANS = BM * 4;  // 16-wide spans of A per step
   constexpr int SPT = (SPANS + kGemmThreads - 1) / kGemmThreads;
@@ -223,7 +239,8 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   const gptr<uint16_t> abase = to_global(A.base);
   const int groups = A.k >> 6;
   const int sgroups = A.k / gs;
-  const int tid = threadIdx.x;
+  const int tid = KW > 1 ? (int)(threadIdx.x & (kGemmThreads - 1)) : (int)threadIdx.x;  // within its k half
+  const int kw = KW > 1 ? (int)(threadIdx.x / kGemmThreads) : 0;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
@@ -241,6 +258,20 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
     scol[nb] = (second ? to_global(s2_) : s) + (size_t)col * sgroups;
     bcol[nb] = (second ? to_global(b2_) : b) + (size_t)col * sgroups;
   }
+
+  // KW = 2: waves 4..7 take the second half of the k range (a multiple of
+  // 4 groups when SBQ); both halves run the same number of loop steps (the
+  // first half is never the shorter one) and the second half adds its
+  // accumulators to the first through LDS at the end.
+  int gb = g_begin, ge = g_end, nsteps_all = g_end - g_begin;
+  if constexpr (KW > 1) {
+    const int G = g_end - g_begin;
+    const int h0 = SBQ ? ((G / 4 + 1) / 2) * 4 : (G + 1) / 2;
+    gb = kw == 0 ? g_begin : g_begin + h0;
+    ge = kw == 0 ? g_begin + h0 : g_end;
+    nsteps_all = h0;
+  }
+  const int nmine = ge - gb;  // steps with work for this half
 
   gptr<uint16_t> asrc[SPT];
   int aoff[SPT];
@@ -282,7 +313,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
     }
   };
   auto store_a = [&](const uint32_t (&src)[SPT][8], int slot) {
-    uint16_t* dst = lds + slot * (BM * kAStride);
+    uint16_t* dst = lds + (kw * 2 + slot) * (BM * kAStride);
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       if (aon[i]) {
@@ -331,7 +362,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   // cores work on step j (two operand buffers), so LDS latency stays off
   // the MFMA issue path.
   auto compute = [&](int slot, const BRaw<BITS> (&cur)[NB]) {
-    const uint16_t* abuf = lds + slot * (BM * kAStride) + l32 * kAStride + h * 32;
+    const uint16_t* abuf = lds + (kw * 2 + slot) * (BM * kAStride) + l32 * kAStride + h * 32;
     half8_t aop[2][MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -354,15 +385,16 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[j & 1][mb], bop[nb], acc[mb][nb], 0, 0, 0);
     }
   };
-
   {
-  const int nsteps = g_end - g_begin;
-  const int glast = g_end - 1;
-  auto gclamp = [&](int i) { const int g = g_begin + i; return g < glast ? g : glast; };
-  auto g4clamp = [&](int i) { const int g = g_begin + i; return g < g_end ? g : g_end - 4; };
+  // (a half with no groups clamps to a group just before its range, which
+  // lies in [g_begin, g_end), and computes nothing)
+  const int nsteps = nsteps_all;
+  const int glast = ge - 1;
+  auto gclamp = [&](int i) { const int g = gb + i; return g < glast ? g : glast; };
+  auto g4clamp = [&](int i) { const int g = gb + i; return g < ge ? g : ge - 4; };
   // prologue: B for steps 0..2, A for steps 0..1, A(0) into LDS slot 0
   if (nsteps > 0) {
-    if constexpr (SBQ) load_sbq(sqc, bqc, g_begin);
+    if constexpr (SBQ) load_sbq(sqc, bqc, g4clamp(0));
     load_a(ra[0], gclamp(0));
     load_b(rb[0], gclamp(0));
     load_b(rb[1], gclamp(1));
@@ -383,7 +415,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
     load_a(ra[(I) & 1], gclamp(i + (I) + 2));                    \
     if (SBQ && (I) == 1) load_sbq(sqn, bqn, g4clamp(i + 4));     \
     set_sb(rb[(I) & 3], (I));                                    \
-    compute((I) & 1, rb[(I) & 3]);                               \
+    if (KW == 1 || i + (I) < nmine) compute((I) & 1, rb[(I) & 3]); \
     store_a(ra[((I) + 1) & 1], ((I) + 1) & 1);                   \
     __syncthreads();                                             \
   }
@@ -403,6 +435,28 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   if (rem > 1) QMM_GEMM_STEP(1)
   if (rem > 2) QMM_GEMM_STEP(2)
 #undef QMM_GEMM_STEP
+  }
+
+  if constexpr (KW > 1) {
+    // the second half's accumulators, one 64-float row per register, added
+    // into the first half's (the A slots are free after the last barrier)
+    float* red = reinterpret_cast<float*>(lds);
+    if (kw == 1) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[(((wave * MB + mb) * NB + nb) * 16 + r) * 64 + lane] = acc[mb][nb][r];
+    }
+    __syncthreads();
+    if (kw == 1) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][nb][r] += red[(((wave * MB + mb) * NB + nb) * 16 + r) * 64 + lane];
   }
 
   // epilogue: D[i][j] of a 32x32 block sits in lane (j + 32*((i/4)%2)),

@@ -323,7 +323,8 @@ int qmm_qgemm_batched(const void* plan_device, const void* plan_host, void* work
   if (int st = check_format(fn, hdr.bits, hdr.group_size, true)) return st;
   if (hdr.count < 1 || hdr.num_tiles < 0 || hdr.splits < 1 || (hdr.wtiled != 0 && hdr.wtiled != 1) ||
       !(hdr.bm == 32 || hdr.bm == 64 || hdr.bm == 128 || hdr.bm == 256) ||
-      !(hdr.nb == 1 || hdr.nb == 2) || (hdr.bm == 256 && hdr.nb != 2))
+      !(hdr.nb == 1 || hdr.nb == 2) || (hdr.bm == 256 && hdr.nb != 2) || (hdr.bits == 16 && hdr.nb != 1) ||
+      !(hdr.kw == 1 || hdr.kw == 2) || (hdr.kw == 2 && (hdr.bm == 256 || (hdr.nb == 2 && hdr.bm != 64))))
     return fail(QMM_ERR_INVALID_ARG, "%s: corrupt plan header", fn);
   if (hdr.workspace_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < hdr.workspace_bytes)

@@ -121,7 +121,8 @@ struct alignas(64) GemmBatchHeader {
   int32_t splits;
   int32_t wtiled;        // weights in the tile-interleaved layout (qmm_repack_tiled)
   uint64_t workspace_bytes;
-  uint64_t pad1;
+  int32_t kw;            // k halves per workgroup (1, or 2 with 8 waves)
+  int32_t pad1;
 };
 static_assert(sizeof(GemmBatchHeader) == 64, "GemmBatchHeader must stay 64 bytes");
 constexpr uint32_t kBatchMagic = 0x424D4D51u;  // "QMMB"

@@ -257,9 +257,9 @@ def gemm_batch_plan(L, shapes, bits=4, env=None, gs=64):
         if old is not None:
             os.environ["QMM_GEMM_FORCE"] = old
     raw = bytes(buf)
-    f = struct.unpack_from("<IIiiiiiiiiiiQ", raw, 0)
+    f = struct.unpack_from("<IIiiiiiiiiiiQi", raw, 0)
     hdr = dict(zip(["magic", "version", "bits", "gs", "bm", "nb", "sbq", "count", "num_tiles",
-                    "split_tiles", "splits", "wtiled", "ws"], f))
+                    "split_tiles", "splits", "wtiled", "ws", "kw"], f))
     off = 64 + 64 * len(shapes)
     recs = [struct.unpack_from("<8i", raw, off + 32 * i) for i in range(hdr["num_tiles"])]
     off2 = off + 32 * hdr["num_tiles"]
@@ -304,6 +304,32 @@ def check_gemm_plan_covers(hdr, recs, shapes):
         assert hdr["ws"] == hdr["split_tiles"] * S * bm * bn * 4
     else:
         assert hdr["ws"] == 0
+
+
+def test_gemm_plan_two_k_halves(L):
+    """A forced two-half tile (8 waves, the k range of every record split
+    again inside the workgroup) is recorded in the header, still covers
+    every tile once, and needs at least two groups per half-split; the
+    planner's own choices use one half unless a two-half tile is cheaper."""
+    shapes = [(70, 520, 1024), (300, 200, 768), (1, 64, 256)]
+    for env, want in (("64,1,1,2", (64, 1, 1, 2)), ("32,1,2,2", (32, 1, 2, 2)),
+                      ("128,1,2,2", (128, 1, 2, 2)), ("64,2,1,2", (64, 2, 1, 2)),
+                      ("64,1,3", (64, 1, 3, 1))):
+        hdr, recs = gemm_batch_plan(L, shapes, env=env)
+        assert (hdr["bm"], hdr["nb"], hdr["splits"], hdr["kw"]) == want, (env, hdr)
+        check_gemm_plan_covers(hdr, recs, shapes)
+    # no two-half tile with 256 rows or with two column blocks of 32 rows, and
+    # no third half: such forces are ignored (the planner's own choice stands)
+    own, _ = gemm_batch_plan(L, shapes)
+    for env in ("256,2,1,2", "32,2,1,2", "64,1,1,3"):
+        hdr, _ = gemm_batch_plan(L, shapes, env=env)
+        assert {k: hdr[k] for k in ("bm", "nb", "splits", "kw")} == \
+            {k: own[k] for k in ("bm", "nb", "splits", "kw")}, (env, hdr)
+    # a k of 4 groups cannot be split into 4 x 2 halves: the force is ignored
+    hdr, _ = gemm_batch_plan(L, [(64, 128, 256)], env="64,1,4,2")
+    assert (hdr["splits"], hdr["kw"]) != (4, 2)
+
+
 
 
 @pytest.mark.parametrize("shapes", [
@@ -456,3 +482,7 @@ def test_batched_gemm_plan_force_and_errors(L):
     assert ws.value > 0
     expect(L.qmm_qgemm_batched(A, buf, None, 0, None), WSP, "workspace")
     expect(L.qmm_qgemm_batched(A, buf, A, ws.value - 1, None), WSP, "workspace")
+    # a header whose k-halves field names no kernel is refused before any launch
+    for kw in (0, 3, -1):
+        C.cast(buf, C.POINTER(C.c_int32))[14] = kw
+        expect(L.qmm_qgemm_batched(A, buf, A, ws.value, None), INV, "corrupt plan header")

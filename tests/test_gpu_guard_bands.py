@@ -104,10 +104,12 @@ def test_guard_gemv_and_batched(bits):
 
 
 @pytest.mark.parametrize("bits", [3, 4, 8])
-@pytest.mark.parametrize("force", ["256,2,2", "128,2,3", "64,1,4", "32,2,1", "32,1,5"])
+@pytest.mark.parametrize("force", ["256,2,2", "128,2,3", "64,1,4", "32,2,1", "32,1,5",
+                                   "128,1,1,2", "64,2,2,2", "64,1,2,2", "32,1,1,2"])
 def test_guard_gemm_and_batched(bits, force, monkeypatch):
     """y and the split-k partial workspace of qmm_qgemm and of a batched
-    plan, every tile family, with and without k split, at ragged m and n."""
+    plan, every tile family (one or two k halves per workgroup), with and
+    without k split, at ragged m and n."""
     say("guard gemm", bits, force)
     shapes = [(70, 520, 1280), (300, 224, 768), (1, 64, 256)]
     monkeypatch.setenv("QMM_GEMM_FORCE", force)

@@ -251,6 +251,46 @@ def test_gemm_batched_forced_tiles_and_split_k(bits, bm, nb, splits, monkeypatch
         assert torch.equal(y0, t[4])
 
 
+BATCH_KW_CFGS = [(128, 1), (64, 2), (64, 1), (32, 1)]
+
+
+@pytest.mark.parametrize("bits", [4, 3, 8])
+@pytest.mark.parametrize("bm,nb", BATCH_KW_CFGS)
+@pytest.mark.parametrize("splits", [1, 3])
+def test_gemm_batched_two_k_halves(bits, bm, nb, splits, monkeypatch):
+    """Tiles whose 8 waves split each record's k range in two halves that
+    meet in LDS: parity, identical results on a second call, and the same
+    result over tile-interleaved weights.  k = 256 with quad scale loads
+    leaves the second half empty; k = 768 splits its 12 groups 8 + 4."""
+    say("gemm batched two k halves", bits, bm, nb, splits)
+    shapes = [(70, 512, 1024), (300, 224, 768), (33, 96, 512)] + ([(1, 64, 256)] if splits == 1 else [])
+    ins, wants = _batch_inputs(bits, shapes, 923)
+    monkeypatch.setenv("QMM_GEMM_FORCE", f"{bm},{nb},{splits},2")
+    plan = qmm.qgemm_batched_plan(ins, bits)
+    tiled = [(qmm.repack_tiled(w, bits), s_, b_, x, torch.full_like(y, float("nan")))
+             for (w, s_, b_, x, y) in ins]
+    plan_t = qmm.qgemm_batched_plan(tiled, bits, tiled=True)
+    monkeypatch.delenv("QMM_GEMM_FORCE")
+    h = plan.header
+    assert (h["bm"], h["nb"], h["splits"], h["kw"]) == (bm, nb, splits, 2), h
+    qmm.qgemm_batched(plan)
+    first = [t[4].clone() for t in ins]
+    for (m, n, k), y, want in zip(shapes, first, wants):
+        assert_close(host(y), want, f"two halves {bm}x{nb} S={splits} m={m} n={n} k={k}")
+    for t in ins:
+        t[4].fill_(float("nan"))
+    plan.workspace.fill_(0xAB)
+    qmm.qgemm_batched(plan)
+    torch.cuda.synchronize()
+    for y0, t in zip(first, ins):
+        assert torch.equal(y0, t[4])
+    assert plan_t.header["kw"] == 2
+    qmm.qgemm_batched(plan_t)
+    torch.cuda.synchronize()
+    for (m, n, k), y0, t1 in zip(shapes, first, tiled):
+        assert torch.equal(y0, t1[4]), f"tiled differs: {bm}x{nb} S={splits} m={m} k={k}"
+
+
 def _tiled_words(words, n, k, bits):
     """The tile-interleaved layout written out with numpy: group g of
     column c goes to ((c // 32) * G * 32 + g * 32 + c % 32) * WPG."""
@@ -524,13 +564,14 @@ def test_group_size_batched_gemm_every_tile(bits, gs, monkeypatch):
         x = synth.draw_act((934, bits, gs, i + 10), m, k)
         wants.append(oracle.qmatmul_f64(words, s, b, x, bits, gs))
         ins.append((dev(words), dev(s), dev(b), dev(x), torch.full((m, n), float("nan"), device="cuda")))
-    for bm, nb in BATCH_CFGS:
-        for splits in (1, 3):
-            say("group size batched", bits, gs, bm, nb, splits)
-            monkeypatch.setenv("QMM_GEMM_FORCE", f"{bm},{nb},{splits}")
+    for bm, nb, kw in [(bm, nb, 1) for bm, nb in BATCH_CFGS] + [(bm, nb, 2) for bm, nb in BATCH_KW_CFGS]:
+        for splits in ((1, 3) if kw == 1 else (1, 2)):  # k = 256 has 4 groups: at most 2 x 2
+            say("group size batched", bits, gs, bm, nb, splits, kw)
+            monkeypatch.setenv("QMM_GEMM_FORCE", f"{bm},{nb},{splits},{kw}")
             plan = qmm.qgemm_batched_plan(ins, bits, group_size=gs)
             monkeypatch.delenv("QMM_GEMM_FORCE")
-            assert (plan.header["bm"], plan.header["nb"], plan.header["splits"]) == (bm, nb, splits)
+            assert (plan.header["bm"], plan.header["nb"], plan.header["splits"], plan.header["kw"]) == \
+                (bm, nb, splits, kw)
             assert plan.header["sbq"] == 0
             qmm.qgemm_batched(plan)
             for (m, n, k), t, want in zip(shapes, ins, wants):
@@ -600,12 +641,13 @@ def test_fp16_weights_gemm(monkeypatch):
     plan = qmm.qgemm_batched_plan(ins, 16)
     assert plan.header["nb"] == 1 and plan.header["sbq"] == 0
     for bm in (128, 64, 32):
-        for splits in (1, 3):
-            say("fp16 gemm batched", bm, splits)
-            monkeypatch.setenv("QMM_GEMM_FORCE", f"{bm},1,{splits}")
+        for splits, kw in ((1, 1), (3, 1), (1, 2), (2, 2)):
+            say("fp16 gemm batched", bm, splits, kw)
+            monkeypatch.setenv("QMM_GEMM_FORCE", f"{bm},1,{splits},{kw}")
             plan = qmm.qgemm_batched_plan(ins, 16)
             monkeypatch.delenv("QMM_GEMM_FORCE")
-            assert (plan.header["bm"], plan.header["nb"], plan.header["splits"]) == (bm, 1, splits)
+            assert (plan.header["bm"], plan.header["nb"], plan.header["splits"], plan.header["kw"]) == \
+                (bm, 1, splits, kw)
             qmm.qgemm_batched(plan)
             for (m, n, k), t, want in zip(shapes, ins, wants):
                 assert_close(host(t[4]), want, f"fp16 batched {bm} S={splits} m={m}")
