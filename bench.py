@@ -65,9 +65,9 @@ TRAFFIC = {
     # (KiB per dispatch of qgemv_batched_kernel<4,16,4,64>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 166755.8, "fetch_scale": 1073741824 / (524301.3 * 1024),
-    "write_kib": 1938.6, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "930899746c41ab2d2905f5f5fa9d8b2f56ec7e532b18d36df56b54d6a11fff14",
+    "fetch_kib": 166771.8, "fetch_scale": 1073741824 / (524301.3 * 1024),
+    "write_kib": 1938.7, "write_scale": 1073741824 / (1048576.0 * 1024),
+    "sources_sha256": "25e3d45c9c446f73672b1ea04b135cff6bed33044d5e94456baa287838a50d60",
 }
 
 
@@ -249,6 +249,27 @@ def bench_projections(torch, qmm, wl, sets, launches=20):
         out[name] = {"n": n, "k": k, "us_per_launch": round(ms * 1e3, 2),
                      "gb_per_s": round(gemv_bytes(n, k, wl.bits) / (ms * 1e-3) / 1e9, 1)}
     return out
+
+
+def bench_streaming_reference(torch, nbytes, steps=20, warmup=3):
+    """Library streaming rates on the same part, for scale: torch's int32 sum
+    over `nbytes` (a read-only reduction: one pass over the bytes, no
+    arithmetic worth the name) rotating over two copies, and a 1 GiB
+    device-to-device copy (read + write).  Neither is this library's code;
+    they say what plain streaming reaches on the box the decode ran on."""
+    stream = torch.cuda.current_stream()
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(2)]
+    ms_sum, _ = time_launches(torch, lambda i: bufs[i % 2].sum(), steps, warmup, stream)
+    del bufs
+    src = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    ms_copy, _ = time_launches(torch, lambda i: dst.copy_(src), 10, 2, stream)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"sum_int32": {"bytes_read": nbytes, "ms": round(ms_sum, 5),
+                          "gb_per_s": round(nbytes / (ms_sum * 1e-3) / 1e9, 1)},
+            "copy_1gib": {"bytes_moved": 2 << 30, "ms": round(ms_copy, 4),
+                          "gb_per_s": round((2 << 30) / (ms_copy * 1e-3) / 1e9, 1)}}
 
 
 def bench_decode_extras(torch, qmm, wl, sets, steps=20, warmup=3):
@@ -772,6 +793,8 @@ def main():
                     help="run benchmark launches --steps times each and exit (for profilers): a "
                          "comma-separated list of prefill:M:{qkv,o,gateup,down} and moe:M:{gate,up,down,swiglu}")
     ap.add_argument("--ms", metavar="M[,M...]", help="prefill/moe: only these M")
+    ap.add_argument("--decode-bits", type=int, choices=[2, 3, 4, 5, 6, 8, 16], default=4,
+                    help="with --only decode: the decode pass at another weight width (for counters)")
     ap.add_argument("--forces", metavar="F;F...",
                     help="with --launch: time every launch under each QMM_GEMM_FORCE value "
                          "(bm,nb,splits; empty = the planner's choice)")
@@ -838,6 +861,11 @@ def main():
         return
 
     wl = synth.QWEN3_0_6B_Q4_DECODE
+    if args.decode_bits != wl.bits:
+        if args.only != "decode":
+            print("--decode-bits needs --only decode", file=sys.stderr)
+            sys.exit(2)
+        wl = dataclasses.replace(wl, bits=args.decode_bits, name=f"{wl.name}@q{args.decode_bits}")
     log("decode: preparing", wl.name)
     d = bench_decode(torch, qmm, wl, args.steps, args.warmup)
     # one step is one launch of the batched kernel, so the kernel's average
@@ -869,7 +897,8 @@ def main():
                    "weight_copies_alternated": 2},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "qgemv_batched_kernel<4,16,4,64>",
+                     "traffic": traffic if wl.bits == 4 else None,
+                     "kernel": "qgemv_batched_kernel<4,16,4,64>" if wl.bits == 4 else "qgemv_batched_kernel",
                      "bytes_per_launch": d["step_bytes"],
                      "launch_ms_mean": round(d["ms_step"], 5)},
     }
@@ -878,6 +907,7 @@ def main():
         result["decode_context"] = bench_decode_extras(torch, qmm, wl, d["sets"])
         result["decode_context"]["host_dispatch_c"] = dispatch_cost()
         result["decode_context"]["host_dispatch_python"] = python_dispatch_cost(torch, qmm)
+        result["decode_context"]["streaming_reference"] = bench_streaming_reference(torch, d["step_bytes"])
     if args.only == "projections":
         result["projections"] = bench_projections(torch, qmm, wl, d["sets"])
     del d
