@@ -56,6 +56,7 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(f"built {LIB}")
     build_dispatch_cost(verbose)
+    build_stream_probe(verbose)
     return LIB
 
 
@@ -74,6 +75,22 @@ def build_dispatch_cost(verbose: bool = False) -> str:
     if verbose:
         print(f"built {DISPATCH_BIN}")
     return DISPATCH_BIN
+
+
+# Streaming-rate harness (stream_probe.hip): a stand-alone program (no
+# library code) that bench.py runs for the read-only rate of the GPU.
+STREAM_SRC = os.path.join(PKG, "stream_probe.hip")
+STREAM_BIN = os.path.join(PKG, "qmm_stream_probe")
+
+
+def build_stream_probe(verbose: bool = False) -> str:
+    cmd = [HIPCC, *CFLAGS, "-O2", STREAM_SRC, "-o", STREAM_BIN]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on stream_probe.hip:\n{' '.join(cmd)}\n{r.stderr}")
+    if verbose:
+        print(f"built {STREAM_BIN}")
+    return STREAM_BIN
 
 
 # Host-sanitizer build (AddressSanitizer + UndefinedBehaviorSanitizer on the
