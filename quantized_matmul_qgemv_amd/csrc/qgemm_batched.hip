@@ -176,12 +176,15 @@ bool splits_ok(const GemmBatchProblem* probs, int count, int S) {
 // divisible: only split counts that divide every problem's group count
 // and one k half per workgroup (the single-GEMM kernel).
 // f16w: unquantized fp16 weights hold 4x the register bytes of a 4-bit
-// weight ring, so only the one-column-block tiles (nb = 1) are used.
+// weight ring, so only the one-column-block tiles (nb = 1) are used.  The
+// same holds for 5- to 8-bit weights (1.25-2x): on the 2048 x 9728 x 2560
+// GEMM their two-column-block tiles measured 5-20 % slower than 128 x 128
+// (the cost model's constants come from 4-bit launches).
 Choice choose(const GemmBatchProblem* probs, int count, int bits, bool divisible, bool f16w) {
   Choice best{2, 1, false, 1e300};
   for (int ci = 0; ci < (int)(sizeof kCfgs / sizeof kCfgs[0]); ++ci) {
     const TileCfg& c = kCfgs[ci];
-    if (f16w && c.nb != 1) continue;
+    if ((f16w || bits >= 5) && c.nb != 1) continue;
     if (divisible && c.kw != 1) continue;
     const int bn = c.nb * 128;
     for (int S : kSplitChoices) {
