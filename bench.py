@@ -735,7 +735,8 @@ def profile_launch(torch, qmm, spec, reps):
     weights of PROFILE_LAYERS layers, 8 x 57 MB, so that every launch reads
     its weights from HBM as in a full prefill step rather than from the
     last-level cache) or "moe:M:PROJ" (PROJ = gate, up, down or swiglu;
-    routed, over tile-interleaved weights)."""
+    routed, over tile-interleaved weights, rotating over 3 copies of the
+    expert weights for the same reason)."""
     kind, m, what = spec.split(":")
     m = int(m)
     stream = torch.cuda.current_stream()
@@ -758,21 +759,21 @@ def profile_launch(torch, qmm, spec, reps):
                 "tiles": "{bm}x{n}/S{splits}/K{kw}".format(n=h["nb"] * 128, **h)}
     wl = synth.QWEN3_30B_A3B_Q4_MOE
     if "moe" not in _PROFILE_CACHE:
-        _PROFILE_CACHE["moe"] = moe_weights(torch, qmm, wl, 1)[0]
-    wset = _PROFILE_CACHE["moe"]
+        _PROFILE_CACHE["moe"] = moe_weights(torch, qmm, wl, 3)
+    wsets = _PROFILE_CACHE["moe"]
     pi = {"gate": 0, "up": 1, "down": 2, "swiglu": 0}[what]
     a, ids, _ = synth.draw_moe_inputs(wl, m, pi)
     A, I = torch.from_numpy(a).cuda(), torch.from_numpy(ids).cuda()
     plan = qmm.moe_route(I, wl.experts)
-    W, S, B, n, k, per_pair = wset[pi]
+    _, _, _, n, k, per_pair = wsets[0][pi]
     if what == "swiglu":
-        (Wu, Su, Bu, *_) = wset[1]
         H = torch.empty((m * wl.top_k, n), dtype=torch.float16, device="cuda")
-        fn = lambda i: qmm.moe_gate_up_swiglu((W, S, B), (Wu, Su, Bu), A, I, plan, wl.bits, h=H, tiled=True)
+        fn = lambda i: qmm.moe_gate_up_swiglu(wsets[i % 3][0][:3], wsets[i % 3][1][:3], A, I, plan, wl.bits,
+                                              h=H, tiled=True)
         flops = 2 * 2.0 * m * wl.top_k * n * k
     else:
         Y = torch.empty((m * wl.top_k, n), dtype=torch.float32, device="cuda")
-        fn = lambda i: qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, plan=plan, tiled=True)
+        fn = lambda i: qmm.qgemm_grouped(*wsets[i % 3][pi][:3], A, I, wl.bits, per_pair, y=Y, plan=plan, tiled=True)
         flops = 2.0 * m * wl.top_k * n * k
     ms, _ = time_launches(torch, fn, reps, 2, stream)
     return {"launch": spec, "ms_per_launch": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
