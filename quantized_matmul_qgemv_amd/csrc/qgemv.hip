@@ -140,12 +140,12 @@ __device__ __forceinline__ void stage_quarter(const uint32_t (&d)[8], int g, int
 
 template <int BITS, int GS>
 __device__ __forceinline__ void stage_x_store(gptr<uint16_t> x, int groups, const XStage& xs,
-                                              unsigned char* xp, float* cx) {
+                                              unsigned char* xp, float* cx, bool stager) {
   const int quarters = 4 * groups;
 #pragma unroll
   for (int r = 0; r < kXRounds; ++r) {
     const int t = threadIdx.x + r * kGemvThreads;
-    stage_quarter<BITS, GS>(xs.d[r], t >> 2, t & 3, t < quarters, xp, cx);
+    if (r > 0 || stager) stage_quarter<BITS, GS>(xs.d[r], t >> 2, t & 3, t < quarters, xp, cx);
   }
   // quarters beyond the register rounds (k > 8192): load and stage directly
   const int rounds = (quarters + kGemvThreads - 1) / kGemvThreads;  // uniform
@@ -159,6 +159,55 @@ __device__ __forceinline__ void stage_x_store(gptr<uint16_t> x, int groups, cons
     d[4] = v1.x; d[5] = v1.y; d[6] = v1.z; d[7] = v1.w;
     stage_quarter<BITS, GS>(d, t0 >> 2, t0 & 3, t0 < quarters, xp, cx);
   }
+}
+
+// a.x*b.x + a.y*b.y with fp32 accumulation, starting from zero: the
+// three-operand form with an inline 0, where the compiler's own choice (the
+// two-operand form that accumulates in place) first needs a move of 0.
+__device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b) {
+  float d;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// Moves between lanes of one 16-lane row through the DPP operand modifier
+// (no LDS round trip): lane i reads lane i ^ 8 (row_ror:8), i ^ 7
+// (row_half_mirror), i ^ 2 and i ^ 1 (quad permutes).
+constexpr int kDppRor8 = 0x128, kDppHalfMirror = 0x141, kDppXor2 = 0x4E, kDppXor1 = 0xB1;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_read(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sums each of UR per-row partials over the 16 lanes of a row (lane lr =
+// 0..15 of the row's lanes) with the exchanges transposed: the first two
+// exchanges each halve the values a lane carries (a lane keeps the rows its
+// partner does not), so every lane ends with the total of row
+// lr / (16 / UR), held by 16 / UR lanes.  For UR = 4 that is 11 VALU
+// instructions instead of 16 additions and 16 LDS permutes.
+template <int UR>
+__device__ __forceinline__ float row_sum16(const float (&a)[UR], int lr) {
+  static_assert(UR == 1 || UR == 2 || UR == 4, "row_sum16 takes 1, 2 or 4 rows");
+  const bool b3 = (lr & 8) != 0, b2 = (lr & 4) != 0;
+  float v;
+  if constexpr (UR == 4) {
+    // i ^ 8: lanes with bit 3 clear keep rows 0, 1, the others rows 2, 3
+    const float k0 = (b3 ? a[2] : a[0]) + dpp_read<kDppRor8>(b3 ? a[0] : a[2]);
+    const float k1 = (b3 ? a[3] : a[1]) + dpp_read<kDppRor8>(b3 ? a[1] : a[3]);
+    // i ^ 7 flips bit 2: bit 2 picks one row of the pair
+    v = (b2 ? k1 : k0) + dpp_read<kDppHalfMirror>(b2 ? k0 : k1);
+  } else if constexpr (UR == 2) {
+    const float k = (b3 ? a[1] : a[0]) + dpp_read<kDppRor8>(b3 ? a[0] : a[1]);
+    v = k + dpp_read<kDppHalfMirror>(k);
+  } else {
+    v = a[0] + dpp_read<kDppRor8>(a[0]);
+    v += dpp_read<kDppHalfMirror>(v);
+  }
+  // lanes {i, i^8, i^7, i^15} are summed; i ^ 2 and i ^ 1 add the other 12
+  v += dpp_read<kDppXor2>(v);
+  v += dpp_read<kDppXor1>(v);
+  return v;
 }
 
 // Register buffer of one step: UR rows x one group per lane.  3/5/6-bit
@@ -285,8 +334,8 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
           const u32x4 wv = bf.w[u][q];
-          a0[u] = dot2(wv.x, xv.x, a0[u]);
-          a1[u] = dot2(wv.y, xv.y, a1[u]);
+          a0[u] = q == 0 ? dot2_first(wv.x, xv.x) : dot2(wv.x, xv.x, a0[u]);
+          a1[u] = q == 0 ? dot2_first(wv.y, xv.y) : dot2(wv.y, xv.y, a1[u]);
           a0[u] = dot2(wv.z, xv.z, a0[u]);
           a1[u] = dot2(wv.w, xv.w, a1[u]);
         }
@@ -305,13 +354,13 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
           if constexpr (GS == 32) {
             // chunks 0..3 are the first 32-code scale group, 4..7 the second
             float& a = m < 4 ? a0[u] : a1[u];
-            a = dot2(h[0], xr[0], a);
+            a = m % 4 == 0 ? dot2_first(h[0], xr[0]) : dot2(h[0], xr[0], a);
             a = dot2(h[1], xr[1], a);
             a = dot2(h[2], xr[2], a);
             a = dot2(h[3], xr[3], a);
           } else {
-            a0[u] = dot2(h[0], xr[0], a0[u]);
-            a1[u] = dot2(h[1], xr[1], a1[u]);
+            a0[u] = m == 0 ? dot2_first(h[0], xr[0]) : dot2(h[0], xr[0], a0[u]);
+            a1[u] = m == 0 ? dot2_first(h[1], xr[1]) : dot2(h[1], xr[1], a1[u]);
             a0[u] = dot2(h[2], xr[2], a0[u]);
             a1[u] = dot2(h[3], xr[3], a1[u]);
           }
@@ -351,11 +400,11 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
         for (int p = 0; p < PPW; ++p) {
           if constexpr (GS == 32) {
             // words 0 .. WPG/2-1 hold the first 32-code scale group
-            if (j < WPG / 2) a0[u] = dot2(h[p], xr[p], a0[u]);
-            else             a1[u] = dot2(h[p], xr[p], a1[u]);
+            if (j < WPG / 2) a0[u] = j == 0 && p == 0 ? dot2_first(h[p], xr[p]) : dot2(h[p], xr[p], a0[u]);
+            else             a1[u] = j == WPG / 2 && p == 0 ? dot2_first(h[p], xr[p]) : dot2(h[p], xr[p], a1[u]);
           } else {
-            if ((p & 1) == 0) a0[u] = dot2(h[p], xr[p], a0[u]);
-            else              a1[u] = dot2(h[p], xr[p], a1[u]);
+            if ((p & 1) == 0) a0[u] = j == 0 && p == 0 ? dot2_first(h[p], xr[p]) : dot2(h[p], xr[p], a0[u]);
+            else              a1[u] = j == 0 && p == 1 ? dot2_first(h[p], xr[p]) : dot2(h[p], xr[p], a1[u]);
           }
         }
       }
@@ -384,14 +433,23 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
     if (++ct == tcount) {
       if constexpr (WK == 1) {
         // end of a pass: reduce over the row's lanes and store
+        if constexpr (LPR == 16 && UR <= 4) {
+          constexpr int kHold = 16 / UR;  // lanes that end with one row's total
+          const float v = row_sum16<UR>(acc, lr);
+          const int r = lane_row + cp * Cfg::ROWS + (lr / kHold) * Cfg::RPW;
+          if (lr % kHold == 0 && r < row_end) Y[r] = v;
 #pragma unroll
-        for (int u = 0; u < UR; ++u) {
-          float v = acc[u];
+          for (int u = 0; u < UR; ++u) acc[u] = 0.0f;
+        } else {
 #pragma unroll
-          for (int m = LPR / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-          const int r = lane_row + cp * Cfg::ROWS + u * Cfg::RPW;
-          if (lr == 0 && r < row_end) Y[r] = v;
-          acc[u] = 0.0f;
+          for (int u = 0; u < UR; ++u) {
+            float v = acc[u];
+#pragma unroll
+            for (int m = LPR / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+            const int r = lane_row + cp * Cfg::ROWS + u * Cfg::RPW;
+            if (lr == 0 && r < row_end) Y[r] = v;
+            acc[u] = 0.0f;
+          }
         }
       }
       ct = 0;
@@ -404,10 +462,16 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   // after the activation loads, so the staging below waits for x only.
   Buf b0, b1;
   const gptr<uint16_t> X = to_global(P.x);
+  // A wave whose 64 quarter groups of the first staging round all lie past
+  // the end loads and pairs nothing (a wave-uniform branch).  At k = 1024
+  // only the first wave has quarters; the other three would otherwise issue
+  // the whole pairing and (C, X) sequence for nothing, which the 2- and
+  // 3-bit kernels, bound by instruction issue, pay for.
+  const bool stager = (int)(threadIdx.x & ~63u) < 4 * groups;
   XStage xs;
-  stage_x_load(X, groups, xs);
+  if (stager) stage_x_load(X, groups, xs);
   issue(b0);
-  stage_x_store<BITS, GS>(X, groups, xs, xp, cx);
+  stage_x_store<BITS, GS>(X, groups, xs, xp, cx, stager);
   __syncthreads();
 
   for (int st = 0; st < nsteps; st += 2) {
