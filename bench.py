@@ -65,9 +65,9 @@ TRAFFIC = {
     # (KiB per dispatch of qgemv_batched_kernel<4,16,4,64>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 166771.8, "fetch_scale": 1073741824 / (524301.3 * 1024),
-    "write_kib": 1938.7, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "25e3d45c9c446f73672b1ea04b135cff6bed33044d5e94456baa287838a50d60",
+    "fetch_kib": 166885.5, "fetch_scale": 1073741824 / (524301.3 * 1024),
+    "write_kib": 1939.3, "write_scale": 1073741824 / (1048576.0 * 1024),
+    "sources_sha256": "27154c88f91701a78d5bec8214b0a9ecce5f44ea600935c0c39181ea3892df73",
 }
 
 
