@@ -219,7 +219,8 @@ int qmm_qgemm_batched(const void* plan_device, const void* plan_host, void* work
  *   word 0  row tiles in the list     word 1  rows per row tile
  *   word 2  pairs (T * top_k)         word 3  experts E
  *   word 4  pairs whose expert id was outside [0, E)  (byte offset 16)
- *   words 5..7 zero; then the bucketed pair list and the row-tile list.
+ *   words 5..7 zero; then the bucketed pair list, the row-tile list and
+ *   the per-chunk expert counts that the bucketing launches pass between them.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
 size_t qmm_qgemm_grouped_workspace_size(int t, int top_k, int e, int n, int k, int bits,
                                         int group_size);
@@ -237,7 +238,7 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
  * call on it until the process ends; the call allocates nothing, frees
  * nothing and calls no allocating library routine.  The scratch serves
  * every (t, top_k, e) whose qmm_qgemm_grouped_workspace_size is at most
- * 1 MiB (up to about 239,000 pairs, e.g. 29,900 tokens at top-8, with
+ * 1 MiB (up to about 231,000 pairs, e.g. 28,900 tokens at top-8, with
  * E = 128); larger problems are refused with QMM_ERR_WORKSPACE before any
  * launch.  Every call on one GPU shares that GPU's array, so calls that
  * overlap on one GPU (several streams, several host threads) race and must

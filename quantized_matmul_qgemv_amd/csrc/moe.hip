@@ -55,11 +55,15 @@ static int max_row_tiles(int pairs, int experts, int bm) {
   return by_pairs < pairs ? (int)by_pairs : (pairs > 0 ? pairs : 1);
 }
 
+static int route_chunks(int pairs, int experts, int* chunk);
+
 size_t grouped_workspace_bytes(int t, int top_k, int e, int n) {
   (void)n;
   const long pairs = (long)t * top_k;
   const long tiles = max_row_tiles((int)pairs, e, 32);
-  return align_up((size_t)(kPlanHeaderInts + pairs + 3 * tiles) * sizeof(int32_t), 256);
+  int chunk;
+  const long counts = (long)route_chunks((int)pairs, e, &chunk) * (e + 1);
+  return align_up((size_t)(kPlanHeaderInts + pairs + 3 * tiles + counts) * sizeof(int32_t), 256);
 }
 
 // Inclusive sum over the 64 lanes of a wave.
@@ -73,50 +77,100 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
-// Ids held in registers per thread (pairs beyond 16 * 1024 are read twice).
-constexpr int kBucketIdsPerThread = 16;
+// Bucketing runs as two launches over chunks of the pair list, so that the
+// LDS atomics that count and place the pairs are spread over many CUs (one
+// workgroup doing all of them was bound by same-address conflicts on its one
+// LDS: about 20 us for 16384 pairs).
+//   count:   workgroup c histograms the expert ids of pairs
+//            [c * chunk, (c + 1) * chunk) into counts[c][0 .. E] (slot E:
+//            out-of-range ids).
+//   scatter: every workgroup sums the count columns (all chunks, and the
+//            chunks before its own), scans them over the experts into bucket
+//            starts, and places its own chunk's pairs from there; workgroup
+//            0 also writes the tile list and the header.
+// The counts (chunks x (E + 1) words) follow the tile list in the workspace.
+constexpr int kCountThreads = 256;
+constexpr int kRouteChunkMin = 256;     // pairs per chunk at least
+constexpr int kRouteMaxChunks = 64;
+constexpr int kRouteCountWords = 32768; // chunks x (E + 1) at most
 
-__global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
-    const int32_t* __restrict__ ids, int pairs, int experts, int bm, int32_t* __restrict__ ws) {
+static int route_chunks(int pairs, int experts, int* chunk) {
+  int g = kRouteCountWords / (experts + 1);
+  g = g < 1 ? 1 : (g > kRouteMaxChunks ? kRouteMaxChunks : g);
+  int c = (pairs + g - 1) / g;
+  c = c < kRouteChunkMin ? kRouteChunkMin : c;
+  *chunk = c;
+  return pairs > 0 ? (pairs + c - 1) / c : 1;
+}
+
+static int32_t* route_counts(int32_t* ws, int pairs, int experts) {
+  return ws + kPlanHeaderInts + pairs + 3 * (size_t)max_row_tiles(pairs, experts, 32);
+}
+
+__global__ __launch_bounds__(kCountThreads) void moe_count_kernel(const int32_t* __restrict__ ids, int pairs,
+                                                                   int experts, int chunk,
+                                                                   int32_t* __restrict__ counts) {
+  __shared__ int32_t h[kMaxExperts + 1];
+  for (int i = threadIdx.x; i <= experts; i += kCountThreads) h[i] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * chunk;
+  const int p1 = p0 + chunk < pairs ? p0 + chunk : pairs;
+  for (int p = p0 + threadIdx.x; p < p1; p += kCountThreads) {
+    const int e = ids[p];
+    atomicAdd(&h[e >= 0 && e < experts ? e : experts], 1);
+  }
+  __syncthreads();
+  int32_t* row = counts + (size_t)blockIdx.x * (experts + 1);
+  for (int i = threadIdx.x; i <= experts; i += kCountThreads) row[i] = h[i];
+}
+
+__global__ __launch_bounds__(kBucketThreads) void moe_scatter_kernel(
+    const int32_t* __restrict__ ids, int pairs, int experts, int bm, int chunk, int chunks,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ ws) {
   static_assert(kBucketThreads == kMaxExperts, "one thread per expert slot");
   constexpr int kWaves = kBucketThreads / 64;
-  __shared__ int32_t cnt[kMaxExperts];
   __shared__ int32_t cursor[kMaxExperts];
+  __shared__ int32_t total[kMaxExperts + 1];   // per slot: pairs in all chunks
+  __shared__ int32_t earlier[kMaxExperts + 1]; // per slot: pairs in the chunks before this one
   __shared__ int32_t wtot[2][kWaves];
-  __shared__ int32_t bad_count;   // pairs with an id outside [0, experts)
   __shared__ int32_t bad_cursor;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int me = blockIdx.x;
   int32_t* sorted = ws + kPlanHeaderInts;
   MoeTile* tiles = reinterpret_cast<MoeTile*>(ws + kPlanHeaderInts + pairs);
+  const int stride = experts + 1;
 
-  cnt[tid] = 0;
-  if (tid == 0) bad_count = 0;
-  int myid[kBucketIdsPerThread];
+  // column sums over the chunks x (E + 1) counts, all threads taking words
+  // in turn: a batch of independent loads per thread, then LDS additions
+  for (int i = tid; i <= experts; i += kBucketThreads) total[i] = earlier[i] = 0;
+  __syncthreads();
+  const int ncounts = chunks * stride;
+  constexpr int kSumLoads = 16;
+  for (int base = 0; base < ncounts; base += kBucketThreads * kSumLoads) {
+    int v[kSumLoads];
 #pragma unroll
-  for (int i = 0; i < kBucketIdsPerThread; ++i) {
-    const int p = tid + i * kBucketThreads;
-    const int e = p < pairs ? ids[p] : -1;
-    // -1: no pair; -2: a pair whose id is out of range
-    myid[i] = p >= pairs ? -1 : (e >= 0 && e < experts) ? e : -2;
+    for (int j = 0; j < kSumLoads; ++j) {
+      const int i = base + j * kBucketThreads + tid;
+      v[j] = i < ncounts ? counts[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kSumLoads; ++j) {
+      if (v[j] == 0) continue;
+      const int i = base + j * kBucketThreads + tid;
+      const int w = i / stride;
+      const int e = i - w * stride;
+      atomicAdd(&total[e], v[j]);
+      if (w < me) atomicAdd(&earlier[e], v[j]);
+    }
   }
   __syncthreads();
-  // histogram of expert ids; out-of-range ids are counted apart
-#pragma unroll
-  for (int i = 0; i < kBucketIdsPerThread; ++i) {
-    if (myid[i] >= 0) atomicAdd(&cnt[myid[i]], 1);
-    else if (myid[i] == -2) atomicAdd(&bad_count, 1);
-  }
-  for (int p = tid + kBucketIdsPerThread * kBucketThreads; p < pairs; p += kBucketThreads) {
-    const int e = ids[p];
-    if (e >= 0 && e < experts) atomicAdd(&cnt[e], 1);
-    else atomicAdd(&bad_count, 1);
-  }
-  __syncthreads();
+  const int c = tid < experts ? total[tid] : 0;
+  const int before = tid < experts ? earlier[tid] : 0;
+  const int bad = tid == 0 ? total[experts] : 0;
   // exclusive scans of the pair counts and of the row-tile counts:
   // within each wave by lane shuffles, then over the 16 wave totals
-  const int c = tid < experts ? cnt[tid] : 0;
   const int tl = (c + bm - 1) / bm;
   const int ic = wave_inclusive_sum(c);
   const int it = wave_inclusive_sum(tl);
@@ -134,47 +188,61 @@ __global__ __launch_bounds__(kBucketThreads) void moe_bucket_kernel(
       wtot[0][lane] = s0 - a0;  // exclusive prefix of the wave totals
       wtot[1][lane] = s1 - a1;
     }
-    if (lane == kWaves - 1) {
-      // the out-of-range pairs follow every valid bucket, with tiles of their own
-      const int bad = bad_count;
-      const int bad_tiles = (bad + bm - 1) / bm;
-      bad_cursor = s0;
+    // the out-of-range pairs follow every valid bucket, with tiles of their own
+    const int valid = __shfl(s0, kWaves - 1, 64);
+    const int tiles_valid = __shfl(s1, kWaves - 1, 64);
+    const int nbad = __shfl(bad, 0, 64);
+    if (lane == 0) bad_cursor = valid + earlier[experts];
+    if (me == 0 && lane == 0) {
+      const int bad_tiles = (nbad + bm - 1) / bm;
       for (int i = 0; i < bad_tiles; ++i)
-        tiles[s1 + i] = MoeTile{-1, s0 + i * bm, bad - i * bm < bm ? bad - i * bm : bm};
-      ws[0] = s1 + bad_tiles;
-      ws[4] = bad;
+        tiles[tiles_valid + i] = MoeTile{-1, valid + i * bm, nbad - i * bm < bm ? nbad - i * bm : bm};
+      ws[0] = tiles_valid + bad_tiles;
+      ws[4] = nbad;
     }
   }
   __syncthreads();
   const int start = wtot[0][wave] + ic - c;
   const int tstart = wtot[1][wave] + it - tl;
-  cursor[tid] = start;
+  cursor[tid] = start + before;
   __syncthreads();
-  // scatter pair indices into their expert's bucket
-#pragma unroll
-  for (int i = 0; i < kBucketIdsPerThread; ++i) {
-    if (myid[i] >= 0) sorted[atomicAdd(&cursor[myid[i]], 1)] = tid + i * kBucketThreads;
-    else if (myid[i] == -2) sorted[atomicAdd(&bad_cursor, 1)] = tid + i * kBucketThreads;
-  }
-  for (int p = tid + kBucketIdsPerThread * kBucketThreads; p < pairs; p += kBucketThreads) {
+  // place this chunk's pairs in their expert's bucket
+  const int p0 = me * chunk;
+  const int p1 = p0 + chunk < pairs ? p0 + chunk : pairs;
+  for (int p = p0 + tid; p < p1; p += kBucketThreads) {
     const int e = ids[p];
-    if (e >= 0 && e < experts) sorted[atomicAdd(&cursor[e], 1)] = p;
-    else sorted[atomicAdd(&bad_cursor, 1)] = p;
+    sorted[e >= 0 && e < experts ? atomicAdd(&cursor[e], 1) : atomicAdd(&bad_cursor, 1)] = p;
   }
-  if (tid < experts) {
-    for (int i = 0; i < tl; ++i) {
-      const int rows = c - i * bm < bm ? c - i * bm : bm;
-      tiles[tstart + i] = MoeTile{tid, start + i * bm, rows};
+  if (me == 0) {
+    if (tid < experts) {
+      for (int i = 0; i < tl; ++i) {
+        const int rows = c - i * bm < bm ? c - i * bm : bm;
+        tiles[tstart + i] = MoeTile{tid, start + i * bm, rows};
+      }
+    }
+    if (tid == 0) {  // what the plan was built for (checked by every grouped kernel)
+      ws[1] = bm;
+      ws[2] = pairs;
+      ws[3] = experts;
+      ws[5] = 0;
+      ws[6] = 0;
+      ws[7] = 0;
     }
   }
-  if (tid == 0) {  // what the plan was built for (checked by every grouped kernel)
-    ws[1] = bm;
-    ws[2] = pairs;
-    ws[3] = experts;
-    ws[5] = 0;
-    ws[6] = 0;
-    ws[7] = 0;
-  }
+}
+
+static hipError_t launch_bucket(const int32_t* ids, int pairs, int experts, int bm, int32_t* ws,
+                                hipStream_t st) {
+  int chunk;
+  const int chunks = route_chunks(pairs, experts, &chunk);
+  int32_t* counts = route_counts(ws, pairs, experts);
+  hipLaunchKernelGGL(moe_count_kernel, dim3(chunks), dim3(kCountThreads), 0, st, ids, pairs, experts, chunk,
+                     counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(chunks), dim3(kBucketThreads), 0, st, ids, pairs, experts, bm,
+                     chunk, chunks, counts, ws);
+  return hipGetLastError();
 }
 
 // Output of a grouped launch that cannot be computed: a plan built for
@@ -439,9 +507,7 @@ hipError_t grouped_scratch(void** ptr) {
 hipError_t launch_moe_route(const int32_t* ids, int t, int top_k, int e, void* plan, hipStream_t st) {
   int bm, nb;
   moe_tile(t * top_k, e, &bm, &nb);
-  hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(kBucketThreads), 0, st, ids, t * top_k, e, bm,
-                     reinterpret_cast<int32_t*>(plan));
-  return hipGetLastError();
+  return launch_bucket(ids, t * top_k, e, bm, reinterpret_cast<int32_t*>(plan), st);
 }
 
 template <int BITS, int BM, int NB, bool SBQ>
@@ -449,9 +515,7 @@ static hipError_t launch_grouped_tile(const GroupedArgs& a, int32_t* ws, bool bu
   constexpr int BN = 4 * NB * 32;
   const int pairs = a.t * a.top_k;
   if (bucket) {
-    hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(kBucketThreads), 0, st, a.ids, pairs, a.e,
-                       BM, ws);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_bucket(a.ids, pairs, a.e, BM, ws, st);
     if (err != hipSuccess) return err;
   }
   const int n_tiles = (a.n + BN - 1) / BN;
@@ -537,8 +601,39 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   y[i] = acc;
 }
 
+// The same over four adjacent columns per thread (16-byte loads and stores;
+// n a multiple of 4, both row arrays 16-byte aligned): each column's sum is
+// formed exactly as above, so the results are bit-identical.
+__global__ __launch_bounds__(256) void moe_combine4_kernel(const float4* __restrict__ y_pairs,
+                                                           const float* __restrict__ weights,
+                                                           float4* __restrict__ y, int t, int top_k,
+                                                           int n4) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)t * n4) return;
+  const long tok = i / n4;
+  const long col = i % n4;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 8
+  for (int j = 0; j < top_k; ++j) {
+    const float w = weights[tok * top_k + j];
+    const float4 v = y_pairs[(tok * top_k + j) * n4 + col];
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
+  y[i] = acc;
+}
+
 hipError_t launch_moe_combine(const float* y_pairs, const float* weights, float* y, int t, int top_k,
                               int n, hipStream_t st) {
+  if (n % 4 == 0 && reinterpret_cast<uintptr_t>(y_pairs) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) {
+    const long count = (long)t * (n / 4);
+    hipLaunchKernelGGL(moe_combine4_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<const float4*>(y_pairs), weights, reinterpret_cast<float4*>(y), t,
+                       top_k, n / 4);
+    return hipGetLastError();
+  }
   const long count = (long)t * n;
   hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
                      y_pairs, weights, y, t, top_k, n);

@@ -130,7 +130,7 @@ def test_grouped_noalloc_errors(L):
     refuses, before any HIP call, a problem whose bucket lists exceed its
     1 MiB static scratch."""
     assert _lib.QMM_GROUPED_SCRATCH_BYTES == 1 << 20
-    ok = L.qmm_qgemm_grouped_workspace_size(29000, 8, 128, 768, 2048, 4, 64)
+    ok = L.qmm_qgemm_grouped_workspace_size(28900, 8, 128, 768, 2048, 4, 64)
     assert ok <= _lib.QMM_GROUPED_SCRATCH_BYTES
     big = L.qmm_qgemm_grouped_workspace_size(40000, 8, 128, 768, 2048, 4, 64)
     assert big > _lib.QMM_GROUPED_SCRATCH_BYTES
@@ -151,11 +151,17 @@ def test_route_size_counts_out_of_range_bucket(L):
     """The plan has an 8-word header, one word per pair and three per row
     tile; the row-tile bound counts the E valid buckets plus one for pairs
     whose expert id is out of range (every tile holds at least one pair, so
-    never more tiles than pairs)."""
-    for t, top_k, e in ((512, 8, 128), (2048, 8, 128), (1, 1, 1), (3, 2, 1000), (5, 8, 4)):
+    never more tiles than pairs).  After them come E + 1 counts per chunk of
+    the pair list: chunks of at least 256 pairs, at most 64 chunks and at
+    most 32768 counts."""
+    for t, top_k, e in ((512, 8, 128), (2048, 8, 128), (1, 1, 1), (3, 2, 1000), (5, 8, 4),
+                        (40000, 8, 128), (300, 8, 1000)):
         pairs = t * top_k
         tiles = min((pairs + 31) // 32 + e + 1, pairs)
-        want = -(-(8 + pairs + 3 * tiles) * 4 // 256) * 256
+        g = max(1, min(64, 32768 // (e + 1)))
+        chunk = max(256, -(-pairs // g))
+        chunks = -(-pairs // chunk)
+        want = -(-(8 + pairs + 3 * tiles + chunks * (e + 1)) * 4 // 256) * 256
         assert L.qmm_moe_route_size(t, top_k, e) == want, (t, top_k, e)
         assert L.qmm_qgemm_grouped_workspace_size(t, top_k, e, 768, 2048, 4, 64) == want
 

@@ -729,19 +729,20 @@ def test_routed_grouped_equals_grouped():
     assert bool(torch.isnan(hh).all()), "SwiGLU output over a foreign plan must be all NaN"
 
 
-@pytest.mark.parametrize("bits", [4, 8])
-def test_moe_out_of_range_ids_nan_and_counted(bits):
+@pytest.mark.parametrize("bits,t", [(4, 40), (8, 40), (4, 300)])
+def test_moe_out_of_range_ids_nan_and_counted(bits, t):
     """Pairs whose expert id lies outside [0, E) (here -1, E, E + 100 and a
     large negative id) are not computed: their output rows are NaN in the
     self-bucketing, routed and fused SwiGLU products, every other row matches
-    the oracle, and the plan header (byte offset 16) counts them."""
-    say("moe out-of-range ids", bits)
-    t, top_k, e, hidden, inter = 40, 4, 8, 128, 160
-    r = np.random.default_rng([948, bits])
+    the oracle, and the plan header (byte offset 16) counts them.  At t = 300
+    the 1200 pairs are bucketed in several chunks, with bad ids in three."""
+    say("moe out-of-range ids", bits, t)
+    top_k, e, hidden, inter = 4, 8, 128, 160
+    r = np.random.default_rng([948, bits, t])
     ids = np.ascontiguousarray(synth.topk_ids(r.standard_normal((t, e)), top_k), dtype=np.int32)
     flat = ids.reshape(-1)
-    bad_at = [0, 5, 6, 17, 63, t * top_k - 1]
-    for i, v in zip(bad_at, (-1, e, e + 100, -(1 << 30), e, -1)):
+    bad_at = [0, 5, 6, 17, 63, t * top_k - 1] + ([700, 701] if t * top_k > 800 else [])
+    for i, v in zip(bad_at, (-1, e, e + 100, -(1 << 30), e, -1, e + 1, -5)):
         flat[i] = v
     bad = np.zeros(t * top_k, dtype=bool)
     bad[bad_at] = True
@@ -768,6 +769,40 @@ def test_moe_out_of_range_ids_nan_and_counted(bits):
         assert_close(got[~bad], (hw if name == "swiglu" else want)[~bad], f"{name} valid rows")
     assert torch.equal(torch.nan_to_num(y0, nan=-7.0), torch.nan_to_num(y1, nan=-7.0)), \
         "routed differs from self-bucketing"
+
+
+@pytest.mark.parametrize("t,top_k,e", [(2048, 8, 128), (37, 3, 5), (700, 8, 1000)])
+def test_moe_route_plan_is_a_bucketing(t, top_k, e):
+    """The routing plan is checked for what is unique about it: the header
+    words, a sorted pair list that is a permutation of the pairs with each
+    expert's pairs contiguous and the buckets in expert order (out-of-range
+    pairs last), and a tile list that covers every bucket in order with
+    tiles of at most the header's row count.  The order of pairs inside a
+    bucket is not fixed (atomic placement) and is not compared."""
+    say("moe route plan", t, top_k, e)
+    r = np.random.default_rng([947, t, e])
+    ids = np.ascontiguousarray(synth.topk_ids(r.standard_normal((t, e)), min(top_k, e)), dtype=np.int32)
+    flat = ids.reshape(-1)
+    bad = r.choice(flat.size, size=min(9, flat.size // 4), replace=False)
+    flat[bad] = np.where(np.arange(bad.size) % 2 == 0, -1, e + 3)
+    plan = qmm.moe_route(dev(ids), e)
+    torch.cuda.synchronize()
+    words = host(plan.view(torch.int32)).astype(np.int64)
+    pairs = flat.size
+    ntiles, bm, hp, he, nbad = (int(v) for v in words[:5])
+    assert (hp, he, nbad) == (pairs, e, bad.size) and list(words[5:8]) == [0, 0, 0]
+    sorted_ = words[8:8 + pairs]
+    assert np.array_equal(np.sort(sorted_), np.arange(pairs)), "sorted list is not a permutation"
+    key = np.where((flat >= 0) & (flat < e), flat, e)   # out-of-range pairs sort last
+    assert np.all(np.diff(key[sorted_]) >= 0), "buckets are not contiguous in expert order"
+    tiles = words[8 + pairs:8 + pairs + 3 * ntiles].reshape(ntiles, 3)
+    pos = 0
+    for ex, start, rows in tiles:
+        assert start == pos and 1 <= rows <= bm, (ex, start, rows, pos)
+        seg = key[sorted_[start:start + rows]]
+        assert np.all(seg == (e if ex < 0 else ex)), (ex, start, rows)
+        pos += rows
+    assert pos == pairs, "tiles do not cover the pair list"
 
 
 # ---------------------------------------------------- MoE FFN block (fused) --
@@ -888,6 +923,16 @@ def test_moe_ffn_block_chain():
     yp = r.standard_normal((t * top_k, 333)).astype(np.float32)
     got = qmm.moe_combine(torch.from_numpy(yp).cuda(), W)
     assert_close(host(got), oracle.moe_combine_f64(yp, wts.astype(np.float32)), "combine")
+    # the four-column kernel (n a multiple of 4, 16-byte aligned rows) and the
+    # one-column kernel (the same rows 4 bytes further on) give identical bits
+    yp4 = torch.from_numpy(r.standard_normal((t * top_k, 336)).astype(np.float32)).cuda()
+    buf = torch.empty(yp4.numel() + 1, dtype=torch.float32, device="cuda")
+    buf[1:].copy_(yp4.reshape(-1))
+    shifted = buf[1:].view(t * top_k, 336)
+    assert shifted.data_ptr() % 16 != 0
+    y4 = qmm.moe_combine(yp4, W)
+    assert torch.equal(y4, qmm.moe_combine(shifted, W)), "combine: vector and scalar kernels differ"
+    assert_close(host(y4), oracle.moe_combine_f64(host(yp4), wts.astype(np.float32)), "combine n=336")
 
 
 
