@@ -49,42 +49,153 @@ struct GemvCfg {
   static constexpr int ROWS = WR * UR * RPW;   // rows per workgroup pass
 };
 
+// a.x*b.x + a.y*b.y with fp32 accumulation, starting from zero: the
+// three-operand form with an inline 0, where the compiler's own choice (the
+// two-operand form that accumulates in place) first needs a move of 0.
+__device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b) {
+  float d;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// 3-bit pairing of the GEMV.  A 32-code half of a 64-code group is 96 bits
+// (three words); code c sits at bit 3c.  Each pair (c1, c2) is read from a
+// 32-bit window of the half starting at bit s: c1 at offset o1 = 3*c1 - s of
+// the low 16 bits, c2 at offset o2 = 3*c2 - s - 16 of the high 16 bits, both
+// with o + 3 <= 10, so that ONE AND-OR with the magic 2^(10-o) per half turns
+// the window into the fp16 pair (2^(10-o1) + q1, 2^(10-o2) + q2).  Windows at
+// s = 0, 32, 64 are the words themselves; the others cost one funnel shift
+// (s = 6, 12, 41) or one shift (s = 71, inside the third word), so a half
+// costs 4 shifts + 16 AND-ORs + 16 dot products (72 VALU per group, against
+// 102 for the byte-permute chunk unpack).  The 16 (s, c1, c2) were chosen by
+// an exact-cover search over all windows for the fewest shifts and then the
+// fewest distinct (o1, o2) (7, i.e. 7 magics held in registers).  Slot p of
+// a half is the pair below; the staging writes (x[c1], x[c2]) there.
+struct Pair3 {
+  int s, c1, c2;
+  constexpr int o1() const { return 3 * c1 - s; }
+  constexpr int o2() const { return 3 * c2 - s - 16; }
+};
+constexpr Pair3 kPair3[16] = {{0, 0, 6},   {0, 1, 7},   {6, 2, 8},   {6, 3, 9},
+                              {12, 4, 10}, {12, 5, 11}, {32, 12, 17}, {32, 13, 18},
+                              {41, 14, 19}, {41, 15, 20}, {41, 16, 21}, {64, 22, 28},
+                              {64, 23, 27}, {71, 24, 29}, {71, 25, 30}, {71, 26, 31}};
+
+constexpr bool pair3_table_ok() {
+  bool seen[32] = {};
+  for (const Pair3& p : kPair3) {
+    if (p.o1() < 0 || p.o1() + 3 > 10 || p.o2() < 0 || p.o2() + 3 > 10) return false;
+    if (seen[p.c1] || seen[p.c2]) return false;
+    seen[p.c1] = seen[p.c2] = true;
+  }
+  return true;
+}
+static_assert(pair3_table_ok(), "3-bit pairs must cover the half once, each code inside its window");
+
+// Code bits kept and magic exponents set by the AND-OR of a pair.
+constexpr uint32_t pair3_mask(const Pair3& p) { return (7u << p.o1()) | (7u << (16 + p.o2())); }
+constexpr uint32_t pair3_magic(const Pair3& p) {
+  return ((uint32_t)(25 - p.o1()) << 10) | ((uint32_t)(25 - p.o2()) << 26);
+}
+
+// Window of the half w[0..2] starting at bit s (bits past the half read 0
+// and are masked off).
+template <int S>
+__device__ __forceinline__ uint32_t half_window(const uint32_t* w) {
+  constexpr int j = S / 32, r = S % 32;
+  if constexpr (r == 0) return w[j];
+  else if constexpr (j + 1 < 3) return __builtin_amdgcn_alignbit(w[j + 1], w[j], r);
+  else return w[j] >> r;
+}
+
+// Pair slot P of a half: window, AND-OR into the fp16 pair, dot product
+// with the staged activations (the first slot of a half starts from zero).
+template <int P>
+__device__ __forceinline__ void slot3(const uint32_t* w, uint32_t x, float& a) {
+  constexpr Pair3 p = kPair3[P];
+  const uint32_t hp = and_or(half_window<p.s>(w), pair3_mask(p), pair3_magic(p));
+  a = P == 0 ? dot2_first(hp, x) : dot2(hp, x, a);
+}
+
 // Stage x[0 .. 64*groups) into LDS: paired halves plus (C[g], X[g]).  Four
 // consecutive threads share a group (16 codes each), so the staging that
 // every workgroup waits for at its barrier is short.  It is split in two:
 // stage_x_load issues the activation loads (before the weight loads, so
 // that waiting for x never waits for the weight stream, loads completing
-// in order) and stage_x_store pairs, sums and writes them to LDS.
+// in order) and stage_x_store pairs, sums and writes them to LDS.  For
+// 3-bit weights a thread builds 8 pair slots of one 32-code half, whose
+// codes lie anywhere in the half, so it holds the whole half (32 codes).
 constexpr int kXRounds = 1;  // quarter-groups per thread held in registers (k <= 4096)
 
+template <int BITS>
+constexpr int x_words() { return BITS == 3 ? 16 : 8; }  // activation dwords per thread
+
+template <int BITS>
 struct XStage {
-  uint32_t d[kXRounds][8];
+  uint32_t d[kXRounds][x_words<BITS>()];
 };
 
-__device__ __forceinline__ void stage_x_load(gptr<uint16_t> x, int groups, XStage& xs) {
+// The activations a staging thread t needs: its quarter (16 codes), or for
+// 3-bit weights the 32-code half its quarter belongs to.
+template <int BITS>
+__device__ __forceinline__ void load_quarter(gptr<uint16_t> x, int t, uint32_t (&d)[x_words<BITS>()]) {
+  constexpr int NV = x_words<BITS>() / 4;
+  const size_t off = BITS == 3 ? (size_t)(t >> 2) * 64 + ((t >> 1) & 1) * 32 : (size_t)(t >> 2) * 64 + (t & 3) * 16;
+  gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(x + off);
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const u32x4 q = src[v];
+    d[4 * v] = q.x; d[4 * v + 1] = q.y; d[4 * v + 2] = q.z; d[4 * v + 3] = q.w;
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void stage_x_load(gptr<uint16_t> x, int groups, XStage<BITS>& xs) {
 #pragma unroll
   for (int r = 0; r < kXRounds; ++r) {
     int t = threadIdx.x + r * kGemvThreads;
     const int last = 4 * groups - 1;
     t = t < last ? t : last;  // unpredicated: repeat the last quarter
-    gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(x + (size_t)(t >> 2) * 64 + (t & 3) * 16);
-    const u32x4 v0 = src[0], v1 = src[1];
-    xs.d[r][0] = v0.x; xs.d[r][1] = v0.y; xs.d[r][2] = v0.z; xs.d[r][3] = v0.w;
-    xs.d[r][4] = v1.x; xs.d[r][5] = v1.y; xs.d[r][6] = v1.z; xs.d[r][7] = v1.w;
+    load_quarter<BITS>(x, t, xs.d[r]);
   }
 }
 
-// One quarter group (16 codes) -> paired halves in LDS and its share of (C, X).
-template <int BITS, int GS>
-__device__ __forceinline__ void stage_quarter(const uint32_t (&d)[8], int g, int part, bool on,
-                                              unsigned char* xp, float* cx) {
+// fp16 bits of activation c from dwords holding activations in natural order.
+template <int N>
+__device__ __forceinline__ uint32_t x_half(const uint32_t (&d)[N], int c) {
+  return (d[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
+}
+
+// Pair slots and (C, X) shares of one staging thread: out[0..7] are the 8
+// dwords it writes at pair index part*8 of its group.
+template <int BITS>
+__device__ __forceinline__ void build_quarter(const uint32_t (&d)[x_words<BITS>()], int part, uint32_t (&out)[8],
+                                              float& csum, float& xsum) {
   using F = Fmt<BITS>;
-  float csum = 0.0f, xsum = 0.0f;
-  uint32_t out[8];
+  csum = 0.0f;
+  xsum = 0.0f;
   if constexpr (F::F16W) {
     // fp16 weights: x in natural order, no magic offsets (C = 0)
 #pragma unroll
     for (int i = 0; i < 8; ++i) out[i] = d[i];
+  } else if constexpr (BITS == 3) {
+    // slots sub*8 .. sub*8+7 of the thread's half (sub = part & 1)
+    const bool sub = (part & 1) != 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const Pair3 p0 = kPair3[j], p1 = kPair3[8 + j];
+      const uint32_t v0 = x_half(d, p0.c1) | (x_half(d, p0.c2) << 16);
+      const uint32_t v1 = x_half(d, p1.c1) | (x_half(d, p1.c2) << 16);
+      out[j] = sub ? v1 : v0;
+      const float xl = f16_bits_to_f32((uint16_t)(out[j] & 0xFFFFu));
+      const float xh = f16_bits_to_f32((uint16_t)(out[j] >> 16));
+      const float ml = sub ? (float)(1 << (10 - p1.o1())) : (float)(1 << (10 - p0.o1()));
+      const float mh = sub ? (float)(1 << (10 - p1.o2())) : (float)(1 << (10 - p0.o2()));
+      csum += ml * xl;
+      csum += mh * xh;
+      xsum += xl;
+      xsum += xh;
+    }
   } else if constexpr (F::CHUNKED) {
     // chunk pairs are adjacent codes: x stays in natural order
 #pragma unroll
@@ -108,8 +219,8 @@ __device__ __forceinline__ void stage_quarter(const uint32_t (&d)[8], int g, int
       for (int p = 0; p < PPW; ++p) {
         const int klo = wd * C + pair_lo<BITS>(p);
         const int khi = wd * C + pair_hi<BITS>(p);
-        const uint32_t lo = (d[klo >> 1] >> (16 * (klo & 1))) & 0xFFFFu;
-        const uint32_t hi = (d[khi >> 1] >> (16 * (khi & 1))) & 0xFFFFu;
+        const uint32_t lo = x_half(d, klo);
+        const uint32_t hi = x_half(d, khi);
         out[wd * PPW + p] = lo | (hi << 16);
         const float xl = f16_bits_to_f32((uint16_t)lo);
         const float xh = f16_bits_to_f32((uint16_t)hi);
@@ -120,6 +231,15 @@ __device__ __forceinline__ void stage_quarter(const uint32_t (&d)[8], int g, int
       }
     }
   }
+}
+
+// One quarter group -> its pair slots in LDS and its share of (C, X).
+template <int BITS, int GS>
+__device__ __forceinline__ void stage_quarter(const uint32_t (&d)[x_words<BITS>()], int g, int part, bool on,
+                                              unsigned char* xp, float* cx) {
+  float csum, xsum;
+  uint32_t out[8];
+  build_quarter<BITS>(d, part, out, csum, xsum);
   if (on) {
     // pairs of this quarter: 8 dwords at pair index part*8 of the group
     u32x4* dst = reinterpret_cast<u32x4*>(xp + (size_t)g * kXStride + part * 32);
@@ -139,7 +259,7 @@ __device__ __forceinline__ void stage_quarter(const uint32_t (&d)[8], int g, int
 }
 
 template <int BITS, int GS>
-__device__ __forceinline__ void stage_x_store(gptr<uint16_t> x, int groups, const XStage& xs,
+__device__ __forceinline__ void stage_x_store(gptr<uint16_t> x, int groups, const XStage<BITS>& xs,
                                               unsigned char* xp, float* cx, bool stager) {
   const int quarters = 4 * groups;
 #pragma unroll
@@ -147,27 +267,15 @@ __device__ __forceinline__ void stage_x_store(gptr<uint16_t> x, int groups, cons
     const int t = threadIdx.x + r * kGemvThreads;
     if (r > 0 || stager) stage_quarter<BITS, GS>(xs.d[r], t >> 2, t & 3, t < quarters, xp, cx);
   }
-  // quarters beyond the register rounds (k > 8192): load and stage directly
+  // quarters beyond the register rounds (k > 4096): load and stage directly
   const int rounds = (quarters + kGemvThreads - 1) / kGemvThreads;  // uniform
   for (int r = kXRounds; r < rounds; ++r) {
     const int t0 = threadIdx.x + r * kGemvThreads;
     const int t = t0 < quarters ? t0 : quarters - 1;
-    gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(x + (size_t)(t >> 2) * 64 + (t & 3) * 16);
-    uint32_t d[8];
-    const u32x4 v0 = src[0], v1 = src[1];
-    d[0] = v0.x; d[1] = v0.y; d[2] = v0.z; d[3] = v0.w;
-    d[4] = v1.x; d[5] = v1.y; d[6] = v1.z; d[7] = v1.w;
+    uint32_t d[x_words<BITS>()];
+    load_quarter<BITS>(x, t, d);
     stage_quarter<BITS, GS>(d, t0 >> 2, t0 & 3, t0 < quarters, xp, cx);
   }
-}
-
-// a.x*b.x + a.y*b.y with fp32 accumulation, starting from zero: the
-// three-operand form with an inline 0, where the compiler's own choice (the
-// two-operand form that accumulates in place) first needs a move of 0.
-__device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b) {
-  float d;
-  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
-  return d;
 }
 
 // Moves between lanes of one 16-lane row through the DPP operand modifier
@@ -340,6 +448,33 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
           a1[u] = dot2(wv.w, xv.w, a1[u]);
         }
       }
+    } else if constexpr (BITS == 3) {
+      // window pairs (kPair3): half h of the group is words 3h .. 3h+2 and
+      // its 16 pair slots are dwords 16h .. 16h+15 of the group's x; the
+      // two halves accumulate apart (they are the two scale groups of 32)
+      auto half = [&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        auto quad = [&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          const u32x4 xv = reinterpret_cast<const u32x4*>(xg)[4 * h + q];
+          const uint32_t xr[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int u = 0; u < UR; ++u) {
+            float& a = h == 0 ? a0[u] : a1[u];
+            const uint32_t* w = bf.w[u] + 3 * h;
+            slot3<4 * q + 0>(w, xr[0], a);
+            slot3<4 * q + 1>(w, xr[1], a);
+            slot3<4 * q + 2>(w, xr[2], a);
+            slot3<4 * q + 3>(w, xr[3], a);
+          }
+        };
+        quad(std::integral_constant<int, 0>{});
+        quad(std::integral_constant<int, 1>{});
+        quad(std::integral_constant<int, 2>{});
+        quad(std::integral_constant<int, 3>{});
+      };
+      half(std::integral_constant<int, 0>{});
+      half(std::integral_constant<int, 1>{});
     } else if constexpr (F::CHUNKED) {
       // chunk-major: 8 codes = 4 natural pairs of x (16 bytes of LDS)
       auto chunk = [&](auto mc) {
@@ -468,8 +603,8 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   // the whole pairing and (C, X) sequence for nothing, which the 2- and
   // 3-bit kernels, bound by instruction issue, pay for.
   const bool stager = (int)(threadIdx.x & ~63u) < 4 * groups;
-  XStage xs;
-  if (stager) stage_x_load(X, groups, xs);
+  XStage<BITS> xs;
+  if (stager) stage_x_load<BITS>(X, groups, xs);
   issue(b0);
   stage_x_store<BITS, GS>(X, groups, xs, xp, cx, stager);
   __syncthreads();
