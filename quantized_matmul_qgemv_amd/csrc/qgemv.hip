@@ -58,62 +58,99 @@ __device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b) {
   return d;
 }
 
-// 3-bit pairing of the GEMV.  A 32-code half of a 64-code group is 96 bits
-// (three words); code c sits at bit 3c.  Each pair (c1, c2) is read from a
-// 32-bit window of the half starting at bit s: c1 at offset o1 = 3*c1 - s of
-// the low 16 bits, c2 at offset o2 = 3*c2 - s - 16 of the high 16 bits, both
-// with o + 3 <= 10, so that ONE AND-OR with the magic 2^(10-o) per half turns
-// the window into the fp16 pair (2^(10-o1) + q1, 2^(10-o2) + q2).  Windows at
-// s = 0, 32, 64 are the words themselves; the others cost one funnel shift
-// (s = 6, 12, 41) or one shift (s = 71, inside the third word), so a half
-// costs 4 shifts + 16 AND-ORs + 16 dot products (72 VALU per group, against
-// 102 for the byte-permute chunk unpack).  The 16 (s, c1, c2) were chosen by
-// an exact-cover search over all windows for the fewest shifts and then the
-// fewest distinct (o1, o2) (7, i.e. 7 magics held in registers).  Slot p of
-// a half is the pair below; the staging writes (x[c1], x[c2]) there.
-struct Pair3 {
+// Window pairing of 3-, 5- and 6-bit codes in the GEMV.  A 32-code half of
+// a 64-code group is BITS words; code c sits at bit BITS*c.  Each pair
+// (c1, c2) is read from a 32-bit window of the half starting at bit s: c1 at
+// offset o1 = BITS*c1 - s of the low 16 bits, c2 at o2 = BITS*c2 - s - 16 of
+// the high 16 bits, both with o + BITS <= 10, so that ONE AND-OR with the
+// magic 2^(10-o) per half turns the window into the fp16 pair
+// (2^(10-o1) + q1, 2^(10-o2) + q2).  Windows at multiples of 32 bits are
+// the words themselves; the others cost one funnel shift (or one shift
+// inside the last word).  The 16 (s, c1, c2) of each width were chosen by an
+// exact-cover search over all windows for the fewest shifts, then the fewest
+// distinct (o1, o2) (the magics held in registers):
+//   3 bits: 4 shifts per half, 72 VALU per 64 codes (102 for the byte-permute
+//           chunk unpack of qmm_device.h), 7 magics;
+//   5 bits: 12 shifts, 88 VALU (about 115), 4 magics;
+//   6 bits: 10 shifts, 84 VALU (about 111), 3 magics.
+// Slot p of a half holds the pair below; the staging writes (x[c1], x[c2])
+// there.
+struct WinPair {
   int s, c1, c2;
-  constexpr int o1() const { return 3 * c1 - s; }
-  constexpr int o2() const { return 3 * c2 - s - 16; }
 };
-constexpr Pair3 kPair3[16] = {{0, 0, 6},   {0, 1, 7},   {6, 2, 8},   {6, 3, 9},
-                              {12, 4, 10}, {12, 5, 11}, {32, 12, 17}, {32, 13, 18},
-                              {41, 14, 19}, {41, 15, 20}, {41, 16, 21}, {64, 22, 28},
-                              {64, 23, 27}, {71, 24, 29}, {71, 25, 30}, {71, 26, 31}};
 
-constexpr bool pair3_table_ok() {
+template <int BITS>
+struct WinPairs;
+template <>
+struct WinPairs<3> {
+  static constexpr WinPair p[16] = {{0, 0, 6},   {0, 1, 7},   {6, 2, 8},   {6, 3, 9},
+                                    {12, 4, 10}, {12, 5, 11}, {32, 12, 17}, {32, 13, 18},
+                                    {41, 14, 19}, {41, 15, 20}, {41, 16, 21}, {64, 22, 28},
+                                    {64, 23, 27}, {71, 24, 29}, {71, 25, 30}, {71, 26, 31}};
+};
+template <>
+struct WinPairs<5> {
+  static constexpr WinPair p[16] = {{0, 0, 4},    {5, 1, 5},    {10, 2, 6},   {15, 3, 7},
+                                    {36, 8, 11},  {43, 9, 12},  {49, 10, 14}, {64, 13, 17},
+                                    {73, 15, 18}, {78, 16, 19}, {96, 20, 23}, {103, 21, 24},
+                                    {108, 22, 25}, {128, 26, 29}, {131, 27, 30}, {138, 28, 31}};
+};
+template <>
+struct WinPairs<6> {
+  static constexpr WinPair p[16] = {{0, 0, 3},    {6, 1, 4},    {12, 2, 5},   {32, 6, 8},
+                                    {42, 7, 10},  {52, 9, 12},  {64, 11, 14}, {74, 13, 15},
+                                    {96, 16, 19}, {102, 17, 20}, {108, 18, 21}, {128, 22, 24},
+                                    {136, 23, 26}, {150, 25, 28}, {160, 27, 30}, {170, 29, 31}};
+};
+
+template <int BITS>
+constexpr bool win_pairs() { return BITS == 3 || BITS == 5 || BITS == 6; }
+template <int BITS>
+constexpr int win_o1(const WinPair& p) { return BITS * p.c1 - p.s; }
+template <int BITS>
+constexpr int win_o2(const WinPair& p) { return BITS * p.c2 - p.s - 16; }
+
+template <int BITS>
+constexpr bool win_table_ok() {
   bool seen[32] = {};
-  for (const Pair3& p : kPair3) {
-    if (p.o1() < 0 || p.o1() + 3 > 10 || p.o2() < 0 || p.o2() + 3 > 10) return false;
-    if (seen[p.c1] || seen[p.c2]) return false;
+  for (const WinPair& p : WinPairs<BITS>::p) {
+    const int o1 = win_o1<BITS>(p), o2 = win_o2<BITS>(p);
+    if (o1 < 0 || o1 + BITS > 10 || o2 < 0 || o2 + BITS > 10) return false;
+    if (p.c1 < 0 || p.c1 > 31 || p.c2 < 0 || p.c2 > 31 || seen[p.c1] || seen[p.c2]) return false;
     seen[p.c1] = seen[p.c2] = true;
   }
   return true;
 }
-static_assert(pair3_table_ok(), "3-bit pairs must cover the half once, each code inside its window");
+static_assert(win_table_ok<3>() && win_table_ok<5>() && win_table_ok<6>(),
+              "window pairs must cover the half once, each code inside its window");
 
 // Code bits kept and magic exponents set by the AND-OR of a pair.
-constexpr uint32_t pair3_mask(const Pair3& p) { return (7u << p.o1()) | (7u << (16 + p.o2())); }
-constexpr uint32_t pair3_magic(const Pair3& p) {
-  return ((uint32_t)(25 - p.o1()) << 10) | ((uint32_t)(25 - p.o2()) << 26);
+template <int BITS>
+constexpr uint32_t win_mask(const WinPair& p) {
+  constexpr uint32_t m = (1u << BITS) - 1;
+  return (m << win_o1<BITS>(p)) | (m << (16 + win_o2<BITS>(p)));
+}
+template <int BITS>
+constexpr uint32_t win_magic(const WinPair& p) {
+  return ((uint32_t)(25 - win_o1<BITS>(p)) << 10) | ((uint32_t)(25 - win_o2<BITS>(p)) << 26);
 }
 
-// Window of the half w[0..2] starting at bit s (bits past the half read 0
-// and are masked off).
-template <int S>
+// Window of the half w[0 .. NW) starting at bit S (bits past the half read
+// 0 and are masked off).
+template <int S, int NW>
 __device__ __forceinline__ uint32_t half_window(const uint32_t* w) {
   constexpr int j = S / 32, r = S % 32;
   if constexpr (r == 0) return w[j];
-  else if constexpr (j + 1 < 3) return __builtin_amdgcn_alignbit(w[j + 1], w[j], r);
+  else if constexpr (j + 1 < NW) return __builtin_amdgcn_alignbit(w[j + 1], w[j], r);
   else return w[j] >> r;
 }
 
 // Pair slot P of a half: window, AND-OR into the fp16 pair, dot product
 // with the staged activations (the first slot of a half starts from zero).
-template <int P>
-__device__ __forceinline__ void slot3(const uint32_t* w, uint32_t x, float& a) {
-  constexpr Pair3 p = kPair3[P];
-  const uint32_t hp = and_or(half_window<p.s>(w), pair3_mask(p), pair3_magic(p));
+template <int BITS, int P>
+__device__ __forceinline__ void win_slot(const uint32_t* w, uint32_t x, float& a) {
+  constexpr WinPair p = WinPairs<BITS>::p[P];
+  const uint32_t hp = and_or(half_window<p.s, BITS>(w), win_mask<BITS>(p), win_magic<BITS>(p));
   a = P == 0 ? dot2_first(hp, x) : dot2(hp, x, a);
 }
 
@@ -128,7 +165,7 @@ __device__ __forceinline__ void slot3(const uint32_t* w, uint32_t x, float& a) {
 constexpr int kXRounds = 1;  // quarter-groups per thread held in registers (k <= 4096)
 
 template <int BITS>
-constexpr int x_words() { return BITS == 3 ? 16 : 8; }  // activation dwords per thread
+constexpr int x_words() { return win_pairs<BITS>() ? 16 : 8; }  // activation dwords per thread
 
 template <int BITS>
 struct XStage {
@@ -140,7 +177,7 @@ struct XStage {
 template <int BITS>
 __device__ __forceinline__ void load_quarter(gptr<uint16_t> x, int t, uint32_t (&d)[x_words<BITS>()]) {
   constexpr int NV = x_words<BITS>() / 4;
-  const size_t off = BITS == 3 ? (size_t)(t >> 2) * 64 + ((t >> 1) & 1) * 32 : (size_t)(t >> 2) * 64 + (t & 3) * 16;
+  const size_t off = win_pairs<BITS>() ? (size_t)(t >> 2) * 64 + ((t >> 1) & 1) * 32 : (size_t)(t >> 2) * 64 + (t & 3) * 16;
   gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(x + off);
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
@@ -178,24 +215,32 @@ __device__ __forceinline__ void build_quarter(const uint32_t (&d)[x_words<BITS>(
     // fp16 weights: x in natural order, no magic offsets (C = 0)
 #pragma unroll
     for (int i = 0; i < 8; ++i) out[i] = d[i];
-  } else if constexpr (BITS == 3) {
+  } else if constexpr (win_pairs<BITS>()) {
     // slots sub*8 .. sub*8+7 of the thread's half (sub = part & 1)
     const bool sub = (part & 1) != 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const Pair3 p0 = kPair3[j], p1 = kPair3[8 + j];
+    auto slot = [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr WinPair p0 = WinPairs<BITS>::p[j], p1 = WinPairs<BITS>::p[8 + j];
+      constexpr float ml0 = (float)(1 << (10 - win_o1<BITS>(p0))), ml1 = (float)(1 << (10 - win_o1<BITS>(p1)));
+      constexpr float mh0 = (float)(1 << (10 - win_o2<BITS>(p0))), mh1 = (float)(1 << (10 - win_o2<BITS>(p1)));
       const uint32_t v0 = x_half(d, p0.c1) | (x_half(d, p0.c2) << 16);
       const uint32_t v1 = x_half(d, p1.c1) | (x_half(d, p1.c2) << 16);
       out[j] = sub ? v1 : v0;
       const float xl = f16_bits_to_f32((uint16_t)(out[j] & 0xFFFFu));
       const float xh = f16_bits_to_f32((uint16_t)(out[j] >> 16));
-      const float ml = sub ? (float)(1 << (10 - p1.o1())) : (float)(1 << (10 - p0.o1()));
-      const float mh = sub ? (float)(1 << (10 - p1.o2())) : (float)(1 << (10 - p0.o2()));
-      csum += ml * xl;
-      csum += mh * xh;
+      csum += (sub ? ml1 : ml0) * xl;
+      csum += (sub ? mh1 : mh0) * xh;
       xsum += xl;
       xsum += xh;
-    }
+    };
+    slot(std::integral_constant<int, 0>{});
+    slot(std::integral_constant<int, 1>{});
+    slot(std::integral_constant<int, 2>{});
+    slot(std::integral_constant<int, 3>{});
+    slot(std::integral_constant<int, 4>{});
+    slot(std::integral_constant<int, 5>{});
+    slot(std::integral_constant<int, 6>{});
+    slot(std::integral_constant<int, 7>{});
   } else if constexpr (F::CHUNKED) {
     // chunk pairs are adjacent codes: x stays in natural order
 #pragma unroll
@@ -448,10 +493,11 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
           a1[u] = dot2(wv.w, xv.w, a1[u]);
         }
       }
-    } else if constexpr (BITS == 3) {
-      // window pairs (kPair3): half h of the group is words 3h .. 3h+2 and
-      // its 16 pair slots are dwords 16h .. 16h+15 of the group's x; the
-      // two halves accumulate apart (they are the two scale groups of 32)
+    } else if constexpr (win_pairs<BITS>()) {
+      // window pairs (WinPairs): half h of the group is words BITS*h ..
+      // BITS*h+BITS-1 and its 16 pair slots are dwords 16h .. 16h+15 of the
+      // group's x; the two halves accumulate apart (they are the two scale
+      // groups of 32)
       auto half = [&](auto hc) {
         constexpr int h = decltype(hc)::value;
         auto quad = [&](auto qc) {
@@ -461,11 +507,11 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
 #pragma unroll
           for (int u = 0; u < UR; ++u) {
             float& a = h == 0 ? a0[u] : a1[u];
-            const uint32_t* w = bf.w[u] + 3 * h;
-            slot3<4 * q + 0>(w, xr[0], a);
-            slot3<4 * q + 1>(w, xr[1], a);
-            slot3<4 * q + 2>(w, xr[2], a);
-            slot3<4 * q + 3>(w, xr[3], a);
+            const uint32_t* w = bf.w[u] + BITS * h;
+            win_slot<BITS, 4 * q + 0>(w, xr[0], a);
+            win_slot<BITS, 4 * q + 1>(w, xr[1], a);
+            win_slot<BITS, 4 * q + 2>(w, xr[2], a);
+            win_slot<BITS, 4 * q + 3>(w, xr[3], a);
           }
         };
         quad(std::integral_constant<int, 0>{});
