@@ -65,9 +65,9 @@ TRAFFIC = {
     # (KiB per dispatch of qgemv_batched_kernel<4,16,4,64>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 166885.5, "fetch_scale": 1073741824 / (524301.3 * 1024),
-    "write_kib": 1939.3, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "27154c88f91701a78d5bec8214b0a9ecce5f44ea600935c0c39181ea3892df73",
+    "fetch_kib": 166890.3, "fetch_scale": 1073741824 / (524301.3 * 1024),
+    "write_kib": 1939.6, "write_scale": 1073741824 / (1048576.0 * 1024),
+    "sources_sha256": "786a73b70876e5b3563d07f34230a817cd5462deabc6f9e04e2920fb4e71a6b1",
 }
 
 
