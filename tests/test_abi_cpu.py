@@ -152,15 +152,15 @@ def test_route_size_counts_out_of_range_bucket(L):
     tile; the row-tile bound counts the E valid buckets plus one for pairs
     whose expert id is out of range (every tile holds at least one pair, so
     never more tiles than pairs).  After them come E + 1 counts per chunk of
-    the pair list: chunks of at least 256 pairs, at most 64 chunks and at
-    most 32768 counts."""
+    the pair list: one chunk up to 4096 pairs, else chunks of at least 256
+    pairs, at most 64 chunks and at most 32768 counts."""
     for t, top_k, e in ((512, 8, 128), (2048, 8, 128), (1, 1, 1), (3, 2, 1000), (5, 8, 4),
                         (40000, 8, 128), (300, 8, 1000)):
         pairs = t * top_k
         tiles = min((pairs + 31) // 32 + e + 1, pairs)
         g = max(1, min(64, 32768 // (e + 1)))
         chunk = max(256, -(-pairs // g))
-        chunks = -(-pairs // chunk)
+        chunks = 1 if pairs <= 4096 else -(-pairs // chunk)
         want = -(-(8 + pairs + 3 * tiles + chunks * (e + 1)) * 4 // 256) * 256
         assert L.qmm_moe_route_size(t, top_k, e) == want, (t, top_k, e)
         assert L.qmm_qgemm_grouped_workspace_size(t, top_k, e, 768, 2048, 4, 64) == want

@@ -729,19 +729,19 @@ def test_routed_grouped_equals_grouped():
     assert bool(torch.isnan(hh).all()), "SwiGLU output over a foreign plan must be all NaN"
 
 
-@pytest.mark.parametrize("bits,t", [(4, 40), (8, 40), (4, 300)])
+@pytest.mark.parametrize("bits,t", [(4, 40), (8, 40), (4, 1200)])
 def test_moe_out_of_range_ids_nan_and_counted(bits, t):
     """Pairs whose expert id lies outside [0, E) (here -1, E, E + 100 and a
     large negative id) are not computed: their output rows are NaN in the
     self-bucketing, routed and fused SwiGLU products, every other row matches
-    the oracle, and the plan header (byte offset 16) counts them.  At t = 300
-    the 1200 pairs are bucketed in several chunks, with bad ids in three."""
+    the oracle, and the plan header (byte offset 16) counts them.  At t = 1200
+    the 4800 pairs are bucketed in several chunks, with bad ids in three."""
     say("moe out-of-range ids", bits, t)
     top_k, e, hidden, inter = 4, 8, 128, 160
     r = np.random.default_rng([948, bits, t])
     ids = np.ascontiguousarray(synth.topk_ids(r.standard_normal((t, e)), top_k), dtype=np.int32)
     flat = ids.reshape(-1)
-    bad_at = [0, 5, 6, 17, 63, t * top_k - 1] + ([700, 701] if t * top_k > 800 else [])
+    bad_at = [0, 5, 6, 17, 63, t * top_k - 1] + ([2700, 2701] if t * top_k > 4096 else [])
     for i, v in zip(bad_at, (-1, e, e + 100, -(1 << 30), e, -1, e + 1, -5)):
         flat[i] = v
     bad = np.zeros(t * top_k, dtype=bool)
@@ -771,7 +771,7 @@ def test_moe_out_of_range_ids_nan_and_counted(bits, t):
         "routed differs from self-bucketing"
 
 
-@pytest.mark.parametrize("t,top_k,e", [(2048, 8, 128), (37, 3, 5), (700, 8, 1000)])
+@pytest.mark.parametrize("t,top_k,e", [(2048, 8, 128), (37, 3, 5), (512, 8, 128), (700, 8, 1000)])
 def test_moe_route_plan_is_a_bucketing(t, top_k, e):
     """The routing plan is checked for what is unique about it: the header
     words, a sorted pair list that is a permutation of the pairs with each
