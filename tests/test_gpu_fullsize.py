@@ -4,6 +4,8 @@ bench.py times, on sampled outputs the oracle computes one by one.
 Weights are quantized on the GPU here (as in the benchmark); the oracle
 quantizes the sampled rows from the same seeded fp32 weights itself, so the
 test also checks the GPU quantizer bit for bit at full size."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -28,8 +30,15 @@ def sample_rows(n, count, seed):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("wl", [synth.QWEN3_0_6B_Q4_DECODE, synth.LLAMA32_3B_Q8_DECODE],
-                         ids=lambda w: w.name)
+def _decode_at(bits):
+    """The Qwen3-0.6B-shaped decode pass with its weights at another width,
+    as bench.py's decode_formats times it."""
+    wl = synth.QWEN3_0_6B_Q4_DECODE
+    return dataclasses.replace(wl, bits=bits, name=f"{wl.name}@q{bits}")
+
+
+@pytest.mark.parametrize("wl", [synth.QWEN3_0_6B_Q4_DECODE, synth.LLAMA32_3B_Q8_DECODE] +
+                         [_decode_at(b) for b in (2, 3, 5, 6)], ids=lambda w: w.name)
 def test_decode_sweep_batched_sampled(wl):
     say("full decode sweep", wl.name)
     sets = bench.prepare_dense(torch, qmm, wl, 1)
