@@ -67,7 +67,7 @@ TRAFFIC = {
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
     "fetch_kib": 166890.3, "fetch_scale": 1073741824 / (524301.3 * 1024),
     "write_kib": 1939.6, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "786a73b70876e5b3563d07f34230a817cd5462deabc6f9e04e2920fb4e71a6b1",
+    "sources_sha256": "318bdb1f1e905956bfa32864933ceb7feafb61c6e8dab4b99d55b0d0ad8a1437",
 }
 
 

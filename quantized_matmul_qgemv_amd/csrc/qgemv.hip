@@ -28,9 +28,9 @@
 //     C[g] = sum_{k in g} magic(k) * x[k]       X[g] = sum_{k in g} x[k]
 // so that   sum_k q_k x_k = dot(magic + q, x) - C[g]   needs no per-code
 // subtraction: each packed 4-bit word costs one shift, four AND-ORs and
-// four v_dot2_f32_f16.  3/5/6-bit codes are unpacked per 8-code chunk
-// (unpack_chunk in qmm_device.h) into pairs of adjacent codes, so for those
-// widths x stays in natural order in LDS.
+// four v_dot2_f32_f16.  3-, 5- and 6-bit codes straddle words; they are
+// read as window pairs (WinPairs below), one AND-OR per pair from a 32-bit
+// window of the group's words, and the staging writes x in that pair order.
 #include <type_traits>
 
 #include "qmm_device.h"
@@ -105,6 +105,9 @@ struct WinPairs<6> {
 
 template <int BITS>
 constexpr bool win_pairs() { return BITS == 3 || BITS == 5 || BITS == 6; }
+static_assert(win_pairs<3>() == Fmt<3>::CHUNKED && win_pairs<5>() == Fmt<5>::CHUNKED &&
+                  win_pairs<6>() == Fmt<6>::CHUNKED && !Fmt<2>::CHUNKED && !Fmt<4>::CHUNKED && !Fmt<8>::CHUNKED,
+              "every width whose codes straddle words is read as window pairs");
 template <int BITS>
 constexpr int win_o1(const WinPair& p) { return BITS * p.c1 - p.s; }
 template <int BITS>
@@ -241,18 +244,6 @@ __device__ __forceinline__ void build_quarter(const uint32_t (&d)[x_words<BITS>(
     slot(std::integral_constant<int, 5>{});
     slot(std::integral_constant<int, 6>{});
     slot(std::integral_constant<int, 7>{});
-  } else if constexpr (F::CHUNKED) {
-    // chunk pairs are adjacent codes: x stays in natural order
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      out[i] = d[i];
-      const float xl = f16_bits_to_f32((uint16_t)(d[i] & 0xFFFFu));
-      const float xh = f16_bits_to_f32((uint16_t)(d[i] >> 16));
-      csum += chunk_magic_value<BITS>((2 * i) & 7) * xl;
-      csum += chunk_magic_value<BITS>((2 * i + 1) & 7) * xh;
-      xsum += xl;
-      xsum += xh;
-    }
   } else {
     constexpr int C = F::CODES_PER_WORD;
     constexpr int PPW = F::PAIRS_PER_WORD;
@@ -521,40 +512,6 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
       };
       half(std::integral_constant<int, 0>{});
       half(std::integral_constant<int, 1>{});
-    } else if constexpr (F::CHUNKED) {
-      // chunk-major: 8 codes = 4 natural pairs of x (16 bytes of LDS)
-      auto chunk = [&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        const u32x4 xv = reinterpret_cast<const u32x4*>(xg)[m];
-        const uint32_t xr[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-        for (int u = 0; u < UR; ++u) {
-          uint32_t vlo, vhi, h[4];
-          chunk_window<BITS * m, WPG>(bf.w[u], vlo, vhi);
-          unpack_chunk<BITS>(vlo, vhi, h);
-          if constexpr (GS == 32) {
-            // chunks 0..3 are the first 32-code scale group, 4..7 the second
-            float& a = m < 4 ? a0[u] : a1[u];
-            a = m % 4 == 0 ? dot2_first(h[0], xr[0]) : dot2(h[0], xr[0], a);
-            a = dot2(h[1], xr[1], a);
-            a = dot2(h[2], xr[2], a);
-            a = dot2(h[3], xr[3], a);
-          } else {
-            a0[u] = m == 0 ? dot2_first(h[0], xr[0]) : dot2(h[0], xr[0], a0[u]);
-            a1[u] = m == 0 ? dot2_first(h[1], xr[1]) : dot2(h[1], xr[1], a1[u]);
-            a0[u] = dot2(h[2], xr[2], a0[u]);
-            a1[u] = dot2(h[3], xr[3], a1[u]);
-          }
-        }
-      };
-      chunk(std::integral_constant<int, 0>{});
-      chunk(std::integral_constant<int, 1>{});
-      chunk(std::integral_constant<int, 2>{});
-      chunk(std::integral_constant<int, 3>{});
-      chunk(std::integral_constant<int, 4>{});
-      chunk(std::integral_constant<int, 5>{});
-      chunk(std::integral_constant<int, 6>{});
-      chunk(std::integral_constant<int, 7>{});
     } else {
     // word-major: the activation pairs of one word are read from LDS once
     // and used for all UR rows, so only PPW of them are live at a time
