@@ -81,14 +81,39 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1)
 }
 
 // y[i] = sum over splits of partial[split * stride + i], in split order.
+// S > 0: the split count as a template argument, so that all S loads are
+// issued before the first addition (split order kept); S = 0: run-time count.
+template <int S>
 __global__ __launch_bounds__(256) void qgemm_reduce_kernel(const float* __restrict__ partial,
                                                            float* __restrict__ y, long count,
                                                            long stride, int splits) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
-  float acc = partial[i];
-  for (int s = 1; s < splits; ++s) acc += partial[(size_t)s * stride + i];
+  float acc;
+  if constexpr (S > 0) {
+    float v[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) v[s] = partial[(size_t)s * stride + i];
+    acc = v[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) acc += v[s];
+  } else {
+    acc = partial[i];
+    for (int s = 1; s < splits; ++s) acc += partial[(size_t)s * stride + i];
+  }
   y[i] = acc;
+}
+
+static void launch_reduce(const float* ws, float* y, long count, long stride, int splits, hipStream_t st) {
+  const dim3 grid((unsigned)((count + 255) / 256));
+  switch (splits) {
+#define QMM_REDUCE_CASE(S) \
+    case S: hipLaunchKernelGGL(qgemm_reduce_kernel<S>, grid, dim3(256), 0, st, ws, y, count, stride, S); break;
+    QMM_REDUCE_CASE(2) QMM_REDUCE_CASE(3) QMM_REDUCE_CASE(4) QMM_REDUCE_CASE(5) QMM_REDUCE_CASE(6)
+    QMM_REDUCE_CASE(8) QMM_REDUCE_CASE(10) QMM_REDUCE_CASE(12) QMM_REDUCE_CASE(16)
+#undef QMM_REDUCE_CASE
+    default: hipLaunchKernelGGL(qgemm_reduce_kernel<0>, grid, dim3(256), 0, st, ws, y, count, stride, splits);
+  }
 }
 
 // Partial tiles of one split are `partial_stride` floats apart (a multiple
@@ -131,8 +156,7 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmPlan& p, float* ws, h
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const long count = (long)a.m * a.n;
-  hipLaunchKernelGGL(qgemm_reduce_kernel, dim3(ceil_div(count, 256)), dim3(256), 0, st, ws, a.y,
-                     count, gr.stride, p.splits);
+  launch_reduce(ws, a.y, count, gr.stride, p.splits, st);
   return hipGetLastError();
 }
 
@@ -150,8 +174,7 @@ static hipError_t launch_wide(const GemmArgs& a, const GemmPlan& p, float* ws, h
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const long count = (long)a.m * a.n;
-  hipLaunchKernelGGL(qgemm_reduce_kernel, dim3(ceil_div(count, 256)), dim3(256), 0, st, ws, a.y,
-                     count, gr.stride, p.splits);
+  launch_reduce(ws, a.y, count, gr.stride, p.splits, st);
   return hipGetLastError();
 }
 

@@ -38,6 +38,12 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 // y tile of split tile `sid` = sum of its partial tiles in split order.
 // One workgroup reduces 1024 outputs of one tile (4 per thread, 16-byte
 // loads of every partial issued together).
+// The split count is a template argument so that all S partial loads of a
+// thread are issued before the first addition (with a run-time trip count
+// each load waited for the previous sum: S memory latencies in a row); the
+// sum is still taken in split order 0, 1, ..., S-1.  S = 0: the count is
+// the run-time `splits` (a forced split count the planner never chooses).
+template <int S>
 __global__ __launch_bounds__(256) void qgemm_batched_reduce_kernel(
     const GemmBatchProblem* __restrict__ probs, const GemmSplitTile* __restrict__ st,
     const float* __restrict__ partials, int bm, int bn, int splits) {
@@ -46,11 +52,22 @@ __global__ __launch_bounds__(256) void qgemm_batched_reduce_kernel(
   const int e0 = (blockIdx.x % per_tile) * 1024 + threadIdx.x * 4;
   const GemmSplitTile t = st[sid];
   const GemmBatchProblem P = probs[t.problem];
+  const int ns = S > 0 ? S : splits;
   const gptr<float4_t> src = reinterpret_cast<gptr<float4_t>>(to_global(partials)) +
-                             ((size_t)sid * splits * bm * bn + e0) / 4;
+                             ((size_t)sid * ns * bm * bn + e0) / 4;
   const size_t stride = (size_t)bm * bn / 4;
-  float4_t acc = src[0];
-  for (int sp = 1; sp < splits; ++sp) acc += src[sp * stride];
+  float4_t acc;
+  if constexpr (S > 0) {
+    float4_t v[S];
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp) v[sp] = src[sp * stride];
+    acc = v[0];
+#pragma unroll
+    for (int sp = 1; sp < S; ++sp) acc += v[sp];
+  } else {
+    acc = src[0];
+    for (int sp = 1; sp < splits; ++sp) acc += src[sp * stride];
+  }
   const int r = e0 / bn;
   const int c = e0 % bn;
   const int row = t.m0 + r;
@@ -394,8 +411,17 @@ hipError_t launch_qgemm_batched(const void* plan_device, const GemmBatchHeader& 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || h.splits == 1 || h.split_tiles == 0) return e;
   const int bn = h.nb * 128;
-  hipLaunchKernelGGL(qgemm_batched_reduce_kernel, dim3(h.split_tiles * (h.bm * bn / 1024)), dim3(256),
-                     0, st, probs, sts, partials, h.bm, bn, h.splits);
+  const dim3 grid(h.split_tiles * (h.bm * bn / 1024));
+  switch (h.splits) {
+#define QMM_REDUCE_CASE(S) \
+    case S: hipLaunchKernelGGL(qgemm_batched_reduce_kernel<S>, grid, dim3(256), 0, st, probs, sts, partials, h.bm, bn, S); break;
+    QMM_REDUCE_CASE(2) QMM_REDUCE_CASE(3) QMM_REDUCE_CASE(4) QMM_REDUCE_CASE(5) QMM_REDUCE_CASE(6)
+    QMM_REDUCE_CASE(8) QMM_REDUCE_CASE(10) QMM_REDUCE_CASE(12) QMM_REDUCE_CASE(16)
+#undef QMM_REDUCE_CASE
+    default:
+      hipLaunchKernelGGL(qgemm_batched_reduce_kernel<0>, grid, dim3(256), 0, st, probs, sts, partials, h.bm, bn,
+                         h.splits);
+  }
   return hipGetLastError();
 }
 
