@@ -283,7 +283,14 @@ def bench_decode_extras(torch, qmm, wl, sets, steps=20, warmup=3):
       graph_197    the decode pass as 197 sequential qmm_qgemv launches (the
                    order a dependent decode would need) replayed as one HIP graph;
       graph_floor  the same graph shape with 197 one-element kernels: the
-                   per-launch floor that the sequential form pays."""
+                   per-launch floor that the sequential form pays;
+      graph_layer_batched  a dependent decode step batched only where one
+                   step allows it: per layer q+k+v as one GEMV over the
+                   weights stacked along n, o, gate+up likewise stacked, down
+                   (the projections that read the same activations share a
+                   launch), then the lm_head: 4 x 28 + 1 = 113 launches
+                   replayed as one HIP graph (the stacked q+k+v and gate+up
+                   read the first projection's activations)."""
     stream = torch.cuda.current_stream()
     copies = len(sets)
     out = {}
@@ -335,6 +342,39 @@ def bench_decode_extras(torch, qmm, wl, sets, steps=20, warmup=3):
     ms_0, _ = time_launches(torch, lambda i: g0.replay(), steps, warmup, stream)
     out["graph_floor"] = {"launches": len(sets[0]), "us_per_launch": round(ms_0 * 1e3 / len(sets[0]), 3)}
     del graphs, g0
+
+    names = [p.name for p in wl.projs]
+    groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    if all(nm in names for grp in groups for nm in grp):
+        def layer_launches(st):
+            seq_l = []
+            for layer in range(wl.layers):
+                base = layer * len(names)
+                for grp in groups:
+                    parts = [st[base + names.index(nm)] for nm in grp]
+                    if len(parts) == 1:
+                        w, s_, b, x, y, n, k = parts[0]
+                    else:
+                        w, s_, b = (torch.cat([t[j] for t in parts]) for j in range(3))
+                        x, k = parts[0][3], parts[0][6]
+                        n = int(w.shape[0])
+                        y = torch.empty(n, dtype=torch.float32, device="cuda")
+                    seq_l.append((w, s_, b, x, y))
+            w, s_, b, x, y, n, k = st[-1]   # lm_head
+            seq_l.append((w, s_, b, x, y))
+            return seq_l
+        stacked = [layer_launches(st) for st in sets]
+
+        def seq_layers(lst):
+            def body():
+                for (w, s_, b, x, y) in lst:
+                    qmm.qgemv(w, s_, b, x, wl.bits, y=y)
+            return body
+        graphs = [capture(seq_layers(lst)) for lst in stacked]
+        ms_l, _ = time_launches(torch, lambda i: graphs[i % copies].replay(), steps, warmup, stream)
+        out["graph_layer_batched"] = {"launches": len(stacked[0]), "ms_per_pass": round(ms_l, 4),
+                                      "gb_per_s": round(step_bytes / (ms_l * 1e-3) / 1e9, 1)}
+        del graphs, stacked
     return out
 
 
