@@ -842,8 +842,9 @@ def main():
     ap.add_argument("--decode-bits", type=int, choices=[2, 3, 4, 5, 6, 8, 16], default=4,
                     help="with --only decode: the decode pass at another weight width (for counters)")
     ap.add_argument("--forces", metavar="F;F...",
-                    help="with --launch: time every launch under each QMM_GEMM_FORCE value "
-                         "(bm,nb,splits; empty = the planner's choice)")
+                    help="with --launch: time every launch under each forced tile: QMM_GEMM_FORCE "
+                         "for prefill launches (bm,nb,splits[,kw]), QMM_MOE_FORCE for moe launches "
+                         "(bm,nb); empty = the planner's or the routing rule's choice")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -884,10 +885,11 @@ def main():
         for spec in args.launch.split(","):
             for f in forces:
                 if f is not None:
+                    var = "QMM_MOE_FORCE" if spec.startswith("moe") else "QMM_GEMM_FORCE"
                     if f:
-                        os.environ["QMM_GEMM_FORCE"] = f
+                        os.environ[var] = f
                     else:
-                        os.environ.pop("QMM_GEMM_FORCE", None)
+                        os.environ.pop(var, None)
                 r = profile_launch(torch, qmm, spec, args.steps)
                 if f is not None:
                     r["force"] = f
