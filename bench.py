@@ -65,9 +65,9 @@ TRAFFIC = {
     # (KiB per dispatch of qgemv_batched_kernel<4,16,4,64>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 166890.3, "fetch_scale": 1073741824 / (524301.3 * 1024),
-    "write_kib": 1939.6, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "318bdb1f1e905956bfa32864933ceb7feafb61c6e8dab4b99d55b0d0ad8a1437",
+    "fetch_kib": 166904.1, "fetch_scale": 1073741824 / (524301.3 * 1024),
+    "write_kib": 1939.2, "write_scale": 1073741824 / (1048576.0 * 1024),
+    "sources_sha256": "dc8b27ec76c25e1c7814c9fe76968ccec2d198f5c878fa9ad9f994da88e08327",
 }
 
 
