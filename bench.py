@@ -65,9 +65,9 @@ TRAFFIC = {
     # (KiB per dispatch of qgemv_batched_kernel<4,16,4,64>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 166904.1, "fetch_scale": 1073741824 / (524301.3 * 1024),
-    "write_kib": 1939.2, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "dc8b27ec76c25e1c7814c9fe76968ccec2d198f5c878fa9ad9f994da88e08327",
+    "fetch_kib": 171921.4, "fetch_scale": 1073741824 / (524301.3 * 1024),
+    "write_kib": 1937.6, "write_scale": 1073741824 / (1048576.0 * 1024),
+    "sources_sha256": "67814a18150cc72eebc89077ad352dc8bf2ad8a0b10b3e2e628ca4ad1bca02bc",
 }
 
 
@@ -253,10 +253,10 @@ def bench_projections(torch, qmm, wl, sets, launches=20):
 
 def bench_streaming_reference(torch, nbytes):
     """Plain streaming rates of the same GPU, for scale: the best of a
-    read-only kernel over `nbytes` (16-byte loads, several grid sizes, two
-    buffers alternating so every launch reads HBM; the stand-alone harness
-    stream_probe.hip, no library code), and a 1 GiB device-to-device copy
-    (read + write) through torch."""
+    read-only kernel over `nbytes` (16-byte loads, several grid sizes, with
+    ordinary and with non-temporal loads, two buffers alternating so every
+    launch reads HBM; the stand-alone harness stream_probe.hip, no library
+    code), and a 1 GiB device-to-device copy (read + write) through torch."""
     import subprocess
     out = {}
     exe = os.path.join(ROOT, "quantized_matmul_qgemv_amd", "qmm_stream_probe")

@@ -11,7 +11,10 @@
 //     scale and one fp16 bias;
 //   * LPR consecutive lanes share a row; lane lr takes the row's groups
 //     lr, lr + LPR, lr + 2*LPR, ...  so one wave-wide 128-bit load covers
-//     64/LPR rows with contiguous, fully used 16-byte pieces;
+//     64/LPR rows with contiguous, fully used 16-byte pieces (4-bit codes in
+//     64-code scale groups: a lane takes half of two groups per step
+//     instead, so that each of its two loads reads whole contiguous lines;
+//     see gemv_block);
 //   * each lane keeps UR rows in flight (128 bytes of codes per lane for 4
 //     and 8 bits, 64 for 2 bits), and
 //     the loads of the next step are issued before the current step is
@@ -354,17 +357,16 @@ __device__ __forceinline__ float row_sum16(const float (&a)[UR], int lr) {
   return v;
 }
 
-// Weight-stream loads (codes, scales and biases): non-temporal for the
-// widths in kNtWidths.  A 2-bit lane reads its whole 16-byte group with one
-// load, so one wave-wide load consumes every 128-byte line it touches, and
-// the stream need not stay in L2: 2-bit decode passes measured 5-9 % faster
-// this way.  The other widths read a lane's group with several loads, each
-// covering part of every line; there the same policy measured 5 % (3 bits)
-// to 38 % (8 bits) slower.
-constexpr unsigned kNtWidths = 1u << 2;
-template <int BITS, typename T>
+// Weight-stream loads (codes, scales and biases), non-temporal (NT) where
+// every wave-wide load consumes whole 128-byte lines: the 2-bit groups (one
+// 16-byte load per lane) and the 4-bit half-group lanes below.  The stream is
+// read once and need not stay in L2; a plain read kernel over the same bytes
+// streams 7-10 % faster with such loads.  Where a lane reads its group with
+// several loads, each covering part of every line (3, 5, 6 and 8 bits, and
+// 4 bits with whole groups per lane), the same policy measured 5-38 % slower.
+template <bool NT, typename T>
 __device__ __forceinline__ T stream_load(gptr<T> p) {
-  if constexpr (((kNtWidths >> BITS) & 1u) != 0) return __builtin_nontemporal_load(p);
+  if constexpr (NT) return __builtin_nontemporal_load(p);
   else return *p;
 }
 
@@ -402,6 +404,16 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   constexpr int V4 = F::VEC4_PER_GROUP;
   constexpr int WPG = F::WORDS_PER_GROUP;
   constexpr int PPW = F::PAIRS_PER_WORD;
+  // Half-group lanes (4-bit codes, 64-code scale groups): at a k-step over
+  // groups sb .. sb+LPR-1 of a row, lane lr loads the 16-byte pieces
+  // 2*sb + lr and 2*sb + LPR + lr, i.e. half (lr & 1) of groups
+  // j0 = sb + lr/2 and j1 = j0 + LPR/2, so each wave-wide load reads whole
+  // contiguous lines (with one group per lane, the two loads of a lane's
+  // 32 bytes each took every other 16-byte piece).  The two lanes of a pair
+  // then hold both halves of j0 and of j1; one DPP exchange gives the even
+  // lane j0's dot product and the odd lane j1's, and each folds one group.
+  constexpr bool HALF = BITS == 4 && GS == 64 && LPR >= 2;
+  constexpr bool NT = BITS == 2 || HALF;
   constexpr int SBN = GS == 32 ? 2 : 1;
   using Buf = StepBuf<BITS, UR, SBN>;
 
@@ -435,6 +447,24 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   auto issue = [&](Buf& bf) {
     int g = (wk + it * WK) * LPR + lr;
     g = g < groups ? g : groups - 1;  // only a wave with no k-steps (WK > 1) goes past
+    if constexpr (HALF) {
+      int sb = (wk + it * WK) * LPR;
+      sb = sb < groups ? sb : groups - LPR;  // (LPR divides groups)
+      const int j0 = sb + (lr >> 1), j1 = j0 + LPR / 2, hh = lr & 1;
+#pragma unroll
+      for (int u = 0; u < UR; ++u) {
+        int r = lane_row + ip * Cfg::ROWS + u * Cfg::RPW;
+        r = r < row_end ? r : row_end - 1;
+        const gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(W + (size_t)r * rstride);
+        bf.w[u][0] = stream_load<NT>(src + 2 * j0 + hh);
+        bf.w[u][1] = stream_load<NT>(src + 2 * j1 + hh);
+        // the lane folds group j0 (even lanes) or j1 (odd lanes)
+        bf.s[u][0] = stream_load<NT>(S + (size_t)r * sgroups + (hh ? j1 : j0));
+        bf.b[u][0] = stream_load<NT>(B + (size_t)r * sgroups + (hh ? j1 : j0));
+      }
+      if (++it == tcount) { it = 0; ++ip; }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
       int r = lane_row + ip * Cfg::ROWS + u * Cfg::RPW;
@@ -445,28 +475,28 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
           gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(W + (size_t)r * rstride + (size_t)g * WPG);
 #pragma unroll
           for (int v = 0; v < GL::NV; ++v) {
-            const u32x4 t = stream_load<BITS>(src + v);
+            const u32x4 t = stream_load<NT>(src + v);
             bf.w[u][4 * v] = t.x; bf.w[u][4 * v + 1] = t.y; bf.w[u][4 * v + 2] = t.z; bf.w[u][4 * v + 3] = t.w;
           }
         } else {
           gptr<u32x2> src = reinterpret_cast<gptr<u32x2>>(W + (size_t)r * rstride + (size_t)g * WPG);
 #pragma unroll
           for (int v = 0; v < GL::NV; ++v) {
-            const u32x2 t = stream_load<BITS>(src + v);
+            const u32x2 t = stream_load<NT>(src + v);
             bf.w[u][2 * v] = t.x; bf.w[u][2 * v + 1] = t.y;
           }
         }
       } else {
         gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(W + (size_t)r * rstride + (size_t)g * WPG);
 #pragma unroll
-        for (int v = 0; v < V4; ++v) bf.w[u][v] = stream_load<BITS>(src + v);
+        for (int v = 0; v < V4; ++v) bf.w[u][v] = stream_load<NT>(src + v);
       }
       if constexpr (!F::F16W) {
 #pragma unroll
         for (int q = 0; q < SBN; ++q) {
           const size_t si = (size_t)r * sgroups + (GS == 32 ? 2 * g + q : GS == 128 ? (g >> 1) : g);
-          bf.s[u][q] = stream_load<BITS>(S + si);
-          bf.b[u][q] = stream_load<BITS>(B + si);
+          bf.s[u][q] = stream_load<NT>(S + si);
+          bf.b[u][q] = stream_load<NT>(B + si);
         }
       }
     }
@@ -484,7 +514,43 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
     float a0[UR], a1[UR];
 #pragma unroll
     for (int u = 0; u < UR; ++u) a0[u] = a1[u] = 0.0f;
-    if constexpr (F::F16W) {
+    if constexpr (HALF) {
+      // half hh of groups j0 and j1 (their x pairs: bytes 64*hh .. 64*hh+63
+      // of each group's staging), one accumulator per group
+      const int sb = (wk + ct * WK) * LPR;
+      const int j0 = sb + (lr >> 1), j1 = j0 + LPR / 2, hh = lr & 1;
+      const unsigned char* x0 = xp + (size_t)j0 * kXStride + 64 * hh;
+      const unsigned char* x1 = xp + (size_t)j1 * kXStride + 64 * hh;
+      // word-major as below: words 0..3 are group j0's, 4..7 group j1's
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>((j < 4 ? x0 : x1) + 16 * (j & 3));
+        const uint32_t xr[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          const u32x4 wv = bf.w[u][j >> 2];
+          const uint32_t word = (j & 3) == 0 ? wv.x : (j & 3) == 1 ? wv.y : (j & 3) == 2 ? wv.z : wv.w;
+          uint32_t h[4];
+          unpack_word<4>(word, h);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            if (j < 4) a0[u] = j == 0 && p == 0 ? dot2_first(h[p], xr[p]) : dot2(h[p], xr[p], a0[u]);
+            else       a1[u] = j == 4 && p == 0 ? dot2_first(h[p], xr[p]) : dot2(h[p], xr[p], a1[u]);
+          }
+        }
+      }
+      // partner lanes (lr, lr ^ 1) hold the two halves of j0 and of j1:
+      // the even lane collects j0's whole dot product, the odd lane j1's
+      const float2 c = reinterpret_cast<const float2*>(cx)[hh ? j1 : j0];
+#pragma unroll
+      for (int u = 0; u < UR; ++u) {
+        const float mine = hh ? a1[u] : a0[u];
+        const float dot = mine + dpp_read<kDppXor1>(hh ? a0[u] : a1[u]);
+        const float s = f16_bits_to_f32(bf.s[u][0]);
+        const float b = f16_bits_to_f32(bf.b[u][0]);
+        acc[u] = fmaf(s, dot - c.x, fmaf(b, c.y, acc[u]));
+      }
+    } else if constexpr (F::F16W) {
       // 16 bytes of weights (8 fp16) against 16 bytes of x at a time
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -562,7 +628,9 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
       }
     }
     }
-    if constexpr (F::F16W) {
+    if constexpr (HALF) {
+      // folded above
+    } else if constexpr (F::F16W) {
 #pragma unroll
       for (int u = 0; u < UR; ++u) acc[u] += a0[u] + a1[u];
     } else if constexpr (GS == 32) {
