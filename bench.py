@@ -65,9 +65,9 @@ TRAFFIC = {
     # (KiB per dispatch of qgemv_batched_kernel<4,16,4,64>) and on
     # `bench.py --copy-calib` (a 1 GiB device copy: FETCH_SIZE reads 524,300
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
-    "fetch_kib": 171921.4, "fetch_scale": 1073741824 / (524301.3 * 1024),
-    "write_kib": 1937.6, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "67814a18150cc72eebc89077ad352dc8bf2ad8a0b10b3e2e628ca4ad1bca02bc",
+    "fetch_kib": 171951.3, "fetch_scale": 1073741824 / (524301.3 * 1024),
+    "write_kib": 1937.5, "write_scale": 1073741824 / (1048576.0 * 1024),
+    "sources_sha256": "003e68ddcb4fe3f00face50d74735c036e7e98783a0815eb5ebb7e9cc42c0536",
 }
 
 

@@ -11,10 +11,10 @@
 //     scale and one fp16 bias;
 //   * LPR consecutive lanes share a row; lane lr takes the row's groups
 //     lr, lr + LPR, lr + 2*LPR, ...  so one wave-wide 128-bit load covers
-//     64/LPR rows with contiguous, fully used 16-byte pieces (4-bit codes in
-//     64-code scale groups: a lane takes half of two groups per step
-//     instead, so that each of its two loads reads whole contiguous lines;
-//     see gemv_block);
+//     64/LPR rows with contiguous, fully used 16-byte pieces (4- and 8-bit
+//     codes in 64-code scale groups: a lane takes a half or a quarter of
+//     two or four groups per step instead, so that each of its loads reads
+//     whole contiguous lines; see gemv_block);
 //   * each lane keeps UR rows in flight (128 bytes of codes per lane for 4
 //     and 8 bits, 64 for 2 bits), and
 //     the loads of the next step are issued before the current step is
@@ -357,13 +357,32 @@ __device__ __forceinline__ float row_sum16(const float (&a)[UR], int lr) {
   return v;
 }
 
+// Partial dot products a[v] of part q (= lane % NP) of NP groups, held by
+// the NP consecutive lanes of a cluster: returns the cluster's total for
+// group v = q, with the exchanges transposed (a lane keeps the groups its
+// partner does not): one quad permute for NP = 2, two for NP = 4.
+template <int NP>
+__device__ __forceinline__ float cluster_sum(const float (&a)[NP], int q) {
+  static_assert(NP == 2 || NP == 4, "clusters of 2 or 4 lanes");
+  if constexpr (NP == 2) {
+    return (q ? a[1] : a[0]) + dpp_read<kDppXor1>(q ? a[0] : a[1]);
+  } else {
+    // i ^ 2: lanes with bit 1 clear keep groups 0, 1, the others 2, 3
+    const bool b1 = (q & 2) != 0;
+    const float k0 = (b1 ? a[2] : a[0]) + dpp_read<kDppXor2>(b1 ? a[0] : a[2]);
+    const float k1 = (b1 ? a[3] : a[1]) + dpp_read<kDppXor2>(b1 ? a[1] : a[3]);
+    return ((q & 1) ? k1 : k0) + dpp_read<kDppXor1>((q & 1) ? k0 : k1);
+  }
+}
+
 // Weight-stream loads (codes, scales and biases), non-temporal (NT) where
 // every wave-wide load consumes whole 128-byte lines: the 2-bit groups (one
-// 16-byte load per lane) and the 4-bit half-group lanes below.  The stream is
-// read once and need not stay in L2; a plain read kernel over the same bytes
-// streams 7-10 % faster with such loads.  Where a lane reads its group with
-// several loads, each covering part of every line (3, 5, 6 and 8 bits, and
-// 4 bits with whole groups per lane), the same policy measured 5-38 % slower.
+// 16-byte load per lane) and the 4- and 8-bit split-group lanes below.  The
+// stream is read once and need not stay in L2; a plain read kernel over the
+// same bytes streams 7-10 % faster with such loads.  Where a lane reads its
+// group with several loads, each covering part of every line (3, 5 and 6
+// bits, and 4 and 8 bits with whole groups per lane), the same policy
+// measured 5-38 % slower, so those keep ordinary loads.
 template <bool NT, typename T>
 __device__ __forceinline__ T stream_load(gptr<T> p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -404,16 +423,18 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   constexpr int V4 = F::VEC4_PER_GROUP;
   constexpr int WPG = F::WORDS_PER_GROUP;
   constexpr int PPW = F::PAIRS_PER_WORD;
-  // Half-group lanes (4-bit codes, 64-code scale groups): at a k-step over
-  // groups sb .. sb+LPR-1 of a row, lane lr loads the 16-byte pieces
-  // 2*sb + lr and 2*sb + LPR + lr, i.e. half (lr & 1) of groups
-  // j0 = sb + lr/2 and j1 = j0 + LPR/2, so each wave-wide load reads whole
-  // contiguous lines (with one group per lane, the two loads of a lane's
-  // 32 bytes each took every other 16-byte piece).  The two lanes of a pair
-  // then hold both halves of j0 and of j1; one DPP exchange gives the even
-  // lane j0's dot product and the odd lane j1's, and each folds one group.
-  constexpr bool HALF = BITS == 4 && GS == 64 && LPR >= 2;
-  constexpr bool NT = BITS == 2 || HALF;
+  // Split-group lanes (4- and 8-bit codes, 64-code scale groups): a group
+  // is NP = 2 or 4 sixteen-byte pieces.  At a k-step over groups
+  // sb .. sb+LPR-1 of a row, lane lr loads pieces NP*sb + LPR*v + lr
+  // (v < NP): part q = lr % NP of groups sb + (LPR/NP)*v + lr/NP, so each
+  // wave-wide load reads whole contiguous lines (with one group per lane,
+  // each of a lane's NP loads took every NP-th piece of the lines).  The NP
+  // lanes of a cluster (lr / NP) then hold every part of NP groups; DPP
+  // exchanges (cluster_sum) leave each lane the whole dot product of group
+  // v = q, and each lane folds that one group.
+  constexpr int NP = F::GROUP_BYTES / 16;
+  constexpr bool SPLIT = (BITS == 4 || BITS == 8) && GS == 64 && LPR % NP == 0;
+  constexpr bool NT = BITS == 2 || SPLIT;
   constexpr int SBN = GS == 32 ? 2 : 1;
   using Buf = StepBuf<BITS, UR, SBN>;
 
@@ -447,20 +468,19 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   auto issue = [&](Buf& bf) {
     int g = (wk + it * WK) * LPR + lr;
     g = g < groups ? g : groups - 1;  // only a wave with no k-steps (WK > 1) goes past
-    if constexpr (HALF) {
+    if constexpr (SPLIT) {
       int sb = (wk + it * WK) * LPR;
       sb = sb < groups ? sb : groups - LPR;  // (LPR divides groups)
-      const int j0 = sb + (lr >> 1), j1 = j0 + LPR / 2, hh = lr & 1;
+      const int jm = sb + (LPR / NP) * (lr % NP) + lr / NP;  // the group this lane folds
 #pragma unroll
       for (int u = 0; u < UR; ++u) {
         int r = lane_row + ip * Cfg::ROWS + u * Cfg::RPW;
         r = r < row_end ? r : row_end - 1;
-        const gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(W + (size_t)r * rstride);
-        bf.w[u][0] = stream_load<NT>(src + 2 * j0 + hh);
-        bf.w[u][1] = stream_load<NT>(src + 2 * j1 + hh);
-        // the lane folds group j0 (even lanes) or j1 (odd lanes)
-        bf.s[u][0] = stream_load<NT>(S + (size_t)r * sgroups + (hh ? j1 : j0));
-        bf.b[u][0] = stream_load<NT>(B + (size_t)r * sgroups + (hh ? j1 : j0));
+        const gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(W + (size_t)r * rstride) + (size_t)NP * sb + lr;
+#pragma unroll
+        for (int v = 0; v < NP; ++v) bf.w[u][v] = stream_load<NT>(src + LPR * v);
+        bf.s[u][0] = stream_load<NT>(S + (size_t)r * sgroups + jm);
+        bf.b[u][0] = stream_load<NT>(B + (size_t)r * sgroups + jm);
       }
       if (++it == tcount) { it = 0; ++ip; }
       return;
@@ -514,41 +534,44 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
     float a0[UR], a1[UR];
 #pragma unroll
     for (int u = 0; u < UR; ++u) a0[u] = a1[u] = 0.0f;
-    if constexpr (HALF) {
-      // half hh of groups j0 and j1 (their x pairs: bytes 64*hh .. 64*hh+63
-      // of each group's staging), one accumulator per group
+    if constexpr (SPLIT) {
+      // part q of groups sb + (LPR/NP)*v + c, v < NP (their x pairs: bytes
+      // (128/NP)*q .. of each group's staging), one partial sum per group
       const int sb = (wk + ct * WK) * LPR;
-      const int j0 = sb + (lr >> 1), j1 = j0 + LPR / 2, hh = lr & 1;
-      const unsigned char* x0 = xp + (size_t)j0 * kXStride + 64 * hh;
-      const unsigned char* x1 = xp + (size_t)j1 * kXStride + 64 * hh;
-      // word-major as below: words 0..3 are group j0's, 4..7 group j1's
+      const int q = lr % NP, c = lr / NP;
+      float a[UR][NP];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>((j < 4 ? x0 : x1) + 16 * (j & 3));
-        const uint32_t xr[4] = {v.x, v.y, v.z, v.w};
+      for (int v = 0; v < NP; ++v) {
+        const unsigned char* xv = xp + (size_t)(sb + (LPR / NP) * v + c) * kXStride + (128 / NP) * q;
 #pragma unroll
-        for (int u = 0; u < UR; ++u) {
-          const u32x4 wv = bf.w[u][j >> 2];
-          const uint32_t word = (j & 3) == 0 ? wv.x : (j & 3) == 1 ? wv.y : (j & 3) == 2 ? wv.z : wv.w;
-          uint32_t h[4];
-          unpack_word<4>(word, h);
+        for (int jw = 0; jw < 4; ++jw) {
+          uint32_t xr[PPW];
+          if constexpr (PPW == 2) {
+            const uint2 t = *reinterpret_cast<const uint2*>(xv + 8 * jw);
+            xr[0] = t.x; xr[1] = t.y;
+          } else {
+            const u32x4 t = *reinterpret_cast<const u32x4*>(xv + 16 * jw);
+            xr[0] = t.x; xr[1] = t.y; xr[2] = t.z; xr[3] = t.w;
+          }
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            if (j < 4) a0[u] = j == 0 && p == 0 ? dot2_first(h[p], xr[p]) : dot2(h[p], xr[p], a0[u]);
-            else       a1[u] = j == 4 && p == 0 ? dot2_first(h[p], xr[p]) : dot2(h[p], xr[p], a1[u]);
+          for (int u = 0; u < UR; ++u) {
+            const u32x4 wv = bf.w[u][v];
+            const uint32_t word = jw == 0 ? wv.x : jw == 1 ? wv.y : jw == 2 ? wv.z : wv.w;
+            uint32_t h[PPW];
+            unpack_word<BITS>(word, h);
+#pragma unroll
+            for (int p = 0; p < PPW; ++p)
+              a[u][v] = jw == 0 && p == 0 ? dot2_first(h[p], xr[p]) : dot2(h[p], xr[p], a[u][v]);
           }
         }
       }
-      // partner lanes (lr, lr ^ 1) hold the two halves of j0 and of j1:
-      // the even lane collects j0's whole dot product, the odd lane j1's
-      const float2 c = reinterpret_cast<const float2*>(cx)[hh ? j1 : j0];
+      const float2 cxy = reinterpret_cast<const float2*>(cx)[sb + (LPR / NP) * q + c];
 #pragma unroll
       for (int u = 0; u < UR; ++u) {
-        const float mine = hh ? a1[u] : a0[u];
-        const float dot = mine + dpp_read<kDppXor1>(hh ? a0[u] : a1[u]);
+        const float dot = cluster_sum<NP>(a[u], q);
         const float s = f16_bits_to_f32(bf.s[u][0]);
         const float b = f16_bits_to_f32(bf.b[u][0]);
-        acc[u] = fmaf(s, dot - c.x, fmaf(b, c.y, acc[u]));
+        acc[u] = fmaf(s, dot - cxy.x, fmaf(b, cxy.y, acc[u]));
       }
     } else if constexpr (F::F16W) {
       // 16 bytes of weights (8 fp16) against 16 bytes of x at a time
@@ -628,7 +651,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
       }
     }
     }
-    if constexpr (HALF) {
+    if constexpr (SPLIT) {
       // folded above
     } else if constexpr (F::F16W) {
 #pragma unroll
