@@ -67,7 +67,7 @@ TRAFFIC = {
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
     "fetch_kib": 171951.3, "fetch_scale": 1073741824 / (524301.3 * 1024),
     "write_kib": 1937.5, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "003e68ddcb4fe3f00face50d74735c036e7e98783a0815eb5ebb7e9cc42c0536",
+    "sources_sha256": "3ffad6a244b4ec7ae42fb7535012dd268246e4c336c5677d2d9b265821a99735",
 }
 
 

@@ -12,9 +12,10 @@
 //   * LPR consecutive lanes share a row; lane lr takes the row's groups
 //     lr, lr + LPR, lr + 2*LPR, ...  so one wave-wide 128-bit load covers
 //     64/LPR rows with contiguous, fully used 16-byte pieces (4- and 8-bit
-//     codes in 64-code scale groups: a lane takes a half or a quarter of
-//     two or four groups per step instead, so that each of its loads reads
-//     whole contiguous lines; see gemv_block);
+//     codes in 64-code scale groups and fp16 weights: a lane takes a half,
+//     a quarter or an eighth of two, four or eight groups per step instead,
+//     so that each of its loads reads whole contiguous lines; see
+//     gemv_block);
 //   * each lane keeps UR rows in flight (128 bytes of codes per lane for 4
 //     and 8 bits, 64 for 2 bits), and
 //     the loads of the next step are issued before the current step is
@@ -377,7 +378,7 @@ __device__ __forceinline__ float cluster_sum(const float (&a)[NP], int q) {
 
 // Weight-stream loads (codes, scales and biases), non-temporal (NT) where
 // every wave-wide load consumes whole 128-byte lines: the 2-bit groups (one
-// 16-byte load per lane) and the 4- and 8-bit split-group lanes below.  The
+// 16-byte load per lane) and the split-group lanes below (4 and 8 bits, fp16).  The
 // stream is read once and need not stay in L2; a plain read kernel over the
 // same bytes streams 7-10 % faster with such loads.  Where a lane reads its
 // group with several loads, each covering part of every line (3, 5 and 6
@@ -423,17 +424,18 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
   constexpr int V4 = F::VEC4_PER_GROUP;
   constexpr int WPG = F::WORDS_PER_GROUP;
   constexpr int PPW = F::PAIRS_PER_WORD;
-  // Split-group lanes (4- and 8-bit codes, 64-code scale groups): a group
-  // is NP = 2 or 4 sixteen-byte pieces.  At a k-step over groups
+  // Split-group lanes (4- and 8-bit codes in 64-code scale groups, and
+  // fp16 weights): a group is NP = 2, 4 or 8 sixteen-byte pieces.  At a k-step over groups
   // sb .. sb+LPR-1 of a row, lane lr loads pieces NP*sb + LPR*v + lr
   // (v < NP): part q = lr % NP of groups sb + (LPR/NP)*v + lr/NP, so each
   // wave-wide load reads whole contiguous lines (with one group per lane,
   // each of a lane's NP loads took every NP-th piece of the lines).  The NP
   // lanes of a cluster (lr / NP) then hold every part of NP groups; DPP
   // exchanges (cluster_sum) leave each lane the whole dot product of group
-  // v = q, and each lane folds that one group.
+  // v = q, and each lane folds that one group (fp16 weights have no fold:
+  // every piece goes straight into the row sum).
   constexpr int NP = F::GROUP_BYTES / 16;
-  constexpr bool SPLIT = (BITS == 4 || BITS == 8) && GS == 64 && LPR % NP == 0;
+  constexpr bool SPLIT = ((BITS == 4 || BITS == 8) && GS == 64 || F::F16W) && LPR % NP == 0;
   constexpr bool NT = BITS == 2 || SPLIT;
   constexpr int SBN = GS == 32 ? 2 : 1;
   using Buf = StepBuf<BITS, UR, SBN>;
@@ -479,8 +481,10 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
         const gptr<u32x4> src = reinterpret_cast<gptr<u32x4>>(W + (size_t)r * rstride) + (size_t)NP * sb + lr;
 #pragma unroll
         for (int v = 0; v < NP; ++v) bf.w[u][v] = stream_load<NT>(src + LPR * v);
-        bf.s[u][0] = stream_load<NT>(S + (size_t)r * sgroups + jm);
-        bf.b[u][0] = stream_load<NT>(B + (size_t)r * sgroups + jm);
+        if constexpr (!F::F16W) {
+          bf.s[u][0] = stream_load<NT>(S + (size_t)r * sgroups + jm);
+          bf.b[u][0] = stream_load<NT>(B + (size_t)r * sgroups + jm);
+        }
       }
       if (++it == tcount) { it = 0; ++ip; }
       return;
@@ -534,7 +538,24 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
     float a0[UR], a1[UR];
 #pragma unroll
     for (int u = 0; u < UR; ++u) a0[u] = a1[u] = 0.0f;
-    if constexpr (SPLIT) {
+    if constexpr (SPLIT && F::F16W) {
+      // fp16 weights have no per-group fold: every piece's dot product goes
+      // straight into the row sum (x in natural order, 16 bytes per piece)
+      const int sb = (wk + ct * WK) * LPR;
+      const int q = lr % NP, c = lr / NP;
+#pragma unroll
+      for (int v = 0; v < NP; ++v) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xp + (size_t)(sb + (LPR / NP) * v + c) * kXStride + 16 * q);
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          const u32x4 wv = bf.w[u][v];
+          a0[u] = v == 0 ? dot2_first(wv.x, xv.x) : dot2(wv.x, xv.x, a0[u]);
+          a1[u] = v == 0 ? dot2_first(wv.y, xv.y) : dot2(wv.y, xv.y, a1[u]);
+          a0[u] = dot2(wv.z, xv.z, a0[u]);
+          a1[u] = dot2(wv.w, xv.w, a1[u]);
+        }
+      }
+    } else if constexpr (SPLIT) {
       // part q of groups sb + (LPR/NP)*v + c, v < NP (their x pairs: bytes
       // (128/NP)*q .. of each group's staging), one partial sum per group
       const int sb = (wk + ct * WK) * LPR;
@@ -651,7 +672,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem& P, int row0, int n
       }
     }
     }
-    if constexpr (SPLIT) {
+    if constexpr (SPLIT && !F::F16W) {
       // folded above
     } else if constexpr (F::F16W) {
 #pragma unroll
