@@ -203,13 +203,17 @@ def bench_gemm_formats(torch, qmm, m=2048, n=9728, k=2560, bits_list=(2, 3, 4, 5
     stream = torch.cuda.current_stream()
     for bits in bits_list:
         wq = (wf.half().view(torch.int32), None, None) if bits == 16 else qmm.quantize(wf, bits)
-        wq = (qmm.repack_tiled(wq[0], bits), wq[1], wq[2])  # tile-interleaved copy, once
+        stiled = PREFILL_SCALES_TILED and bits != 16
+        # tile-interleaved copy (and interleaved scales), once
+        wq = (qmm.repack_tiled(wq[0], bits), qmm.repack_scales_tiled(wq[1], wq[2]) if stiled else wq[1],
+              None if stiled else wq[2])
         wbytes = sum(t.numel() * t.element_size() for t in wq if t is not None)
         copies = max(2, -(-LLC_EVICT_BYTES // wbytes))
         sets = [wq] + [tuple(None if t is None else t.clone() for t in wq) for _ in range(copies - 1)]
         ws = torch.empty(max(qmm.qgemm_workspace_size(m, n, k, bits), 16), dtype=torch.uint8, device="cuda")
         ms_call, _ = time_launches(
-            torch, lambda i: qmm.qgemm(*sets[i % copies], x, bits, y=y, workspace=ws, tiled=True),
+            torch, lambda i: qmm.qgemm(*sets[i % copies], x, bits, y=y, workspace=ws, tiled=True,
+                                       scales_tiled=stiled),
             steps, warmup, stream)
         tfl = 2.0 * m * n * k / (ms_call * 1e-3) / 1e12
         out["f16" if bits == 16 else f"q{bits}"] = {"ms_per_call": round(ms_call, 4), "tflops": round(tfl, 1),
@@ -383,7 +387,11 @@ def bench_decode_extras(torch, qmm, wl, sets, steps=20, warmup=3):
 PREFILL_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 
 
-PREFILL_WEIGHTS = "tile-interleaved copy (qmm_repack_tiled, once at load)"
+# The dense prefill GEMMs read interleaved scales and biases
+# (qmm_repack_scales_tiled) unless --row-major-scales is given.
+PREFILL_SCALES_TILED = True
+PREFILL_WEIGHTS = ("tile-interleaved copy (qmm_repack_tiled, once at load); dense GEMMs with interleaved "
+                   "scales and biases (qmm_repack_scales_tiled, once at load)")
 
 
 def prefill_layers(torch, qmm, wl, batched=True):
@@ -396,9 +404,14 @@ def prefill_layers(torch, qmm, wl, batched=True):
     for i, p in enumerate(wl.projs):
         wf = torch.from_numpy(synth.draw_weight((wl.wid, 0, i, synth.STREAM_W), p.n, p.k)).cuda()
         words, s_, b_ = qmm.quantize(wf, wl.bits)
-        base[i] = (qmm.repack_tiled(words, wl.bits), s_, b_) if batched else (words, s_, b_)
+        if not batched:
+            base[i] = (words, s_, b_)
+        elif PREFILL_SCALES_TILED:
+            base[i] = (qmm.repack_tiled(words, wl.bits), qmm.repack_scales_tiled(s_, b_), None)
+        else:
+            base[i] = (qmm.repack_tiled(words, wl.bits), s_, b_)
         del wf, words
-    layers = [[tuple(t.clone() for t in base[i]) if layer else base[i]
+    layers = [[tuple(None if t is None else t.clone() for t in base[i]) if layer else base[i]
                for i in range(len(wl.projs))] for layer in range(wl.layers)]
     torch.cuda.synchronize()
     return layers
@@ -415,7 +428,7 @@ def prefill_plans(qmm, wl, layers, xs, ys, groups=PREFILL_GROUPS):
     names = [p.name for p in wl.projs]
     return [[qmm.qgemm_batched_plan(
         [(*L[names.index(nm)], xs[names.index(nm)], ys[names.index(nm)]) for nm in grp],
-        wl.bits, tiled=True) for grp in groups] for L in layers]
+        wl.bits, tiled=True, scales_tiled=PREFILL_SCALES_TILED) for grp in groups] for L in layers]
 
 
 def prefill_work(wl, m):
@@ -841,11 +854,18 @@ def main():
     ap.add_argument("--ms", metavar="M[,M...]", help="prefill/moe: only these M")
     ap.add_argument("--decode-bits", type=int, choices=[2, 3, 4, 5, 6, 8, 16], default=4,
                     help="with --only decode: the decode pass at another weight width (for counters)")
+    ap.add_argument("--row-major-scales", action="store_true",
+                    help="dense prefill GEMMs read row-major scales and biases instead of the "
+                         "interleaved copy (for comparisons)")
     ap.add_argument("--forces", metavar="F;F...",
                     help="with --launch: time every launch under each forced tile: QMM_GEMM_FORCE "
                          "for prefill launches (bm,nb,splits[,kw]), QMM_MOE_FORCE for moe launches "
                          "(bm,nb); empty = the planner's or the routing rule's choice")
     args = ap.parse_args()
+    if args.row_major_scales:
+        global PREFILL_SCALES_TILED, PREFILL_WEIGHTS
+        PREFILL_SCALES_TILED = False
+        PREFILL_WEIGHTS = "tile-interleaved copy (qmm_repack_tiled, once at load); row-major scales and biases"
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(this library has no multi-GPU path).", file=sys.stderr)

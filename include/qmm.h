@@ -171,9 +171,14 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
  * everywhere else; `bits | QMM_WEIGHTS_TILED` means every w was produced by
  * qmm_repack_tiled (then every n must be a multiple of 32), which the
  * prefill tiles read with fewer, fully contiguous loads.  Scales and biases
- * stay row-major either way.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE,
- * HIP. */
+ * are row-major unless `bits` also carries QMM_SCALES_TILED: then every
+ * `scales` pointer is an interleaved scale-and-bias array produced by
+ * qmm_repack_scales_tiled (16-byte aligned; `biases` is not read and may be
+ * NULL), which needs QMM_WEIGHTS_TILED, group_size 64, 2- to 8-bit codes and
+ * k a multiple of 256.  The two scale layouts give identical results.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
 #define QMM_WEIGHTS_TILED 0x100
+#define QMM_SCALES_TILED 0x200
 typedef struct {
   const uint32_t* w;
   const uint16_t* scales;
@@ -342,6 +347,22 @@ int qmm_convert_bf16(const uint16_t* src, uint16_t* dst, size_t count, qmm_strea
  * multiple of 32).  The decode GEMV keeps reading row-major weights.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
 int qmm_repack_tiled(const uint32_t* w, uint32_t* out, int n, int k, int bits, qmm_stream stream);
+
+/* Interleaved scales and biases for the prefill GEMM over tile-interleaved
+ * weights (load time; a layout of this library's own, not from the pages):
+ * out holds every scale and bias of the row-major scales and biases
+ * [n, k/64] (groups of 64 codes), for each block of 32 columns and each
+ * quad of 4 groups the 32 columns' 16-byte {s[4q .. 4q+3], b[4q .. 4q+3]}
+ * next to each other:
+ *   scales[c * G + g] -> out[((c / 32) * (G / 4) * 32 + c % 32) * 8 + (g / 4) * 256 + g % 4]
+ *   biases[c * G + g] -> the same index + 4,      with G = k / 64,
+ * so one wave's scale loads read whole lines.  n must be a multiple of 32 and
+ * k of 256; scales and biases are device arrays of n * k / 64 fp16 (2-byte
+ * aligned), out one of 2 * n * k / 64 fp16 (16-byte aligned, overlapping
+ * neither); out is used as `scales` with QMM_SCALES_TILED.
+ * Errors: INVALID_ARG, HIP. */
+int qmm_repack_scales_tiled(const uint16_t* scales, const uint16_t* biases, uint16_t* out, int n, int k,
+                            qmm_stream stream);
 
 /* ------------------------------------------------------------- diagnostics
  * Expose the device-side stages of the hot path for bit-exact checking.

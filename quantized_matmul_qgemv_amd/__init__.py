@@ -9,8 +9,8 @@ from .api import (  # noqa: F401
     moe_route, moe_route_size, qgemm, qgemm_batched, qgemm_batched_plan, qgemm_grouped,
     qgemm_grouped_noalloc,
     qgemm_grouped_workspace_size,
-    qgemm_workspace_size, qgemv, qgemv_batched, qgemv_batched_plan, quantize, repack_tiled,
-    unpack_codes,
+    qgemm_workspace_size, qgemv, qgemv_batched, qgemv_batched_plan, quantize, repack_scales_tiled,
+    repack_tiled, unpack_codes,
 )
 
 __all__ = [
@@ -18,5 +18,5 @@ __all__ = [
     "convert_bf16", "moe_combine", "moe_gate_up_swiglu", "moe_plan_dropped", "moe_route",
     "moe_route_size", "qgemm_batched", "qgemm_grouped_noalloc", "qgemm_batched_plan", "qgemm_grouped",
     "qgemm_grouped_workspace_size", "qgemm_workspace_size", "qgemv", "qgemv_batched",
-    "qgemv_batched_plan", "quantize", "repack_tiled", "unpack_codes",
+    "qgemv_batched_plan", "quantize", "repack_scales_tiled", "repack_tiled", "unpack_codes",
 ]

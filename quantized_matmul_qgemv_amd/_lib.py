@@ -20,6 +20,7 @@ QMM_ERR_UNSUPPORTED = 2
 QMM_ERR_WORKSPACE = 3
 QMM_ERR_HIP = 4
 QMM_WEIGHTS_TILED = 0x100  # bits flag: weights from qmm_repack_tiled
+QMM_SCALES_TILED = 0x200  # bits flag: scales from qmm_repack_scales_tiled (biases unused)
 QMM_GROUPED_SCRATCH_BYTES = 1 << 20  # static scratch of qmm_qgemm_grouped_noalloc
 
 STATUS_NAMES = {0: "QMM_OK", 1: "QMM_ERR_INVALID_ARG", 2: "QMM_ERR_UNSUPPORTED",
@@ -66,6 +67,7 @@ SIGNATURES = {
     "qmm_moe_combine": (I, [P, P, P, I, I, I, P]),
     "qmm_convert_bf16": (I, [P, P, SZ, P]),
     "qmm_repack_tiled": (I, [P, P, I, I, I, P]),
+    "qmm_repack_scales_tiled": (I, [P, P, P, I, I, P]),
     "qmm_quantize": (I, [P, P, P, P, I, I, I, I, P]),
     "qmm_unpack_codes": (I, [P, P, I, I, I, P]),
     "qmm_dequant": (I, [P, P, P, P, I, I, I, I, I, P]),

@@ -108,9 +108,10 @@ def qgemm_workspace_size(m, n, k, bits, group_size=GROUP) -> int:
 
 
 def qgemm(w, scales, biases, x, bits: int, y=None, group_size: int = GROUP, workspace=None,
-          stream=None, tiled: bool = False):
+          stream=None, tiled: bool = False, scales_tiled: bool = False):
     """y[m, n] = sum_k x[m, k] * W_hat[n, k] via qmm_qgemm (tiled=True when w
-    comes from repack_tiled)."""
+    comes from repack_tiled; scales_tiled=True when scales comes from
+    repack_scales_tiled, which then holds the biases too)."""
     m, k = x.shape
     n = w.shape[0]
     if y is None:
@@ -120,9 +121,11 @@ def qgemm(w, scales, biases, x, bits: int, y=None, group_size: int = GROUP, work
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=w.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    check(lib().qmm_qgemm(_dev(w, "w", _W), _sb(scales, "scales", bits), _sb(biases, "biases", bits),
+    check(lib().qmm_qgemm(_dev(w, "w", _W), _sb(scales, "scales", bits),
+                          None if scales_tiled else _sb(biases, "biases", bits),
                           _dev(x, "x", _X), _dev(y, "y", _Y), m, n, k,
-                          bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0), group_size,
+                          bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0)
+                          | (_lib.QMM_SCALES_TILED if scales_tiled else 0), group_size,
                           ws_ptr, ws_len, _stream(stream)))
     return y
 
@@ -144,16 +147,19 @@ class GemmBatchPlan:
         f = __import__("struct").unpack("<IIiiiiiiiiiiQii", raw)
         return {"bits": f[2], "bm": f[4], "nb": f[5], "sbq": f[6], "count": f[7],
                 "num_tiles": f[8], "split_tiles": f[9], "splits": f[10], "wtiled": f[11],
-                "kw": f[13]}
+                "kw": f[13], "stiled": f[14]}
 
 
-def qgemm_batched_plan(problems, bits: int, group_size: int = GROUP, tiled: bool = False) -> GemmBatchPlan:
+def qgemm_batched_plan(problems, bits: int, group_size: int = GROUP, tiled: bool = False,
+                       scales_tiled: bool = False) -> GemmBatchPlan:
     """Plan one launch for a list of (w, scales, biases, x, y) GEMM problems;
-    tiled=True when every w comes from repack_tiled."""
-    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0)
+    tiled=True when every w comes from repack_tiled, scales_tiled=True when
+    every scales comes from repack_scales_tiled (biases then unused)."""
+    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0) | (_lib.QMM_SCALES_TILED if scales_tiled else 0)
     arr = (GemmProblem * len(problems))()
     for i, (w, s, b, x, y) in enumerate(problems):
-        arr[i] = GemmProblem(_dev(w, "w", _W), _sb(s, "scales", bits), _sb(b, "biases", bits),
+        arr[i] = GemmProblem(_dev(w, "w", _W), _sb(s, "scales", bits),
+                             None if scales_tiled else _sb(b, "biases", bits),
                              _dev(x, "x", _X), _dev(y, "y", _Y), x.shape[0], w.shape[0],
                              x.shape[1])
     need, ws = C.c_size_t(0), C.c_size_t(0)
@@ -299,6 +305,19 @@ def repack_tiled(w, bits: int, out=None, stream=None):
     if out is None:
         out = torch.empty_like(w)
     check(lib().qmm_repack_tiled(_dev(w, "w", _W), _dev(out, "out", _W), n, k, bits, _stream(stream)))
+    return out
+
+
+def repack_scales_tiled(scales, biases, out=None, stream=None):
+    """Interleaved scales and biases [n, k/64] (fp16 bits, groups of 64) for
+    the prefill GEMM with scales_tiled=True, via qmm_repack_scales_tiled:
+    one array of 2 * n * k/64 fp16 holding both."""
+    n = scales.numel() // scales.shape[-1]
+    k = scales.shape[-1] * 64
+    if out is None:
+        out = torch.empty(2 * scales.numel(), dtype=scales.dtype, device=scales.device)
+    check(lib().qmm_repack_scales_tiled(_dev(scales, "scales", _SB), _dev(biases, "biases", _SB),
+                                        _dev(out, "out", _SB), n, k, _stream(stream)))
     return out
 
 

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int g1 = g0 + gr.gps_split;
   gemm_tile<BITS, BM, NB, SBQ>(ARows{a.x, a.k}, a_row, c_row, a.w, a.s, a.b, out + n0, a.n, n0,
                                a.n, g0, g1, lds, a.group_size, nullptr, nullptr, nullptr, nullptr,
-                               a.wtiled);
+                               a.wtiled, a.stiled);
 }
 
 // 256 x 256 tiles, one workgroup per CU (qgemm_wide.h); same tile order as
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1)
   const int g0 = split * gr.gps_split;
   const int g1 = g0 + gr.gps_split;
   gemm_tile_wide<BITS, SBQ>(ARows{a.x, a.k}, a_row, c_row, a.w, a.s, a.b, out + n0, a.n, n0, a.n,
-                            g0, g1, lds, a.group_size, a.wtiled);
+                            g0, g1, lds, a.group_size, a.wtiled, a.stiled);
 }
 
 // y[i] = sum over splits of partial[split * stride + i], in split order.

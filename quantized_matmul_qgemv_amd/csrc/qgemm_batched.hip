@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void qgemm_batched_reduce_kernel(
 template <int BITS, int BM, int NB, bool SBQ, int KW>
 __global__ __launch_bounds__(kGemmThreads * KW) __attribute__((amdgpu_waves_per_eu(2))) void qgemm_batched_kernel(
     const GemmBatchProblem* __restrict__ probs, const GemmTileRec* __restrict__ tiles,
-    float* partials, int gs, int wtiled) {
+    float* partials, int gs, int wtiled, int stiled) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[gemm_lds_halves(BM, NB, KW)];
   constexpr int BN = 4 * NB * 32;
   const GemmTileRec t = tiles[blockIdx.x];
@@ -97,13 +97,13 @@ __global__ __launch_bounds__(kGemmThreads * KW) __attribute__((amdgpu_waves_per_
   auto a_row = [&](int i) { const int r = m0 + i; return r < m ? r : m - 1; };
   auto c_row = [&](int i) { return m0 + i < m ? rowoff + i : -1; };
   gemm_tile<BITS, BM, NB, SBQ, false, KW>(ARows{P.x, P.k}, a_row, c_row, P.w, P.s, P.b, ytile, ldy, t.n0,
-                               P.n, t.g0, t.g1, lds, gs, nullptr, nullptr, nullptr, nullptr, wtiled);
+                               P.n, t.g0, t.g1, lds, gs, nullptr, nullptr, nullptr, nullptr, wtiled, stiled);
 }
 
 template <int BITS, bool SBQ>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1))) void qgemm_batched_wide_kernel(
     const GemmBatchProblem* __restrict__ probs, const GemmTileRec* __restrict__ tiles,
-    float* partials, int gs, int wtiled) {
+    float* partials, int gs, int wtiled, int stiled) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kWideLdsHalves];
   constexpr int BM = kWideBM;
   constexpr int BN = 256;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1)
   auto a_row = [&](int i) { const int r = m0 + i; return r < m ? r : m - 1; };
   auto c_row = [&](int i) { return m0 + i < m ? rowoff + i : -1; };
   gemm_tile_wide<BITS, SBQ>(ARows{P.x, P.k}, a_row, c_row, P.w, P.s, P.b, ytile, ldy, t.n0, P.n,
-                            t.g0, t.g1, lds, gs, wtiled);
+                            t.g0, t.g1, lds, gs, wtiled, stiled);
 }
 
 // ------------------------------------------------------------------ host --
@@ -262,7 +262,7 @@ void gemm_choose(int m, int n, int k, int bits, int* bm, int* nb, int* splits) {
 }
 
 size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, int group_size,
-                        int wtiled, void* out, size_t out_bytes) {
+                        int wtiled, int stiled, void* out, size_t out_bytes) {
   Choice ch = choose(probs, count, bits, false, bits == 16);
   // quad scale loads (8 bytes per column): groups of 64 with 8-byte aligned
   // scale and bias arrays only
@@ -300,6 +300,7 @@ size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, int 
   hdr.split_tiles = (int32_t)split_tiles;
   hdr.splits = S;
   hdr.wtiled = wtiled ? 1 : 0;
+  hdr.stiled = stiled ? 1 : 0;
   hdr.workspace_bytes = S > 1 ? (size_t)split_tiles * S * c.bm * bn * 4 : 0;
   unsigned char* base = static_cast<unsigned char*>(out);
   memcpy(base, &hdr, sizeof hdr);
@@ -346,10 +347,10 @@ static void launch_batched_cfg(const GemmBatchProblem* probs, const GemmTileRec*
                                const GemmBatchHeader& h, float* partials, hipStream_t st) {
   if (h.sbq)
     hipLaunchKernelGGL((qgemm_batched_kernel<BITS, BM, NB, true, KW>), dim3(h.num_tiles),
-                       dim3(kGemmThreads * KW), 0, st, probs, tiles, partials, h.group_size, h.wtiled);
+                       dim3(kGemmThreads * KW), 0, st, probs, tiles, partials, h.group_size, h.wtiled, h.stiled);
   else
     hipLaunchKernelGGL((qgemm_batched_kernel<BITS, BM, NB, false, KW>), dim3(h.num_tiles),
-                       dim3(kGemmThreads * KW), 0, st, probs, tiles, partials, h.group_size, h.wtiled);
+                       dim3(kGemmThreads * KW), 0, st, probs, tiles, partials, h.group_size, h.wtiled, h.stiled);
 }
 
 template <int BITS>
@@ -373,10 +374,10 @@ static void launch_batched_bits(const GemmBatchProblem* probs, const GemmTileRec
     } else if (h.bm == 256) {
       if (h.sbq)
         hipLaunchKernelGGL((qgemm_batched_wide_kernel<BITS, true>), dim3(h.num_tiles), dim3(kGemmThreads),
-                           0, st, probs, tiles, partials, h.group_size, h.wtiled);
+                           0, st, probs, tiles, partials, h.group_size, h.wtiled, h.stiled);
       else
         hipLaunchKernelGGL((qgemm_batched_wide_kernel<BITS, false>), dim3(h.num_tiles), dim3(kGemmThreads),
-                           0, st, probs, tiles, partials, h.group_size, h.wtiled);
+                           0, st, probs, tiles, partials, h.group_size, h.wtiled, h.stiled);
     } else if (h.bm == 128) {
       if (h.nb == 2) launch_batched_cfg<BITS, 128, 2>(probs, tiles, h, partials, st);
       else launch_batched_cfg<BITS, 128, 1>(probs, tiles, h, partials, st);

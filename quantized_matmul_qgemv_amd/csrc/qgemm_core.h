@@ -91,9 +91,26 @@ __device__ __forceinline__ size_t weight_column_offset(int col, int groups, int 
   return wtiled ? ((size_t)(col >> 5) * groups * 32 + (col & 31)) * wpg : (size_t)col * groups * wpg;
 }
 
+// Scale/bias layouts.  Row-major (stiled = 0): column c's scale and bias of
+// scale group i at s[c * SG + i] and b[c * SG + i] (SG = k / gs).
+// Interleaved (stiled = 1, qmm_repack_scales_tiled; groups of 64 codes and
+// k a multiple of 256): for every block of 32 columns and every quad of 4
+// groups, the 32 columns' {s[4q .. 4q+3], b[4q .. 4q+3]} (16 bytes each)
+// are contiguous, so a wave's quad loads read 4 whole lines instead of
+// parts of 32.  Column c's base (in halves, b == s then):
+// ((c / 32) * (G / 4) * 32 + c % 32) * 8; group g's scale at base +
+// (g / 4) * 256 + g % 4 and its bias 4 halves later.  The two layouts use
+// the same loads (no branch around a load: it would drain the pipeline).
+__device__ __forceinline__ size_t scale_column_offset(int col, int sgroups, int stiled) {
+  return stiled ? ((size_t)(col >> 5) * (sgroups >> 2) * 32 + (col & 31)) * 8 : (size_t)col * sgroups;
+}
+
+__device__ __forceinline__ int scale_quad_offset(int g4, int stiled) { return stiled ? (g4 >> 2) * 256 : g4; }
+
 template <int BITS, bool WITH_SB = true>
 __device__ __forceinline__ void load_braw(BRaw<BITS>& r, gptr<uint32_t> wcol, gptr<uint16_t> scol,
-                                          gptr<uint16_t> bcol, int g, int h, int gs, int gstride) {
+                                          gptr<uint16_t> bcol, int g, int h, int gs, int gstride,
+                                          int stiled = 0) {
   constexpr int WPG = Fmt<BITS>::WORDS_PER_GROUP;
   gptr<uint32_t> p = wcol + (size_t)g * gstride + h * (WPG / 2);
   if constexpr (BITS == 6) {
@@ -118,9 +135,9 @@ __device__ __forceinline__ void load_braw(BRaw<BITS>& r, gptr<uint32_t> wcol, gp
     }
   }
   if constexpr (WITH_SB) {
-    const int si = sb_index(g, h, gs);
+    const int si = stiled ? (g >> 2) * 256 + (g & 3) : sb_index(g, h, gs);
     r.s = scol[si];
-    r.b = bcol[si];
+    r.b = bcol[stiled ? si + 4 : si];
   }
 }
 
@@ -224,7 +241,7 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
                                           const uint16_t* __restrict__ s2_ = nullptr,
                                           const uint16_t* __restrict__ b2_ = nullptr,
                                           uint16_t* __restrict__ h_tile = nullptr,
-                                          int wtiled = 0) {
+                                          int wtiled = 0, int stiled = 0) {
   static_assert(!SWIGLU || NB == 2, "SwiGLU pairs a gate and an up column block");
   static_assert(KW == 1 || KW == 2, "one or two k halves per workgroup");
   constexpr int MB = BM / 32;
@@ -255,8 +272,8 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
     col = col < n ? col : n - 1;
     const bool second = SWIGLU && nb == 1;
     wcol[nb] = (second ? to_global(w2_) : w) + weight_column_offset(col, groups, WPG, wtiled);
-    scol[nb] = (second ? to_global(s2_) : s) + (size_t)col * sgroups;
-    bcol[nb] = (second ? to_global(b2_) : b) + (size_t)col * sgroups;
+    scol[nb] = (second ? to_global(s2_) : s) + scale_column_offset(col, sgroups, stiled);
+    bcol[nb] = stiled ? scol[nb] : (second ? to_global(b2_) : b) + (size_t)col * sgroups;
   }
 
   // KW = 2: waves 4..7 take the second half of the k range (a multiple of
@@ -333,7 +350,8 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   auto load_b = [&](BRaw<BITS> (&dst)[NB], int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      load_braw<BITS, !SBQ && !Fmt<BITS>::F16W>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs, gstride);
+      load_braw<BITS, !SBQ && !Fmt<BITS>::F16W>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs, gstride,
+                                                stiled);
   };
   // SBQ: scales and biases of four consecutive groups come in one 8-byte
   // load per column (a 2-byte load touches as many cache lines as a wide
@@ -343,8 +361,9 @@ __device__ __forceinline__ void gemm_tile(const ARows A, ARowFn a_row, CRowFn c_
   auto load_sbq = [&](u32x2 (&sq)[NB], u32x2 (&bq)[NB], int g4) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      sq[nb] = *reinterpret_cast<gptr<u32x2>>(scol[nb] + g4);
-      bq[nb] = *reinterpret_cast<gptr<u32x2>>(bcol[nb] + g4);
+      const int so = scale_quad_offset(g4, stiled);
+      sq[nb] = *reinterpret_cast<gptr<u32x2>>(scol[nb] + so);
+      bq[nb] = *reinterpret_cast<gptr<u32x2>>(bcol[nb] + (stiled ? so + 4 : so));
     }
   };
   auto set_sb = [&](BRaw<BITS> (&cur)[NB], int q) {

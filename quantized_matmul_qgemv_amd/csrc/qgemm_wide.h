@@ -34,7 +34,7 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
                                                const uint16_t* __restrict__ b_,
                                                float* __restrict__ y_tile, int ldy, int n0, int n,
                                                int g_begin, int g_end, uint16_t* lds, int gs = 64,
-                                               int wtiled = 0) {
+                                               int wtiled = 0, int stiled = 0) {
   constexpr int BM = kWideBM;
   constexpr int MB = BM / 32;
   constexpr int NB = 2;
@@ -63,8 +63,8 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
     int col = n0 + (wave * NB + nb) * 32 + l32;
     col = col < n ? col : n - 1;
     wcol[nb] = w + weight_column_offset(col, groups, WPG, wtiled);
-    scol[nb] = s + (size_t)col * sgroups;
-    bcol[nb] = b + (size_t)col * sgroups;
+    scol[nb] = s + scale_column_offset(col, sgroups, stiled);
+    bcol[nb] = stiled ? scol[nb] : b + (size_t)col * sgroups;
   }
   gptr<uint16_t> asrc[SPT];
   int aoff[SPT];
@@ -117,13 +117,15 @@ __device__ __forceinline__ void gemm_tile_wide(const ARows A, ARowFn a_row, CRow
   auto load_b = [&](BRaw<BITS> (&dst)[NB], int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      load_braw<BITS, !SBQ && !Fmt<BITS>::F16W>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs, gstride);
+      load_braw<BITS, !SBQ && !Fmt<BITS>::F16W>(dst[nb], wcol[nb], scol[nb], bcol[nb], g, h, gs, gstride,
+                                                stiled);
   };
   auto load_sbq = [&](u32x2 (&sq)[NB], u32x2 (&bq)[NB], int g4) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      sq[nb] = *reinterpret_cast<gptr<u32x2>>(scol[nb] + g4);
-      bq[nb] = *reinterpret_cast<gptr<u32x2>>(bcol[nb] + g4);
+      const int so = scale_quad_offset(g4, stiled);
+      sq[nb] = *reinterpret_cast<gptr<u32x2>>(scol[nb] + so);
+      bq[nb] = *reinterpret_cast<gptr<u32x2>>(bcol[nb] + (stiled ? so + 4 : so));
     }
   };
   auto set_sb = [&](BRaw<BITS> (&cur)[NB], int q) {

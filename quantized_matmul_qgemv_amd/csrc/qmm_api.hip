@@ -212,8 +212,19 @@ int qmm_qgemv_batched(const void* plan_device, const void* plan_host, qmm_stream
                     fn);
 }
 
+// Scale layout flag of the GEMM entry points: interleaved scales need
+// tile-interleaved weights, groups of 64, quantized codes and k % 256 == 0.
+static int check_stiled(const char* fn, int stiled, int wtiled, int bits, int group_size, int k) {
+  if (!stiled) return QMM_OK;
+  if (!wtiled) return fail(QMM_ERR_INVALID_ARG, "%s: QMM_SCALES_TILED needs QMM_WEIGHTS_TILED", fn);
+  if (bits == 16) return fail(QMM_ERR_INVALID_ARG, "%s: fp16 weights have no scales to interleave", fn);
+  if (group_size != 64 || k % 256 != 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: interleaved scales need group_size 64 and k %% 256 == 0 (k=%d)", fn, k);
+  return QMM_OK;
+}
+
 size_t qmm_qgemm_workspace_size(int m, int n, int k, int bits, int group_size) {
-  bits &= ~QMM_WEIGHTS_TILED;  // the layout does not change the split-k workspace
+  bits &= ~(QMM_WEIGHTS_TILED | QMM_SCALES_TILED);  // the layouts do not change the split-k workspace
   if (m < 1 || n < 1 || k < 64 || k % 64 != 0) return 0;
   if ((group_size != 32 && group_size != 64 && group_size != 128) || k % group_size != 0) return 0;
   if ((bits < 2 || bits > 8 || bits == 7) && bits != 16) return 0;
@@ -226,15 +237,19 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
   const char* fn = "qmm_qgemm";
   clear_error();
   const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
-  bits &= ~QMM_WEIGHTS_TILED;
+  const int stiled = (bits & QMM_SCALES_TILED) ? 1 : 0;
+  bits &= ~(QMM_WEIGHTS_TILED | QMM_SCALES_TILED);
   if (int st = check_format(fn, bits, group_size, true)) return st;
   if (m < 0) return fail(QMM_ERR_INVALID_ARG, "%s: m=%d must be >= 0", fn, m);
   if (int st = check_nk(fn, n, k, group_size)) return st;
   if (wtiled && n % 32 != 0)
     return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32 for tile-interleaved weights", fn, n);
+  if (int st = check_stiled(fn, stiled, wtiled, bits, group_size, k)) return st;
   if (m == 0) return QMM_OK;
   CHECK_PTR(w, 16);
-  if (bits != 16) {  // fp16 weights have no scales or biases
+  if (stiled) {  // one interleaved array holds the scales and the biases
+    CHECK_PTR(scales, 16);
+  } else if (bits != 16) {  // fp16 weights have no scales or biases
     CHECK_PTR(scales, 2);
     CHECK_PTR(biases, 2);
   }
@@ -246,7 +261,7 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
       return fail(QMM_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
     CHECK_PTR(workspace, 16);
   }
-  qmm::GemmArgs a{w, scales, biases, x, y, m, n, k, group_size, wtiled};
+  qmm::GemmArgs a{w, scales, stiled ? nullptr : biases, x, y, m, n, k, group_size, wtiled, stiled};
   return hip_status(qmm::launch_qgemm(a, bits, workspace, (hipStream_t)stream), fn);
 }
 
@@ -256,8 +271,12 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
   const char* fn = "qmm_qgemm_batched_plan";
   clear_error();
   const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
-  bits &= ~QMM_WEIGHTS_TILED;
+  const int stiled = (bits & QMM_SCALES_TILED) ? 1 : 0;
+  bits &= ~(QMM_WEIGHTS_TILED | QMM_SCALES_TILED);
   if (int st = check_format(fn, bits, group_size, true)) return st;
+  if (stiled && !wtiled) return fail(QMM_ERR_INVALID_ARG, "%s: QMM_SCALES_TILED needs QMM_WEIGHTS_TILED", fn);
+  if (stiled && (bits == 16 || group_size != 64))
+    return fail(QMM_ERR_INVALID_ARG, "%s: interleaved scales need quantized codes and group_size 64", fn);
   if (count < 1) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d must be >= 1", fn, count);
   if (count > (1 << 20)) return fail(QMM_ERR_INVALID_ARG, "%s: count=%d too large", fn, count);
   if (problems == nullptr) return fail(QMM_ERR_INVALID_ARG, "%s: null problems", fn);
@@ -272,27 +291,29 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
     const qmm_gemm_problem& q = problems[i];
     int bad = 0;
     // an empty problem (m = 0) is never read or written: x and y may be null
-    if (q.m < 0 || check_nk(fn, q.n, q.k, group_size) || (wtiled && q.n % 32 != 0)) bad = 1;
-    else if (!q.w || (bits != 16 && (!q.scales || !q.biases)) || (q.m > 0 && (!q.x || !q.y))) bad = 2;
+    if (q.m < 0 || check_nk(fn, q.n, q.k, group_size) || (wtiled && q.n % 32 != 0) ||
+        (stiled && q.k % 256 != 0)) bad = 1;
+    else if (!q.w || (bits != 16 && (!q.scales || (!stiled && !q.biases))) || (q.m > 0 && (!q.x || !q.y))) bad = 2;
     else if (!aligned(q.w, 16) || !aligned(q.x, 16) || !aligned(q.y, 4) ||
-             !aligned(q.scales, 2) || !aligned(q.biases, 2)) bad = 3;
+             !aligned(q.scales, stiled ? 16 : 2) || (!stiled && !aligned(q.biases, 2))) bad = 3;
     if (bad) {
       free(probs);
       return fail(QMM_ERR_INVALID_ARG, "%s: problem %d: %s", fn, i,
-                  bad == 1 ? (wtiled ? "bad m, n or k (tile-interleaved weights need n % 32 == 0)"
-                                     : "bad m, n or k")
+                  bad == 1 ? (stiled ? "bad m, n or k (interleaved scales need n % 32 == 0 and k % 256 == 0)"
+                              : wtiled ? "bad m, n or k (tile-interleaved weights need n % 32 == 0)"
+                                       : "bad m, n or k")
                            : bad == 2 ? "null pointer" : "misaligned pointer");
     }
     probs[i].w = q.w;
     probs[i].s = q.scales;
-    probs[i].b = q.biases;
+    probs[i].b = stiled ? nullptr : q.biases;
     probs[i].x = q.x;
     probs[i].y = q.y;
     probs[i].m = q.m;
     probs[i].n = q.n;
     probs[i].k = q.k;
   }
-  const size_t need = qmm::gemm_batch_build(probs, count, bits, group_size, wtiled, nullptr, 0);
+  const size_t need = qmm::gemm_batch_build(probs, count, bits, group_size, wtiled, stiled, nullptr, 0);
   if (plan_bytes_needed) *plan_bytes_needed = need;
   if (plan == nullptr || plan_bytes < need) {
     free(probs);
@@ -302,7 +323,7 @@ int qmm_qgemm_batched_plan(const qmm_gemm_problem* problems, int count, int bits
     free(probs);
     return fail(QMM_ERR_INVALID_ARG, "%s: plan is not 8-byte aligned", fn);
   }
-  qmm::gemm_batch_build(probs, count, bits, group_size, wtiled, plan, plan_bytes);
+  qmm::gemm_batch_build(probs, count, bits, group_size, wtiled, stiled, plan, plan_bytes);
   free(probs);
   qmm::GemmBatchHeader hdr;
   memcpy(&hdr, plan, sizeof hdr);
@@ -322,6 +343,7 @@ int qmm_qgemm_batched(const void* plan_device, const void* plan_host, void* work
     return fail(QMM_ERR_INVALID_ARG, "%s: plan_host is not a batched-GEMM plan image", fn);
   if (int st = check_format(fn, hdr.bits, hdr.group_size, true)) return st;
   if (hdr.count < 1 || hdr.num_tiles < 0 || hdr.splits < 1 || (hdr.wtiled != 0 && hdr.wtiled != 1) ||
+      (hdr.stiled != 0 && hdr.stiled != 1) || (hdr.stiled == 1 && (hdr.wtiled != 1 || hdr.group_size != 64)) ||
       !(hdr.bm == 32 || hdr.bm == 64 || hdr.bm == 128 || hdr.bm == 256) ||
       !(hdr.nb == 1 || hdr.nb == 2) || (hdr.bm == 256 && hdr.nb != 2) || (hdr.bits == 16 && hdr.nb != 1) ||
       !(hdr.kw == 1 || hdr.kw == 2) || (hdr.kw == 2 && (hdr.bm == 256 || (hdr.nb == 2 && hdr.bm != 64))))
@@ -565,6 +587,23 @@ int qmm_repack_tiled(const uint32_t* w, uint32_t* out, int n, int k, int bits, q
   const uintptr_t a = (uintptr_t)w, b = (uintptr_t)out;
   if (a < b + bytes && b < a + bytes) return fail(QMM_ERR_INVALID_ARG, "%s: w and out overlap", fn);
   return hip_status(qmm::launch_repack_tiled(w, out, n, k, bits, (hipStream_t)stream), fn);
+}
+
+int qmm_repack_scales_tiled(const uint16_t* scales, const uint16_t* biases, uint16_t* out, int n, int k,
+                            qmm_stream stream) {
+  const char* fn = "qmm_repack_scales_tiled";
+  clear_error();
+  if (int st = check_nk(fn, n, k)) return st;
+  if (n % 32 != 0) return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32", fn, n);
+  if (k % 256 != 0) return fail(QMM_ERR_INVALID_ARG, "%s: k=%d must be a multiple of 256", fn, k);
+  CHECK_PTR(scales, 2);
+  CHECK_PTR(biases, 2);
+  CHECK_PTR(out, 16);
+  const size_t half = (size_t)n * (size_t)(k / 64) * 2;  // bytes of scales (and of biases)
+  const uintptr_t o = (uintptr_t)out, sp = (uintptr_t)scales, bp = (uintptr_t)biases;
+  if ((o < sp + half && sp < o + 2 * half) || (o < bp + half && bp < o + 2 * half))
+    return fail(QMM_ERR_INVALID_ARG, "%s: out overlaps scales or biases", fn);
+  return hip_status(qmm::launch_repack_scales_tiled(scales, biases, out, n, k, (hipStream_t)stream), fn);
 }
 
 int qmm_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,

@@ -74,6 +74,7 @@ struct GemmArgs {
   int m, n, k;
   int group_size;  // codes per scale/bias group: 32, 64 or 128
   int wtiled;      // weights in the tile-interleaved layout (qmm_repack_tiled)
+  int stiled;      // scales and biases interleaved (qmm_repack_scales_tiled; s holds both)
 };
 size_t gemm_workspace_bytes(int m, int n, int k, int bits);
 hipError_t launch_qgemm(const GemmArgs& a, int bits, void* workspace, hipStream_t st);
@@ -122,7 +123,7 @@ struct alignas(64) GemmBatchHeader {
   int32_t wtiled;        // weights in the tile-interleaved layout (qmm_repack_tiled)
   uint64_t workspace_bytes;
   int32_t kw;            // k halves per workgroup (1, or 2 with 8 waves)
-  int32_t pad1;
+  int32_t stiled;        // scales and biases interleaved (qmm_repack_scales_tiled)
 };
 static_assert(sizeof(GemmBatchHeader) == 64, "GemmBatchHeader must stay 64 bytes");
 constexpr uint32_t kBatchMagic = 0x424D4D51u;  // "QMMB"
@@ -135,7 +136,7 @@ void gemm_choose(int m, int n, int k, int bits, int* bm, int* nb, int* splits);
 // Choose the tile and split count for a batch and write the plan image.
 // Returns the image size; writes nothing when out is null or too small.
 size_t gemm_batch_build(const GemmBatchProblem* probs, int count, int bits, int group_size,
-                        int wtiled, void* out, size_t out_bytes);
+                        int wtiled, int stiled, void* out, size_t out_bytes);
 hipError_t launch_qgemm_batched(const void* plan_device, const GemmBatchHeader& hdr,
                                 void* workspace, hipStream_t st);
 
@@ -170,6 +171,8 @@ hipError_t launch_quantize(const float* w, uint32_t* words, uint16_t* s, uint16_
                            int k, int bits, int group_size, hipStream_t st);
 hipError_t launch_convert_bf16(const uint16_t* src, uint16_t* dst, long count, hipStream_t st);
 hipError_t launch_repack_tiled(const uint32_t* w, uint32_t* out, int n, int k, int bits, hipStream_t st);
+hipError_t launch_repack_scales_tiled(const uint16_t* s, const uint16_t* b, uint16_t* out, int n, int k,
+                                      hipStream_t st);
 hipError_t launch_unpack_codes(const uint32_t* w, uint8_t* codes, int n, int k, int bits,
                                hipStream_t st);
 hipError_t launch_dequant(const uint32_t* w, const uint16_t* s, const uint16_t* b, void* out,

@@ -251,6 +251,32 @@ hipError_t launch_repack_tiled(const uint32_t* w, uint32_t* out, int n, int k, i
   return hipGetLastError();
 }
 
+// Interleaved scales and biases (one thread per column and group of 64):
+// column c's scale and bias of group g move from s[c * G + g], b[c * G + g]
+// to halves ((c / 32) * (G / 4) * 32 + c % 32) * 8 + (g / 4) * 256 + g % 4
+// and 4 halves after it, i.e. for every 32-column block and quad of groups
+// the 32 columns' {s[4q .. 4q+3], b[4q .. 4q+3]} lie next to each other.
+__global__ __launch_bounds__(256) void repack_scales_tiled_kernel(const uint16_t* __restrict__ s,
+                                                                  const uint16_t* __restrict__ b,
+                                                                  uint16_t* __restrict__ dst, long count,
+                                                                  int groups) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  const long col = i / groups;
+  const int g = (int)(i - col * groups);
+  const long o = (((col >> 5) * (groups >> 2) + (g >> 2)) * 32 + (col & 31)) * 8 + (g & 3);
+  dst[o] = s[i];
+  dst[o + 4] = b[i];
+}
+
+hipError_t launch_repack_scales_tiled(const uint16_t* s, const uint16_t* b, uint16_t* out, int n, int k,
+                                      hipStream_t st) {
+  const long count = (long)n * (k / 64);
+  hipLaunchKernelGGL(repack_scales_tiled_kernel, dim3(blocks_for(count)), dim3(256), 0, st, s, b, out, count,
+                     k / 64);
+  return hipGetLastError();
+}
+
 template <int GS>
 static hipError_t launch_quantize_gs(const float* w, uint32_t* words, uint16_t* s, uint16_t* b,
                                      int n, int k, int bits, hipStream_t st) {

@@ -263,9 +263,9 @@ def gemm_batch_plan(L, shapes, bits=4, env=None, gs=64):
         if old is not None:
             os.environ["QMM_GEMM_FORCE"] = old
     raw = bytes(buf)
-    f = struct.unpack_from("<IIiiiiiiiiiiQi", raw, 0)
+    f = struct.unpack_from("<IIiiiiiiiiiiQii", raw, 0)
     hdr = dict(zip(["magic", "version", "bits", "gs", "bm", "nb", "sbq", "count", "num_tiles",
-                    "split_tiles", "splits", "wtiled", "ws", "kw"], f))
+                    "split_tiles", "splits", "wtiled", "ws", "kw", "stiled"], f))
     off = 64 + 64 * len(shapes)
     recs = [struct.unpack_from("<8i", raw, off + 32 * i) for i in range(hdr["num_tiles"])]
     off2 = off + 32 * hdr["num_tiles"]
@@ -423,6 +423,51 @@ def test_repack_tiled_errors_and_plan_flag(L):
     expect(L.qmm_qgemv(A, A, A, A, A, 64, 128, 4 | tiled, 64, None), UNS, "bits")
     expect(L.qmm_dequant(A, A, A, A, 0, 64, 128, 4 | tiled, 64, None), UNS, "bits")
     expect(L.qmm_repack_tiled(A, B, 64, 128, 4 | tiled, None), UNS, "bits")
+
+
+def test_scales_tiled_host_checks(L):
+    """QMM_SCALES_TILED (interleaved scales from qmm_repack_scales_tiled)
+    needs tile-interleaved weights, quantized codes, groups of 64, k % 256
+    == 0 and 16-byte aligned scales; biases may be NULL; plans record the
+    flag; entry points without the layout refuse it; the repack checks its
+    shapes, pointers and overlap on the host."""
+    B = A + (1 << 24)
+    st, wt = _lib.QMM_SCALES_TILED, _lib.QMM_WEIGHTS_TILED
+    expect(L.qmm_qgemm(A, A, None, A, A, 8, 64, 256, 4 | st, 64, A, 1 << 20, None), INV, "QMM_WEIGHTS_TILED")
+    expect(L.qmm_qgemm(A, A, None, A, A, 8, 64, 320, 4 | st | wt, 64, A, 1 << 20, None), INV, "k % 256")
+    expect(L.qmm_qgemm(A, A, None, A, A, 8, 64, 256, 4 | st | wt, 32, A, 1 << 20, None), INV, "group_size 64")
+    expect(L.qmm_qgemm(A, A, None, A, A, 8, 64, 256, 16 | st | wt, 64, A, 1 << 20, None), INV, "fp16")
+    expect(L.qmm_qgemm(A, A + 8, None, A, A, 8, 64, 256, 4 | st | wt, 64, A, 1 << 20, None), INV, "aligned")
+    hdr, recs = gemm_batch_plan(L, [(70, 512, 1024), (300, 224, 768)], bits=4 | wt | st)
+    assert hdr["stiled"] == 1 and hdr["wtiled"] == 1 and hdr["bits"] == 4
+    check_gemm_plan_covers(hdr, recs, [(70, 512, 1024), (300, 224, 768)])
+    assert gemm_batch_plan(L, [(70, 512, 1024)], bits=4 | wt)[0]["stiled"] == 0
+    probs = (GemmProblem * 1)()
+    need, ws = C.c_size_t(0), C.c_size_t(0)
+    probs[0] = GemmProblem(A, A, 0, A, A, 64, 256, 320)
+    expect(L.qmm_qgemm_batched_plan(probs, 1, 4 | wt | st, 64, None, 0, C.byref(need), C.byref(ws)), INV,
+           "k % 256")
+    probs[0] = GemmProblem(A, A + 8, 0, A, A, 64, 256, 512)
+    expect(L.qmm_qgemm_batched_plan(probs, 1, 4 | wt | st, 64, None, 0, C.byref(need), C.byref(ws)), INV,
+           "misaligned")
+    expect(L.qmm_qgemm_batched_plan(probs, 1, 4 | st, 64, None, 0, C.byref(need), C.byref(ws)), INV,
+           "QMM_WEIGHTS_TILED")
+    assert L.qmm_qgemm_workspace_size(128, 2560, 9728, 4 | wt | st, 64) == \
+        L.qmm_qgemm_workspace_size(128, 2560, 9728, 4, 64)
+    # entry points without the interleaved scale layout refuse the flag
+    expect(L.qmm_qgemm_grouped(A, A, A, A, 0, A, A, 8, 2, 4, 256, 256, 4 | wt | st, 64, A, 1 << 20, None),
+           UNS, "bits")
+    expect(L.qmm_moe_gate_up_swiglu(A, A, A, A, A, A, A, A, 1 << 20, A, 8, 2, 4, 256, 256, 4 | wt | st, 64,
+                                    None), UNS, "bits")
+    expect(L.qmm_qgemv(A, A, A, A, A, 64, 256, 4 | st, 64, None), UNS, "bits")
+    # the repack
+    expect(L.qmm_repack_scales_tiled(A, A, B, 48, 256, None), INV, "multiple of 32")
+    expect(L.qmm_repack_scales_tiled(A, A, B, 64, 320, None), INV, "multiple of 256")
+    expect(L.qmm_repack_scales_tiled(A, A, B, 64, 100, None), INV, "k=100")
+    expect(L.qmm_repack_scales_tiled(None, A, B, 64, 256, None), INV, "null pointer")
+    expect(L.qmm_repack_scales_tiled(A, A, MIS, 64, 256, None), INV, "aligned")
+    expect(L.qmm_repack_scales_tiled(A, A + (1 << 20), A + 64, 64, 256, None), INV, "overlap")
+    expect(L.qmm_repack_scales_tiled(A, A + (1 << 20), A + (1 << 20) + 64, 64, 256, None), INV, "overlap")
 
 
 def test_batched_gemm_plan_group_sizes(L):
