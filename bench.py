@@ -387,11 +387,11 @@ def bench_decode_extras(torch, qmm, wl, sets, steps=20, warmup=3):
 PREFILL_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 
 
-# The dense prefill GEMMs read interleaved scales and biases
+# The prefill and MoE GEMMs read interleaved scales and biases
 # (qmm_repack_scales_tiled) unless --row-major-scales is given.
 PREFILL_SCALES_TILED = True
-PREFILL_WEIGHTS = ("tile-interleaved copy (qmm_repack_tiled, once at load); dense GEMMs with interleaved "
-                   "scales and biases (qmm_repack_scales_tiled, once at load)")
+PREFILL_WEIGHTS = ("tile-interleaved copy (qmm_repack_tiled, once at load) with interleaved scales and "
+                   "biases (qmm_repack_scales_tiled, once at load)")
 
 
 def prefill_layers(torch, qmm, wl, batched=True):
@@ -508,9 +508,12 @@ def moe_weights(torch, qmm, wl, copies=2):
             ws.append(w_); ss.append(s_); bs.append(b_)
         W = qmm.repack_tiled(torch.stack(ws), wl.bits)
         S, B = torch.stack(ss), torch.stack(bs)
+        if PREFILL_SCALES_TILED:  # interleaved scales and biases, one array
+            S, B = qmm.repack_scales_tiled(S, B), None
         del ws, ss, bs
         for c in range(copies):
-            sets[c].append((W, S, B, n, k, per_pair) if c == 0 else (W.clone(), S.clone(), B.clone(), n, k, per_pair))
+            sets[c].append((W, S, B, n, k, per_pair) if c == 0 else
+                           (W.clone(), S.clone(), None if B is None else B.clone(), n, k, per_pair))
     torch.cuda.synchronize()
     return sets
 
@@ -545,12 +548,14 @@ def bench_moe(torch, qmm, steps=20, warmup=3, copies=2):
             ws = wsets[i % copies]
             qmm.moe_route(ids0, wl.experts, plan=plan)
             for (W, S, B, n, k, _), (A, I, per_pair, Y, WS) in zip(ws, ins):
-                qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, plan=plan, tiled=True)
+                qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, plan=plan, tiled=True,
+                                  scales_tiled=PREFILL_SCALES_TILED)
 
         def step_unshared(i):
             ws = wsets[i % copies]
             for (W, S, B, n, k, _), (A, I, per_pair, Y, WS) in zip(ws, ins):
-                qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, workspace=WS, tiled=True)
+                qmm.qgemm_grouped(W, S, B, A, I, wl.bits, per_pair, y=Y, workspace=WS, tiled=True,
+                                  scales_tiled=PREFILL_SCALES_TILED)
         st = step_stats(time_steps(torch, step, steps, warmup, stream))
         st_un = step_stats(time_steps(torch, step_unshared, steps, warmup, stream))
         t = st["ms_per_step_median"] * 1e-3
@@ -575,8 +580,10 @@ def bench_moe(torch, qmm, steps=20, warmup=3, copies=2):
         def block(i):
             (Wg, Sg, Bg, *_), (Wu, Su, Bu, *_), (Wd, Sd, Bd, *_) = wsets[i % copies]
             qmm.moe_route(ids0, wl.experts, plan=plan)
-            qmm.moe_gate_up_swiglu((Wg, Sg, Bg), (Wu, Su, Bu), A, ids0, plan, wl.bits, h=H, tiled=True)
-            qmm.qgemm_grouped(Wd, Sd, Bd, H, ids0, wl.bits, True, y=Yd, plan=plan, tiled=True)
+            qmm.moe_gate_up_swiglu((Wg, Sg, Bg), (Wu, Su, Bu), A, ids0, plan, wl.bits, h=H, tiled=True,
+                                   scales_tiled=PREFILL_SCALES_TILED)
+            qmm.qgemm_grouped(Wd, Sd, Bd, H, ids0, wl.bits, True, y=Yd, plan=plan, tiled=True,
+                              scales_tiled=PREFILL_SCALES_TILED)
             qmm.moe_combine(Yd, Wts, y=Yout)
         stb = step_stats(time_steps(torch, block, steps, warmup, stream))
         used = np.unique(ids0.cpu().numpy()).size
@@ -822,11 +829,12 @@ def profile_launch(torch, qmm, spec, reps):
     if what == "swiglu":
         H = torch.empty((m * wl.top_k, n), dtype=torch.float16, device="cuda")
         fn = lambda i: qmm.moe_gate_up_swiglu(wsets[i % 3][0][:3], wsets[i % 3][1][:3], A, I, plan, wl.bits,
-                                              h=H, tiled=True)
+                                              h=H, tiled=True, scales_tiled=PREFILL_SCALES_TILED)
         flops = 2 * 2.0 * m * wl.top_k * n * k
     else:
         Y = torch.empty((m * wl.top_k, n), dtype=torch.float32, device="cuda")
-        fn = lambda i: qmm.qgemm_grouped(*wsets[i % 3][pi][:3], A, I, wl.bits, per_pair, y=Y, plan=plan, tiled=True)
+        fn = lambda i: qmm.qgemm_grouped(*wsets[i % 3][pi][:3], A, I, wl.bits, per_pair, y=Y, plan=plan, tiled=True,
+                                         scales_tiled=PREFILL_SCALES_TILED)
         flops = 2.0 * m * wl.top_k * n * k
     ms, _ = time_launches(torch, fn, reps, 2, stream)
     return {"launch": spec, "ms_per_launch": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
@@ -855,7 +863,7 @@ def main():
     ap.add_argument("--decode-bits", type=int, choices=[2, 3, 4, 5, 6, 8, 16], default=4,
                     help="with --only decode: the decode pass at another weight width (for counters)")
     ap.add_argument("--row-major-scales", action="store_true",
-                    help="dense prefill GEMMs read row-major scales and biases instead of the "
+                    help="prefill and MoE GEMMs read row-major scales and biases instead of the "
                          "interleaved copy (for comparisons)")
     ap.add_argument("--forces", metavar="F;F...",
                     help="with --launch: time every launch under each forced tile: QMM_GEMM_FORCE "

@@ -175,7 +175,10 @@ int qmm_qgemm(const uint32_t* w, const uint16_t* scales, const uint16_t* biases,
  * `scales` pointer is an interleaved scale-and-bias array produced by
  * qmm_repack_scales_tiled (16-byte aligned; `biases` is not read and may be
  * NULL), which needs QMM_WEIGHTS_TILED, group_size 64, 2- to 8-bit codes and
- * k a multiple of 256.  The two scale layouts give identical results.
+ * k a multiple of 256.  The two scale layouts give identical results.  The
+ * flag is taken the same way by qmm_qgemm and by the grouped MoE calls
+ * (qmm_qgemm_grouped, _noalloc, _routed and qmm_moe_gate_up_swiglu, whose
+ * stacked expert scales [E, n, k/64] repack as one [E*n, k/64] array).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
 #define QMM_WEIGHTS_TILED 0x100
 #define QMM_SCALES_TILED 0x200
@@ -359,7 +362,9 @@ int qmm_repack_tiled(const uint32_t* w, uint32_t* out, int n, int k, int bits, q
  * so one wave's scale loads read whole lines.  n must be a multiple of 32 and
  * k of 256; scales and biases are device arrays of n * k / 64 fp16 (2-byte
  * aligned), out one of 2 * n * k / 64 fp16 (16-byte aligned, overlapping
- * neither); out is used as `scales` with QMM_SCALES_TILED.
+ * neither); out is used as `scales` with QMM_SCALES_TILED (stacked MoE expert
+ * scales and biases [E, n, k/64] repack as one [E*n, k/64] matrix, which
+ * keeps each expert's block whole when n is a multiple of 32).
  * Errors: INVALID_ARG, HIP. */
 int qmm_repack_scales_tiled(const uint16_t* scales, const uint16_t* biases, uint16_t* out, int n, int k,
                             qmm_stream stream);

@@ -189,12 +189,15 @@ def qgemm_grouped_workspace_size(t, top_k, e, n, k, bits, group_size=GROUP) -> i
 
 def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: bool,
                   y=None, group_size: int = GROUP, workspace=None, stream=None, plan=None,
-                  tiled: bool = False):
+                  tiled: bool = False, scales_tiled: bool = False):
     """Grouped MoE product via qmm_qgemm_grouped; returns y [T*top_k, n].
     With `plan` (from moe_route on the same expert_ids) it calls
     qmm_qgemm_grouped_routed and skips the bucketing.  tiled=True when w
-    comes from repack_tiled (of the stacked [E*n, ...] words)."""
-    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0)
+    comes from repack_tiled (of the stacked [E*n, ...] words); scales_tiled=True
+    when scales comes from repack_scales_tiled (biases then unused)."""
+    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0) | (_lib.QMM_SCALES_TILED if scales_tiled else 0)
+    if scales_tiled:
+        biases = None
     e, n = w.shape[0], w.shape[1]
     t, top_k = expert_ids.shape
     k = a.shape[1]
@@ -202,7 +205,7 @@ def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: b
         y = torch.empty((t * top_k, n), dtype=torch.float32, device=w.device)
     if plan is not None:
         check(lib().qmm_qgemm_grouped_routed(_dev(w, "w", _W), _sb(scales, "scales", bits),
-                                             _sb(biases, "biases", bits), _dev(a, "a", _X),
+                                             (None if scales_tiled else _sb(biases, "biases", bits)), _dev(a, "a", _X),
                                              int(bool(a_row_per_pair)), plan.data_ptr(), _nbytes(plan),
                                              _dev(y, "y", _Y),
                                              t, top_k, e, n, k, flag_bits, group_size, _stream(stream)))
@@ -211,7 +214,7 @@ def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: b
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=w.device)
     check(lib().qmm_qgemm_grouped(_dev(w, "w", _W), _sb(scales, "scales", bits),
-                                  _sb(biases, "biases", bits), _dev(a, "a", _X),
+                                  (None if scales_tiled else _sb(biases, "biases", bits)), _dev(a, "a", _X),
                                   int(bool(a_row_per_pair)), _dev(expert_ids, "expert_ids", (torch.int32,)),
                                   _dev(y, "y", _Y), t, top_k, e, n, k, flag_bits, group_size,
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -220,16 +223,17 @@ def qgemm_grouped(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: b
 
 
 def qgemm_grouped_noalloc(w, scales, biases, a, expert_ids, bits: int, a_row_per_pair: bool, y,
-                          group_size: int = GROUP, stream=None, tiled: bool = False):
+                          group_size: int = GROUP, stream=None, tiled: bool = False,
+                          scales_tiled: bool = False):
     """qmm_qgemm_grouped_noalloc: the grouped product into a caller-given y
     [T*top_k, n] with the library's static device scratch instead of a
     workspace (nothing is allocated; calls on one GPU must not overlap)."""
-    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0)
+    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0) | (_lib.QMM_SCALES_TILED if scales_tiled else 0)
     e, n = w.shape[0], w.shape[1]
     t, top_k = expert_ids.shape
     k = a.shape[1]
     check(lib().qmm_qgemm_grouped_noalloc(_dev(w, "w", _W), _sb(scales, "scales", bits),
-                                          _sb(biases, "biases", bits), _dev(a, "a", _X),
+                                          (None if scales_tiled else _sb(biases, "biases", bits)), _dev(a, "a", _X),
                                           int(bool(a_row_per_pair)),
                                           _dev(expert_ids, "expert_ids", (torch.int32,)),
                                           _dev(y, "y", _Y), t, top_k, e, n, k, flag_bits, group_size,
@@ -255,11 +259,12 @@ def moe_route(expert_ids, e: int, plan=None, stream=None):
 
 
 def moe_gate_up_swiglu(gate, up, x, expert_ids, plan, bits: int, h=None, group_size: int = GROUP,
-                       stream=None, tiled: bool = False):
+                       stream=None, tiled: bool = False, scales_tiled: bool = False):
     """h [T*top_k, n] fp16 = silu(x W_gate^T) * (x W_up^T) per pair, via
     qmm_moe_gate_up_swiglu; gate and up are (words, scales, biases), both
-    from repack_tiled when tiled=True."""
-    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0)
+    from repack_tiled when tiled=True; their scales from repack_scales_tiled
+    when scales_tiled=True (biases then unused)."""
+    flag_bits = bits | (_lib.QMM_WEIGHTS_TILED if tiled else 0) | (_lib.QMM_SCALES_TILED if scales_tiled else 0)
     wg, sg, bg = gate
     wu, su, bu = up
     e, n = wg.shape[0], wg.shape[1]
@@ -267,8 +272,8 @@ def moe_gate_up_swiglu(gate, up, x, expert_ids, plan, bits: int, h=None, group_s
     k = x.shape[1]
     if h is None:
         h = torch.empty((t * top_k, n), dtype=torch.float16, device=wg.device)
-    check(lib().qmm_moe_gate_up_swiglu(_dev(wg, "w_gate", _W), _sb(sg, "s_gate", bits), _sb(bg, "b_gate", bits),
-                                       _dev(wu, "w_up", _W), _sb(su, "s_up", bits), _sb(bu, "b_up", bits),
+    check(lib().qmm_moe_gate_up_swiglu(_dev(wg, "w_gate", _W), _sb(sg, "s_gate", bits), (None if scales_tiled else _sb(bg, "b_gate", bits)),
+                                       _dev(wu, "w_up", _W), _sb(su, "s_up", bits), (None if scales_tiled else _sb(bu, "b_up", bits)),
                                        _dev(x, "x", _X), plan.data_ptr(), _nbytes(plan), _dev(h, "h", _X),
                                        t, top_k, e, n, k, flag_bits, group_size, _stream(stream)))
     return h

@@ -358,11 +358,13 @@ void grouped_kernel(GroupedArgs a, const int32_t* __restrict__ ws, int n_tiles, 
   auto c_row = [&](int i) { return i < rows ? pair_of[i] : -1; };
   const int groups = a.k >> 6;
   const size_t wstride = (size_t)a.n * groups * Fmt<BITS>::WORDS_PER_GROUP;
-  const size_t sstride = (size_t)a.n * (a.k / a.group_size);
+  // interleaved scales hold the biases too: twice the halves per expert
+  const size_t sstride = (size_t)a.n * (a.k / a.group_size) * (a.stiled ? 2 : 1);
   gemm_tile<BITS, BM, NB, SBQ>(ARows{a.a, a.k}, a_row, c_row, a.w + mt.expert * wstride,
-                               a.s + mt.expert * sstride, a.b + mt.expert * sstride, a.y + tn * BN,
+                               a.s + mt.expert * sstride, a.stiled ? nullptr : a.b + mt.expert * sstride,
+                               a.y + tn * BN,
                                a.n, tn * BN, a.n, 0, groups, lds, a.group_size, nullptr, nullptr, nullptr,
-                               nullptr, a.wtiled);
+                               nullptr, a.wtiled, a.stiled);
 }
 
 // Fused gate + up with the SwiGLU epilogue: one workgroup computes, for
@@ -382,6 +384,7 @@ struct SwigluArgs {
   uint16_t* h;
   int t, top_k, e, n, k, group_size;
   int wtiled;  // weights in the tile-interleaved layout (qmm_repack_tiled)
+  int stiled;  // scales and biases interleaved (qmm_repack_scales_tiled; sg, su hold both)
 };
 
 template <int BITS, int BM, bool SBQ>
@@ -413,13 +416,14 @@ void swiglu_kernel(SwigluArgs a, const int32_t* __restrict__ ws, int n_tiles, in
   auto c_row = [&](int i) { return i < rows ? pair_of[i] : -1; };
   const int groups = a.k >> 6;
   const size_t wstride = (size_t)a.n * groups * Fmt<BITS>::WORDS_PER_GROUP;
-  const size_t sstride = (size_t)a.n * (a.k / a.group_size);
+  const size_t sstride = (size_t)a.n * (a.k / a.group_size) * (a.stiled ? 2 : 1);
   const size_t eo = (size_t)mt.expert;
   gemm_tile<BITS, BM, 2, SBQ, true>(ARows{a.x, a.k}, a_row, c_row, a.wg + eo * wstride,
-                                    a.sg + eo * sstride, a.bg + eo * sstride, nullptr, a.n,
+                                    a.sg + eo * sstride, a.stiled ? nullptr : a.bg + eo * sstride, nullptr, a.n,
                                     tn * 128, a.n, 0, groups, lds, a.group_size,
-                                    a.wu + eo * wstride, a.su + eo * sstride, a.bu + eo * sstride,
-                                    a.h + tn * 128, a.wtiled);
+                                    a.wu + eo * wstride, a.su + eo * sstride,
+                                    a.stiled ? nullptr : a.bu + eo * sstride, a.h + tn * 128, a.wtiled,
+                                    a.stiled);
 }
 
 template <int BITS, bool SBQ>
@@ -588,8 +592,9 @@ hipError_t launch_qgemm_grouped(const GroupedArgs& a, int bits, void* ws, bool b
 hipError_t launch_moe_swiglu(const uint32_t* wg, const uint16_t* sg, const uint16_t* bg,
                              const uint32_t* wu, const uint16_t* su, const uint16_t* bu,
                              const uint16_t* x, const void* plan, uint16_t* h, int t, int top_k,
-                             int e, int n, int k, int bits, int group_size, int wtiled, hipStream_t st) {
-  const SwigluArgs a{wg, sg, bg, wu, su, bu, x, h, t, top_k, e, n, k, group_size, wtiled};
+                             int e, int n, int k, int bits, int group_size, int wtiled, int stiled,
+                             hipStream_t st) {
+  const SwigluArgs a{wg, sg, bg, wu, su, bu, x, h, t, top_k, e, n, k, group_size, wtiled, stiled};
   const int32_t* p = static_cast<const int32_t*>(plan);
   switch (bits) {
     case 2: return launch_swiglu_bits<2>(a, p, st);

@@ -373,7 +373,8 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
   const char* fn = "qmm_qgemm_grouped";
   clear_error();
   const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
-  bits &= ~QMM_WEIGHTS_TILED;
+  const int stiled = (bits & QMM_SCALES_TILED) ? 1 : 0;
+  bits &= ~(QMM_WEIGHTS_TILED | QMM_SCALES_TILED);
   if (int st = check_format(fn, bits, group_size, true)) return st;
   if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
   if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
@@ -384,10 +385,13 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
   if (int st = check_nk(fn, n, k, group_size)) return st;
   if (wtiled && n % 32 != 0)
     return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32 for tile-interleaved weights", fn, n);
+  if (int st = check_stiled(fn, stiled, wtiled, bits, group_size, k)) return st;
   if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
   if (t == 0) return QMM_OK;
   CHECK_PTR(w, 16);
-  if (bits != 16) {  // fp16 weights have no scales or biases
+  if (stiled) {  // one interleaved array holds the scales and the biases
+    CHECK_PTR(scales, 16);
+  } else if (bits != 16) {  // fp16 weights have no scales or biases
     CHECK_PTR(scales, 2);
     CHECK_PTR(biases, 2);
   }
@@ -398,7 +402,7 @@ int qmm_qgemm_grouped(const uint32_t* w, const uint16_t* scales, const uint16_t*
   if (workspace == nullptr || workspace_bytes < need)
     return fail(QMM_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
   CHECK_PTR(workspace, 16);
-  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, expert_ids, y, t, top_k, e, n, k, group_size, wtiled};
+  qmm::GroupedArgs ga{w, scales, stiled ? nullptr : biases, a, a_row_per_pair, expert_ids, y, t, top_k, e, n, k, group_size, wtiled, stiled};
   return hip_status(qmm::launch_qgemm_grouped(ga, bits, workspace, true, (hipStream_t)stream), fn);
 }
 
@@ -409,7 +413,8 @@ int qmm_qgemm_grouped_noalloc(const uint32_t* w, const uint16_t* scales, const u
   const char* fn = "qmm_qgemm_grouped_noalloc";
   clear_error();
   const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
-  bits &= ~QMM_WEIGHTS_TILED;
+  const int stiled = (bits & QMM_SCALES_TILED) ? 1 : 0;
+  bits &= ~(QMM_WEIGHTS_TILED | QMM_SCALES_TILED);
   if (int st = check_format(fn, bits, group_size, true)) return st;
   if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
   if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
@@ -420,10 +425,13 @@ int qmm_qgemm_grouped_noalloc(const uint32_t* w, const uint16_t* scales, const u
   if (int st = check_nk(fn, n, k, group_size)) return st;
   if (wtiled && n % 32 != 0)
     return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32 for tile-interleaved weights", fn, n);
+  if (int st = check_stiled(fn, stiled, wtiled, bits, group_size, k)) return st;
   if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
   if (t == 0) return QMM_OK;
   CHECK_PTR(w, 16);
-  if (bits != 16) {
+  if (stiled) {  // one interleaved array holds the scales and the biases
+    CHECK_PTR(scales, 16);
+  } else if (bits != 16) {  // fp16 weights have no scales or biases
     CHECK_PTR(scales, 2);
     CHECK_PTR(biases, 2);
   }
@@ -438,7 +446,7 @@ int qmm_qgemm_grouped_noalloc(const uint32_t* w, const uint16_t* scales, const u
                 fn, t, top_k, e, need, qmm::kGroupedScratchBytes);
   void* scratch = nullptr;
   if (int st = hip_status(qmm::grouped_scratch(&scratch), fn)) return st;
-  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, expert_ids, y, t, top_k, e, n, k, group_size, wtiled};
+  qmm::GroupedArgs ga{w, scales, stiled ? nullptr : biases, a, a_row_per_pair, expert_ids, y, t, top_k, e, n, k, group_size, wtiled, stiled};
   return hip_status(qmm::launch_qgemm_grouped(ga, bits, scratch, true, (hipStream_t)stream), fn);
 }
 
@@ -473,7 +481,8 @@ int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const ui
   const char* fn = "qmm_qgemm_grouped_routed";
   clear_error();
   const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
-  bits &= ~QMM_WEIGHTS_TILED;
+  const int stiled = (bits & QMM_SCALES_TILED) ? 1 : 0;
+  bits &= ~(QMM_WEIGHTS_TILED | QMM_SCALES_TILED);
   if (int st = check_format(fn, bits, group_size, true)) return st;
   if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
   if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
@@ -484,10 +493,13 @@ int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const ui
   if (int st = check_nk(fn, n, k, group_size)) return st;
   if (wtiled && n % 32 != 0)
     return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32 for tile-interleaved weights", fn, n);
+  if (int st = check_stiled(fn, stiled, wtiled, bits, group_size, k)) return st;
   if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
   if (t == 0) return QMM_OK;
   CHECK_PTR(w, 16);
-  if (bits != 16) {
+  if (stiled) {  // one interleaved array holds the scales and the biases
+    CHECK_PTR(scales, 16);
+  } else if (bits != 16) {  // fp16 weights have no scales or biases
     CHECK_PTR(scales, 2);
     CHECK_PTR(biases, 2);
   }
@@ -495,7 +507,7 @@ int qmm_qgemm_grouped_routed(const uint32_t* w, const uint16_t* scales, const ui
   CHECK_PTR(plan, 16);
   CHECK_PTR(y, 4);
   if (int st = check_plan_size(fn, plan_bytes, t, top_k, e)) return st;
-  qmm::GroupedArgs ga{w, scales, biases, a, a_row_per_pair, nullptr, y, t, top_k, e, n, k, group_size, wtiled};
+  qmm::GroupedArgs ga{w, scales, stiled ? nullptr : biases, a, a_row_per_pair, nullptr, y, t, top_k, e, n, k, group_size, wtiled, stiled};
   return hip_status(qmm::launch_qgemm_grouped(ga, bits, const_cast<void*>(plan), false,
                                               (hipStream_t)stream), fn);
 }
@@ -508,7 +520,8 @@ int qmm_moe_gate_up_swiglu(const uint32_t* w_gate, const uint16_t* s_gate, const
   const char* fn = "qmm_moe_gate_up_swiglu";
   clear_error();
   const int wtiled = (bits & QMM_WEIGHTS_TILED) ? 1 : 0;
-  bits &= ~QMM_WEIGHTS_TILED;
+  const int stiled = (bits & QMM_SCALES_TILED) ? 1 : 0;
+  bits &= ~(QMM_WEIGHTS_TILED | QMM_SCALES_TILED);
   if (int st = check_format(fn, bits, group_size, true)) return st;
   if (t < 0) return fail(QMM_ERR_INVALID_ARG, "%s: t=%d must be >= 0", fn, t);
   if (top_k < 1) return fail(QMM_ERR_INVALID_ARG, "%s: top_k=%d must be >= 1", fn, top_k);
@@ -517,11 +530,15 @@ int qmm_moe_gate_up_swiglu(const uint32_t* w_gate, const uint16_t* s_gate, const
   if (int st = check_nk(fn, n, k, group_size)) return st;
   if (wtiled && n % 32 != 0)
     return fail(QMM_ERR_INVALID_ARG, "%s: n=%d must be a multiple of 32 for tile-interleaved weights", fn, n);
+  if (int st = check_stiled(fn, stiled, wtiled, bits, group_size, k)) return st;
   if ((long)t * top_k > 0x7FFFFFFFL / 4) return fail(QMM_ERR_INVALID_ARG, "%s: too many pairs", fn);
   if (t == 0) return QMM_OK;
   CHECK_PTR(w_gate, 16);
   CHECK_PTR(w_up, 16);
-  if (bits != 16) {
+  if (stiled) {  // interleaved arrays hold the scales and the biases
+    CHECK_PTR(s_gate, 16);
+    CHECK_PTR(s_up, 16);
+  } else if (bits != 16) {
     CHECK_PTR(s_gate, 2);
     CHECK_PTR(b_gate, 2);
     CHECK_PTR(s_up, 2);
@@ -531,8 +548,9 @@ int qmm_moe_gate_up_swiglu(const uint32_t* w_gate, const uint16_t* s_gate, const
   CHECK_PTR(plan, 16);
   CHECK_PTR(h, 2);
   if (int st = check_plan_size(fn, plan_bytes, t, top_k, e)) return st;
-  return hip_status(qmm::launch_moe_swiglu(w_gate, s_gate, b_gate, w_up, s_up, b_up, x, plan, h, t,
-                                           top_k, e, n, k, bits, group_size, wtiled, (hipStream_t)stream),
+  return hip_status(qmm::launch_moe_swiglu(w_gate, s_gate, stiled ? nullptr : b_gate, w_up, s_up,
+                                           stiled ? nullptr : b_up, x, plan, h, t, top_k, e, n, k, bits,
+                                           group_size, wtiled, stiled, (hipStream_t)stream),
                     fn);
 }
 

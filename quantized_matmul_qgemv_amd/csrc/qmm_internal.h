@@ -151,6 +151,7 @@ struct GroupedArgs {
   int t, top_k, e, n, k;
   int group_size;
   int wtiled;  // weights in the tile-interleaved layout (qmm_repack_tiled)
+  int stiled;  // scales and biases interleaved (qmm_repack_scales_tiled; s holds both)
 };
 size_t grouped_workspace_bytes(int t, int top_k, int e, int n);
 // Static device scratch of the allocation-free grouped GEMM: its size, and
@@ -163,7 +164,8 @@ hipError_t launch_moe_route(const int32_t* ids, int t, int top_k, int e, void* p
 hipError_t launch_moe_swiglu(const uint32_t* wg, const uint16_t* sg, const uint16_t* bg,
                              const uint32_t* wu, const uint16_t* su, const uint16_t* bu,
                              const uint16_t* x, const void* plan, uint16_t* h, int t, int top_k,
-                             int e, int n, int k, int bits, int group_size, int wtiled, hipStream_t st);
+                             int e, int n, int k, int bits, int group_size, int wtiled, int stiled,
+                             hipStream_t st);
 hipError_t launch_moe_combine(const float* y_pairs, const float* weights, float* y, int t, int top_k,
                               int n, hipStream_t st);
 

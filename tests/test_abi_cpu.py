@@ -454,12 +454,18 @@ def test_scales_tiled_host_checks(L):
            "QMM_WEIGHTS_TILED")
     assert L.qmm_qgemm_workspace_size(128, 2560, 9728, 4 | wt | st, 64) == \
         L.qmm_qgemm_workspace_size(128, 2560, 9728, 4, 64)
+    # the grouped MoE calls check the flag the same way
+    expect(L.qmm_qgemm_grouped(A, A, A, A, 0, A, A, 8, 2, 4, 256, 256, 4 | st, 64, A, 1 << 20, None),
+           INV, "QMM_WEIGHTS_TILED")
+    expect(L.qmm_qgemm_grouped_noalloc(A, A, A, A, 0, A, A, 8, 2, 4, 256, 320, 4 | wt | st, 64, None),
+           INV, "k % 256")
+    expect(L.qmm_qgemm_grouped_routed(A, A + 8, None, A, 0, A, 1 << 20, A, 8, 2, 4, 256, 256, 4 | wt | st,
+                                      64, None), INV, "aligned")
+    expect(L.qmm_moe_gate_up_swiglu(A, A, A, A, A, A, A, A, 1 << 20, A, 8, 2, 4, 256, 256, 4 | wt | st, 32,
+                                    None), INV, "group_size 64")
     # entry points without the interleaved scale layout refuse the flag
-    expect(L.qmm_qgemm_grouped(A, A, A, A, 0, A, A, 8, 2, 4, 256, 256, 4 | wt | st, 64, A, 1 << 20, None),
-           UNS, "bits")
-    expect(L.qmm_moe_gate_up_swiglu(A, A, A, A, A, A, A, A, 1 << 20, A, 8, 2, 4, 256, 256, 4 | wt | st, 64,
-                                    None), UNS, "bits")
     expect(L.qmm_qgemv(A, A, A, A, A, 64, 256, 4 | st, 64, None), UNS, "bits")
+    expect(L.qmm_dequant(A, A, A, A, 0, 64, 256, 4 | st, 64, None), UNS, "bits")
     # the repack
     expect(L.qmm_repack_scales_tiled(A, A, B, 48, 256, None), INV, "multiple of 32")
     expect(L.qmm_repack_scales_tiled(A, A, B, 64, 320, None), INV, "multiple of 256")

@@ -5,7 +5,8 @@ that reads it must equal the same call over row-major scales bit for bit
 (only the addressing of the scale loads differs), and the oracle within
 tolerance.  Covered: every quantized width, the quad scale loads and the
 per-group loads (a k split whose ranges are not whole quads), the 256 x 256
-tile, two k halves per workgroup, split k, and several problems per plan."""
+tile, two k halves per workgroup, split k, several problems per plan, and
+the grouped MoE calls and the fused gate/up SwiGLU over stacked experts."""
 import numpy as np
 import pytest
 
@@ -113,3 +114,46 @@ def test_gemm_batched_scales_tiled_several_problems(force, monkeypatch):
         assert torch.equal(a[4], c[4]), f"differs: {force} m={m} n={n} k={k}"
         if m:
             assert_close(host(c[4]), want, f"scales tiled {force} m={m} n={n} k={k}")
+
+
+def _experts(key, e, n, k, bits):
+    qs = [quantized(key + (ei,), n, k, bits) for ei in range(e)]
+    return dev(np.stack([q[2] for q in qs])), dev(np.stack([q[3] for q in qs])), dev(np.stack([q[4] for q in qs]))
+
+
+@pytest.mark.parametrize("bits", [4, 3, 8])
+@pytest.mark.parametrize("bm,nb", [(32, 1), (64, 2), (64, 1), (128, 1), (160, 1)])
+def test_moe_scales_tiled(bits, bm, nb, monkeypatch):
+    """Grouped GEMMs (self-bucketing, routed and allocation-free) and the
+    fused gate/up SwiGLU over tile-interleaved expert weights with
+    interleaved expert scales (the stacked [E, n, k/64] arrays repacked as
+    one) equal the runs over row-major scales bit for bit, for every row
+    tile, at k = 256 and 768."""
+    e, inter, t, top_k = 6, 320, 150, 4
+    for hidden in (256, 768):
+        say("moe scales tiled", bits, bm, nb, hidden)
+        r = np.random.default_rng([973, bits, hidden])
+        ids = np.ascontiguousarray(synth.topk_ids(r.standard_normal((t, e)), top_k), dtype=np.int32)
+        x = dev(synth.draw_act((973, bits, hidden), t, hidden))
+        gw, gs_, gb = _experts((974, bits, hidden), e, inter, hidden, bits)
+        uw, us, ub = _experts((975, bits, hidden), e, inter, hidden, bits)
+        gate = (qmm.repack_tiled(gw, bits), gs_, gb)
+        up = (qmm.repack_tiled(uw, bits), us, ub)
+        gate_s = (gate[0], qmm.repack_scales_tiled(gs_, gb), None)
+        up_s = (up[0], qmm.repack_scales_tiled(us, ub), None)
+        monkeypatch.setenv("QMM_MOE_FORCE", f"{bm},{nb}")
+        I = dev(ids)
+        plan = qmm.moe_route(I, e)
+        y0 = qmm.qgemm_grouped(*gate, x, I, bits, False, plan=plan, tiled=True)
+        y1 = qmm.qgemm_grouped(*gate_s, x, I, bits, False, plan=plan, tiled=True, scales_tiled=True)
+        y2 = qmm.qgemm_grouped(*gate_s, x, I, bits, False, tiled=True, scales_tiled=True)
+        y3 = torch.full_like(y0, float("nan"))
+        qmm.qgemm_grouped_noalloc(*gate_s, x, I, bits, False, y3, tiled=True, scales_tiled=True)
+        h0 = qmm.moe_gate_up_swiglu(gate, up, x, I, plan, bits, tiled=True)
+        h1 = qmm.moe_gate_up_swiglu(gate_s, up_s, x, I, plan, bits, tiled=True, scales_tiled=True)
+        torch.cuda.synchronize()
+        monkeypatch.delenv("QMM_MOE_FORCE")
+        assert torch.equal(y0, y1) and torch.equal(y0, y2) and torch.equal(y0, y3), \
+            f"grouped scales tiled differs bits={bits} {bm}x{nb} k={hidden}"
+        assert torch.equal(h0, h1), f"swiglu scales tiled differs bits={bits} {bm}x{nb} k={hidden}"
+        assert not torch.isnan(y0).any()
