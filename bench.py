@@ -67,7 +67,7 @@ TRAFFIC = {
     # KiB for 1 GiB read, WRITE_SIZE 1,048,576 KiB for 1 GiB written).
     "fetch_kib": 171951.3, "fetch_scale": 1073741824 / (524301.3 * 1024),
     "write_kib": 1937.5, "write_scale": 1073741824 / (1048576.0 * 1024),
-    "sources_sha256": "9016f7021240e458c619f74a5ce878622ab5d9059eb1c136225cd6ffba00ce07",
+    "sources_sha256": "ea51f520baa2af36c0ee180ce6299d4b0cda6ce07b3a48f84671f36ce5f2fcc1",
 }
 
 

@@ -624,6 +624,36 @@ def test_fp16_weights_gemv():
         assert_close(host(t[4]), want, "fp16 batched gemv")
 
 
+@pytest.mark.parametrize("bits", [4, 8, 16])
+def test_gemv_split_lanes_every_lane_count(bits):
+    """The split-group lanes (a lane reads a half, quarter or eighth of two,
+    four or eight groups per step and partner lanes join the parts) at every
+    lanes-per-row count they apply to: k = 128, 256, 512, 1024 and 2560 give
+    2, 4, 8, 16 and 8 lanes per row (fewer lanes than parts per group fall
+    back to whole groups), with and without the in-workgroup k split (small
+    n), single and batched launches."""
+    shapes = [(3, 128), (5, 256), (33, 512), (130, 1024), (7, 2560), (600, 256), (41, 8192)]
+    probs, wants = [], []
+    for i, (n, k) in enumerate(shapes):
+        say("gemv split lanes", bits, n, k)
+        x = synth.draw_act((944, bits, i), 1, k)
+        if bits == 16:
+            w16, words = fp16_weight((943, i, n), n, k)
+            W, S, B = dev(words), None, None
+            want = oracle.hmatmul_f64(w16, x)[0]
+        else:
+            _, _, words, s16, b16 = quantized((943, bits, i), n, k, bits)
+            W, S, B = dev(words), dev(s16), dev(b16)
+            want = oracle.qmatmul_f64(words, s16, b16, x, bits)[0]
+        y = qmm.qgemv(W, S, B, dev(x[0]), bits)
+        assert_close(host(y), want, f"split lanes bits={bits} n={n} k={k}")
+        probs.append((W, S, B, dev(x[0]), torch.full((n,), float("nan"), device="cuda")))
+        wants.append(want)
+    qmm.qgemv_batched(qmm.qgemv_batched_plan(probs, bits))
+    for (n, k), t, want in zip(shapes, probs, wants):
+        assert_close(host(t[4]), want, f"split lanes batched bits={bits} n={n} k={k}")
+
+
 def test_fp16_weights_gemm(monkeypatch):
     for m, n, k in ((1, 32, 64), (17, 300, 320), (128, 1024, 2560), (300, 1000, 1024), (16, 2048, 8192)):
         say("fp16 gemm", m, n, k)
