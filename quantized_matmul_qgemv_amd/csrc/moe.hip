@@ -371,7 +371,7 @@ void grouped_kernel(GroupedArgs a, const int32_t* __restrict__ ws, int n_tiles, 
 // its row tile and 128 columns, both products of the token rows with the
 // expert's gate and up weights and writes h = silu(gate) * up in fp16 (the
 // down projection's input), so neither fp32 product goes to memory.
-static void moe_tile(int pairs, int experts, int* bm_out, int* nb_out);
+static void moe_tile(int pairs, int experts, int stiled, int* bm_out, int* nb_out);
 
 struct SwigluArgs {
   const uint32_t* wg;
@@ -428,8 +428,8 @@ void swiglu_kernel(SwigluArgs a, const int32_t* __restrict__ ws, int n_tiles, in
 
 template <int BITS, bool SBQ>
 static hipError_t launch_swiglu_sbq(const SwigluArgs& a, const int32_t* plan, hipStream_t st) {
-  int bm, nb;
-  moe_tile(a.t * a.top_k, a.e, &bm, &nb);
+  int bm, nb;  // the fused tile is always 128 columns wide
+  moe_tile(a.t * a.top_k, a.e, a.stiled, &bm, &nb);
   const int n_tiles = (a.n + 127) / 128;
   const int m_tiles = max_row_tiles(a.t * a.top_k, a.e, bm);
   const int run = kMoeRun;
@@ -468,15 +468,22 @@ static hipError_t launch_swiglu_bits(const SwigluArgs& a, const int32_t* plan, h
 // 160-row tile, and the repeated weight columns mostly come from L2 or the
 // last-level cache.  At 512 tokens (32 per expert) 64 rows are best too;
 // 32 rows below 16 per expert, 128 above 160 per expert (each expert's
-// weights then stream once per 128 pairs).
+// weights then stream once per 128 pairs).  Column tile of the plain
+// grouped GEMM: 256 columns (nb = 2) over interleaved scales from 64 pairs
+// per expert on average, where it measured 5-7 % faster than 128 (2048
+// tokens: gate 100.8 vs 107.2 us, up 100.6 vs 108.2, down 115.8 vs 122.1;
+// 1024 tokens: gate 69.1 vs 74.8, down 77.0 vs 79.6); at 512 tokens (32 per
+// expert) and over row-major scales 128 columns stay faster, as the wider
+// tile halves the workgroups per expert.
 // QMM_MOE_FORCE="bm,nb" overrides the tile (tuning sweeps).  The bucketing
 // and the grouped GEMM must agree on it, so both take it from here.
 // QMM_MOE_FORCE is read on every call (tuning sweeps change it between
 // calls); a routing plan built under one value and used under another is
 // caught on the device by the plan-header check (the output becomes NaN).
-static void moe_tile(int pairs, int experts, int* bm_out, int* nb_out) {
+static void moe_tile(int pairs, int experts, int stiled, int* bm_out, int* nb_out) {
   const int mean = (pairs + experts - 1) / experts;
-  int bm = mean <= 16 ? 32 : mean <= 160 ? 64 : 128, nb = 1;
+  int bm = mean <= 16 ? 32 : mean <= 160 ? 64 : 128;
+  int nb = stiled && bm == 64 && mean >= 64 ? 2 : 1;
   if (const char* env = getenv("QMM_MOE_FORCE")) {
     int fb = 0, fn = 0;
     if (sscanf(env, "%d,%d", &fb, &fn) == 2 && (fb == 32 || fb == 64 || fb == 128 || (fb == 160 && fn == 1)) &&
@@ -528,8 +535,8 @@ hipError_t grouped_scratch(void** ptr) {
 }
 
 hipError_t launch_moe_route(const int32_t* ids, int t, int top_k, int e, void* plan, hipStream_t st) {
-  int bm, nb;
-  moe_tile(t * top_k, e, &bm, &nb);
+  int bm, nb;  // the routing plan depends on the row tile only
+  moe_tile(t * top_k, e, 0, &bm, &nb);
   return launch_bucket(ids, t * top_k, e, bm, reinterpret_cast<int32_t*>(plan), st);
 }
 
@@ -549,12 +556,10 @@ static hipError_t launch_grouped_tile(const GroupedArgs& a, int32_t* ws, bool bu
   return hipGetLastError();
 }
 
-// 128-wide column tiles (nb = 1) double the workgroups per expert, which
-// measured faster on the Qwen3-30B-A3B-shaped layers at 512 and 2048 tokens.
 template <int BITS, bool SBQ>
 static hipError_t launch_grouped_sbq(const GroupedArgs& a, int32_t* ws, bool bucket, hipStream_t st) {
   int bm, nb;
-  moe_tile(a.t * a.top_k, a.e, &bm, &nb);
+  moe_tile(a.t * a.top_k, a.e, a.stiled, &bm, &nb);
   if constexpr (BITS == 16) {  // fp16 weights: one column block per wave, no scales
     if (bm == 32) return launch_grouped_tile<16, 32, 1, false>(a, ws, bucket, st);
     if (bm == 64) return launch_grouped_tile<16, 64, 1, false>(a, ws, bucket, st);

@@ -180,7 +180,6 @@ static hipError_t launch_wide(const GemmArgs& a, const GemmPlan& p, float* ws, h
 
 template <int BITS, int BM>
 static hipError_t launch_bm(const GemmArgs& a, const GemmPlan& p, float* ws, hipStream_t st) {
-  // quad scale loads need every split to start and end on a multiple of 4 groups
   // quad scale loads (8 bytes per column): groups of 64, whole quads per
   // split, and 8-byte aligned scale and bias arrays
   const bool sbq = ((a.k / 64) / p.splits) % 4 == 0 && a.group_size == 64 &&

@@ -122,13 +122,15 @@ def _experts(key, e, n, k, bits):
 
 
 @pytest.mark.parametrize("bits", [4, 3, 8])
-@pytest.mark.parametrize("bm,nb", [(32, 1), (64, 2), (64, 1), (128, 1), (160, 1)])
+@pytest.mark.parametrize("bm,nb", [(32, 1), (64, 2), (64, 1), (128, 1), (160, 1), (None, None)])
 def test_moe_scales_tiled(bits, bm, nb, monkeypatch):
     """Grouped GEMMs (self-bucketing, routed and allocation-free) and the
     fused gate/up SwiGLU over tile-interleaved expert weights with
     interleaved expert scales (the stacked [E, n, k/64] arrays repacked as
     one) equal the runs over row-major scales bit for bit, for every row
-    tile, at k = 256 and 768."""
+    tile, at k = 256 and 768.  Unforced (100 pairs per expert), the grouped
+    GEMMs over interleaved scales take 64 x 256 tiles, and must equal the
+    row-major run forced to that tile."""
     e, inter, t, top_k = 6, 320, 150, 4
     for hidden in (256, 768):
         say("moe scales tiled", bits, bm, nb, hidden)
@@ -141,10 +143,15 @@ def test_moe_scales_tiled(bits, bm, nb, monkeypatch):
         up = (qmm.repack_tiled(uw, bits), us, ub)
         gate_s = (gate[0], qmm.repack_scales_tiled(gs_, gb), None)
         up_s = (up[0], qmm.repack_scales_tiled(us, ub), None)
-        monkeypatch.setenv("QMM_MOE_FORCE", f"{bm},{nb}")
+        if bm is not None:
+            monkeypatch.setenv("QMM_MOE_FORCE", f"{bm},{nb}")
         I = dev(ids)
         plan = qmm.moe_route(I, e)
+        if bm is None:
+            monkeypatch.setenv("QMM_MOE_FORCE", "64,2")
         y0 = qmm.qgemm_grouped(*gate, x, I, bits, False, plan=plan, tiled=True)
+        if bm is None:
+            monkeypatch.delenv("QMM_MOE_FORCE")
         y1 = qmm.qgemm_grouped(*gate_s, x, I, bits, False, plan=plan, tiled=True, scales_tiled=True)
         y2 = qmm.qgemm_grouped(*gate_s, x, I, bits, False, tiled=True, scales_tiled=True)
         y3 = torch.full_like(y0, float("nan"))
@@ -152,7 +159,7 @@ def test_moe_scales_tiled(bits, bm, nb, monkeypatch):
         h0 = qmm.moe_gate_up_swiglu(gate, up, x, I, plan, bits, tiled=True)
         h1 = qmm.moe_gate_up_swiglu(gate_s, up_s, x, I, plan, bits, tiled=True, scales_tiled=True)
         torch.cuda.synchronize()
-        monkeypatch.delenv("QMM_MOE_FORCE")
+        monkeypatch.delenv("QMM_MOE_FORCE", raising=False)
         assert torch.equal(y0, y1) and torch.equal(y0, y2) and torch.equal(y0, y3), \
             f"grouped scales tiled differs bits={bits} {bm}x{nb} k={hidden}"
         assert torch.equal(h0, h1), f"swiglu scales tiled differs bits={bits} {bm}x{nb} k={hidden}"
